@@ -1,0 +1,165 @@
+"""Seeded synthetic inputs for the Gated DeltaNet mixer workloads.
+
+Every array is drawn from ``numpy.random.Generator(PCG64(seed))`` in a fixed
+order, then rounded to its storage dtype.  bf16 arrays are held as ``uint16``
+bit patterns (numpy has no bf16); ``to_f64`` decodes them exactly.  The
+rounded values are the inputs of both the GPU path and the oracle.
+
+Distributions (the workload table of the project statement; "N(0, s)" reads
+s as the standard deviation):
+  q, k   : N(0,1) per element, then each head vector scaled to unit length
+           (i.e. uniform direction on the sphere), then rounded.
+  v, a, b, z, qkv : N(0,1);  A_log : U(-1,1);  dt_bias : N(0,0.1)
+  carried state : N(0,0.05);  conv weights : N(0,0.5) rounded to bf16 and
+  stored as f32;  norm weight w : N(0,0.1) (the scale is 1+w).
+Dimensions: 16 q/k heads, 48 value heads, width 128, conv 10240 channels of
+width 4 ("Qwen3.8 27B" model card, command-line bindings).
+"""
+import numpy as np
+
+__all__ = ["HK", "HV", "D", "CONV_CH", "CONV_W", "WORKLOADS", "bf16_round", "f32_round",
+           "to_f64", "is_bf16", "recurrence_inputs", "decode_inputs", "mixer_inputs",
+           "make_workload", "unit_heads"]
+
+HK, HV, D = 16, 48, 128
+CONV_CH = 2 * HK * D + HV * D  # 10240
+CONV_W = 4
+
+
+def f32_round(x):
+    """Round to f32 (round-to-nearest-even)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def bf16_round(x):
+    """Round to bf16 (RNE), returned as uint16 bit patterns.  f64 inputs are
+    first rounded to f32 (RNE), then to bf16 (RNE)."""
+    f = np.ascontiguousarray(np.asarray(x).astype(np.float32, copy=False))
+    u = f.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def is_bf16(a):
+    return isinstance(a, np.ndarray) and a.dtype == np.uint16
+
+
+def to_f64(a):
+    """Exact f64 value of an f32 array or of a bf16 bit-pattern array."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _round(x, dt):
+    if dt == "bf16":
+        return bf16_round(x)
+    if dt == "f32":
+        return f32_round(x)
+    raise ValueError(dt)
+
+
+def unit_heads(x):
+    """Scale each vector along the last axis to unit length (the draw of a
+    uniformly random direction)."""
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+
+
+def recurrence_inputs(B, T, Hk=HK, Hv=HV, d=D, qkv_dt="f32", gate_dt="f32", seed=0,
+                      state_std=None, A_log_range=(-1.0, 1.0), dt_bias_std=0.1,
+                      unit_qk=True):
+    """Inputs of one prefill call: q, k [B,T,Hk,d]; v [B,T,Hv,d]; a, b [B,T,Hv];
+    A_log, dt_bias [Hv] f32; state [B,Hv,d,d] f32 or None."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, T, Hk, d))
+    k = rng.standard_normal((B, T, Hk, d))
+    if unit_qk:
+        q, k = unit_heads(q), unit_heads(k)
+    v = rng.standard_normal((B, T, Hv, d))
+    a = rng.standard_normal((B, T, Hv))
+    b = rng.standard_normal((B, T, Hv))
+    A_log = rng.uniform(A_log_range[0], A_log_range[1], Hv)
+    dt_bias = rng.normal(0.0, dt_bias_std, Hv)
+    state = None if state_std is None else rng.normal(0.0, state_std, (B, Hv, d, d))
+    return {
+        "q": _round(q, qkv_dt), "k": _round(k, qkv_dt), "v": _round(v, qkv_dt),
+        "a": _round(a, gate_dt), "b": _round(b, gate_dt),
+        "A_log": f32_round(A_log), "dt_bias": f32_round(dt_bias),
+        "state": None if state is None else f32_round(state),
+    }
+
+
+def decode_inputs(R, Hk=HK, Hv=HV, d=D, qkv_dt="bf16", gate_dt="bf16", seed=1,
+                  state_std=0.05, max_len=8192):
+    """Inputs of one decode_rows call: q, k [R,Hk,d]; v [R,Hv,d]; a, b [R,Hv];
+    A_log, dt_bias [Hv]; state [R,Hv,d,d] f32; lengths [R] int32 ~ U{1..max_len}."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = unit_heads(rng.standard_normal((R, Hk, d)))
+    k = unit_heads(rng.standard_normal((R, Hk, d)))
+    v = rng.standard_normal((R, Hv, d))
+    a = rng.standard_normal((R, Hv))
+    b = rng.standard_normal((R, Hv))
+    A_log = rng.uniform(-1.0, 1.0, Hv)
+    dt_bias = rng.normal(0.0, 0.1, Hv)
+    lengths = rng.integers(1, max_len + 1, R).astype(np.int32)
+    state = rng.standard_normal((R, Hv, d, d), dtype=np.float32) * np.float32(state_std)
+    return {
+        "q": _round(q, qkv_dt), "k": _round(k, qkv_dt), "v": _round(v, qkv_dt),
+        "a": _round(a, gate_dt), "b": _round(b, gate_dt),
+        "A_log": f32_round(A_log), "dt_bias": f32_round(dt_bias),
+        "state": state.astype(np.float32), "lengths": lengths,
+    }
+
+
+def mixer_inputs(B, T, Hk=HK, Hv=HV, d=D, dt="bf16", seed=3, conv_w_std=0.5,
+                 norm_w_std=0.1):
+    """Inputs of the whole mixer: qkv [B,T,2*Hk*d+Hv*d]; conv_w [C,4] f32
+    (bf16-rounded values); z [B,T,Hv*d]; a, b [B,T,Hv]; A_log, dt_bias [Hv];
+    norm_w [d] f32.  Big arrays are drawn in f32 to bound host memory."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    C = 2 * Hk * d + Hv * d
+    qkv = rng.standard_normal((B, T, C), dtype=np.float32)
+    conv_w = rng.normal(0.0, conv_w_std, (C, CONV_W))
+    z = rng.standard_normal((B, T, Hv * d), dtype=np.float32)
+    a = rng.standard_normal((B, T, Hv))
+    b = rng.standard_normal((B, T, Hv))
+    A_log = rng.uniform(-1.0, 1.0, Hv)
+    dt_bias = rng.normal(0.0, 0.1, Hv)
+    norm_w = rng.normal(0.0, norm_w_std, d)
+    return {
+        "qkv": _round(qkv, dt), "z": _round(z, dt), "a": _round(a, dt), "b": _round(b, dt),
+        "conv_w": to_f64(bf16_round(conv_w)).astype(np.float32),
+        "A_log": f32_round(A_log), "dt_bias": f32_round(dt_bias),
+        "norm_w": f32_round(norm_w),
+    }
+
+
+# The five workloads, by name.  Sizes follow the model's layer; the seeds are
+# fixed so every run (tests, bench, oracle) sees identical inputs.
+WORKLOADS = {
+    "recurrence_f32_b1_t64": dict(kind="prefill", B=1, T=64, qkv_dt="f32", gate_dt="f32",
+                                  state_std=None, seed=1000),
+    "decode_rows_r64": dict(kind="decode", R=64, qkv_dt="bf16", gate_dt="bf16", seed=1001),
+    "prefill_bf16_b1_t4096": dict(kind="prefill", B=1, T=4096, qkv_dt="bf16", gate_dt="f32",
+                                  state_std=0.05, seed=1002),
+    "mixer_bf16_b4_t8192": dict(kind="mixer", B=4, T=8192, dt="bf16", seed=1003),
+    "prefill_bf16_b1_t65536_x16": dict(kind="prefill", B=1, T=65536, qkv_dt="bf16",
+                                       gate_dt="f32", state_std=None, seed=1004,
+                                       calls=16),
+}
+
+
+def make_workload(name, **overrides):
+    """Inputs of a named workload; keyword overrides (e.g. a smaller T) allowed."""
+    cfg = dict(WORKLOADS[name])
+    cfg.update(overrides)
+    kind = cfg.pop("kind")
+    cfg.pop("calls", None)
+    if kind == "prefill":
+        return recurrence_inputs(**cfg)
+    if kind == "decode":
+        return decode_inputs(**cfg)
+    if kind == "mixer":
+        return mixer_inputs(**cfg)
+    raise ValueError(kind)
