@@ -1,0 +1,197 @@
+"""ctypes binding of libgdn.so (include/gdn.h), one wrapper per C entry point
+with the same name.  Only argument marshalling happens here: torch supplies
+device memory and the current stream; every step of the computation runs in
+the library's HIP kernels.  There is no fallback: if the library is missing
+or fails to load, every call raises.
+"""
+import ctypes
+import os
+
+import torch  # loaded first so libgdn binds to the HIP runtime torch uses
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+GDN_ALGO_AUTO, GDN_ALGO_SEQUENTIAL, GDN_ALGO_CHUNKED = 0, 1, 2
+_ALGOS = {"auto": GDN_ALGO_AUTO, "sequential": GDN_ALGO_SEQUENTIAL, "chunked": GDN_ALGO_CHUNKED}
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__(f"{fn}: {gdn_status_str(status)} (status {status})")
+
+
+class gdn_dims(ctypes.Structure):
+    _fields_ = [("n_qk_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
+                ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdn.so; raises if it was never built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libgdn.so not found at {LIB_PATH}; build it with "
+                               "`python -m gated_deltanet_mixer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.gdn_status_str.argtypes = [ctypes.c_int]
+        L.gdn_status_str.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = ctypes.c_int
+        L.gdn_conv_silu.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, P]
+        L.gdn_conv_silu.restype = ctypes.c_int
+        L.gdn_prefill_workspace_bytes.argtypes = [i32, i32, gdn_dims, i32, i32]
+        L.gdn_prefill_workspace_bytes.restype = sz
+        L.gdn_prefill.argtypes = [P, i64, P, i64, P, i64, i32, P, P, i32, P, P, P, P, P, i32, i32,
+                                  gdn_dims, f32, i32, P, sz, P]
+        L.gdn_prefill.restype = ctypes.c_int
+        L.gdn_decode_rows.argtypes = [P, i64, P, i64, P, i64, i32, P, P, i32, P, P, P, P, P, i32,
+                                      gdn_dims, f32, P]
+        L.gdn_decode_rows.restype = ctypes.c_int
+        L.gdn_gated_rmsnorm.argtypes = [P, P, P, i32, P, i32, i32, i32, f32, P]
+        L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def gdn_status_str(status):
+    return lib().gdn_status_str(int(status)).decode()
+
+
+def gdn_abi_version():
+    return int(lib().gdn_abi_version())
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(status, fn):
+    if status != 0:
+        raise GDNError(status, fn)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _tok_stride(t, heads, d):
+    """Token stride of a [B, T, heads, d] view whose heads are packed."""
+    B, T = t.shape[0], t.shape[1]
+    if t.shape[2:] != (heads, d):
+        raise ValueError(f"expected a [B, T, {heads}, {d}] view")
+    if t.numel() == 0:
+        return heads * d
+    if t.stride(3) != 1 or t.stride(2) != d:
+        raise ValueError(f"expected a [B, T, {heads}, {d}] view with packed heads")
+    if B > 1 and t.stride(0) != T * t.stride(1):
+        raise ValueError("batch stride must be T * token stride")
+    return t.stride(1)
+
+
+def gdn_conv_silu(x, w, conv_state=None, l2_channels=0, head_dim=128, l2_eps=1e-6, y=None):
+    """Depthwise causal conv (width 4) + silu over x [B, T, C], optional L2 of
+    the first l2_channels channels per head; conv_state [B, 3, C] f32 in/out."""
+    _need_cuda(x, w, conv_state, y)
+    B, T, C = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    assert x.is_contiguous() and y.is_contiguous() and w.is_contiguous()
+    if conv_state is not None:
+        assert conv_state.is_contiguous() and conv_state.dtype == torch.float32
+    _check(lib().gdn_conv_silu(_ptr(x), _ptr(y), _dt(x), _ptr(w), _ptr(conv_state), B, T, C,
+                               w.shape[1], l2_channels, head_dim, l2_eps, _stream(x)),
+           "gdn_conv_silu")
+    return y
+
+
+def gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk=128, dv=128, qkv_dtype=torch.bfloat16,
+                                algo="auto"):
+    dt = GDN_BF16 if qkv_dtype == torch.bfloat16 else GDN_F32
+    return int(lib().gdn_prefill_workspace_bytes(B, T, gdn_dims(Hk, Hv, dk, dv), dt,
+                                                 _ALGOS[algo]))
+
+
+def gdn_prefill(q, k, v, a, b, A_log, dt_bias, state_in=None, state_out=None, o=None,
+                q_scale=1.0, algo="auto", workspace=None):
+    """Gated delta rule over q, k [B,T,Hk,dk] and v [B,T,Hv,dv] (views with a
+    token stride are accepted), gates a, b [B,T,Hv].  Returns o [B,T,Hv,dv]."""
+    _need_cuda(q, k, v, a, b, A_log, dt_bias, state_in, state_out, o, workspace)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    qs, ks, vs = _tok_stride(q, Hk, dk), _tok_stride(k, Hk, dk), _tok_stride(v, Hv, dv)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=v.dtype, device=v.device)
+    assert o.is_contiguous() and a.is_contiguous() and b.is_contiguous()
+    for s in (state_in, state_out):
+        if s is not None:
+            assert s.is_contiguous() and s.dtype == torch.float32
+    need = gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk, dv, q.dtype, algo)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_prefill(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _dt(q), _ptr(a), _ptr(b),
+                             _dt(a), _ptr(A_log), _ptr(dt_bias), _ptr(state_in), _ptr(state_out),
+                             _ptr(o), B, T, gdn_dims(Hk, Hv, dk, dv), q_scale, _ALGOS[algo],
+                             _ptr(workspace), ws_bytes, _stream(q)),
+           "gdn_prefill")
+    return o
+
+
+def gdn_decode_rows(q, k, v, a, b, A_log, dt_bias, state, lengths=None, o=None, q_scale=1.0):
+    """One token per fixed row: q, k [R,Hk,dk], v [R,Hv,dv], a, b [R,Hv]; state
+    [R,Hv,dv,dk] f32 updated in place; lengths [R] int32 (<0 = idle row)."""
+    _need_cuda(q, k, v, a, b, A_log, dt_bias, state, lengths, o)
+    R, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    for t, hh, d in ((q, Hk, dk), (k, Hk, dk), (v, Hv, dv)):
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError("heads must be packed")
+    if o is None:
+        o = torch.empty((R, Hv, dv), dtype=v.dtype, device=v.device)
+    assert state.is_contiguous() and state.dtype == torch.float32
+    if lengths is not None:
+        assert lengths.dtype == torch.int32 and lengths.is_contiguous()
+    _check(lib().gdn_decode_rows(_ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+                                 _dt(q), _ptr(a), _ptr(b), _dt(a), _ptr(A_log), _ptr(dt_bias),
+                                 _ptr(state), _ptr(lengths), _ptr(o), R,
+                                 gdn_dims(Hk, Hv, dk, dv), q_scale, _stream(q)),
+           "gdn_decode_rows")
+    return o
+
+
+def gdn_gated_rmsnorm(x, z, w, eps=1e-6, y=None):
+    """y = x / sqrt(mean(x^2) + eps) * (1 + w) * silu(z) over the last axis
+    (width 128); x, z viewed as [N, H, 128]."""
+    _need_cuda(x, z, w, y)
+    D = x.shape[-1]
+    H = x.shape[-2]
+    N = x.numel() // (H * D) if x.numel() else 0
+    if y is None:
+        y = torch.empty_like(x)
+    assert x.is_contiguous() and z.is_contiguous() and y.is_contiguous()
+    assert z.numel() == x.numel() and y.numel() == x.numel()
+    _check(lib().gdn_gated_rmsnorm(_ptr(x), _ptr(z), _ptr(y), _dt(x), _ptr(w), N, H, D, eps,
+                                   _stream(x)),
+           "gdn_gated_rmsnorm")
+    return y

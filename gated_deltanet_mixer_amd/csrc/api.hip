@@ -1,0 +1,163 @@
+// The C ABI (include/gdn.h): host-side validation, then one or two launches on
+// the caller's stream.  Nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include "../../include/gdn.h"
+#include "launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+bool dtype_ok(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
+size_t dsize(int32_t d) { return d == GDN_BF16 ? 2 : 4; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
+
+// Shared checks of the recurrence inputs.
+int check_dims(const gdn_dims& d) {
+  if (d.n_qk_heads <= 0 || d.n_v_heads <= 0 || d.head_k_dim <= 0 || d.head_v_dim <= 0)
+    return GDN_ERR_SHAPE;
+  if (d.n_v_heads % d.n_qk_heads != 0) return GDN_ERR_SHAPE;
+  if (d.head_k_dim != 128 || d.head_v_dim != 128) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_str(int status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: a size or stride is out of range";
+    case GDN_ERR_DTYPE: return "GDN_ERR_DTYPE: unsupported dtype";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer or stride misaligned";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: valid but not implemented";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown gdn_status";
+  }
+}
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+int gdn_conv_silu(const void* x, void* y, int32_t dt, const float* w, float* conv_state,
+                  int32_t B, int32_t T, int32_t C, int32_t W, int32_t l2_channels,
+                  int32_t head_dim, float l2_eps, void* stream) {
+  if (!x || !y || !w) return GDN_ERR_NULL;
+  if (!dtype_ok(dt)) return GDN_ERR_DTYPE;
+  if (B < 0 || T < 0 || C <= 0 || W < 1 || l2_channels < 0 || l2_channels > C)
+    return GDN_ERR_SHAPE;
+  if (W != 4) return GDN_ERR_UNSUPPORTED;
+  if (C % 8 != 0) return GDN_ERR_SHAPE;
+  if (l2_channels > 0) {
+    if (head_dim <= 0 || l2_channels % head_dim != 0) return GDN_ERR_SHAPE;
+    if (head_dim != 128) return GDN_ERR_UNSUPPORTED;
+  }
+  if (B > 65535 || (T + 63) / 64 > 65535) return GDN_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16) ||
+      (conv_state && !aligned(conv_state, 16)))
+    return GDN_ERR_ALIGN;
+  const size_t bytes = (size_t)B * T * C * dsize(dt);
+  const char* xs = static_cast<const char*>(x);
+  const char* ys = static_cast<const char*>(y);
+  if (bytes > 0 && xs < ys + bytes && ys < xs + bytes) return GDN_ERR_SHAPE;  // y overlaps x
+  if (B == 0 || T == 0) return GDN_OK;
+  return launch_status(gdn::launch_conv_silu(x, y, dt, w, conv_state, B, T, C, l2_channels,
+                                             l2_eps, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t qkv_dt,
+                                   int32_t algo) {
+  if (B <= 0 || T <= 0 || check_dims(dims) != GDN_OK) return 0;
+  const bool chunked = algo == GDN_ALGO_CHUNKED || (algo == GDN_ALGO_AUTO && qkv_dt == GDN_BF16);
+  if (!chunked) return 0;
+  return gdn::prefill_chunked_workspace_bytes(B, T, dims.n_qk_heads, dims.n_v_heads);
+}
+
+int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
+                const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
+                const float* state_in, float* state_out, void* o, int32_t B, int32_t T,
+                gdn_dims dims, float q_scale, int32_t algo, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !o) return GDN_ERR_NULL;
+  if (!dtype_ok(qkv_dt) || !dtype_ok(gate_dt)) return GDN_ERR_DTYPE;
+  if (algo != GDN_ALGO_AUTO && algo != GDN_ALGO_SEQUENTIAL && algo != GDN_ALGO_CHUNKED)
+    return GDN_ERR_SHAPE;
+  int st = check_dims(dims);
+  if (st != GDN_OK) return st;
+  const int Hk = dims.n_qk_heads, Hv = dims.n_v_heads;
+  if (B < 0 || T < 0) return GDN_ERR_SHAPE;
+  if (q_tok_stride < (int64_t)Hk * 128 || k_tok_stride < (int64_t)Hk * 128 ||
+      v_tok_stride < (int64_t)Hv * 128)
+    return GDN_ERR_SHAPE;
+  if ((int64_t)B * Hv * 8 > INT32_MAX || (int64_t)B * T > INT32_MAX) return GDN_ERR_SHAPE;
+  if (q_tok_stride % 8 || k_tok_stride % 8 || v_tok_stride % 8) return GDN_ERR_ALIGN;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(a, dsize(gate_dt)) || !aligned(b, dsize(gate_dt)) || !aligned(A_log, 4) ||
+      !aligned(dt_bias, 4) || (state_in && !aligned(state_in, 16)) ||
+      (state_out && !aligned(state_out, 16)))
+    return GDN_ERR_ALIGN;
+  const bool chunked = algo == GDN_ALGO_CHUNKED || (algo == GDN_ALGO_AUTO && qkv_dt == GDN_BF16);
+  if (chunked && qkv_dt != GDN_BF16) return GDN_ERR_DTYPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0) return GDN_OK;
+  if (chunked && T > 0) {
+    const size_t need = gdn::prefill_chunked_workspace_bytes(B, T, Hk, Hv);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
+    return launch_status(gdn::launch_prefill_chunked(
+        q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, a, b, gate_dt, A_log, dt_bias,
+        state_in, state_out, o, B, T, Hk, Hv, q_scale, workspace, s));
+  }
+  // Sequential algorithm (also the T == 0 state pass-through).
+  return launch_status(gdn::launch_prefill_sequential(
+      q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, a, b, gate_dt, A_log, dt_bias,
+      state_in, state_out, o, B, T, Hk, Hv, q_scale, s));
+}
+
+int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                    const void* v, int64_t v_row_stride, int32_t qkv_dt, const void* a,
+                    const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
+                    float* state, const int32_t* lengths, void* o, int32_t R, gdn_dims dims,
+                    float q_scale, void* stream) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state || !o) return GDN_ERR_NULL;
+  if (!dtype_ok(qkv_dt) || !dtype_ok(gate_dt)) return GDN_ERR_DTYPE;
+  int st = check_dims(dims);
+  if (st != GDN_OK) return st;
+  const int Hk = dims.n_qk_heads, Hv = dims.n_v_heads;
+  if (R < 0) return GDN_ERR_SHAPE;
+  if (q_row_stride < (int64_t)Hk * 128 || k_row_stride < (int64_t)Hk * 128 ||
+      v_row_stride < (int64_t)Hv * 128)
+    return GDN_ERR_SHAPE;
+  if ((int64_t)R * Hv > INT32_MAX) return GDN_ERR_SHAPE;
+  if (q_row_stride % 8 || k_row_stride % 8 || v_row_stride % 8) return GDN_ERR_ALIGN;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(state, 16) || !aligned(a, dsize(gate_dt)) || !aligned(b, dsize(gate_dt)) ||
+      !aligned(A_log, 4) || !aligned(dt_bias, 4) || (lengths && !aligned(lengths, 4)))
+    return GDN_ERR_ALIGN;
+  if (R == 0) return GDN_OK;
+  return launch_status(gdn::launch_decode_rows(q, q_row_stride, k, k_row_stride, v, v_row_stride,
+                                               qkv_dt, a, b, gate_dt, A_log, dt_bias, state,
+                                               lengths, o, R, Hk, Hv, q_scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const float* w,
+                      int32_t N, int32_t H, int32_t D, float eps, void* stream) {
+  if (!x || !z || !y || !w) return GDN_ERR_NULL;
+  if (!dtype_ok(dt)) return GDN_ERR_DTYPE;
+  if (N < 0 || H < 0 || D <= 0) return GDN_ERR_SHAPE;
+  if (D != 128) return GDN_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)N * H;
+  if ((rows + 63) / 64 > INT32_MAX) return GDN_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(w, 16))
+    return GDN_ERR_ALIGN;
+  if (rows == 0) return GDN_OK;
+  return launch_status(
+      gdn::launch_gated_rmsnorm(x, z, y, dt, w, rows, eps, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Depthwise causal conv (width 4) + silu over the q|k|v channels, with the L2
+// normalisation of each q and k head fused in, and the per-row conv history
+// read and rewritten in f32 ("Qwen3.8 27B" model card, Gated DeltaNet bullet
+// and state paragraph; llm-arch-viz module tree: conv1d 10240x1x4, no bias).
+//
+// y[b,t,c] = silu(sum_i w[c,i] * xhat[b,t+i,c]),  xhat = [hist (3 rows); x],
+// then for c < l2_channels each head_dim group of y is divided by
+// sqrt(sum of squares + l2_eps).  hist_out = the last 3 rows of xhat.
+//
+// Mapping: one thread owns 8 consecutive channels (one 16-byte bf16 load per
+// token) and walks CONV_TB consecutive tokens, keeping the previous 3 inputs
+// in registers, so every input element is read once (plus a 3-token halo per
+// block).  A 128-channel head is 16 lanes, so the L2 sum is a DPP row
+// reduction.  HBM-bound: one read of x and one write of y.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+constexpr int CONV_TB = 64;       // tokens per workgroup
+constexpr int CONV_THREADS = 256;  // 8 channels each -> 2048 channels per workgroup
+
+template <typename T>
+__global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
+    const T* __restrict__ x, T* __restrict__ y, const float* __restrict__ w,
+    float* conv_state, int Tlen, int C, int l2_channels, float l2_eps) {
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * CONV_TB;
+  const int t1 = min(Tlen, t0 + CONV_TB);
+  const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
+  if (c0 >= C) return;  // C % 8 == 0; a 16-lane head group is all in or all out
+
+  const T* xb = x + (int64_t)b * Tlen * C + c0;
+  T* yb = y + (int64_t)b * Tlen * C + c0;
+
+  float wt[4][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 wv = *reinterpret_cast<const float4*>(w + (int64_t)(c0 + i) * 4);
+    wt[0][i] = wv.x; wt[1][i] = wv.y; wt[2][i] = wv.z; wt[3][i] = wv.w;
+  }
+
+  // h[j] = xhat row (t0 + j) = input at token t0 - 3 + j.
+  float h[3][8];
+  if (t0 == 0) {
+    float* cs = conv_state ? conv_state + (int64_t)b * 3 * C + c0 : nullptr;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (cs) load8(cs + (int64_t)j * C, h[j]);
+      else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[j][i] = 0.0f;
+      }
+    }
+    // The first token block owns the history update, so an in/out buffer is
+    // read before it is written and by the same thread.
+    if (cs) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int r = Tlen + j;  // xhat row
+        float nv[8];
+        if (r < 3) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) nv[i] = h[r][i];
+        } else {
+          load8(xb + (int64_t)(r - 3) * C, nv);
+        }
+        store8(cs + (int64_t)j * C, nv);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) load8(xb + (int64_t)(t0 - 3 + j) * C, h[j]);
+  }
+
+  const bool l2 = c0 < l2_channels;
+  constexpr int U = 4;
+  for (int t = t0; t < t1; t += U) {
+    float xs[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (t + u < t1) load8(xb + (int64_t)(t + u) * C, xs[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t + u < t1) {
+        float yv[8];
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float acc = wt[0][i] * h[0][i];
+          acc = fmaf(wt[1][i], h[1][i], acc);
+          acc = fmaf(wt[2][i], h[2][i], acc);
+          acc = fmaf(wt[3][i], xs[u][i], acc);
+          yv[i] = silu_f(acc);
+          ss = fmaf(yv[i], yv[i], ss);
+        }
+        if (l2) {
+          ss = sum16(ss);
+          const float r = rsqrtf(ss + l2_eps);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) yv[i] *= r;
+        }
+        store8(yb + (int64_t)(t + u) * C, yv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          h[0][i] = h[1][i];
+          h[1][i] = h[2][i];
+          h[2][i] = xs[u][i];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_conv_silu(const void* x, void* y, int dt, const float* w, float* conv_state,
+                            int B, int T, int C, int l2_channels, float l2_eps,
+                            hipStream_t stream) {
+  dim3 grid((C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8), (T + CONV_TB - 1) / CONV_TB, B);
+  if (dt == 1) {
+    hipLaunchKernelGGL(conv_silu_kernel<uint16_t>, grid, dim3(CONV_THREADS), 0, stream,
+                       (const uint16_t*)x, (uint16_t*)y, w, conv_state, T, C, l2_channels, l2_eps);
+  } else {
+    hipLaunchKernelGGL(conv_silu_kernel<float>, grid, dim3(CONV_THREADS), 0, stream,
+                       (const float*)x, (float*)y, w, conv_state, T, C, l2_channels, l2_eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,236 @@
+// The gated delta rule evaluated token by token in f32, for decode_rows and
+// for the sequential prefill ("Qwen3.8 27B" model card, Gated DeltaNet bullet
+// and state paragraph; the update S_t = a_t S_{t-1}(I - b_t k_t k_t^T) +
+// b_t v_t k_t^T, o_t = S_t q_t).
+//
+// Row i of S (value channel i) evolves on its own given k, q, v_i and the
+// gates:  u_i = S_i . k,  d_i = b (v_i - a u_i),  S_i <- a S_i + d_i k,
+// o_i = S_i . q = a (S_i . q)_old + d_i (k . q).
+// Both kernels give each row to 16 lanes, 8 contiguous f32 per lane, so a row
+// is one coalesced 512-byte access and its dot products are DPP row sums.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+__device__ __forceinline__ float dot8(const float* a, const float* b) {
+  float s = a[0] * b[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) s = fmaf(a[i], b[i], s);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// decode_rows: one new token per fixed row, state [R, Hv, 128, 128] updated in
+// place.  One workgroup per (row, value head); wave w owns value rows
+// [32w, 32w+32); each 16-lane group owns one row per step, 8 steps, with all
+// 8 state loads in flight before any arithmetic.  HBM-bound: 64 KiB read and
+// 64 KiB written per (row, head).
+constexpr int DEC_THREADS = 256;
+
+template <typename T, typename G>
+__global__ __launch_bounds__(DEC_THREADS) void decode_rows_kernel(
+    const T* __restrict__ q, int64_t q_rs, const T* __restrict__ k, int64_t k_rs,
+    const T* __restrict__ v, int64_t v_rs, const G* __restrict__ a, const G* __restrict__ b,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float* __restrict__ state,
+    const int32_t* __restrict__ lengths, T* __restrict__ o, int Hk, int Hv, float q_scale) {
+  const int r = blockIdx.x / Hv;
+  const int h = blockIdx.x - r * Hv;
+  const int kh = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, grp = lane >> 4, l16 = lane & 15;
+  T* ob = o + ((int64_t)r * Hv + h) * 128;
+  if (lengths && lengths[r] < 0) {  // idle row: state untouched, output zero
+    if (tid < 128) store1(ob + tid, 0.0f);
+    return;
+  }
+  float* Sb = state + ((int64_t)r * Hv + h) * (128 * 128);
+  float s[8][8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) load8(Sb + (32 * wave + 4 * it + grp) * 128 + l16 * 8, s[it]);
+
+  float kv[8], qv[8];
+  load8(k + r * k_rs + kh * 128 + l16 * 8, kv);
+  load8(q + r * q_rs + kh * 128 + l16 * 8, qv);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qv[i] *= q_scale;
+  float vr[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) vr[it] = load1(v + r * v_rs + h * 128 + 32 * wave + 4 * it + grp);
+  const float al = expf(gate_log_alpha(load1(a + (int64_t)r * Hv + h), A_log[h], dt_bias[h]));
+  const float be = gate_beta(load1(b + (int64_t)r * Hv + h));
+  const float kq = sum16(dot8(kv, qv));
+
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = 32 * wave + 4 * it + grp;
+    const float su = sum16(dot8(s[it], kv));
+    const float sq = sum16(dot8(s[it], qv));
+    const float d = be * (vr[it] - al * su);
+    float sn[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sn[i] = fmaf(al, s[it][i], d * kv[i]);
+    store8(Sb + row * 128 + l16 * 8, sn);
+    if (l16 == 0) store1(ob + row, fmaf(al, sq, d * kq));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sequential prefill: state rows live in registers for the whole sequence.
+// One workgroup per (batch, value head, block of 16 value rows); tokens are
+// staged SEQ_TT at a time in LDS (k, q as f32, this block's v, the gates),
+// then each 16-lane group runs the recurrence for its row.
+constexpr int SEQ_THREADS = 256;
+constexpr int SEQ_TT = 32;
+
+template <typename T, typename G>
+__global__ __launch_bounds__(SEQ_THREADS) void recurrent_prefill_kernel(
+    const T* __restrict__ q, int64_t q_ts, const T* __restrict__ k, int64_t k_ts,
+    const T* __restrict__ v, int64_t v_ts, const G* __restrict__ a, const G* __restrict__ b,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    const float* state_in, float* state_out, T* __restrict__ o, int Tlen, int Hk, int Hv,
+    float q_scale) {
+  __shared__ float ks[SEQ_TT][128];
+  __shared__ float qs[SEQ_TT][128];
+  __shared__ float vs[SEQ_TT][16];
+  __shared__ float als[SEQ_TT], bes[SEQ_TT];
+
+  const int blk = blockIdx.x & 7;
+  const int bh = blockIdx.x >> 3;
+  const int h = bh % Hv;
+  const int bb = bh / Hv;
+  const int kh = h / (Hv / Hk);
+  const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+  const int row = blk * 16 + grp;
+  const float Al = A_log[h], Db = dt_bias[h];
+
+  const int64_t sbase = ((int64_t)bb * Hv + h) * (128 * 128) + (int64_t)row * 128 + l16 * 8;
+  float s[8];
+  if (state_in) load8(state_in + sbase, s);
+  else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = 0.0f;
+  }
+
+  const T* qb = q + (int64_t)bb * Tlen * q_ts + kh * 128;
+  const T* kb = k + (int64_t)bb * Tlen * k_ts + kh * 128;
+  const T* vb = v + (int64_t)bb * Tlen * v_ts + h * 128 + blk * 16;
+  const G* ab = a + (int64_t)bb * Tlen * Hv + h;
+  const G* bbp = b + (int64_t)bb * Tlen * Hv + h;
+  T* obp = o + ((int64_t)bb * Tlen * Hv + h) * 128 + row;
+
+  for (int t0 = 0; t0 < Tlen; t0 += SEQ_TT) {
+    const int n = min(SEQ_TT, Tlen - t0);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int tt = grp + 16 * half;
+      if (tt < n) {
+        float tmp[8];
+        load8(kb + (int64_t)(t0 + tt) * k_ts + l16 * 8, tmp);
+        *reinterpret_cast<float4*>(&ks[tt][l16 * 8]) = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        *reinterpret_cast<float4*>(&ks[tt][l16 * 8 + 4]) = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
+        load8(qb + (int64_t)(t0 + tt) * q_ts + l16 * 8, tmp);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tmp[i] *= q_scale;
+        *reinterpret_cast<float4*>(&qs[tt][l16 * 8]) = make_float4(tmp[0], tmp[1], tmp[2], tmp[3]);
+        *reinterpret_cast<float4*>(&qs[tt][l16 * 8 + 4]) = make_float4(tmp[4], tmp[5], tmp[6], tmp[7]);
+      }
+    }
+#pragma unroll
+    for (int rep = 0; rep < 2; ++rep) {
+      const int idx = tid + rep * SEQ_THREADS;
+      const int tt = idx >> 4, j = idx & 15;
+      if (tt < n) vs[tt][j] = load1(vb + (int64_t)(t0 + tt) * v_ts + j);
+    }
+    if (tid < n) {
+      als[tid] = expf(gate_log_alpha(load1(ab + (int64_t)(t0 + tid) * Hv), Al, Db));
+      bes[tid] = gate_beta(load1(bbp + (int64_t)(t0 + tid) * Hv));
+    }
+    __syncthreads();
+    for (int tt = 0; tt < n; ++tt) {
+      float kv[8], qv[8];
+      const float4 k0 = *reinterpret_cast<const float4*>(&ks[tt][l16 * 8]);
+      const float4 k1 = *reinterpret_cast<const float4*>(&ks[tt][l16 * 8 + 4]);
+      const float4 q0 = *reinterpret_cast<const float4*>(&qs[tt][l16 * 8]);
+      const float4 q1 = *reinterpret_cast<const float4*>(&qs[tt][l16 * 8 + 4]);
+      kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
+      kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
+      qv[0] = q0.x; qv[1] = q0.y; qv[2] = q0.z; qv[3] = q0.w;
+      qv[4] = q1.x; qv[5] = q1.y; qv[6] = q1.z; qv[7] = q1.w;
+      const float al = als[tt], be = bes[tt];
+      const float su = sum16(dot8(s, kv));
+      const float sq = sum16(dot8(s, qv));
+      const float kq = sum16(dot8(kv, qv));
+      const float d = be * (vs[tt][grp] - al * su);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = fmaf(al, s[i], d * kv[i]);
+      if (l16 == 0) store1(obp + (int64_t)(t0 + tt) * Hv * 128, fmaf(al, sq, d * kq));
+    }
+    __syncthreads();
+  }
+  if (state_out) store8(state_out + sbase, s);
+}
+
+template <typename T, typename G>
+static void launch_decode_t(const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                            const void* v, int64_t v_rs, const void* a, const void* b,
+                            const float* A_log, const float* dt_bias, float* state,
+                            const int32_t* lengths, void* o, int R, int Hk, int Hv, float q_scale,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL((decode_rows_kernel<T, G>), dim3(R * Hv), dim3(DEC_THREADS), 0, stream,
+                     (const T*)q, q_rs, (const T*)k, k_rs, (const T*)v, v_rs, (const G*)a,
+                     (const G*)b, A_log, dt_bias, state, lengths, (T*)o, Hk, Hv, q_scale);
+}
+
+hipError_t launch_decode_rows(const void* q, int64_t q_rs, const void* k, int64_t k_rs,
+                              const void* v, int64_t v_rs, int qkv_dt, const void* a,
+                              const void* b, int gate_dt, const float* A_log,
+                              const float* dt_bias, float* state, const int32_t* lengths, void* o,
+                              int R, int Hk, int Hv, float q_scale, hipStream_t stream) {
+  if (qkv_dt == 1 && gate_dt == 1)
+    launch_decode_t<uint16_t, uint16_t>(q, q_rs, k, k_rs, v, v_rs, a, b, A_log, dt_bias, state,
+                                        lengths, o, R, Hk, Hv, q_scale, stream);
+  else if (qkv_dt == 1)
+    launch_decode_t<uint16_t, float>(q, q_rs, k, k_rs, v, v_rs, a, b, A_log, dt_bias, state,
+                                     lengths, o, R, Hk, Hv, q_scale, stream);
+  else if (gate_dt == 1)
+    launch_decode_t<float, uint16_t>(q, q_rs, k, k_rs, v, v_rs, a, b, A_log, dt_bias, state,
+                                     lengths, o, R, Hk, Hv, q_scale, stream);
+  else
+    launch_decode_t<float, float>(q, q_rs, k, k_rs, v, v_rs, a, b, A_log, dt_bias, state,
+                                  lengths, o, R, Hk, Hv, q_scale, stream);
+  return hipGetLastError();
+}
+
+template <typename T, typename G>
+static void launch_seq_t(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const void* v,
+                         int64_t v_ts, const void* a, const void* b, const float* A_log,
+                         const float* dt_bias, const float* state_in, float* state_out, void* o,
+                         int B, int Tlen, int Hk, int Hv, float q_scale, hipStream_t stream) {
+  hipLaunchKernelGGL((recurrent_prefill_kernel<T, G>), dim3(B * Hv * 8), dim3(SEQ_THREADS), 0,
+                     stream, (const T*)q, q_ts, (const T*)k, k_ts, (const T*)v, v_ts, (const G*)a,
+                     (const G*)b, A_log, dt_bias, state_in, state_out, (T*)o, Tlen, Hk, Hv, q_scale);
+}
+
+hipError_t launch_prefill_sequential(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
+                                     const void* v, int64_t v_ts, int qkv_dt, const void* a,
+                                     const void* b, int gate_dt, const float* A_log,
+                                     const float* dt_bias, const float* state_in,
+                                     float* state_out, void* o, int B, int T, int Hk, int Hv,
+                                     float q_scale, hipStream_t stream) {
+  if (qkv_dt == 1 && gate_dt == 1)
+    launch_seq_t<uint16_t, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+                                     state_out, o, B, T, Hk, Hv, q_scale, stream);
+  else if (qkv_dt == 1)
+    launch_seq_t<uint16_t, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+                                  state_out, o, B, T, Hk, Hv, q_scale, stream);
+  else if (gate_dt == 1)
+    launch_seq_t<float, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+                                  state_out, o, B, T, Hk, Hv, q_scale, stream);
+  else
+    launch_seq_t<float, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+                               state_out, o, B, T, Hk, Hv, q_scale, stream);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

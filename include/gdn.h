@@ -1,0 +1,174 @@
+/*
+ * gdn.h -- C ABI of libgdn, the Gated DeltaNet mixer hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation ("Qwen3.8 27B" model card, Gated DeltaNet bullet): the fused
+ * q|k|v projection goes through a depthwise causal conv of width 4 and silu;
+ * q and k are L2-normalised per head; each value head keeps a [dv, dk] f32
+ * state S that the gated delta rule decays by
+ *     alpha_t = exp(-exp(A_log) * softplus(a_t + dt_bias))
+ * and writes at rate beta_t = sigmoid(b_t):
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t (q_scale * q_t);
+ * the head outputs are RMS-normalised (scale 1 + w, f32) and gated by
+ * silu(z).  16 q/k heads serve 48 value heads: value head h reads q/k head
+ * h / (Hv / Hk).  The card's state paragraph: prefill serves one batch,
+ * decode_rows a server's fixed rows each at its own length; every row keeps
+ * its conv history and recurrent state in f32.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *    The library never allocates, frees, synchronises, logs or aborts.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream) and the call returns at once.  Device faults, if
+ *    any, surface at the caller's next synchronisation.
+ *  - All arguments are validated on the host first.  On any error nothing
+ *    is enqueued and a nonzero gdn_status is returned; gdn_status_str()
+ *    names it.  Calls are stateless and thread-safe.
+ *  - dtype arguments take a gdn_dtype value: GDN_F32 or GDN_BF16 (bf16
+ *    stored as its 16-bit pattern).  Arithmetic is f32 (MFMA for the chunked
+ *    prefill: bf16 operands, f32 accumulation).
+ *  - Alignment: f32 state and conv-history pointers 16 bytes; q/k/v/o/x/y/z
+ *    16 bytes with row strides that keep every head 16-byte aligned.
+ *  - Head widths: only dk = dv = 128 is implemented (GDN_ERR_UNSUPPORTED
+ *    otherwise); Hv must be a multiple of Hk.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,       /* a size or stride is out of range */
+  GDN_ERR_DTYPE = 3,       /* unknown or unsupported dtype combination */
+  GDN_ERR_ALIGN = 4,       /* a pointer or stride breaks the alignment rules */
+  GDN_ERR_UNSUPPORTED = 5, /* valid but not implemented (e.g. head width != 128) */
+  GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+  GDN_ERR_LAUNCH = 7       /* the HIP runtime refused the launch */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Prefill algorithm.  AUTO picks CHUNKED for bf16 q/k/v and SEQUENTIAL for
+ * f32 q/k/v.  SEQUENTIAL runs the recurrence token by token in f32 (any
+ * dtype).  CHUNKED (bf16 q/k/v only) uses the chunk-of-64 WY/UT form on
+ * bf16 MFMA with f32 accumulation and an f32 state carried between chunks. */
+typedef enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SEQUENTIAL = 1, GDN_ALGO_CHUNKED = 2 } gdn_algo;
+
+/* Head counts and widths: 16, 48, 128, 128 for the model's layer. */
+typedef struct gdn_dims {
+  int32_t n_qk_heads; /* Hk */
+  int32_t n_v_heads;  /* Hv, a multiple of Hk */
+  int32_t head_k_dim; /* dk (128) */
+  int32_t head_v_dim; /* dv (128) */
+} gdn_dims;
+
+/* Static string naming a status code (never NULL). */
+const char* gdn_status_str(int status);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+/*
+ * gdn_conv_silu -- depthwise causal conv + silu, optional per-head L2.
+ * ("Qwen3.8 27B" card, Gated DeltaNet bullet; llm-arch-viz module tree:
+ * conv1d 10240x1x4 without bias.)
+ *   x, y        [B, T, C] in dtype `dt`; y must not overlap x.
+ *   w           [C, W] f32; w[c][W-1] multiplies the current token,
+ *               w[c][0] the input W-1 tokens back (cross-correlation).
+ *   conv_state  [B, W-1, C] f32, in/out: the last W-1 inputs before this
+ *               call on entry, the last W-1 inputs of [history; x] on exit.
+ *               NULL means a zero history and nothing is written.
+ *   y[b,t,c] = silu(sum_i w[c][i] * xhat[b, t+i, c]) with xhat = [history; x];
+ *   then for c < l2_channels, each group of head_dim channels of y is divided
+ *   by sqrt(sum of squares + l2_eps).
+ * Constraints: W == 4; C % 8 == 0; l2_channels % head_dim == 0 and
+ * l2_channels <= C; head_dim == 128 when l2_channels > 0; T == 0 is a no-op.
+ */
+int gdn_conv_silu(const void* x, void* y, int32_t dt, const float* w, float* conv_state,
+                  int32_t B, int32_t T, int32_t C, int32_t W, int32_t l2_channels,
+                  int32_t head_dim, float l2_eps, void* stream);
+
+/*
+ * Bytes of device workspace gdn_prefill needs for these sizes and algorithm
+ * (0 for the sequential algorithm).  The caller allocates it; its contents
+ * need no initialisation and are scratch after the call.
+ */
+size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t qkv_dt,
+                                   int32_t algo);
+
+/*
+ * gdn_prefill -- the gated delta rule over T tokens of B sequences, with the
+ * state carried in and out (the card's prefill; the chunk continues "from
+ * position pos0" when state_in holds the previous chunk's state_out).
+ *   q, k   [B, T, Hk, dk] in qkv_dt; element (b,t,h,i) at
+ *          b*T*tok_stride + t*tok_stride + h*dk + i (strides in elements),
+ *          so q, k and v may be views into the conv output (stride 10240).
+ *   v      [B, T, Hv, dv] in qkv_dt, same addressing with v_tok_stride.
+ *   a, b   [B, T, Hv] contiguous in gate_dt (the gate pre-activations).
+ *   A_log, dt_bias  [Hv] f32.
+ *   state_in   [B, Hv, dv, dk] f32 (S row-major, dk fastest); NULL = zeros.
+ *   state_out  [B, Hv, dv, dk] f32; NULL = not written; may equal state_in.
+ *   o      [B, T, Hv, dv] contiguous in qkv_dt; o_t uses the state after
+ *          token t's update.
+ *   q_scale multiplies q (1.0 for the model's layer).
+ *   algo   a gdn_algo value.
+ *   workspace  device scratch of at least gdn_prefill_workspace_bytes(...)
+ *          bytes (may be NULL when that is 0), 256-byte aligned.
+ * Errors: GDN_ERR_WORKSPACE if the workspace is too small; GDN_ERR_DTYPE for
+ * CHUNKED with f32 q/k/v.
+ */
+int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
+                const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
+                const float* state_in, float* state_out, void* o, int32_t B, int32_t T,
+                gdn_dims dims, float q_scale, int32_t algo, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_decode_rows -- one new token for each of R fixed rows, each row at its
+ * own length, the state updated in place (the card's decode_rows: "a
+ * server's rows each at its own length (fixed rows)").
+ *   q, k   [R, Hk, dk] in qkv_dt, row r at r*row_stride (elements).
+ *   v      [R, Hv, dv] in qkv_dt, row r at r*v_row_stride.
+ *   a, b   [R, Hv] contiguous in gate_dt.
+ *   A_log, dt_bias  [Hv] f32.
+ *   state  [R, Hv, dv, dk] f32, row r's state at index r; read and written.
+ *   lengths [R] int32 tokens already consumed by each row, or NULL (all rows
+ *          active).  The rule uses no positions, so lengths only mark idle
+ *          rows: lengths[r] < 0 leaves row r's state untouched and writes
+ *          zeros to its output.
+ *   o      [R, Hv, dv] contiguous in qkv_dt.
+ * The conv step for decode is gdn_conv_silu with B = R, T = 1.
+ */
+int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
+                    const void* v, int64_t v_row_stride, int32_t qkv_dt, const void* a,
+                    const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
+                    float* state, const int32_t* lengths, void* o, int32_t R, gdn_dims dims,
+                    float q_scale, void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * (1 + w) * silu(z) per
+ * row of D ("Qwen3.8 27B" card, Gated DeltaNet and Norms bullets;
+ * llm-arch-viz: RMSNormGated of width 128, eps 1e-06).
+ *   x, z, y  [N, H, D] contiguous in dtype `dt`; y may equal x.
+ *   w        [D] f32, shared by all heads.
+ * Constraints: D == 128.
+ */
+int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const float* w,
+                      int32_t N, int32_t H, int32_t D, float eps, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

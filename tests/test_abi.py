@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gdn.h declares, and rejects bad arguments on the host with the
+documented status before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_mixer_amd as gdn
+from gated_deltanet_mixer_amd import gdn_dims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5, 6
+P = 0x10000  # a 256-byte-aligned fake device address: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_exports():
+    L = gdn.lib()
+    names = declared_functions()
+    assert {"gdn_conv_silu", "gdn_prefill", "gdn_decode_rows", "gdn_gated_rmsnorm",
+            "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert gdn.gdn_abi_version() == 1
+    for s in range(8):
+        assert gdn.gdn_status_str(s).startswith("GDN_")
+    assert gdn.gdn_status_str(99) == "unknown gdn_status"
+
+
+def _vp(x):
+    return ctypes.c_void_p(x) if x else None
+
+
+def conv(x=P, y=2 * P, dt=1, w=3 * P, cs=None, B=1, T=8, C=1024, W=4, l2=0, hd=128):
+    return gdn.lib().gdn_conv_silu(_vp(x), _vp(y), dt, _vp(w), _vp(cs), B, T, C, W, l2, hd,
+                                   1e-6, None)
+
+
+def test_conv_validation():
+    assert conv(x=0) == NULL
+    assert conv(w=0) == NULL
+    assert conv(dt=7) == DTYPE
+    assert conv(W=3) == UNSUP
+    assert conv(W=0) == SHAPE
+    assert conv(C=1020) == SHAPE
+    assert conv(l2=2048) == SHAPE        # more than C
+    assert conv(l2=100, hd=64) == SHAPE  # not a whole number of heads
+    assert conv(l2=128, hd=64) == UNSUP
+    assert conv(x=P + 8) == ALIGN
+    assert conv(cs=P + 4) == ALIGN
+    assert conv(y=P + 512) == SHAPE      # y overlaps x
+    assert conv(T=0) == OK               # no-op, nothing launched
+    assert conv(B=0) == OK
+
+
+D16 = gdn_dims(16, 48, 128, 128)
+
+
+def prefill(q=P, qs=2048, k=2 * P, ks=2048, v=3 * P, vs=6144, qdt=1, a=4 * P, b=5 * P, gdt=0,
+            Al=6 * P, db=7 * P, si=None, so=None, o=8 * P, B=1, T=64, dims=D16, algo=0, ws=None,
+            wsb=0):
+    return gdn.lib().gdn_prefill(_vp(q), qs, _vp(k), ks, _vp(v), vs, qdt, _vp(a), _vp(b), gdt,
+                                 _vp(Al), _vp(db), _vp(si), _vp(so), _vp(o), B, T, dims, 1.0, algo,
+                                 _vp(ws), wsb, None)
+
+
+def test_prefill_validation():
+    assert prefill(q=0) == NULL
+    assert prefill(o=0) == NULL
+    assert prefill(qdt=2) == DTYPE
+    assert prefill(qdt=0, algo=2) == DTYPE           # chunked needs bf16
+    assert prefill(dims=gdn_dims(16, 40, 128, 128)) == SHAPE
+    assert prefill(dims=gdn_dims(16, 48, 64, 64)) == UNSUP
+    assert prefill(qs=1024) == SHAPE                 # stride shorter than the heads
+    assert prefill(qs=2052) == ALIGN
+    assert prefill(q=P + 2) == ALIGN
+    assert prefill(si=P + 8) == ALIGN
+    assert prefill(algo=9) == SHAPE
+    assert prefill(B=-1) == SHAPE
+    assert prefill(B=0) == OK
+    need = gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 1, 0)
+    if need > 0:
+        assert prefill(ws=None, wsb=0) == WS
+        assert prefill(ws=9 * P, wsb=need - 1) == WS
+    assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 0, 0) == 0  # f32: sequential
+    assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 1, 1) == 0
+
+
+def decode(q=P, k=2 * P, v=3 * P, qdt=1, st=4 * P, o=5 * P, R=4, dims=D16, lengths=None):
+    return gdn.lib().gdn_decode_rows(_vp(q), 2048, _vp(k), 2048, _vp(v), 6144, qdt, _vp(6 * P),
+                                     _vp(7 * P), 1, _vp(8 * P), _vp(9 * P), _vp(st), _vp(lengths),
+                                     _vp(o), R, dims, 1.0, None)
+
+
+def test_decode_validation():
+    assert decode(st=0) == NULL
+    assert decode(qdt=5) == DTYPE
+    assert decode(dims=gdn_dims(16, 48, 96, 128)) == UNSUP
+    assert decode(R=-1) == SHAPE
+    assert decode(st=P + 4) == ALIGN
+    assert decode(lengths=P + 2) == ALIGN
+    assert decode(R=0) == OK
+
+
+def test_norm_validation():
+    L = gdn.lib()
+    f = lambda x=P, z=2 * P, y=3 * P, w=4 * P, dt=1, N=4, H=48, D=128: L.gdn_gated_rmsnorm(
+        _vp(x), _vp(z), _vp(y), dt, _vp(w), N, H, D, 1e-6, None)
+    assert f(z=0) == NULL
+    assert f(dt=3) == DTYPE
+    assert f(D=64) == UNSUP
+    assert f(N=-2) == SHAPE
+    assert f(w=P + 4) == ALIGN
+    assert f(N=0) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from gated_deltanet_mixer_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libgdn.so not found"):
+        _binding.lib()
