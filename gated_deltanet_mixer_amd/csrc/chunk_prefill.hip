@@ -1,19 +1,516 @@
-// Chunked prefill (placeholder until the MFMA kernels land).
+// Chunked prefill of the gated delta rule on bf16 MFMA (gfx950), for bf16
+// q/k/v.  The rule ("Qwen3.8 27B" model card, Gated DeltaNet bullet):
+//   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t.
+//
+// Chunk form (exact in exact arithmetic).  For a chunk of n <= 64 tokens with
+// G_t = sum_{s<=t} log a_s, gamma_t = e^{G_t}, H = S^T [dk, dv]:
+//   A_tj = b_t e^{G_t - G_j} (k_t . k_j)  (j < t),   T = (I + A)^{-1}
+//   W  = T diag(b gamma) K,   Ut = T diag(b) V
+//   U  = Ut - W H
+//   O  = diag(gamma) Q H + (M o Q K^T) U,   M_tj = e^{G_t - G_j} (j <= t)
+//   H' = gamma_last H + K^T diag(e^{G_last - G_s}) U
+// Only non-positive exponents are ever taken.  Padding rows of a short last
+// chunk carry g = 0, b = 0 and zero k/q/v, which leaves every formula exact.
+//
+// Two kernels:
+//  * chunk_prep: one wave per (batch, value head, chunk), fully parallel.
+//    Gates and their prefix sum, K K^T and Q K^T on MFMA, the unit lower
+//    triangular inverse by column forward substitution in f32 (lane j owns
+//    column j), then W and Ut on MFMA.  Writes W, Ut^T, P = q_scale M o QK^T,
+//    G and (once per q/k head) K^T to the workspace, all bf16 except G.
+//  * chunk_chain: one workgroup per (batch, value head, 32-column slice of
+//    dv), sequential over chunks.  The f32 state slice lives in MFMA
+//    accumulator registers; its bf16 copy and U^T are staged in LDS.  The dv
+//    columns of H are independent, which is what allows the slicing.
+//
+// MFMA operand layout (v_mfma_f32_16x16x32_bf16, checked on the device):
+// lane l holds A[l%16][8(l/16)..8(l/16)+7], B[8(l/16)..+7][l%16], and the
+// result D[4(l/16)+r][l%16], r = 0..3.  Every operand below is read as 16
+// contiguous bytes along the contraction index.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace gdn {
 
-size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
-  (void)B; (void)T; (void)Hk; (void)Hv;
-  return 0;
+namespace {
+
+constexpr int CK = 64;   // chunk length
+constexpr int DH = 128;  // head width
+constexpr int XP = 72;   // pitch (bf16) of [*, 64] LDS tiles: 144-byte rows, 16-byte aligned
+constexpr int AP = 72;   // pitch (f32) of the A matrix rows
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-hipError_t launch_prefill_chunked(const void*, int64_t, const void*, int64_t, const void*, int64_t,
-                                  const void*, const void*, int, const float*, const float*,
-                                  const float*, float*, void*, int, int, int, int, float, void*,
-                                  hipStream_t) {
-  return hipErrorNotSupported;
+__device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero_frag() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ void st4bf(uint16_t* p, float a, float b, float c, float d) {
+  u16x4 v;
+  v[0] = f2bf(a); v[1] = f2bf(b); v[2] = f2bf(c); v[3] = f2bf(d);
+  *reinterpret_cast<u16x4*>(p) = v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+struct WsLayout {
+  uint16_t* W;   // [B*Hv*NC][64 t][128 dk]
+  uint16_t* Ut;  // [B*Hv*NC][128 dv][64 t]
+  uint16_t* P;   // [B*Hv*NC][64 t][64 s]
+  float* G;      // [B*Hv*NC][64]
+  uint16_t* Kt;  // [B*Hk*NC][128 dk][64 s]
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(void* base, int B, int T, int Hk, int Hv) {
+  const size_t NC = (size_t)(T + CK - 1) / CK;
+  const size_t nch = (size_t)B * Hv * NC, nck = (size_t)B * Hk * NC;
+  char* p = static_cast<char*>(base);
+  WsLayout L;
+  L.W = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * DH * 2);
+  L.Ut = reinterpret_cast<uint16_t*>(p); p += align256(nch * DH * CK * 2);
+  L.P = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * CK * 2);
+  L.G = reinterpret_cast<float*>(p);     p += align256(nch * CK * 4);
+  L.Kt = reinterpret_cast<uint16_t*>(p); p += align256(nck * DH * CK * 2);
+  return L;
+}
+
+}  // namespace
+
+size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
+  const size_t NC = (size_t)(T + CK - 1) / CK;
+  const size_t nch = (size_t)B * Hv * NC, nck = (size_t)B * Hk * NC;
+  return align256(nch * CK * DH * 2) + align256(nch * DH * CK * 2) + align256(nch * CK * CK * 2) +
+         align256(nch * CK * 4) + align256(nck * DH * CK * 2);
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1: per (batch, value head, chunk), one wave.
+template <typename G_T>
+__global__ __launch_bounds__(64) void chunk_prep_kernel(
+    const uint16_t* __restrict__ q, int64_t q_ts, const uint16_t* __restrict__ k, int64_t k_ts,
+    const uint16_t* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
+    const G_T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    WsLayout ws, int T, int Hk, int Hv, int NC, float q_scale) {
+  __shared__ float Ab[CK * AP];                      // A (f32), later T b and T b gamma (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t XT[DH * XP];  // K^T, later V^T
+  __shared__ float Gs[CK], Bs[CK];
+
+  const int c = blockIdx.x % NC;
+  const int bh = blockIdx.x / NC;
+  const int h = bh % Hv, bb = bh / Hv;
+  const int grp = Hv / Hk, kh = h / grp;
+  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+  const int t0 = c * CK;
+  const int n = min(CK, T - t0);
+  const int64_t chunk = (int64_t)bh * NC + c;
+
+  // Gates for token `lane`; padding tokens get g = 0, b = 0.
+  float g = 0.0f, be = 0.0f;
+  if (lane < n) {
+    const int64_t gi = ((int64_t)bb * T + t0 + lane) * Hv + h;
+    g = gate_log_alpha(load1(a + gi), A_log[h], dt_bias[h]);
+    be = gate_beta(load1(b + gi));
+  }
+  const float Gl = wave_scan(g, lane);
+  Gs[lane] = Gl;
+  Bs[lane] = be;
+  ws.G[chunk * CK + lane] = Gl;
+
+  const uint16_t* kbase = k + ((int64_t)bb * T + t0) * k_ts + kh * DH;
+  const uint16_t* qbase = q + ((int64_t)bb * T + t0) * q_ts + kh * DH;
+  const uint16_t* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
+
+  // K^T into LDS: lane = token s, 16 passes over 8-channel groups.
+#pragma unroll 4
+  for (int gi = 0; gi < 16; ++gi) {
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (lane < n) x = *reinterpret_cast<const u16x8*>(kbase + (int64_t)lane * k_ts + gi * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) XT[(gi * 8 + i) * XP + lane] = x[i];
+  }
+
+  // K K^T and Q K^T (transposed) on MFMA, then A and P.
+  {
+    bf16x8 kf[4][4], qf[4][4];  // [row block][k step]
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int t = rb * 16 + li;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (t < n) {
+          kf[rb][kk] = ld_frag(kbase + (int64_t)t * k_ts + kk * 32 + lg * 8);
+          qf[rb][kk] = ld_frag(qbase + (int64_t)t * q_ts + kk * 32 + lg * 8);
+        } else {
+          kf[rb][kk] = zero_frag();
+          qf[rb][kk] = zero_frag();
+        }
+      }
+    }
+    __syncthreads();  // Gs, Bs visible
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {
+        // KK tile [t block tb][s block sb]; only s <= t blocks are needed.
+        if (sb <= tb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = mfma16(kf[tb][kk], kf[sb][kk], acc);
+          const int s = sb * 16 + li;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = tb * 16 + lg * 4 + r;
+            Ab[t * AP + s] = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * acc[r] : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ab[(tb * 16 + lg * 4 + r) * AP + sb * 16 + li] = 0.0f;
+        }
+        // (Q K^T)^T tile [s block sb][t block tb]: C[s][t] = K_s . Q_t.
+        f32x4 pq = {0.f, 0.f, 0.f, 0.f};
+        if (sb <= tb) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) pq = mfma16(kf[sb][kk], qf[tb][kk], pq);
+        }
+        const int t = tb * 16 + li;
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int s = sb * 16 + lg * 4 + r;
+          pv[r] = (s <= t) ? q_scale * __expf(Gs[t] - Gs[s]) * pq[r] : 0.0f;
+        }
+        st4bf(ws.P + (chunk * CK + t) * CK + sb * 16 + lg * 4, pv[0], pv[1], pv[2], pv[3]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // K^T to the workspace once per q/k head (the first value head of the group).
+  if (h % grp == 0) {
+    uint16_t* dst = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const int idx = i * 64 + lane;  // 16-byte piece: row idx/8, piece idx%8
+      const int row = idx >> 3, pc = idx & 7;
+      *reinterpret_cast<u16x8*>(dst + row * CK + pc * 8) =
+          *reinterpret_cast<const u16x8*>(&XT[row * XP + pc * 8]);
+    }
+  }
+
+  // T = (I + A)^{-1}: column j = lane, rows in order (unit lower triangular).
+  float Tc[CK];
+#pragma unroll
+  for (int t = 0; t < CK; ++t) {
+    float acc = (t == lane) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int s4 = 0; s4 < t; s4 += 4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&Ab[t * AP + s4]);
+      acc = fmaf(-a4.x, Tc[s4], acc);
+      if (s4 + 1 < t) acc = fmaf(-a4.y, Tc[s4 + 1], acc);
+      if (s4 + 2 < t) acc = fmaf(-a4.z, Tc[s4 + 2], acc);
+      if (s4 + 3 < t) acc = fmaf(-a4.w, Tc[s4 + 3], acc);
+    }
+    Tc[t] = acc;
+  }
+  __syncthreads();  // every lane is done reading A
+  uint16_t* Tb = reinterpret_cast<uint16_t*>(Ab);  // [64][XP]: T diag(b)
+  uint16_t* Tg = Tb + CK * XP;                     // [64][XP]: T diag(b gamma)
+  {
+    const float bj = Bs[lane], gj = bj * __expf(Gs[lane]);
+#pragma unroll
+    for (int t = 0; t < CK; ++t) {
+      Tb[t * XP + lane] = f2bf(Tc[t] * bj);
+      Tg[t * XP + lane] = f2bf(Tc[t] * gj);
+    }
+  }
+  __syncthreads();
+
+  // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T; stored as W[t][dk].
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    bf16x8 kt0 = ld_frag(&XT[(db * 16 + li) * XP + lg * 8]);
+    bf16x8 kt1 = ld_frag(&XT[(db * 16 + li) * XP + 32 + lg * 8]);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16(kt0, ld_frag(&Tg[(tb * 16 + li) * XP + lg * 8]), acc);
+      if (tb >= 2) acc = mfma16(kt1, ld_frag(&Tg[(tb * 16 + li) * XP + 32 + lg * 8]), acc);
+      const int t = tb * 16 + li, dk = db * 16 + lg * 4;
+      st4bf(ws.W + (chunk * CK + t) * DH + dk, acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+  __syncthreads();  // K^T reads done before V^T overwrites it
+
+  // V^T into LDS.
+#pragma unroll 4
+  for (int gi = 0; gi < 16; ++gi) {
+    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (lane < n) x = *reinterpret_cast<const u16x8*>(vbase + (int64_t)lane * v_ts + gi * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) XT[(gi * 8 + i) * XP + lane] = x[i];
+  }
+  __syncthreads();
+
+  // Ut tiles [t block][dv block] = (T diag(b)) V; stored transposed, Ut^T[dv][t].
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const bf16x8 tb0 = ld_frag(&Tb[(tb * 16 + li) * XP + lg * 8]);
+    const bf16x8 tb1 = ld_frag(&Tb[(tb * 16 + li) * XP + 32 + lg * 8]);
+#pragma unroll
+    for (int vb = 0; vb < 8; ++vb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16(tb0, ld_frag(&XT[(vb * 16 + li) * XP + lg * 8]), acc);
+      if (tb >= 2) acc = mfma16(tb1, ld_frag(&XT[(vb * 16 + li) * XP + 32 + lg * 8]), acc);
+      const int t = tb * 16 + lg * 4, dv = vb * 16 + li;
+      st4bf(ws.Ut + (chunk * DH + dv) * CK + t, acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 2: per (batch, value head, slice of NV value columns), sequential
+// over chunks.  Wave w owns token rows [16w, 16w+16) for U and O, and key
+// rows [32w, 32w+32) of the state slice H.
+template <int NV>
+struct ChainFrags {
+  bf16x8 w[4];       // W rows of this wave's token block, 4 k steps over dk
+  bf16x8 qf[4];      // Q rows, same shape
+  u16x4 ut[NV / 16]; // Ut^T at the wave's U accumulator positions
+  bf16x8 p[2];       // P rows of this wave's token block, 2 k steps over s
+  bf16x8 kt[2][2];   // K^T rows (key block 2w+i), 2 k steps over s
+  float4 gu;         // G at the 4 token rows this lane's U accumulators hold
+  float gt;          // G at token 16w + (lane % 16)
+  float glast;       // G at the last token of the chunk
+};
+
+template <int NV>
+__device__ __forceinline__ void load_chain_frags(ChainFrags<NV>& f, const WsLayout& ws,
+                                                 const uint16_t* __restrict__ q, int64_t q_ts,
+                                                 int bb, int bh, int kh, int c, int T, int Hk,
+                                                 int NC, int dv0, int w, int li, int lg) {
+  const int64_t chunk = (int64_t)bh * NC + c;
+  const int t0 = c * CK;
+  const int n = min(CK, T - t0);
+  const int tr = w * 16 + li;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) f.w[kk] = ld_frag(ws.W + (chunk * CK + tr) * DH + kk * 32 + lg * 8);
+  if (tr < n) {
+    const uint16_t* qp = q + ((int64_t)bb * T + t0 + tr) * q_ts + kh * DH + lg * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) f.qf[kk] = ld_frag(qp + kk * 32);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) f.qf[kk] = zero_frag();
+  }
+#pragma unroll
+  for (int vb = 0; vb < NV / 16; ++vb)
+    f.ut[vb] = *reinterpret_cast<const u16x4*>(ws.Ut + (chunk * DH + dv0 + vb * 16 + li) * CK +
+                                               w * 16 + lg * 4);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) f.p[kk] = ld_frag(ws.P + (chunk * CK + tr) * CK + kk * 32 + lg * 8);
+  const uint16_t* ktp = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      f.kt[i][kk] = ld_frag(ktp + ((2 * w + i) * 16 + li) * CK + kk * 32 + lg * 8);
+  const float* gp = ws.G + chunk * CK;
+  f.gu = *reinterpret_cast<const float4*>(gp + w * 16 + lg * 4);
+  f.gt = gp[tr];
+  f.glast = gp[CK - 1];
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void chunk_chain_kernel(
+    const uint16_t* __restrict__ q, int64_t q_ts, WsLayout ws, const float* state_in,
+    float* state_out, uint16_t* __restrict__ o, int B, int T, int Hk, int Hv, int NC,
+    float q_scale) {
+  constexpr int NSL = DH / NV;  // slices per head
+  constexpr int NVB = NV / 16;  // 16-column blocks per slice
+  constexpr int SP = DH + 8;    // pitch of the bf16 state copy: 272-byte rows
+  __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * SP];  // S slice [dv][dk], bf16
+  __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
+  __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
+
+  // Workgroups whose ids agree mod 8 run on the same XCD: keep the NSL slices
+  // of one head there so they share its L2 for W, P, K^T, G and Q.
+  const int id = blockIdx.x;
+  const int hs = (id >> 3) / NSL * 8 + (id & 7);
+  const int sl = (id >> 3) % NSL;
+  if (hs >= B * Hv) return;
+  const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
+  const int dv0 = sl * NV;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+
+  f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      const int dk = (2 * w + i) * 16 + lg * 4, dv = dv0 + vb * 16 + li;
+      if (state_in) {
+        const float4 s4 =
+            *reinterpret_cast<const float4*>(state_in + ((int64_t)bh * DH + dv) * DH + dk);
+        H[i][vb] = f32x4{s4.x, s4.y, s4.z, s4.w};
+      } else {
+        H[i][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      st4bf(&Sb[(vb * 16 + li) * SP + dk], H[i][vb][0], H[i][vb][1], H[i][vb][2], H[i][vb][3]);
+    }
+  }
+
+  ChainFrags<NV> cur;
+  load_chain_frags<NV>(cur, ws, q, q_ts, bb, bh, kh, 0, T, Hk, NC, dv0, w, li, lg);
+  __syncthreads();
+
+  for (int c = 0; c < NC; ++c) {
+    ChainFrags<NV> nxt;
+    if (c + 1 < NC) load_chain_frags<NV>(nxt, ws, q, q_ts, bb, bh, kh, c + 1, T, Hk, NC, dv0, w, li, lg);
+    const int t0 = c * CK;
+    const int n = min(CK, T - t0);
+
+    // (1) U = Ut - W H and (Q H)^T, both against the bf16 state copy.
+    f32x4 accU[NVB], accQ[NVB];
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      accU[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accQ[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        const bf16x8 sf = ld_frag(&Sb[(vb * 16 + li) * SP + kk * 32 + lg * 8]);
+        accU[vb] = mfma16(cur.w[kk], sf, accU[vb]);
+        accQ[vb] = mfma16(sf, cur.qf[kk], accQ[vb]);
+      }
+    }
+    // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.
+    {
+      const float sc[4] = {__expf(cur.glast - cur.gu.x), __expf(cur.glast - cur.gu.y),
+                           __expf(cur.glast - cur.gu.z), __expf(cur.glast - cur.gu.w)};
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        float u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = bf2f(cur.ut[vb][r]) - accU[vb][r];
+        const int off = (vb * 16 + li) * XP + w * 16 + lg * 4;
+        st4bf(&Utl[off], u[0], u[1], u[2], u[3]);
+        st4bf(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
+      }
+    }
+    __syncthreads();
+
+    // (3) O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token
+    // blocks 0 and 1 need only s < 32.
+    {
+      const float gq = q_scale * __expf(cur.gt);
+      const int tr = w * 16 + li;
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + lg * 8]), cur.p[0], acc);
+        if (w >= 2) acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), cur.p[1], acc);
+        if (tr < n) {
+          const int dv = dv0 + vb * 16 + lg * 4;
+          uint16_t* op = o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv;
+          st4bf(op, fmaf(gq, accQ[vb][0], acc[0]), fmaf(gq, accQ[vb][1], acc[1]),
+                fmaf(gq, accQ[vb][2], acc[2]), fmaf(gq, accQ[vb][3], acc[3]));
+        }
+      }
+    }
+    // (4) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U.
+    {
+      const float gl = __expf(cur.glast);
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        const bf16x8 u0 = ld_frag(&Usl[(vb * 16 + li) * XP + lg * 8]);
+        const bf16x8 u1 = ld_frag(&Usl[(vb * 16 + li) * XP + 32 + lg * 8]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f32x4 hcur = H[i][vb];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hcur[r] *= gl;
+          hcur = mfma16(cur.kt[i][0], u0, hcur);
+          hcur = mfma16(cur.kt[i][1], u1, hcur);
+          H[i][vb] = hcur;
+        }
+      }
+    }
+    // (5) bf16 copy of the new state for the next chunk.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+        st4bf(&Sb[(vb * 16 + li) * SP + (2 * w + i) * 16 + lg * 4], H[i][vb][0], H[i][vb][1],
+              H[i][vb][2], H[i][vb][3]);
+    __syncthreads();
+    if (c + 1 < NC) cur = nxt;
+  }
+
+  if (state_out) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        const int dk = (2 * w + i) * 16 + lg * 4, dv = dv0 + vb * 16 + li;
+        *reinterpret_cast<float4*>(state_out + ((int64_t)bh * DH + dv) * DH + dk) =
+            make_float4(H[i][vb][0], H[i][vb][1], H[i][vb][2], H[i][vb][3]);
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
+                                  const void* v, int64_t v_ts, const void* a, const void* b,
+                                  int gate_dt, const float* A_log, const float* dt_bias,
+                                  const float* state_in, float* state_out, void* o, int B, int T,
+                                  int Hk, int Hv, float q_scale, void* workspace,
+                                  hipStream_t stream) {
+  const int NC = (T + CK - 1) / CK;
+  const WsLayout ws = ws_layout(workspace, B, T, Hk, Hv);
+  const dim3 prep_grid((unsigned)((int64_t)B * Hv * NC));
+  if (gate_dt == 1) {
+    hipLaunchKernelGGL(chunk_prep_kernel<uint16_t>, prep_grid, dim3(64), 0, stream,
+                       (const uint16_t*)q, q_ts, (const uint16_t*)k, k_ts, (const uint16_t*)v,
+                       v_ts, (const uint16_t*)a, (const uint16_t*)b, A_log, dt_bias, ws, T, Hk,
+                       Hv, NC, q_scale);
+  } else {
+    hipLaunchKernelGGL(chunk_prep_kernel<float>, prep_grid, dim3(64), 0, stream,
+                       (const uint16_t*)q, q_ts, (const uint16_t*)k, k_ts, (const uint16_t*)v,
+                       v_ts, (const float*)a, (const float*)b, A_log, dt_bias, ws, T, Hk, Hv, NC,
+                       q_scale);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int NV = 32;
+  constexpr int NSL = DH / NV;
+  const int64_t heads = (int64_t)B * Hv;
+  const int64_t groups = (heads + 7) / 8;  // ids are padded to whole XCD rounds
+  const dim3 chain_grid((unsigned)(groups * 8 * NSL));
+  hipLaunchKernelGGL(chunk_chain_kernel<NV>, chain_grid, dim3(256), 0, stream,
+                     (const uint16_t*)q, q_ts, ws, state_in, state_out, (uint16_t*)o, B, T, Hk, Hv,
+                     NC, q_scale);
+  return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -1,0 +1,148 @@
+"""GPU parity of the chunked (bf16 MFMA) prefill against the f64 oracle, plus
+cross-kernel consistency (chunked vs sequential, decode_rows vs prefill,
+split calls with the state handed over).  Bar: max|x-ref|/max|ref| < 2e-2 for
+bf16 inputs, per output tensor."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import gated_deltanet_mixer_amd as gdn  # noqa: E402
+import oracle  # noqa: E402
+from synth import decode_inputs, make_workload, recurrence_inputs, to_f64  # noqa: E402
+from tests.conftest import max_rel_err  # noqa: E402
+from tests.gpu_util import banner, dev, host_f64  # noqa: E402
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.lib()
+
+
+def _ref(x, S0):
+    al, be, _ = oracle.gates(to_f64(x["a"]), to_f64(x["b"]), x["A_log"], x["dt_bias"])
+    return oracle.recurrence(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), al, be, S0)
+
+
+def _gpu_prefill(x, state=None, algo="chunked", inplace=False):
+    B, T, Hv = x["v"].shape[:3]
+    si = None if state is None else dev(state)
+    so = si if (inplace and si is not None) else torch.empty((B, Hv, 128, 128),
+                                                           dtype=torch.float32, device="cuda")
+    o = gdn.gdn_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["a"]), dev(x["b"]),
+                        dev(x["A_log"]), dev(x["dt_bias"]), si, so, algo=algo)
+    torch.cuda.synchronize()
+    return o, so
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 150])
+@pytest.mark.parametrize("A_range,state", [((-1.0, 1.0), 0.05), ((-6.0, -4.0), 0.5),
+                                           ((-1.0, 1.0), None)])
+def test_chunked_small(T, A_range, state):
+    banner(f"chunked T={T} A_log~U{A_range} state={state}")
+    x = recurrence_inputs(2, T, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=T,
+                          state_std=state, A_log_range=A_range)
+    S0 = None if state is None else to_f64(x["state"])
+    o, S = _gpu_prefill(x, x["state"])
+    o_ref, S_ref = _ref(x, S0)
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(S), S_ref) < TOL
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+def test_chunked_gate_dtypes_and_inplace(gdt):
+    banner(f"chunked in-place state, gates {gdt}")
+    x = recurrence_inputs(1, 200, Hk=2, Hv=6, qkv_dt="bf16", gate_dt=gdt, seed=21, state_std=0.3,
+                          A_log_range=(-5.0, -3.0))
+    o, S = _gpu_prefill(x, x["state"], inplace=True)
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(S), S_ref) < TOL
+
+
+def test_chunked_head_sharing_16_48():
+    banner("chunked Hk=16 Hv=48 T=100")
+    x = recurrence_inputs(1, 100, qkv_dt="bf16", gate_dt="f32", seed=22, state_std=0.05)
+    o, S = _gpu_prefill(x, x["state"])
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(S), S_ref) < TOL
+
+
+def test_chunked_q_scale():
+    banner("chunked q_scale")
+    x = recurrence_inputs(1, 80, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=23, state_std=0.1)
+    si = dev(x["state"])
+    so = torch.empty_like(si)
+    o = gdn.gdn_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["a"]), dev(x["b"]),
+                        dev(x["A_log"]), dev(x["dt_bias"]), si, so, q_scale=128 ** -0.5,
+                        algo="chunked")
+    torch.cuda.synchronize()
+    al, be, _ = oracle.gates(to_f64(x["a"]), to_f64(x["b"]), x["A_log"], x["dt_bias"])
+    o_ref, S_ref = oracle.recurrence(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), al, be,
+                                     to_f64(x["state"]), q_scale=128 ** -0.5)
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(so), S_ref) < TOL
+
+
+def test_chunked_deterministic_and_matches_sequential():
+    banner("chunked determinism and chunked ~ sequential")
+    x = recurrence_inputs(1, 257, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=24,
+                          state_std=0.05)
+    o1, S1 = _gpu_prefill(x, x["state"])
+    o2, S2 = _gpu_prefill(x, x["state"])
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    o3, S3 = _gpu_prefill(x, x["state"], algo="sequential")
+    assert max_rel_err(host_f64(o1), host_f64(o3)) < TOL
+    assert max_rel_err(host_f64(S1), host_f64(S3)) < TOL
+
+
+def test_split_calls_with_state_handoff():
+    banner("chunked 3 calls with handoff vs one oracle pass")
+    x = recurrence_inputs(1, 300, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=25,
+                          state_std=0.05, A_log_range=(-5.0, -2.0))
+    S = dev(x["state"])
+    outs = []
+    for t0, t1 in ((0, 64), (64, 130), (130, 300)):
+        part = {n: (x[n][:, t0:t1] if n in ("q", "k", "v", "a", "b") else x[n]) for n in x}
+        o = gdn.gdn_prefill(dev(part["q"]), dev(part["k"]), dev(part["v"]), dev(part["a"]),
+                            dev(part["b"]), dev(x["A_log"]), dev(x["dt_bias"]), S, S,
+                            algo="chunked")
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    assert max_rel_err(host_f64(torch.cat(outs, dim=1)), o_ref) < TOL
+    assert max_rel_err(host_f64(S), S_ref) < TOL
+
+
+def test_decode_rows_equals_prefill_of_one_token():
+    banner("decode_rows == prefill T=1")
+    x = decode_inputs(3, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=26)
+    st = dev(x["state"])
+    od = gdn.gdn_decode_rows(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["a"]), dev(x["b"]),
+                             dev(x["A_log"]), dev(x["dt_bias"]), st)
+    so = torch.empty_like(st)
+    op = gdn.gdn_prefill(dev(x["q"])[:, None], dev(x["k"])[:, None], dev(x["v"])[:, None],
+                         dev(x["a"])[:, None], dev(x["b"])[:, None], dev(x["A_log"]),
+                         dev(x["dt_bias"]), dev(x["state"]), so, algo="sequential")
+    torch.cuda.synchronize()
+    assert max_rel_err(host_f64(od), host_f64(op[:, 0])) < 1e-2
+    assert max_rel_err(host_f64(st), host_f64(so)) < 1e-5
+
+
+def test_prefill_bf16_b1_t4096():
+    """The prefill workload at full size: B=1, T=4096, chunk 64, 16/48 heads,
+    bf16 q/k/v, f32 gates, carried state ~N(0, 0.05)."""
+    banner("prefill_bf16_b1_t4096 full")
+    x = make_workload("prefill_bf16_b1_t4096")
+    o, S = _gpu_prefill(x, x["state"], algo="auto")
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    e_o, e_s = max_rel_err(host_f64(o), o_ref), max_rel_err(host_f64(S), S_ref)
+    print(f"prefill_bf16_b1_t4096: o err {e_o:.3e}, state err {e_s:.3e}")
+    assert e_o < TOL and e_s < TOL
