@@ -1,0 +1,265 @@
+"""Benchmark of the Gated DeltaNet mixer hot path on one MI355X.
+
+One step = one pass of the whole hot path on seeded synthetic inputs shaped
+like the model's layer (16 q/k heads, 48 value heads, width 128):
+  1. the layer prefill at B=1, T=4096: gdn_conv_silu (10240 channels, width 4,
+     silu, L2 of q/k) -> gdn_prefill (chunked, state carried in and out,
+     q/k/v read as strided views of the conv output) -> gdn_gated_rmsnorm;
+  2. gdn_prefill alone on the prefill workload (B=1, T=4096, bf16 q/k/v, f32
+     gates, carried state ~N(0, 0.05), chunk 64);
+  3. gdn_decode_rows on 64 fixed rows (state [64,48,128,128] f32, in place).
+Each part is timed with HIP events on the stream it runs on.  The inputs of
+every part rotate over three independent buffer sets so that the 256 MB
+last-level cache cannot hold a part's working set between its launches.
+
+Printed: one JSON line.  value = tokens/s of part 2 (the prefill workload);
+decode_rows state GB/s and the layer-prefill tokens/s ride along in the same
+line, with the roofline of the dominant kernel and the f64 oracle timed on the
+host cores as a CPU baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+ROT = 3                       # buffer sets rotated between steps
+
+HK, HV, D, T_PREFILL, R_DECODE = 16, 48, 128, 4096, 64
+C_CONV = 2 * HK * D + HV * D
+
+
+def decode_bytes_per_launch(R=R_DECODE, Hk=HK, Hv=HV, d=D, io_bytes=2, gate_bytes=2):
+    """Algorithmic HBM bytes of one decode_rows launch: the f32 state read and
+    written once, q/k/v/a/b read, o written, lengths read."""
+    state = 2 * R * Hv * d * d * 4
+    qkv = R * (2 * Hk * d + Hv * d) * io_bytes
+    gates = 2 * R * Hv * gate_bytes
+    out = R * Hv * d * io_bytes
+    return state + qkv + gates + out + R * 4 + 2 * Hv * 4
+
+
+def prefill_flops_per_launch(T=T_PREFILL, Hv=HV, d=D, C=64):
+    """Algorithmic flops of the chunked form per launch: per chunk and value
+    head K K^T, Q K^T, W, U~ (2 C^2 d each ... ) and the chain products
+    W H, Q H, K^T U (2 C d^2 each) plus P U (2 C^2 d): 2(5 C^2 d + 3 C d^2)."""
+    nc = (T + C - 1) // C
+    return nc * Hv * 2 * (5 * C * C * d + 3 * C * d * d)
+
+
+def prefill_bytes_per_launch(T=T_PREFILL, Hk=HK, Hv=HV, d=D):
+    """Algorithmic HBM bytes of one prefill call: q, k, v read and o written
+    (bf16), a, b read (f32), state read and written (f32)."""
+    return (2 * T * Hk * d + 2 * T * Hv * d) * 2 + 2 * T * Hv * 4 + 2 * Hv * d * d * 4
+
+
+def _src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_deltanet_mixer_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_files, launches_bytes_fn=None):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("src_hash") != _src_hash(src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(seconds_hint=30.0):
+    """The f64 oracle (as it stands) on the prefill workload: gates plus the
+    token-by-token recurrence over all 48 value heads of B=1, T=4096, on the
+    host's cores.  Returns the JSON object."""
+    import numpy as np
+    import oracle
+    from synth import make_workload, to_f64
+    x = make_workload("prefill_bf16_b1_t4096")
+    q, k, v = (to_f64(x[n]) for n in "qkv")
+    a, b = to_f64(x["a"]), to_f64(x["b"])
+    S0 = to_f64(x["state"])
+    t0 = time.perf_counter()
+    al, be, _ = oracle.gates(a, b, x["A_log"], x["dt_bias"])
+    oracle.recurrence(q, k, v, al, be, S0)
+    dt = time.perf_counter() - t0
+    return {"value": T_PREFILL / dt, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "whole prefill workload once: B=1, T=4096, 48 value heads, f64 gates + "
+                      "sequential recurrence (OpenMP over heads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the mixer shards "
+              "by heads with no exchange inside it, so multi-GPU figures are not measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_mixer_amd as gdn
+    from synth import decode_inputs, make_workload, mixer_inputs, recurrence_inputs
+    from synth.torch_io import dev
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    gdn.lib()
+
+    # ---- inputs (seeded; each part's buffers replicated ROT times)
+    mx = mixer_inputs(1, T_PREFILL, seed=2003)
+    st_layer = recurrence_inputs(1, 1, seed=2004, state_std=0.05)["state"]
+    layer = []
+    for _ in range(ROT):
+        layer.append({
+            "qkv": dev(mx["qkv"]), "z": dev(mx["z"]), "a": dev(mx["a"]), "b": dev(mx["b"]),
+            "conv_w": dev(mx["conv_w"]), "A_log": dev(mx["A_log"]), "dt_bias": dev(mx["dt_bias"]),
+            "norm_w": dev(mx["norm_w"]), "state": dev(st_layer),
+            "conv_state": torch.zeros((1, 3, C_CONV), dtype=torch.float32, device="cuda"),
+            "y": torch.empty((1, T_PREFILL, C_CONV), dtype=torch.bfloat16, device="cuda"),
+            "o": torch.empty((1, T_PREFILL, HV, D), dtype=torch.bfloat16, device="cuda"),
+            "out": torch.empty((1, T_PREFILL, HV, D), dtype=torch.bfloat16, device="cuda"),
+        })
+    px = make_workload("prefill_bf16_b1_t4096")
+    pre = []
+    for _ in range(ROT):
+        pre.append({n: dev(px[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state")})
+        pre[-1]["o"] = torch.empty((1, T_PREFILL, HV, D), dtype=torch.bfloat16, device="cuda")
+    dx = make_workload("decode_rows_r64")
+    dec = []
+    for _ in range(ROT):
+        dec.append({n: dev(dx[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state",
+                                            "lengths")})
+        dec[-1]["o"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = gdn.gdn_prefill_workspace_bytes(1, T_PREFILL, HK, HV)
+    ws = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(ROT)]
+
+    def step(i, ev=None):
+        s = i % ROT
+        L, P, Dd = layer[s], pre[s], dec[s]
+        if ev is not None:
+            ev[0].record()
+        y = gdn.gdn_conv_silu(L["qkv"], L["conv_w"], L["conv_state"], l2_channels=2 * HK * D,
+                              head_dim=D, y=L["y"])
+        q = y[:, :, :HK * D].unflatten(2, (HK, D))
+        k = y[:, :, HK * D:2 * HK * D].unflatten(2, (HK, D))
+        v = y[:, :, 2 * HK * D:].unflatten(2, (HV, D))
+        if ev is not None:
+            ev[1].record()
+        gdn.gdn_prefill(q, k, v, L["a"], L["b"], L["A_log"], L["dt_bias"], L["state"], L["state"],
+                        o=L["o"], workspace=ws[s])
+        if ev is not None:
+            ev[2].record()
+        gdn.gdn_gated_rmsnorm(L["o"], L["z"].view(1, T_PREFILL, HV, D), L["norm_w"], y=L["out"])
+        if ev is not None:
+            ev[3].record()
+        gdn.gdn_prefill(P["q"], P["k"], P["v"], P["a"], P["b"], P["A_log"], P["dt_bias"],
+                        P["state"], P["state"], o=P["o"], workspace=ws[s])
+        if ev is not None:
+            ev[4].record()
+        gdn.gdn_decode_rows(Dd["q"], Dd["k"], Dd["v"], Dd["a"], Dd["b"], Dd["A_log"],
+                            Dd["dt_bias"], Dd["state"], Dd["lengths"], o=Dd["o"])
+        if ev is not None:
+            ev[5].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)]
+                      for i in range(args.steps)])  # ms
+    mean = parts.mean(axis=0)
+    t_conv, t_lpre, t_norm, t_pre, t_dec = mean
+    ms_per_step = wall * 1e3 / args.steps
+
+    prefill_tps = T_PREFILL / (t_pre * 1e-3)
+    layer_tps = T_PREFILL / ((t_conv + t_lpre + t_norm) * 1e-3)
+    dec_bytes = decode_bytes_per_launch()
+    state_bytes = 2 * R_DECODE * HV * D * D * 4
+    dec_gbps = state_bytes / (t_dec * 1e-3) / 1e9
+
+    # Dominant kernel of the step: decode_rows (HBM) vs the chunked prefill call (MFMA).
+    pre_flops = prefill_flops_per_launch()
+    if t_dec >= t_pre:
+        achieved = dec_bytes / (t_dec * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "decode_rows_kernel<bf16,bf16>",
+                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": _traffic("decode_rows", ["recurrent.hip", "common.hpp"]),
+                    "bytes_per_launch": dec_bytes, "avg_launch_us": round(t_dec * 1e3, 2)}
+    else:
+        achieved = pre_flops / (t_pre * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "gdn_prefill chunked (chunk_prep + chunk_chain)",
+                    "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "traffic": _traffic("prefill_chunked", ["chunk_prefill.hip", "common.hpp"]),
+                    "flops_per_launch": pre_flops, "avg_launch_us": round(t_pre * 1e3, 2)}
+
+    out = {
+        "metric": "GDN layer prefill tokens/s (T=4096) + decode_rows state GB/s at 64 rows",
+        "value": round(prefill_tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_bf16_b1_t4096", "B": 1, "T": T_PREFILL, "chunk": 64,
+                   "qk_heads": HK, "v_heads": HV, "head_dim": D,
+                   "step": "layer prefill (conv+silu+L2 -> chunked prefill -> gated RMSNorm) "
+                           "at B=1 T=4096, prefill workload at B=1 T=4096, decode_rows at 64 "
+                           "rows"},
+        "decode_rows": {"value": round(dec_gbps, 1), "unit": "GB/s (state bytes read+written)",
+                        "workload": "decode_rows_r64", "avg_launch_us": round(t_dec * 1e3, 2),
+                        "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4)},
+        "layer_prefill": {"value": round(layer_tps, 1), "unit": "tokens/s",
+                          "workload": "conv+silu+L2 -> chunked prefill -> gated RMSNorm, B=1 "
+                                      "T=4096, 10240 conv channels",
+                          "conv_us": round(t_conv * 1e3, 2), "prefill_us": round(t_lpre * 1e3, 2),
+                          "norm_us": round(t_norm * 1e3, 2)},
+        "prefill": {"avg_launch_us": round(t_pre * 1e3, 2),
+                    "mfma_tflops": round(pre_flops / (t_pre * 1e-3) / 1e12, 2),
+                    "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9,
+                                                  1)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,12 +44,12 @@ def lib():
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         L.gdn_abi_version.restype = ctypes.c_int
-        L.gdn_conv_silu.argtypes = [P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, P]
+        L.gdn_conv_silu.argtypes = [P, i32, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, P]
         L.gdn_conv_silu.restype = ctypes.c_int
         L.gdn_prefill_workspace_bytes.argtypes = [i32, i32, gdn_dims, i32, i32]
         L.gdn_prefill_workspace_bytes.restype = sz
         L.gdn_prefill.argtypes = [P, i64, P, i64, P, i64, i32, P, P, i32, P, P, P, P, P, i32, i32,
-                                  gdn_dims, f32, i32, P, sz, P]
+                                  i32, gdn_dims, f32, i32, P, sz, P]
         L.gdn_prefill.restype = ctypes.c_int
         L.gdn_decode_rows.argtypes = [P, i64, P, i64, P, i64, i32, P, P, i32, P, P, P, P, P, i32,
                                       gdn_dims, f32, P]
@@ -109,18 +109,20 @@ def _tok_stride(t, heads, d):
     return t.stride(1)
 
 
-def gdn_conv_silu(x, w, conv_state=None, l2_channels=0, head_dim=128, l2_eps=1e-6, y=None):
+def gdn_conv_silu(x, w, conv_state=None, l2_channels=0, head_dim=128, l2_eps=1e-6, y=None,
+                  y_dtype=None):
     """Depthwise causal conv (width 4) + silu over x [B, T, C], optional L2 of
-    the first l2_channels channels per head; conv_state [B, 3, C] f32 in/out."""
+    the first l2_channels channels per head; conv_state [B, 3, C] f32 in/out.
+    y_dtype (default x.dtype) selects the output dtype when y is not given."""
     _need_cuda(x, w, conv_state, y)
     B, T, C = x.shape
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
     assert x.is_contiguous() and y.is_contiguous() and w.is_contiguous()
     if conv_state is not None:
         assert conv_state.is_contiguous() and conv_state.dtype == torch.float32
-    _check(lib().gdn_conv_silu(_ptr(x), _ptr(y), _dt(x), _ptr(w), _ptr(conv_state), B, T, C,
-                               w.shape[1], l2_channels, head_dim, l2_eps, _stream(x)),
+    _check(lib().gdn_conv_silu(_ptr(x), _dt(x), _ptr(y), _dt(y), _ptr(w), _ptr(conv_state), B, T,
+                               C, w.shape[1], l2_channels, head_dim, l2_eps, _stream(x)),
            "gdn_conv_silu")
     return y
 
@@ -133,15 +135,16 @@ def gdn_prefill_workspace_bytes(B, T, Hk, Hv, dk=128, dv=128, qkv_dtype=torch.bf
 
 
 def gdn_prefill(q, k, v, a, b, A_log, dt_bias, state_in=None, state_out=None, o=None,
-                q_scale=1.0, algo="auto", workspace=None):
+                q_scale=1.0, algo="auto", workspace=None, o_dtype=None):
     """Gated delta rule over q, k [B,T,Hk,dk] and v [B,T,Hv,dv] (views with a
-    token stride are accepted), gates a, b [B,T,Hv].  Returns o [B,T,Hv,dv]."""
+    token stride are accepted), gates a, b [B,T,Hv].  Returns o [B,T,Hv,dv]
+    (dtype o_dtype, default v.dtype, when o is not given)."""
     _need_cuda(q, k, v, a, b, A_log, dt_bias, state_in, state_out, o, workspace)
     B, T, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
     qs, ks, vs = _tok_stride(q, Hk, dk), _tok_stride(k, Hk, dk), _tok_stride(v, Hv, dv)
     if o is None:
-        o = torch.empty((B, T, Hv, dv), dtype=v.dtype, device=v.device)
+        o = torch.empty((B, T, Hv, dv), dtype=o_dtype or v.dtype, device=v.device)
     assert o.is_contiguous() and a.is_contiguous() and b.is_contiguous()
     for s in (state_in, state_out):
         if s is not None:
@@ -152,7 +155,8 @@ def gdn_prefill(q, k, v, a, b, A_log, dt_bias, state_in=None, state_out=None, o=
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gdn_prefill(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _dt(q), _ptr(a), _ptr(b),
                              _dt(a), _ptr(A_log), _ptr(dt_bias), _ptr(state_in), _ptr(state_out),
-                             _ptr(o), B, T, gdn_dims(Hk, Hv, dk, dv), q_scale, _ALGOS[algo],
+                             _ptr(o), _dt(o), B, T, gdn_dims(Hk, Hv, dk, dv), q_scale,
+                             _ALGOS[algo],
                              _ptr(workspace), ws_bytes, _stream(q)),
            "gdn_prefill")
     return o

@@ -42,11 +42,11 @@ const char* gdn_status_str(int status) {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
-int gdn_conv_silu(const void* x, void* y, int32_t dt, const float* w, float* conv_state,
-                  int32_t B, int32_t T, int32_t C, int32_t W, int32_t l2_channels,
-                  int32_t head_dim, float l2_eps, void* stream) {
+int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const float* w,
+                  float* conv_state, int32_t B, int32_t T, int32_t C, int32_t W,
+                  int32_t l2_channels, int32_t head_dim, float l2_eps, void* stream) {
   if (!x || !y || !w) return GDN_ERR_NULL;
-  if (!dtype_ok(dt)) return GDN_ERR_DTYPE;
+  if (!dtype_ok(x_dt) || !dtype_ok(y_dt)) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || C <= 0 || W < 1 || l2_channels < 0 || l2_channels > C)
     return GDN_ERR_SHAPE;
   if (W != 4) return GDN_ERR_UNSUPPORTED;
@@ -59,13 +59,15 @@ int gdn_conv_silu(const void* x, void* y, int32_t dt, const float* w, float* con
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16) ||
       (conv_state && !aligned(conv_state, 16)))
     return GDN_ERR_ALIGN;
-  const size_t bytes = (size_t)B * T * C * dsize(dt);
+  const size_t xbytes = (size_t)B * T * C * dsize(x_dt);
+  const size_t ybytes = (size_t)B * T * C * dsize(y_dt);
   const char* xs = static_cast<const char*>(x);
   const char* ys = static_cast<const char*>(y);
-  if (bytes > 0 && xs < ys + bytes && ys < xs + bytes) return GDN_ERR_SHAPE;  // y overlaps x
+  if (xbytes > 0 && xs < ys + ybytes && ys < xs + xbytes) return GDN_ERR_SHAPE;  // y overlaps x
   if (B == 0 || T == 0) return GDN_OK;
-  return launch_status(gdn::launch_conv_silu(x, y, dt, w, conv_state, B, T, C, l2_channels,
-                                             l2_eps, static_cast<hipStream_t>(stream)));
+  return launch_status(gdn::launch_conv_silu(x, x_dt, y, y_dt, w, conv_state, B, T, C,
+                                             l2_channels, l2_eps,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t qkv_dt,
@@ -79,11 +81,12 @@ size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t 
 int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
                 const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
                 const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
-                const float* state_in, float* state_out, void* o, int32_t B, int32_t T,
-                gdn_dims dims, float q_scale, int32_t algo, void* workspace,
+                const float* state_in, float* state_out, void* o, int32_t o_dt, int32_t B,
+                int32_t T, gdn_dims dims, float q_scale, int32_t algo, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !o) return GDN_ERR_NULL;
-  if (!dtype_ok(qkv_dt) || !dtype_ok(gate_dt)) return GDN_ERR_DTYPE;
+  if (!A_log || !dt_bias) return GDN_ERR_NULL;
+  if (T != 0 && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_NULL;  // T == 0 reads none
+  if (!dtype_ok(qkv_dt) || !dtype_ok(gate_dt) || !dtype_ok(o_dt)) return GDN_ERR_DTYPE;
   if (algo != GDN_ALGO_AUTO && algo != GDN_ALGO_SEQUENTIAL && algo != GDN_ALGO_CHUNKED)
     return GDN_ERR_SHAPE;
   int st = check_dims(dims);
@@ -101,7 +104,6 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
       (state_out && !aligned(state_out, 16)))
     return GDN_ERR_ALIGN;
   const bool chunked = algo == GDN_ALGO_CHUNKED || (algo == GDN_ALGO_AUTO && qkv_dt == GDN_BF16);
-  if (chunked && qkv_dt != GDN_BF16) return GDN_ERR_DTYPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0) return GDN_OK;
   if (chunked && T > 0) {
@@ -109,13 +111,13 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
     return launch_status(gdn::launch_prefill_chunked(
-        q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, a, b, gate_dt, A_log, dt_bias,
-        state_in, state_out, o, B, T, Hk, Hv, q_scale, workspace, s));
+        q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, a, b, gate_dt, A_log, dt_bias,
+        state_in, state_out, o, o_dt, B, T, Hk, Hv, q_scale, workspace, s));
   }
   // Sequential algorithm (also the T == 0 state pass-through).
   return launch_status(gdn::launch_prefill_sequential(
       q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, a, b, gate_dt, A_log, dt_bias,
-      state_in, state_out, o, B, T, Hk, Hv, q_scale, s));
+      state_in, state_out, o, o_dt, B, T, Hk, Hv, q_scale, s));
 }
 
 int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,

@@ -1,5 +1,5 @@
-// Chunked prefill of the gated delta rule on bf16 MFMA (gfx950), for bf16
-// q/k/v.  The rule ("Qwen3.8 27B" model card, Gated DeltaNet bullet):
+// Chunked prefill of the gated delta rule on bf16 MFMA (gfx950).  The rule
+// ("Qwen3.8 27B" model card, Gated DeltaNet bullet):
 //   S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t.
 //
 // Chunk form (exact in exact arithmetic).  For a chunk of n <= 64 tokens with
@@ -14,19 +14,24 @@
 //
 // Two kernels:
 //  * chunk_prep: one wave per (batch, value head, chunk), fully parallel.
-//    Gates and their prefix sum, K K^T and Q K^T on MFMA, the unit lower
-//    triangular inverse by column forward substitution in f32 (lane j owns
-//    column j), then W and Ut on MFMA.  Writes W, Ut^T, P = q_scale M o QK^T,
-//    G and (once per q/k head) K^T to the workspace, all bf16 except G.
+//    Gates and their prefix sum; K K^T and Q K^T on MFMA; T by blocks: the
+//    four 16x16 diagonal blocks by forward substitution in f32, the six
+//    off-diagonal blocks by three levels of 16x16x16 MFMA products; then W
+//    and Ut on MFMA.  Writes W, Ut^T, P = q_scale M o QK^T, G and (once per
+//    q/k head) K^T to the workspace, all bf16 except G.  With f32 q/k, Q K^T
+//    is formed from a two-term bf16 split of both operands: q . k is small
+//    next to |q||k| (unit vectors in 128 dimensions), so it needs more than
+//    bf16 operand precision; no other product does.
 //  * chunk_chain: one workgroup per (batch, value head, 32-column slice of
 //    dv), sequential over chunks.  The f32 state slice lives in MFMA
-//    accumulator registers; its bf16 copy and U^T are staged in LDS.  The dv
-//    columns of H are independent, which is what allows the slicing.
+//    accumulator registers; its bf16 copy and U^T are staged in LDS; chunk
+//    c+1's operands are loaded while chunk c computes.  The dv columns of H
+//    are independent, which is what allows the slicing.
 //
-// MFMA operand layout (v_mfma_f32_16x16x32_bf16, checked on the device):
-// lane l holds A[l%16][8(l/16)..8(l/16)+7], B[8(l/16)..+7][l%16], and the
-// result D[4(l/16)+r][l%16], r = 0..3.  Every operand below is read as 16
-// contiguous bytes along the contraction index.
+// MFMA operand layouts (checked on the device): v_mfma_f32_16x16x32_bf16 --
+// lane l holds A[l%16][8(l/16)..+7], B[8(l/16)..+7][l%16]; the 16x16x16 form
+// holds A[l%16][4(l/16)..+3], B[4(l/16)..+3][l%16]; both give D[4(l/16)+r][l%16],
+// r = 0..3, which is also the 16x16x16 B layout, so its results chain.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -37,14 +42,33 @@ namespace {
 constexpr int CK = 64;   // chunk length
 constexpr int DH = 128;  // head width
 constexpr int XP = 72;   // pitch (bf16) of [*, 64] LDS tiles: 144-byte rows, 16-byte aligned
-constexpr int AP = 72;   // pitch (f32) of the A matrix rows
+constexpr int ADP = 20;  // pitch (f32) of the diagonal A blocks: 80-byte rows
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16k16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS operations,
+// not for its global loads and stores, so prefetched loads stay in flight.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Within one wave LDS operations complete in order; this only stops the
+// compiler from reordering LDS accesses across the point.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ s16x4 ld_frag4(const uint16_t* p) {
+  return *reinterpret_cast<const s16x4*>(p);
 }
 
 __device__ __forceinline__ bf16x8 zero_frag() {
@@ -54,10 +78,46 @@ __device__ __forceinline__ bf16x8 zero_frag() {
   return z;
 }
 
-__device__ __forceinline__ void st4bf(uint16_t* p, float a, float b, float c, float d) {
+// Element access goes through a whole-vector bit cast: a bit cast of one
+// element of a __bf16 vector does not select that element here.
+__device__ __forceinline__ u16x8 frag_bits(const bf16x8& f) {
+  return __builtin_bit_cast(u16x8, f);
+}
+
+// Eight consecutive q/k/v values as a bf16 operand (hi) and, for f32 input,
+// the bf16 rounding of the remainder (lo), so that hi + lo carries ~16 bits.
+__device__ __forceinline__ void load_row8(const uint16_t* p, bf16x8& hi, bf16x8& lo) {
+  hi = ld_frag(p);
+  lo = zero_frag();
+}
+__device__ __forceinline__ void load_row8(const float* p, bf16x8& hi, bf16x8& lo) {
+  float x[8];
+  load8(p, x);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)x[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(x[i] - (float)h);
+  }
+}
+
+__device__ __forceinline__ s16x4 to_s16x4(float a, float b, float c, float d) {
+  s16x4 r;
+  r[0] = (short)f2bf(a); r[1] = (short)f2bf(b); r[2] = (short)f2bf(c); r[3] = (short)f2bf(d);
+  return r;
+}
+
+template <typename TO>
+__device__ __forceinline__ void st4(TO* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void st4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
   u16x4 v;
   v[0] = f2bf(a); v[1] = f2bf(b); v[2] = f2bf(c); v[3] = f2bf(d);
   *reinterpret_cast<u16x4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
@@ -74,7 +134,7 @@ struct WsLayout {
   uint16_t* W;   // [B*Hv*NC][64 t][128 dk]
   uint16_t* Ut;  // [B*Hv*NC][128 dv][64 t]
   uint16_t* P;   // [B*Hv*NC][64 t][64 s]
-  float* G;      // [B*Hv*NC][64]
+  float* G;      // [B*Hv*NC][128]: G_t (t < 64), then G_last replicated 64 times
   uint16_t* Kt;  // [B*Hk*NC][128 dk][64 s]
 };
 
@@ -88,7 +148,7 @@ WsLayout ws_layout(void* base, int B, int T, int Hk, int Hv) {
   L.W = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * DH * 2);
   L.Ut = reinterpret_cast<uint16_t*>(p); p += align256(nch * DH * CK * 2);
   L.P = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * CK * 2);
-  L.G = reinterpret_cast<float*>(p);     p += align256(nch * CK * 4);
+  L.G = reinterpret_cast<float*>(p);     p += align256(nch * 2 * CK * 4);
   L.Kt = reinterpret_cast<uint16_t*>(p); p += align256(nck * DH * CK * 2);
   return L;
 }
@@ -99,20 +159,28 @@ size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
   const size_t NC = (size_t)(T + CK - 1) / CK;
   const size_t nch = (size_t)B * Hv * NC, nck = (size_t)B * Hk * NC;
   return align256(nch * CK * DH * 2) + align256(nch * DH * CK * 2) + align256(nch * CK * CK * 2) +
-         align256(nch * CK * 4) + align256(nck * DH * CK * 2);
+         align256(nch * 2 * CK * 4) + align256(nck * DH * CK * 2);
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1: per (batch, value head, chunk), one wave.
-template <typename G_T>
+// Phase 1: per (batch, value head, chunk), one wave.  No workgroup barriers:
+// one wave's LDS operations complete in order.
+template <typename TI, typename G_T>
 __global__ __launch_bounds__(64) void chunk_prep_kernel(
-    const uint16_t* __restrict__ q, int64_t q_ts, const uint16_t* __restrict__ k, int64_t k_ts,
-    const uint16_t* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
+    const TI* __restrict__ q, int64_t q_ts, const TI* __restrict__ k, int64_t k_ts,
+    const TI* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
     const G_T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     WsLayout ws, int T, int Hk, int Hv, int NC, float q_scale) {
-  __shared__ float Ab[CK * AP];                      // A (f32), later T b and T b gamma (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t XT[DH * XP];  // K^T, later V^T
+  constexpr bool kSplit = sizeof(TI) == 4;  // f32 q/k: two-term Q K^T
+  // Region R: first the A blocks (diagonal f32, off-diagonal bf16), then K^T,
+  // then V^T (bf16 [128][XP]).
+  __shared__ __attribute__((aligned(16))) uint16_t R[DH * XP];
+  __shared__ __attribute__((aligned(16))) uint16_t Tn[CK * XP];     // T, bf16, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t Tdt[4 * 16 * 16];  // diagonal blocks, transposed
   __shared__ float Gs[CK], Bs[CK];
+  float* Ad = reinterpret_cast<float*>(R);       // [4][16][ADP]
+  uint16_t* Ao = R + 4 * 16 * ADP * 2;           // [64][XP], off-diagonal blocks of A
+  uint16_t* XT = R;
 
   const int c = blockIdx.x % NC;
   const int bh = blockIdx.x / NC;
@@ -123,91 +191,213 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
   const int n = min(CK, T - t0);
   const int64_t chunk = (int64_t)bh * NC + c;
 
-  // Gates for token `lane`; padding tokens get g = 0, b = 0.
-  float g = 0.0f, be = 0.0f;
+  const TI* kbase = k + ((int64_t)bb * T + t0) * k_ts + kh * DH;
+  const TI* qbase = q + ((int64_t)bb * T + t0) * q_ts + kh * DH;
+  const TI* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
+
+  // Every global load is issued here, before any use: the gate inputs, then
+  // all K, Q (and, for bf16 input, V) rows of the chunk as MFMA fragments
+  // (rows >= n are zero).
+  float a_raw = 0.0f, b_raw = 0.0f;
   if (lane < n) {
     const int64_t gi = ((int64_t)bb * T + t0 + lane) * Hv + h;
-    g = gate_log_alpha(load1(a + gi), A_log[h], dt_bias[h]);
-    be = gate_beta(load1(b + gi));
+    a_raw = load1(a + gi);
+    b_raw = load1(b + gi);
   }
-  const float Gl = wave_scan(g, lane);
-  Gs[lane] = Gl;
-  Bs[lane] = be;
-  ws.G[chunk * CK + lane] = Gl;
-
-  const uint16_t* kbase = k + ((int64_t)bb * T + t0) * k_ts + kh * DH;
-  const uint16_t* qbase = q + ((int64_t)bb * T + t0) * q_ts + kh * DH;
-  const uint16_t* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
-
-  // K^T into LDS: lane = token s, 16 passes over 8-channel groups.
-#pragma unroll 4
-  for (int gi = 0; gi < 16; ++gi) {
-    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (lane < n) x = *reinterpret_cast<const u16x8*>(kbase + (int64_t)lane * k_ts + gi * 8);
+  bf16x8 kf[4][4], qf[4][4], kl[4][4], ql[4][4];  // [row block][k step]; kl/ql: split low parts
+  bf16x8 vf[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) XT[(gi * 8 + i) * XP + lane] = x[i];
+  for (int rb = 0; rb < 4; ++rb) {
+    const int t = rb * 16 + li;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (t < n) {
+        load_row8(kbase + (int64_t)t * k_ts + kk * 32 + lg * 8, kf[rb][kk], kl[rb][kk]);
+        load_row8(qbase + (int64_t)t * q_ts + kk * 32 + lg * 8, qf[rb][kk], ql[rb][kk]);
+      } else {
+        kf[rb][kk] = zero_frag(); kl[rb][kk] = zero_frag();
+        qf[rb][kk] = zero_frag(); ql[rb][kk] = zero_frag();
+      }
+    }
   }
-
-  // K K^T and Q K^T (transposed) on MFMA, then A and P.
-  {
-    bf16x8 kf[4][4], qf[4][4];  // [row block][k step]
+  auto load_v = [&]() {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       const int t = rb * 16 + li;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        if (t < n) {
-          kf[rb][kk] = ld_frag(kbase + (int64_t)t * k_ts + kk * 32 + lg * 8);
-          qf[rb][kk] = ld_frag(qbase + (int64_t)t * q_ts + kk * 32 + lg * 8);
-        } else {
-          kf[rb][kk] = zero_frag();
-          qf[rb][kk] = zero_frag();
-        }
+        bf16x8 unused;
+        if (t < n) load_row8(vbase + (int64_t)t * v_ts + kk * 32 + lg * 8, vf[rb][kk], unused);
+        else vf[rb][kk] = zero_frag();
       }
     }
-    __syncthreads();  // Gs, Bs visible
+  };
+  if (!kSplit) load_v();  // f32 input: later, to bound register pressure
+
+  // Gates for token `lane`; padding tokens get g = 0, b = 0.
+  float g = 0.0f, be = 0.0f;
+  if (lane < n) {
+    g = gate_log_alpha(a_raw, A_log[h], dt_bias[h]);
+    be = gate_beta(b_raw);
+  }
+  const float Gl = wave_scan(g, lane);
+  Gs[lane] = Gl;
+  Bs[lane] = be;
+  ws.G[chunk * 2 * CK + lane] = Gl;
+  ws.G[chunk * 2 * CK + CK + lane] = __shfl(Gl, CK - 1);
+  wave_lds_fence();
+
+  // K K^T -> A (lower blocks only) and (Q K^T)^T -> P.
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+  for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        // KK tile [t block tb][s block sb]; only s <= t blocks are needed.
-        if (sb <= tb) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb <= tb; ++sb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc = mfma16(kf[tb][kk], kf[sb][kk], acc);
-          const int s = sb * 16 + li;
+      for (int kk = 0; kk < 4; ++kk) acc = mfma16(kf[tb][kk], kf[sb][kk], acc);
+      const int s = sb * 16 + li;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = tb * 16 + lg * 4 + r;
-            Ab[t * AP + s] = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * acc[r] : 0.0f;
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Ab[(tb * 16 + lg * 4 + r) * AP + sb * 16 + li] = 0.0f;
-        }
-        // (Q K^T)^T tile [s block sb][t block tb]: C[s][t] = K_s . Q_t.
-        f32x4 pq = {0.f, 0.f, 0.f, 0.f};
-        if (sb <= tb) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) pq = mfma16(kf[sb][kk], qf[tb][kk], pq);
-        }
-        const int t = tb * 16 + li;
-        float pv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = sb * 16 + lg * 4 + r;
-          pv[r] = (s <= t) ? q_scale * __expf(Gs[t] - Gs[s]) * pq[r] : 0.0f;
-        }
-        st4bf(ws.P + (chunk * CK + t) * CK + sb * 16 + lg * 4, pv[0], pv[1], pv[2], pv[3]);
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb * 16 + lg * 4 + r;
+        const float av = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * acc[r] : 0.0f;
+        if (sb == tb) Ad[(tb * 16 + lg * 4 + r) * ADP + li] = av;
+        else Ao[t * XP + s] = f2bf(av);
       }
+      // (Q K^T)^T tile [s block sb][t block tb]: C[s][t] = K_s . Q_t.
+      f32x4 pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        pq = mfma16(kf[sb][kk], qf[tb][kk], pq);
+        if (kSplit) {
+          pq = mfma16(kf[sb][kk], ql[tb][kk], pq);
+          pq = mfma16(kl[sb][kk], qf[tb][kk], pq);
+        }
+      }
+      const int tq = tb * 16 + li;
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int sq = sb * 16 + lg * 4 + r;
+        pv[r] = (sq <= tq) ? q_scale * __expf(Gs[tq] - Gs[sq]) * pq[r] : 0.0f;
+      }
+      st4<uint16_t>(ws.P + (chunk * CK + tq) * CK + sb * 16 + lg * 4, pv[0], pv[1], pv[2], pv[3]);
+    }
+    // Blocks above the diagonal of P are zero.
+#pragma unroll
+    for (int sb = tb + 1; sb < 4; ++sb)
+      st4<uint16_t>(ws.P + (chunk * CK + tb * 16 + li) * CK + sb * 16 + lg * 4, 0.f, 0.f, 0.f, 0.f);
+  }
+
+  if (kSplit) load_v();
+  wave_lds_fence();
+
+  // T, diagonal blocks: lane (block lg, column li), forward substitution over
+  // the block's 16 rows in f32.
+  {
+    float x[16];
+    const float* Ab = Ad + lg * 16 * ADP;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float acc = (t == li) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int s4 = 0; s4 < t; s4 += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(Ab + t * ADP + s4);
+        acc = fmaf(-a4.x, x[s4], acc);
+        if (s4 + 1 < t) acc = fmaf(-a4.y, x[s4 + 1], acc);
+        if (s4 + 2 < t) acc = fmaf(-a4.z, x[s4 + 2], acc);
+        if (s4 + 3 < t) acc = fmaf(-a4.w, x[s4 + 3], acc);
+      }
+      x[t] = acc;
+    }
+    u16x8 w0, w1;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const uint16_t xb = f2bf(x[t]);
+      Tn[(lg * 16 + t) * XP + lg * 16 + li] = xb;
+      if (t < 8) w0[t] = xb; else w1[t - 8] = xb;
+    }
+    *reinterpret_cast<u16x8*>(&Tdt[(lg * 16 + li) * 16]) = w0;
+    *reinterpret_cast<u16x8*>(&Tdt[(lg * 16 + li) * 16 + 8]) = w1;
+    // Zero the six blocks above the diagonal (16-byte pieces).
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const int idx = lane + 64 * m;  // 0..191
+      const int blk = idx >> 5, row = (idx & 31) >> 1, half = idx & 1;
+      const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+      const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+      *reinterpret_cast<u16x8*>(&Tn[(bi * 16 + row) * XP + bj * 16 + half * 8]) = z8;
     }
   }
-  __syncthreads();
+  wave_lds_fence();
+
+  // T, off-diagonal blocks: T_ij = -T_ii sum_{j<=m<i} A_im T_mj, level by level.
+  {
+    auto Aof = [&](int i, int j) { return ld_frag4(&Ao[(i * 16 + li) * XP + j * 16 + lg * 4]); };
+    auto Tdiag_b = [&](int j) { return ld_frag4(&Tdt[(j * 16 + li) * 16 + lg * 4]); };
+    auto Tdiag_a = [&](int i) { return ld_frag4(&Tn[(i * 16 + li) * XP + i * 16 + lg * 4]); };
+    auto finish = [&](int i, int j, const f32x4& xsum, s16x4& keep) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      y = mfma16k16(Tdiag_a(i), to_s16x4(xsum[0], xsum[1], xsum[2], xsum[3]), y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Tn[(i * 16 + lg * 4 + r) * XP + j * 16 + li] = f2bf(-y[r]);
+      keep = to_s16x4(-y[0], -y[1], -y[2], -y[3]);
+    };
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    s16x4 t10, t21, t32, t20, t31, t30;
+    finish(1, 0, mfma16k16(Aof(1, 0), Tdiag_b(0), z), t10);
+    finish(2, 1, mfma16k16(Aof(2, 1), Tdiag_b(1), z), t21);
+    finish(3, 2, mfma16k16(Aof(3, 2), Tdiag_b(2), z), t32);
+    finish(2, 0, mfma16k16(Aof(2, 1), t10, mfma16k16(Aof(2, 0), Tdiag_b(0), z)), t20);
+    finish(3, 1, mfma16k16(Aof(3, 2), t21, mfma16k16(Aof(3, 1), Tdiag_b(1), z)), t31);
+    finish(3, 0,
+           mfma16k16(Aof(3, 2), t20,
+                     mfma16k16(Aof(3, 1), t10, mfma16k16(Aof(3, 0), Tdiag_b(0), z))),
+           t30);
+    (void)t32; (void)t31; (void)t30;
+  }
+  wave_lds_fence();
+
+  // Column scales of T for W (b gamma) and Ut (b), for this lane's 16 s values.
+  float sg[2][8], sb8[2][8];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = kk * 32 + lg * 8 + i;
+      sb8[kk][i] = Bs[s];
+      sg[kk][i] = Bs[s] * __expf(Gs[s]);
+    }
+  // T diag(b gamma) rows, as B operands for W^T: [t block][k step].
+  bf16x8 tgf[4][2], tbf[4][2];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u16x8 raw = *reinterpret_cast<const u16x8*>(&Tn[(tb * 16 + li) * XP + kk * 32 + lg * 8]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float tv = bf2f(raw[i]);
+        tgf[tb][kk][i] = (__bf16)(tv * sg[kk][i]);
+        tbf[tb][kk][i] = (__bf16)(tv * sb8[kk][i]);
+      }
+    }
+
+  // K^T into LDS (the A blocks are no longer needed).
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u16x8 bits = frag_bits(kf[rb][kk]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) XT[(kk * 32 + lg * 8 + i) * XP + rb * 16 + li] = bits[i];
+    }
+  wave_lds_fence();
 
   // K^T to the workspace once per q/k head (the first value head of the group).
   if (h % grp == 0) {
     uint16_t* dst = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
-#pragma unroll 4
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int idx = i * 64 + lane;  // 16-byte piece: row idx/8, piece idx%8
       const int row = idx >> 3, pc = idx & 7;
@@ -216,72 +406,44 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
     }
   }
 
-  // T = (I + A)^{-1}: column j = lane, rows in order (unit lower triangular).
-  float Tc[CK];
-#pragma unroll
-  for (int t = 0; t < CK; ++t) {
-    float acc = (t == lane) ? 1.0f : 0.0f;
-#pragma unroll
-    for (int s4 = 0; s4 < t; s4 += 4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&Ab[t * AP + s4]);
-      acc = fmaf(-a4.x, Tc[s4], acc);
-      if (s4 + 1 < t) acc = fmaf(-a4.y, Tc[s4 + 1], acc);
-      if (s4 + 2 < t) acc = fmaf(-a4.z, Tc[s4 + 2], acc);
-      if (s4 + 3 < t) acc = fmaf(-a4.w, Tc[s4 + 3], acc);
-    }
-    Tc[t] = acc;
-  }
-  __syncthreads();  // every lane is done reading A
-  uint16_t* Tb = reinterpret_cast<uint16_t*>(Ab);  // [64][XP]: T diag(b)
-  uint16_t* Tg = Tb + CK * XP;                     // [64][XP]: T diag(b gamma)
-  {
-    const float bj = Bs[lane], gj = bj * __expf(Gs[lane]);
-#pragma unroll
-    for (int t = 0; t < CK; ++t) {
-      Tb[t * XP + lane] = f2bf(Tc[t] * bj);
-      Tg[t * XP + lane] = f2bf(Tc[t] * gj);
-    }
-  }
-  __syncthreads();
-
   // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T; stored as W[t][dk].
+  // T is lower triangular, so t blocks 0 and 1 need only s < 32.
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    bf16x8 kt0 = ld_frag(&XT[(db * 16 + li) * XP + lg * 8]);
-    bf16x8 kt1 = ld_frag(&XT[(db * 16 + li) * XP + 32 + lg * 8]);
+    const bf16x8 kt0 = ld_frag(&XT[(db * 16 + li) * XP + lg * 8]);
+    const bf16x8 kt1 = ld_frag(&XT[(db * 16 + li) * XP + 32 + lg * 8]);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(kt0, ld_frag(&Tg[(tb * 16 + li) * XP + lg * 8]), acc);
-      if (tb >= 2) acc = mfma16(kt1, ld_frag(&Tg[(tb * 16 + li) * XP + 32 + lg * 8]), acc);
+      acc = mfma16(kt0, tgf[tb][0], acc);
+      if (tb >= 2) acc = mfma16(kt1, tgf[tb][1], acc);
       const int t = tb * 16 + li, dk = db * 16 + lg * 4;
-      st4bf(ws.W + (chunk * CK + t) * DH + dk, acc[0], acc[1], acc[2], acc[3]);
+      st4<uint16_t>(ws.W + (chunk * CK + t) * DH + dk, acc[0], acc[1], acc[2], acc[3]);
     }
   }
-  __syncthreads();  // K^T reads done before V^T overwrites it
+  wave_lds_fence();
 
   // V^T into LDS.
-#pragma unroll 4
-  for (int gi = 0; gi < 16; ++gi) {
-    u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (lane < n) x = *reinterpret_cast<const u16x8*>(vbase + (int64_t)lane * v_ts + gi * 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) XT[(gi * 8 + i) * XP + lane] = x[i];
-  }
-  __syncthreads();
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u16x8 bits = frag_bits(vf[rb][kk]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) XT[(kk * 32 + lg * 8 + i) * XP + rb * 16 + li] = bits[i];
+    }
+  wave_lds_fence();
 
   // Ut tiles [t block][dv block] = (T diag(b)) V; stored transposed, Ut^T[dv][t].
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const bf16x8 tb0 = ld_frag(&Tb[(tb * 16 + li) * XP + lg * 8]);
-    const bf16x8 tb1 = ld_frag(&Tb[(tb * 16 + li) * XP + 32 + lg * 8]);
 #pragma unroll
     for (int vb = 0; vb < 8; ++vb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(tb0, ld_frag(&XT[(vb * 16 + li) * XP + lg * 8]), acc);
-      if (tb >= 2) acc = mfma16(tb1, ld_frag(&XT[(vb * 16 + li) * XP + 32 + lg * 8]), acc);
+      acc = mfma16(tbf[tb][0], ld_frag(&XT[(vb * 16 + li) * XP + lg * 8]), acc);
+      if (tb >= 2) acc = mfma16(tbf[tb][1], ld_frag(&XT[(vb * 16 + li) * XP + 32 + lg * 8]), acc);
       const int t = tb * 16 + lg * 4, dv = vb * 16 + li;
-      st4bf(ws.Ut + (chunk * DH + dv) * CK + t, acc[0], acc[1], acc[2], acc[3]);
+      st4<uint16_t>(ws.Ut + (chunk * DH + dv) * CK + t, acc[0], acc[1], acc[2], acc[3]);
     }
   }
 }
@@ -292,21 +454,21 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
 // rows [32w, 32w+32) of the state slice H.
 template <int NV>
 struct ChainFrags {
-  bf16x8 w[4];       // W rows of this wave's token block, 4 k steps over dk
-  bf16x8 qf[4];      // Q rows, same shape
-  u16x4 ut[NV / 16]; // Ut^T at the wave's U accumulator positions
-  bf16x8 p[2];       // P rows of this wave's token block, 2 k steps over s
-  bf16x8 kt[2][2];   // K^T rows (key block 2w+i), 2 k steps over s
-  float4 gu;         // G at the 4 token rows this lane's U accumulators hold
-  float gt;          // G at token 16w + (lane % 16)
-  float glast;       // G at the last token of the chunk
+  bf16x8 w[4];        // W rows of this wave's token block, 4 k steps over dk
+  bf16x8 qf[4];       // Q rows, same shape
+  u16x4 ut[NV / 16];  // Ut^T at the wave's U accumulator positions
+  bf16x8 p[2];        // P rows of this wave's token block, 2 k steps over s
+  bf16x8 kt[2][2];    // K^T rows (key block 2w+i), 2 k steps over s
+  float4 gu;          // G at the 4 token rows this lane's U accumulators hold
+  float gt;           // G at token 16w + (lane % 16)
+  float glast;        // G at the last token of the chunk
 };
 
-template <int NV>
+template <int NV, typename TI>
 __device__ __forceinline__ void load_chain_frags(ChainFrags<NV>& f, const WsLayout& ws,
-                                                 const uint16_t* __restrict__ q, int64_t q_ts,
-                                                 int bb, int bh, int kh, int c, int T, int Hk,
-                                                 int NC, int dv0, int w, int li, int lg) {
+                                                 const TI* __restrict__ q, int64_t q_ts, int bb,
+                                                 int bh, int kh, int c, int T, int Hk, int NC,
+                                                 int dv0, int w, int li, int lg) {
   const int64_t chunk = (int64_t)bh * NC + c;
   const int t0 = c * CK;
   const int n = min(CK, T - t0);
@@ -314,9 +476,12 @@ __device__ __forceinline__ void load_chain_frags(ChainFrags<NV>& f, const WsLayo
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) f.w[kk] = ld_frag(ws.W + (chunk * CK + tr) * DH + kk * 32 + lg * 8);
   if (tr < n) {
-    const uint16_t* qp = q + ((int64_t)bb * T + t0 + tr) * q_ts + kh * DH + lg * 8;
+    const TI* qp = q + ((int64_t)bb * T + t0 + tr) * q_ts + kh * DH + lg * 8;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.qf[kk] = ld_frag(qp + kk * 32);
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 unused;
+      load_row8(qp + kk * 32, f.qf[kk], unused);
+    }
   } else {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) f.qf[kk] = zero_frag();
@@ -333,21 +498,20 @@ __device__ __forceinline__ void load_chain_frags(ChainFrags<NV>& f, const WsLayo
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
       f.kt[i][kk] = ld_frag(ktp + ((2 * w + i) * 16 + li) * CK + kk * 32 + lg * 8);
-  const float* gp = ws.G + chunk * CK;
+  const float* gp = ws.G + chunk * 2 * CK;
   f.gu = *reinterpret_cast<const float4*>(gp + w * 16 + lg * 4);
   f.gt = gp[tr];
-  f.glast = gp[CK - 1];
+  f.glast = gp[CK + (w * 16 + lg * 4 + li) % CK];  // replicated copy: a per-lane (vector) load
 }
 
-template <int NV>
+template <int NV, typename TI, typename TO>
 __global__ __launch_bounds__(256) void chunk_chain_kernel(
-    const uint16_t* __restrict__ q, int64_t q_ts, WsLayout ws, const float* state_in,
-    float* state_out, uint16_t* __restrict__ o, int B, int T, int Hk, int Hv, int NC,
-    float q_scale) {
+    const TI* __restrict__ q, int64_t q_ts, WsLayout ws, const float* state_in,
+    float* state_out, TO* __restrict__ o, int B, int T, int Hk, int Hv, int NC, float q_scale) {
   constexpr int NSL = DH / NV;  // slices per head
   constexpr int NVB = NV / 16;  // 16-column blocks per slice
   constexpr int SP = DH + 8;    // pitch of the bf16 state copy: 272-byte rows
-  __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * SP];  // S slice [dv][dk], bf16
+  __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * SP];   // S slice [dv][dk], bf16
   __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
   __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
 
@@ -374,17 +538,16 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
       } else {
         H[i][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      st4bf(&Sb[(vb * 16 + li) * SP + dk], H[i][vb][0], H[i][vb][1], H[i][vb][2], H[i][vb][3]);
+      st4<uint16_t>(&Sb[(vb * 16 + li) * SP + dk], H[i][vb][0], H[i][vb][1], H[i][vb][2],
+                    H[i][vb][3]);
     }
   }
 
-  ChainFrags<NV> cur;
-  load_chain_frags<NV>(cur, ws, q, q_ts, bb, bh, kh, 0, T, Hk, NC, dv0, w, li, lg);
-  __syncthreads();
-
-  for (int c = 0; c < NC; ++c) {
-    ChainFrags<NV> nxt;
-    if (c + 1 < NC) load_chain_frags<NV>(nxt, ws, q, q_ts, bb, bh, kh, c + 1, T, Hk, NC, dv0, w, li, lg);
+  // Software pipeline of depth two: chunk c+2's operands are loaded while
+  // chunk c computes.  Three named buffers and a loop unrolled by three keep
+  // every buffer in place, so no register copy forces an early wait; loads
+  // past the last chunk re-read it and are never used.
+  auto step = [&](const ChainFrags<NV>& cur, int c) {
     const int t0 = c * CK;
     const int n = min(CK, T - t0);
 
@@ -414,11 +577,11 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) u[r] = bf2f(cur.ut[vb][r]) - accU[vb][r];
         const int off = (vb * 16 + li) * XP + w * 16 + lg * 4;
-        st4bf(&Utl[off], u[0], u[1], u[2], u[3]);
-        st4bf(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
+        st4<uint16_t>(&Utl[off], u[0], u[1], u[2], u[3]);
+        st4<uint16_t>(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // (3) O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token
     // blocks 0 and 1 need only s < 32.
@@ -429,12 +592,13 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + lg * 8]), cur.p[0], acc);
-        if (w >= 2) acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), cur.p[1], acc);
+        if (w >= 2)
+          acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), cur.p[1], acc);
         if (tr < n) {
           const int dv = dv0 + vb * 16 + lg * 4;
-          uint16_t* op = o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv;
-          st4bf(op, fmaf(gq, accQ[vb][0], acc[0]), fmaf(gq, accQ[vb][1], acc[1]),
-                fmaf(gq, accQ[vb][2], acc[2]), fmaf(gq, accQ[vb][3], acc[3]));
+          TO* op = o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv;
+          st4<TO>(op, fmaf(gq, accQ[vb][0], acc[0]), fmaf(gq, accQ[vb][1], acc[1]),
+                  fmaf(gq, accQ[vb][2], acc[2]), fmaf(gq, accQ[vb][3], acc[3]));
         }
       }
     }
@@ -461,11 +625,29 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb)
-        st4bf(&Sb[(vb * 16 + li) * SP + (2 * w + i) * 16 + lg * 4], H[i][vb][0], H[i][vb][1],
-              H[i][vb][2], H[i][vb][3]);
-    __syncthreads();
-    if (c + 1 < NC) cur = nxt;
+        st4<uint16_t>(&Sb[(vb * 16 + li) * SP + (2 * w + i) * 16 + lg * 4], H[i][vb][0],
+                      H[i][vb][1], H[i][vb][2], H[i][vb][3]);
+    lds_barrier();
+  };
+  auto fill = [&](ChainFrags<NV>& f, int c) {
+    load_chain_frags<NV, TI>(f, ws, q, q_ts, bb, bh, kh, min(c, NC - 1), T, Hk, NC, dv0, w, li,
+                             lg);
+  };
+  ChainFrags<NV> f0, f1, f2;
+  fill(f0, 0);
+  fill(f1, 1);
+  lds_barrier();
+  int c = 0;
+  for (; c + 3 <= NC; c += 3) {
+    fill(f2, c + 2);
+    step(f0, c);
+    fill(f0, c + 3);
+    step(f1, c + 1);
+    fill(f1, c + 4);
+    step(f2, c + 2);
   }
+  if (c < NC) step(f0, c);
+  if (c + 1 < NC) step(f1, c + 1);
 
   if (state_out) {
 #pragma unroll
@@ -480,36 +662,73 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
   }
 }
 
-hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
-                                  const void* v, int64_t v_ts, const void* a, const void* b,
-                                  int gate_dt, const float* A_log, const float* dt_bias,
-                                  const float* state_in, float* state_out, void* o, int B, int T,
-                                  int Hk, int Hv, float q_scale, void* workspace,
-                                  hipStream_t stream) {
-  const int NC = (T + CK - 1) / CK;
-  const WsLayout ws = ws_layout(workspace, B, T, Hk, Hv);
-  const dim3 prep_grid((unsigned)((int64_t)B * Hv * NC));
-  if (gate_dt == 1) {
-    hipLaunchKernelGGL(chunk_prep_kernel<uint16_t>, prep_grid, dim3(64), 0, stream,
-                       (const uint16_t*)q, q_ts, (const uint16_t*)k, k_ts, (const uint16_t*)v,
-                       v_ts, (const uint16_t*)a, (const uint16_t*)b, A_log, dt_bias, ws, T, Hk,
-                       Hv, NC, q_scale);
-  } else {
-    hipLaunchKernelGGL(chunk_prep_kernel<float>, prep_grid, dim3(64), 0, stream,
-                       (const uint16_t*)q, q_ts, (const uint16_t*)k, k_ts, (const uint16_t*)v,
-                       v_ts, (const float*)a, (const float*)b, A_log, dt_bias, ws, T, Hk, Hv, NC,
-                       q_scale);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+namespace {
+
+template <typename TI, typename TG>
+void launch_prep(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const void* v,
+                 int64_t v_ts, const void* a, const void* b, const float* A_log,
+                 const float* dt_bias, const WsLayout& ws, int B, int T, int Hk, int Hv, int NC,
+                 float q_scale, hipStream_t stream) {
+  hipLaunchKernelGGL((chunk_prep_kernel<TI, TG>), dim3((unsigned)((int64_t)B * Hv * NC)), dim3(64),
+                     0, stream, (const TI*)q, q_ts, (const TI*)k, k_ts, (const TI*)v, v_ts,
+                     (const TG*)a, (const TG*)b, A_log, dt_bias, ws, T, Hk, Hv, NC, q_scale);
+}
+
+template <typename TI, typename TO>
+void launch_chain(const void* q, int64_t q_ts, const WsLayout& ws, const float* state_in,
+                  float* state_out, void* o, int B, int T, int Hk, int Hv, int NC, float q_scale,
+                  hipStream_t stream) {
   constexpr int NV = 32;
   constexpr int NSL = DH / NV;
   const int64_t heads = (int64_t)B * Hv;
   const int64_t groups = (heads + 7) / 8;  // ids are padded to whole XCD rounds
-  const dim3 chain_grid((unsigned)(groups * 8 * NSL));
-  hipLaunchKernelGGL(chunk_chain_kernel<NV>, chain_grid, dim3(256), 0, stream,
-                     (const uint16_t*)q, q_ts, ws, state_in, state_out, (uint16_t*)o, B, T, Hk, Hv,
-                     NC, q_scale);
+  hipLaunchKernelGGL((chunk_chain_kernel<NV, TI, TO>), dim3((unsigned)(groups * 8 * NSL)),
+                     dim3(256), 0, stream, (const TI*)q, q_ts, ws, state_in, state_out, (TO*)o, B,
+                     T, Hk, Hv, NC, q_scale);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
+                                  const void* v, int64_t v_ts, int qkv_dt, const void* a,
+                                  const void* b, int gate_dt, const float* A_log,
+                                  const float* dt_bias, const float* state_in, float* state_out,
+                                  void* o, int o_dt, int B, int T, int Hk, int Hv, float q_scale,
+                                  void* workspace, hipStream_t stream) {
+  const int NC = (T + CK - 1) / CK;
+  const WsLayout ws = ws_layout(workspace, B, T, Hk, Hv);
+  if (qkv_dt == 1) {
+    if (gate_dt == 1)
+      launch_prep<uint16_t, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T,
+                                      Hk, Hv, NC, q_scale, stream);
+    else
+      launch_prep<uint16_t, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk,
+                                   Hv, NC, q_scale, stream);
+  } else {
+    if (gate_dt == 1)
+      launch_prep<float, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk,
+                                   Hv, NC, q_scale, stream);
+    else
+      launch_prep<float, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk, Hv,
+                                NC, q_scale, stream);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (qkv_dt == 1) {
+    if (o_dt == 1)
+      launch_chain<uint16_t, uint16_t>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC,
+                                       q_scale, stream);
+    else
+      launch_chain<uint16_t, float>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC,
+                                    q_scale, stream);
+  } else {
+    if (o_dt == 1)
+      launch_chain<float, uint16_t>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC,
+                                    q_scale, stream);
+    else
+      launch_chain<float, float>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale,
+                                 stream);
+  }
   return hipGetLastError();
 }
 

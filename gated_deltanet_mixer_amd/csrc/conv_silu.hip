@@ -20,9 +20,9 @@ namespace gdn {
 constexpr int CONV_TB = 64;       // tokens per workgroup
 constexpr int CONV_THREADS = 256;  // 8 channels each -> 2048 channels per workgroup
 
-template <typename T>
+template <typename TX, typename TY>
 __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
-    const T* __restrict__ x, T* __restrict__ y, const float* __restrict__ w,
+    const TX* __restrict__ x, TY* __restrict__ y, const float* __restrict__ w,
     float* conv_state, int Tlen, int C, int l2_channels, float l2_eps) {
   const int b = blockIdx.z;
   const int t0 = blockIdx.y * CONV_TB;
@@ -30,8 +30,8 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
   const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
   if (c0 >= C) return;  // C % 8 == 0; a 16-lane head group is all in or all out
 
-  const T* xb = x + (int64_t)b * Tlen * C + c0;
-  T* yb = y + (int64_t)b * Tlen * C + c0;
+  const TX* xb = x + (int64_t)b * Tlen * C + c0;
+  TY* yb = y + (int64_t)b * Tlen * C + c0;
 
   float wt[4][8];
 #pragma unroll
@@ -112,17 +112,25 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
   }
 }
 
-hipError_t launch_conv_silu(const void* x, void* y, int dt, const float* w, float* conv_state,
-                            int B, int T, int C, int l2_channels, float l2_eps,
-                            hipStream_t stream) {
+template <typename TX, typename TY>
+static void launch_conv_t(const void* x, void* y, const float* w, float* conv_state, int B, int T,
+                          int C, int l2_channels, float l2_eps, hipStream_t stream) {
   dim3 grid((C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8), (T + CONV_TB - 1) / CONV_TB, B);
-  if (dt == 1) {
-    hipLaunchKernelGGL(conv_silu_kernel<uint16_t>, grid, dim3(CONV_THREADS), 0, stream,
-                       (const uint16_t*)x, (uint16_t*)y, w, conv_state, T, C, l2_channels, l2_eps);
-  } else {
-    hipLaunchKernelGGL(conv_silu_kernel<float>, grid, dim3(CONV_THREADS), 0, stream,
-                       (const float*)x, (float*)y, w, conv_state, T, C, l2_channels, l2_eps);
-  }
+  hipLaunchKernelGGL((conv_silu_kernel<TX, TY>), grid, dim3(CONV_THREADS), 0, stream,
+                     (const TX*)x, (TY*)y, w, conv_state, T, C, l2_channels, l2_eps);
+}
+
+hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const float* w,
+                            float* conv_state, int B, int T, int C, int l2_channels, float l2_eps,
+                            hipStream_t stream) {
+  if (x_dt == 1 && y_dt == 1)
+    launch_conv_t<uint16_t, uint16_t>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
+  else if (x_dt == 1)
+    launch_conv_t<uint16_t, float>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
+  else if (y_dt == 1)
+    launch_conv_t<float, uint16_t>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
+  else
+    launch_conv_t<float, float>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
   return hipGetLastError();
 }
 

@@ -7,8 +7,8 @@
 
 namespace gdn {
 
-hipError_t launch_conv_silu(const void* x, void* y, int dt, const float* w, float* conv_state,
-                            int B, int T, int C, int l2_channels, float l2_eps,
+hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const float* w,
+                            float* conv_state, int B, int T, int C, int l2_channels, float l2_eps,
                             hipStream_t stream);
 
 hipError_t launch_gated_rmsnorm(const void* x, const void* z, void* y, int dt, const float* w,
@@ -24,17 +24,17 @@ hipError_t launch_prefill_sequential(const void* q, int64_t q_ts, const void* k,
                                      const void* v, int64_t v_ts, int qkv_dt, const void* a,
                                      const void* b, int gate_dt, const float* A_log,
                                      const float* dt_bias, const float* state_in,
-                                     float* state_out, void* o, int B, int T, int Hk, int Hv,
-                                     float q_scale, hipStream_t stream);
+                                     float* state_out, void* o, int o_dt, int B, int T, int Hk,
+                                     int Hv, float q_scale, hipStream_t stream);
 
-// Chunked (WY/UT form) prefill for bf16 q/k/v.
+// Chunked (WY/UT form) prefill on bf16 MFMA.
 size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv);
 
 hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
-                                  const void* v, int64_t v_ts, const void* a, const void* b,
-                                  int gate_dt, const float* A_log, const float* dt_bias,
-                                  const float* state_in, float* state_out, void* o, int B, int T,
-                                  int Hk, int Hv, float q_scale, void* workspace,
-                                  hipStream_t stream);
+                                  const void* v, int64_t v_ts, int qkv_dt, const void* a,
+                                  const void* b, int gate_dt, const float* A_log,
+                                  const float* dt_bias, const float* state_in, float* state_out,
+                                  void* o, int o_dt, int B, int T, int Hk, int Hv, float q_scale,
+                                  void* workspace, hipStream_t stream);
 
 }  // namespace gdn

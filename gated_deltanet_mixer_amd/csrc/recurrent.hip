@@ -83,12 +83,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_rows_kernel(
 constexpr int SEQ_THREADS = 256;
 constexpr int SEQ_TT = 32;
 
-template <typename T, typename G>
+template <typename T, typename G, typename TO>
 __global__ __launch_bounds__(SEQ_THREADS) void recurrent_prefill_kernel(
     const T* __restrict__ q, int64_t q_ts, const T* __restrict__ k, int64_t k_ts,
     const T* __restrict__ v, int64_t v_ts, const G* __restrict__ a, const G* __restrict__ b,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
-    const float* state_in, float* state_out, T* __restrict__ o, int Tlen, int Hk, int Hv,
+    const float* state_in, float* state_out, TO* __restrict__ o, int Tlen, int Hk, int Hv,
     float q_scale) {
   __shared__ float ks[SEQ_TT][128];
   __shared__ float qs[SEQ_TT][128];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void recurrent_prefill_kernel(
   const T* vb = v + (int64_t)bb * Tlen * v_ts + h * 128 + blk * 16;
   const G* ab = a + (int64_t)bb * Tlen * Hv + h;
   const G* bbp = b + (int64_t)bb * Tlen * Hv + h;
-  T* obp = o + ((int64_t)bb * Tlen * Hv + h) * 128 + row;
+  TO* obp = o + ((int64_t)bb * Tlen * Hv + h) * 128 + row;
 
   for (int t0 = 0; t0 < Tlen; t0 += SEQ_TT) {
     const int n = min(SEQ_TT, Tlen - t0);
@@ -202,33 +202,48 @@ hipError_t launch_decode_rows(const void* q, int64_t q_rs, const void* k, int64_
   return hipGetLastError();
 }
 
-template <typename T, typename G>
+template <typename T, typename G, typename TO>
 static void launch_seq_t(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const void* v,
                          int64_t v_ts, const void* a, const void* b, const float* A_log,
                          const float* dt_bias, const float* state_in, float* state_out, void* o,
                          int B, int Tlen, int Hk, int Hv, float q_scale, hipStream_t stream) {
-  hipLaunchKernelGGL((recurrent_prefill_kernel<T, G>), dim3(B * Hv * 8), dim3(SEQ_THREADS), 0,
+  hipLaunchKernelGGL((recurrent_prefill_kernel<T, G, TO>), dim3(B * Hv * 8), dim3(SEQ_THREADS), 0,
                      stream, (const T*)q, q_ts, (const T*)k, k_ts, (const T*)v, v_ts, (const G*)a,
-                     (const G*)b, A_log, dt_bias, state_in, state_out, (T*)o, Tlen, Hk, Hv, q_scale);
+                     (const G*)b, A_log, dt_bias, state_in, state_out, (TO*)o, Tlen, Hk, Hv,
+                     q_scale);
+}
+
+template <typename T, typename G>
+static void launch_seq_o(int o_dt, const void* q, int64_t q_ts, const void* k, int64_t k_ts,
+                         const void* v, int64_t v_ts, const void* a, const void* b,
+                         const float* A_log, const float* dt_bias, const float* state_in,
+                         float* state_out, void* o, int B, int Tlen, int Hk, int Hv, float q_scale,
+                         hipStream_t stream) {
+  if (o_dt == 1)
+    launch_seq_t<T, G, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+                                 state_out, o, B, Tlen, Hk, Hv, q_scale, stream);
+  else
+    launch_seq_t<T, G, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+                              state_out, o, B, Tlen, Hk, Hv, q_scale, stream);
 }
 
 hipError_t launch_prefill_sequential(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
                                      const void* v, int64_t v_ts, int qkv_dt, const void* a,
                                      const void* b, int gate_dt, const float* A_log,
                                      const float* dt_bias, const float* state_in,
-                                     float* state_out, void* o, int B, int T, int Hk, int Hv,
-                                     float q_scale, hipStream_t stream) {
+                                     float* state_out, void* o, int o_dt, int B, int T, int Hk,
+                                     int Hv, float q_scale, hipStream_t stream) {
   if (qkv_dt == 1 && gate_dt == 1)
-    launch_seq_t<uint16_t, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
-                                     state_out, o, B, T, Hk, Hv, q_scale, stream);
+    launch_seq_o<uint16_t, uint16_t>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias,
+                                     state_in, state_out, o, B, T, Hk, Hv, q_scale, stream);
   else if (qkv_dt == 1)
-    launch_seq_t<uint16_t, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+    launch_seq_o<uint16_t, float>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
                                   state_out, o, B, T, Hk, Hv, q_scale, stream);
   else if (gate_dt == 1)
-    launch_seq_t<float, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+    launch_seq_o<float, uint16_t>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
                                   state_out, o, B, T, Hk, Hv, q_scale, stream);
   else
-    launch_seq_t<float, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
+    launch_seq_o<float, float>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
                                state_out, o, B, T, Hk, Hv, q_scale, stream);
   return hipGetLastError();
 }

@@ -60,8 +60,11 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 /* Prefill algorithm.  AUTO picks CHUNKED for bf16 q/k/v and SEQUENTIAL for
  * f32 q/k/v.  SEQUENTIAL runs the recurrence token by token in f32 (any
- * dtype).  CHUNKED (bf16 q/k/v only) uses the chunk-of-64 WY/UT form on
- * bf16 MFMA with f32 accumulation and an f32 state carried between chunks. */
+ * dtype; the f32 accuracy class).  CHUNKED uses the chunk-of-64 WY/UT form on
+ * bf16 MFMA with f32 accumulation and an f32 state carried between chunks
+ * (the bf16 accuracy class whatever the input dtype).  With f32 q/k it keeps
+ * them unrounded where it matters: Q K^T is formed from a two-term bf16 split
+ * of both operands, because q . k is small next to |q||k|. */
 typedef enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SEQUENTIAL = 1, GDN_ALGO_CHUNKED = 2 } gdn_algo;
 
 /* Head counts and widths: 16, 48, 128, 128 for the model's layer. */
@@ -82,7 +85,9 @@ int gdn_abi_version(void);
  * gdn_conv_silu -- depthwise causal conv + silu, optional per-head L2.
  * ("Qwen3.8 27B" card, Gated DeltaNet bullet; llm-arch-viz module tree:
  * conv1d 10240x1x4 without bias.)
- *   x, y        [B, T, C] in dtype `dt`; y must not overlap x.
+ *   x           [B, T, C] in dtype x_dt.
+ *   y           [B, T, C] in dtype y_dt (f32 output keeps the normalised q/k
+ *               unrounded for the recurrence); y must not overlap x.
  *   w           [C, W] f32; w[c][W-1] multiplies the current token,
  *               w[c][0] the input W-1 tokens back (cross-correlation).
  *   conv_state  [B, W-1, C] f32, in/out: the last W-1 inputs before this
@@ -94,9 +99,9 @@ int gdn_abi_version(void);
  * Constraints: W == 4; C % 8 == 0; l2_channels % head_dim == 0 and
  * l2_channels <= C; head_dim == 128 when l2_channels > 0; T == 0 is a no-op.
  */
-int gdn_conv_silu(const void* x, void* y, int32_t dt, const float* w, float* conv_state,
-                  int32_t B, int32_t T, int32_t C, int32_t W, int32_t l2_channels,
-                  int32_t head_dim, float l2_eps, void* stream);
+int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const float* w,
+                  float* conv_state, int32_t B, int32_t T, int32_t C, int32_t W,
+                  int32_t l2_channels, int32_t head_dim, float l2_eps, void* stream);
 
 /*
  * Bytes of device workspace gdn_prefill needs for these sizes and algorithm
@@ -118,20 +123,21 @@ size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t 
  *   A_log, dt_bias  [Hv] f32.
  *   state_in   [B, Hv, dv, dk] f32 (S row-major, dk fastest); NULL = zeros.
  *   state_out  [B, Hv, dv, dk] f32; NULL = not written; may equal state_in.
- *   o      [B, T, Hv, dv] contiguous in qkv_dt; o_t uses the state after
- *          token t's update.
+ *   o      [B, T, Hv, dv] contiguous in dtype o_dt; o_t uses the state
+ *          after token t's update.
  *   q_scale multiplies q (1.0 for the model's layer).
  *   algo   a gdn_algo value.
  *   workspace  device scratch of at least gdn_prefill_workspace_bytes(...)
  *          bytes (may be NULL when that is 0), 256-byte aligned.
- * Errors: GDN_ERR_WORKSPACE if the workspace is too small; GDN_ERR_DTYPE for
- * CHUNKED with f32 q/k/v.
+ * With T == 0 only the state passes through (state_out = state_in, or
+ * zeros); the token pointers may then be NULL.
+ * Errors: GDN_ERR_WORKSPACE if the workspace is too small.
  */
 int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
                 const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
                 const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
-                const float* state_in, float* state_out, void* o, int32_t B, int32_t T,
-                gdn_dims dims, float q_scale, int32_t algo, void* workspace,
+                const float* state_in, float* state_out, void* o, int32_t o_dt, int32_t B,
+                int32_t T, gdn_dims dims, float q_scale, int32_t algo, void* workspace,
                 size_t workspace_bytes, void* stream);
 
 /*

@@ -40,8 +40,8 @@ def _vp(x):
     return ctypes.c_void_p(x) if x else None
 
 
-def conv(x=P, y=2 * P, dt=1, w=3 * P, cs=None, B=1, T=8, C=1024, W=4, l2=0, hd=128):
-    return gdn.lib().gdn_conv_silu(_vp(x), _vp(y), dt, _vp(w), _vp(cs), B, T, C, W, l2, hd,
+def conv(x=P, y=2 * P, dt=1, ydt=1, w=3 * P, cs=None, B=1, T=8, C=1024, W=4, l2=0, hd=128):
+    return gdn.lib().gdn_conv_silu(_vp(x), dt, _vp(y), ydt, _vp(w), _vp(cs), B, T, C, W, l2, hd,
                                    1e-6, None)
 
 
@@ -49,6 +49,7 @@ def test_conv_validation():
     assert conv(x=0) == NULL
     assert conv(w=0) == NULL
     assert conv(dt=7) == DTYPE
+    assert conv(ydt=-1) == DTYPE
     assert conv(W=3) == UNSUP
     assert conv(W=0) == SHAPE
     assert conv(C=1020) == SHAPE
@@ -66,18 +67,18 @@ D16 = gdn_dims(16, 48, 128, 128)
 
 
 def prefill(q=P, qs=2048, k=2 * P, ks=2048, v=3 * P, vs=6144, qdt=1, a=4 * P, b=5 * P, gdt=0,
-            Al=6 * P, db=7 * P, si=None, so=None, o=8 * P, B=1, T=64, dims=D16, algo=0, ws=None,
-            wsb=0):
+            Al=6 * P, db=7 * P, si=None, so=None, o=8 * P, odt=1, B=1, T=64, dims=D16, algo=0,
+            ws=None, wsb=0):
     return gdn.lib().gdn_prefill(_vp(q), qs, _vp(k), ks, _vp(v), vs, qdt, _vp(a), _vp(b), gdt,
-                                 _vp(Al), _vp(db), _vp(si), _vp(so), _vp(o), B, T, dims, 1.0, algo,
-                                 _vp(ws), wsb, None)
+                                 _vp(Al), _vp(db), _vp(si), _vp(so), _vp(o), odt, B, T, dims, 1.0,
+                                 algo, _vp(ws), wsb, None)
 
 
 def test_prefill_validation():
     assert prefill(q=0) == NULL
     assert prefill(o=0) == NULL
     assert prefill(qdt=2) == DTYPE
-    assert prefill(qdt=0, algo=2) == DTYPE           # chunked needs bf16
+    assert prefill(odt=4) == DTYPE
     assert prefill(dims=gdn_dims(16, 40, 128, 128)) == SHAPE
     assert prefill(dims=gdn_dims(16, 48, 64, 64)) == UNSUP
     assert prefill(qs=1024) == SHAPE                 # stride shorter than the heads
@@ -93,6 +94,7 @@ def test_prefill_validation():
         assert prefill(ws=9 * P, wsb=need - 1) == WS
     assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 0, 0) == 0  # f32: sequential
     assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 1, 1) == 0
+    assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 0, 2) > 0   # chunked takes f32 too
 
 
 def decode(q=P, k=2 * P, v=3 * P, qdt=1, st=4 * P, o=5 * P, R=4, dims=D16, lengths=None):

@@ -55,6 +55,24 @@ def test_chunked_small(T, A_range, state):
     assert max_rel_err(host_f64(S), S_ref) < TOL
 
 
+@pytest.mark.parametrize("T", [64, 150])
+def test_chunked_f32_inputs_and_f32_output(T):
+    """The chunked algorithm on f32 q/k/v (bf16 MFMA operands, Q K^T from a
+    two-term split) with an f32 output: the bf16 accuracy class."""
+    banner(f"chunked f32 q/k/v T={T}")
+    x = recurrence_inputs(2, T, Hk=2, Hv=6, qkv_dt="f32", gate_dt="f32", seed=40 + T,
+                          state_std=0.05)
+    si = dev(x["state"])
+    so = torch.empty_like(si)
+    o = gdn.gdn_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["a"]), dev(x["b"]),
+                        dev(x["A_log"]), dev(x["dt_bias"]), si, so, algo="chunked")
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float32
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(so), S_ref) < TOL
+
+
 @pytest.mark.parametrize("gdt", ["bf16", "f32"])
 def test_chunked_gate_dtypes_and_inplace(gdt):
     banner(f"chunked in-place state, gates {gdt}")
