@@ -233,12 +233,17 @@ def main():
                 "flops_per_launch": pre_flops, "avg_launch_us": round(t_pre * 1e3, 2)}
     roofline, roofline_other = (roof_pre, roof_dec) if t_pre >= t_dec else (roof_dec, roof_pre)
 
+    copy_gbps = None
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
-        for _ in range(3):
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for i in range(3):
+            ce[i].record()
             dst.copy_(src)
+        ce[3].record()
         torch.cuda.synchronize()
+        copy_gbps = round(2 * src.numel() * 4 / (ce[1].elapsed_time(ce[3]) / 2 * 1e-3) / 1e9, 1)
 
     out = {
         "metric": "GDN layer prefill tokens/s (T=4096) + decode_rows state GB/s at 64 rows",
@@ -272,6 +277,7 @@ def main():
                                                   1)},
         "roofline": roofline,
         "roofline_other": roofline_other,
+        "copy_256MiB_GBps": copy_gbps,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

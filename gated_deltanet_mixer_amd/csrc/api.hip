@@ -55,7 +55,7 @@ int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const floa
     if (head_dim <= 0 || l2_channels % head_dim != 0) return GDN_ERR_SHAPE;
     if (head_dim != 128) return GDN_ERR_UNSUPPORTED;
   }
-  if (B > 65535 || (T + 63) / 64 > 65535) return GDN_ERR_SHAPE;
+  if (B > 65535 || (T + 7) / 8 > 65535) return GDN_ERR_SHAPE;  // grid limits (8-token blocks)
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16) ||
       (conv_state && !aligned(conv_state, 16)))
     return GDN_ERR_ALIGN;

@@ -10,14 +10,14 @@
 // Mapping: one thread owns 8 consecutive channels (one 16-byte bf16 load per
 // token) and walks CONV_TB consecutive tokens, keeping the previous 3 inputs
 // in registers, so every input element is read once (plus a 3-token halo per
-// block).  A 128-channel head is 16 lanes, so the L2 sum is a DPP row
+// block, mostly served from L2).  A 128-channel head is 16 lanes, so the L2 sum is a DPP row
 // reduction.  HBM-bound: one read of x and one write of y.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace gdn {
 
-constexpr int CONV_TB = 64;       // tokens per workgroup
+constexpr int CONV_TB = 8;        // tokens per workgroup (measured best of 8, 16, 32, 64)
 constexpr int CONV_THREADS = 256;  // 8 channels each -> 2048 channels per workgroup
 
 template <typename TX, typename TY>
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
   }
 
   const bool l2 = c0 < l2_channels;
-  constexpr int U = 4;
+  constexpr int U = 8;  // loads in flight per thread
   for (int t = t0; t < t1; t += U) {
     float xs[U][8];
 #pragma unroll

@@ -25,7 +25,8 @@ __device__ __forceinline__ float dot8(const float* a, const float* b) {
 // place.  One workgroup per (row, value head); wave w owns value rows
 // [32w, 32w+32); each 16-lane group owns one row per step, 8 steps, with all
 // 8 state loads in flight before any arithmetic.  HBM-bound: 64 KiB read and
-// 64 KiB written per (row, head).
+// 64 KiB written per (row, head).  (Non-temporal loads and stores measured
+// slower here.)
 constexpr int DEC_THREADS = 256;
 
 template <typename T, typename G>
