@@ -13,7 +13,7 @@
 // chunk carry g = 0, b = 0 and zero k/q/v, which leaves every formula exact.
 //
 // Two kernels:
-//  * chunk_prep: one wave per (batch, value head, chunk), fully parallel.
+//  * chunk_prep: four waves per (batch, value head, chunk), fully parallel.
 //    Gates and their prefix sum; K K^T and Q K^T on MFMA; T by blocks: the
 //    four 16x16 diagonal blocks by forward substitution in f32, the six
 //    off-diagonal blocks by three levels of 16x16x16 MFMA products; then W
@@ -24,9 +24,10 @@
 //    bf16 operand precision; no other product does.
 //  * chunk_chain: one workgroup per (batch, value head, 32-column slice of
 //    dv), sequential over chunks.  The f32 state slice lives in MFMA
-//    accumulator registers; its bf16 copy and U^T are staged in LDS; chunk
-//    c+1's operands are loaded while chunk c computes.  The dv columns of H
-//    are independent, which is what allows the slicing.
+//    accumulator registers of four compute waves; its bf16 copy and U^T are
+//    staged in LDS.  Four loader waves keep the next chunk's operands in a
+//    double-buffered LDS stage and the three after it in their registers.
+//    The dv columns of H are independent, which is what allows the slicing.
 //
 // MFMA operand layouts (checked on the device): v_mfma_f32_16x16x32_bf16 --
 // lane l holds A[l%16][8(l/16)..+7], B[8(l/16)..+7][l%16]; the 16x16x16 form
@@ -136,6 +137,15 @@ struct WsLayout {
   uint16_t* P;   // [B*Hv*NC][64 t][64 s]
   float* G;      // [B*Hv*NC][128]: G_t (t < 64), then G_last replicated 64 times
   uint16_t* Kt;  // [B*Hk*NC][128 dk][64 s]
+  uint16_t* Qb;  // [B*Hk*NC][64 t][128 dk]: bf16 Q, written only for f32 input
+};
+
+// bf16 Q rows as the chain reads them: element (b, q/k head, chunk, t, i) at
+// p + b*bs + h*hs + c*cs + t*ts + i -- either the bf16 input itself or the
+// workspace copy made from f32 input.
+struct QRows {
+  const uint16_t* p;
+  int64_t bs, hs, cs, ts;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -150,6 +160,7 @@ WsLayout ws_layout(void* base, int B, int T, int Hk, int Hv) {
   L.P = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * CK * 2);
   L.G = reinterpret_cast<float*>(p);     p += align256(nch * 2 * CK * 4);
   L.Kt = reinterpret_cast<uint16_t*>(p); p += align256(nck * DH * CK * 2);
+  L.Qb = reinterpret_cast<uint16_t*>(p); p += align256(nck * CK * DH * 2);
   return L;
 }
 
@@ -159,14 +170,17 @@ size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
   const size_t NC = (size_t)(T + CK - 1) / CK;
   const size_t nch = (size_t)B * Hv * NC, nck = (size_t)B * Hk * NC;
   return align256(nch * CK * DH * 2) + align256(nch * DH * CK * 2) + align256(nch * CK * CK * 2) +
-         align256(nch * 2 * CK * 4) + align256(nck * DH * CK * 2);
+         align256(nch * 2 * CK * 4) + align256(nck * DH * CK * 2) + align256(nck * CK * DH * 2);
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1: per (batch, value head, chunk), one wave.  No workgroup barriers:
-// one wave's LDS operations complete in order.
+// Phase 1: per (batch, value head, chunk), four waves.  Wave w owns token
+// block w (16 tokens) of every tile loop; the serial parts of the inverse run
+// on wave 0 while the others wait at LDS-only barriers.
+constexpr int PREP_THREADS = 256;
+
 template <typename TI, typename G_T>
-__global__ __launch_bounds__(64) void chunk_prep_kernel(
+__global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     const TI* __restrict__ q, int64_t q_ts, const TI* __restrict__ k, int64_t k_ts,
     const TI* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
     const G_T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
   const int bh = blockIdx.x / NC;
   const int h = bh % Hv, bb = bh / Hv;
   const int grp = Hv / Hk, kh = h / grp;
-  const int lane = threadIdx.x, li = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int t0 = c * CK;
   const int n = min(CK, T - t0);
   const int64_t chunk = (int64_t)bh * NC + c;
@@ -195,61 +209,61 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
   const TI* qbase = q + ((int64_t)bb * T + t0) * q_ts + kh * DH;
   const TI* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
 
-  // Every global load is issued here, before any use: the gate inputs, then
-  // all K, Q (and, for bf16 input, V) rows of the chunk as MFMA fragments
-  // (rows >= n are zero).
+  // Every global load is issued first.  Wave w needs K blocks 0..w (its K K^T
+  // and Q K^T tiles), Q block w and V block w; wave 0 the gate inputs.
   float a_raw = 0.0f, b_raw = 0.0f;
-  if (lane < n) {
+  if (w == 0 && lane < n) {
     const int64_t gi = ((int64_t)bb * T + t0 + lane) * Hv + h;
     a_raw = load1(a + gi);
     b_raw = load1(b + gi);
   }
-  bf16x8 kf[4][4], qf[4][4], kl[4][4], ql[4][4];  // [row block][k step]; kl/ql: split low parts
-  bf16x8 vf[4][4];
+  bf16x8 kf[4][4], kl[4][4], qf[4], ql[4], vf[4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int t = rb * 16 + li;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (t < n) {
+      if (rb <= w && t < n) {
         load_row8(kbase + (int64_t)t * k_ts + kk * 32 + lg * 8, kf[rb][kk], kl[rb][kk]);
-        load_row8(qbase + (int64_t)t * q_ts + kk * 32 + lg * 8, qf[rb][kk], ql[rb][kk]);
       } else {
-        kf[rb][kk] = zero_frag(); kl[rb][kk] = zero_frag();
-        qf[rb][kk] = zero_frag(); ql[rb][kk] = zero_frag();
+        kf[rb][kk] = zero_frag();
+        kl[rb][kk] = zero_frag();
       }
     }
   }
-  auto load_v = [&]() {
+  {
+    const int t = w * 16 + li;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int t = rb * 16 + li;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 unused;
-        if (t < n) load_row8(vbase + (int64_t)t * v_ts + kk * 32 + lg * 8, vf[rb][kk], unused);
-        else vf[rb][kk] = zero_frag();
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 unused;
+      if (t < n) {
+        load_row8(qbase + (int64_t)t * q_ts + kk * 32 + lg * 8, qf[kk], ql[kk]);
+        load_row8(vbase + (int64_t)t * v_ts + kk * 32 + lg * 8, vf[kk], unused);
+      } else {
+        qf[kk] = zero_frag(); ql[kk] = zero_frag(); vf[kk] = zero_frag();
       }
     }
-  };
-  if (!kSplit) load_v();  // f32 input: later, to bound register pressure
-
-  // Gates for token `lane`; padding tokens get g = 0, b = 0.
-  float g = 0.0f, be = 0.0f;
-  if (lane < n) {
-    g = gate_log_alpha(a_raw, A_log[h], dt_bias[h]);
-    be = gate_beta(b_raw);
   }
-  const float Gl = wave_scan(g, lane);
-  Gs[lane] = Gl;
-  Bs[lane] = be;
-  ws.G[chunk * 2 * CK + lane] = Gl;
-  ws.G[chunk * 2 * CK + CK + lane] = __shfl(Gl, CK - 1);
-  wave_lds_fence();
 
-  // K K^T -> A (lower blocks only) and (Q K^T)^T -> P.
+  // Gates for token `lane` (wave 0); padding tokens get g = 0, b = 0.
+  if (w == 0) {
+    float g = 0.0f, be = 0.0f;
+    if (lane < n) {
+      g = gate_log_alpha(a_raw, A_log[h], dt_bias[h]);
+      be = gate_beta(b_raw);
+    }
+    const float Gl = wave_scan(g, lane);
+    Gs[lane] = Gl;
+    Bs[lane] = be;
+    ws.G[chunk * 2 * CK + lane] = Gl;
+    ws.G[chunk * 2 * CK + CK + lane] = __shfl(Gl, CK - 1);
+  }
+  lds_barrier();
+
+  // Token block w: K K^T -> A (lower blocks), (Q K^T)^T -> P rows of block w.
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
+    if (tb != w) continue;
 #pragma unroll
     for (int sb = 0; sb <= tb; ++sb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -267,10 +281,10 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
       f32x4 pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        pq = mfma16(kf[sb][kk], qf[tb][kk], pq);
+        pq = mfma16(kf[sb][kk], qf[kk], pq);
         if (kSplit) {
-          pq = mfma16(kf[sb][kk], ql[tb][kk], pq);
-          pq = mfma16(kl[sb][kk], qf[tb][kk], pq);
+          pq = mfma16(kf[sb][kk], ql[kk], pq);
+          pq = mfma16(kl[sb][kk], qf[kk], pq);
         }
       }
       const int tq = tb * 16 + li;
@@ -287,13 +301,11 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
     for (int sb = tb + 1; sb < 4; ++sb)
       st4<uint16_t>(ws.P + (chunk * CK + tb * 16 + li) * CK + sb * 16 + lg * 4, 0.f, 0.f, 0.f, 0.f);
   }
+  lds_barrier();
 
-  if (kSplit) load_v();
-  wave_lds_fence();
-
-  // T, diagonal blocks: lane (block lg, column li), forward substitution over
-  // the block's 16 rows in f32.
-  {
+  // T, diagonal blocks (wave 0): lane (block lg, column li), forward
+  // substitution over the block's 16 rows in f32.
+  if (w == 0) {
     float x[16];
     const float* Ab = Ad + lg * 16 * ADP;
 #pragma unroll
@@ -318,21 +330,20 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
     }
     *reinterpret_cast<u16x8*>(&Tdt[(lg * 16 + li) * 16]) = w0;
     *reinterpret_cast<u16x8*>(&Tdt[(lg * 16 + li) * 16 + 8]) = w1;
-    // Zero the six blocks above the diagonal (16-byte pieces).
+  } else {
+    // Waves 1-3 zero the six blocks above the diagonal (192 16-byte pieces).
     const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const int idx = lane + 64 * m;  // 0..191
-      const int blk = idx >> 5, row = (idx & 31) >> 1, half = idx & 1;
-      const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-      const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-      *reinterpret_cast<u16x8*>(&Tn[(bi * 16 + row) * XP + bj * 16 + half * 8]) = z8;
-    }
+    const int idx = (w - 1) * 64 + lane;  // 0..191
+    const int blk = idx >> 5, row = (idx & 31) >> 1, half = idx & 1;
+    const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+    const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+    *reinterpret_cast<u16x8*>(&Tn[(bi * 16 + row) * XP + bj * 16 + half * 8]) = z8;
   }
-  wave_lds_fence();
+  lds_barrier();
 
-  // T, off-diagonal blocks: T_ij = -T_ii sum_{j<=m<i} A_im T_mj, level by level.
-  {
+  // T, off-diagonal blocks (wave 0): T_ij = -T_ii sum_{j<=m<i} A_im T_mj,
+  // level by level; each product's result feeds the next as a B operand.
+  if (w == 0) {
     auto Aof = [&](int i, int j) { return ld_frag4(&Ao[(i * 16 + li) * XP + j * 16 + lg * 4]); };
     auto Tdiag_b = [&](int j) { return ld_frag4(&Tdt[(j * 16 + li) * 16 + lg * 4]); };
     auto Tdiag_a = [&](int i) { return ld_frag4(&Tn[(i * 16 + li) * XP + i * 16 + lg * 4]); };
@@ -356,60 +367,72 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
            t30);
     (void)t32; (void)t31; (void)t30;
   }
-  wave_lds_fence();
+  lds_barrier();
 
-  // Column scales of T for W (b gamma) and Ut (b), for this lane's 16 s values.
-  float sg[2][8], sb8[2][8];
+  // K^T of token block w into LDS (the A blocks are no longer needed).
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int s = kk * 32 + lg * 8 + i;
-      sb8[kk][i] = Bs[s];
-      sg[kk][i] = Bs[s] * __expf(Gs[s]);
-    }
-  // T diag(b gamma) rows, as B operands for W^T: [t block][k step].
-  bf16x8 tgf[4][2], tbf[4][2];
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u16x8 raw = *reinterpret_cast<const u16x8*>(&Tn[(tb * 16 + li) * XP + kk * 32 + lg * 8]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float tv = bf2f(raw[i]);
-        tgf[tb][kk][i] = (__bf16)(tv * sg[kk][i]);
-        tbf[tb][kk][i] = (__bf16)(tv * sb8[kk][i]);
-      }
-    }
-
-  // K^T into LDS (the A blocks are no longer needed).
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int rb = 0; rb < 4; ++rb) {
+    if (rb != w) continue;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const u16x8 bits = frag_bits(kf[rb][kk]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) XT[(kk * 32 + lg * 8 + i) * XP + rb * 16 + li] = bits[i];
     }
-  wave_lds_fence();
+  }
+  // Rows of T diag(b gamma) and T diag(b), as MFMA operands: [t block][k step].
+  bf16x8 tgf[4][2], tbf[4][2];
+  {
+    float sg[2][8], sb8[2][8];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int s = kk * 32 + lg * 8 + i;
+        sb8[kk][i] = Bs[s];
+        sg[kk][i] = Bs[s] * __expf(Gs[s]);
+      }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u16x8 raw =
+            *reinterpret_cast<const u16x8*>(&Tn[(tb * 16 + li) * XP + kk * 32 + lg * 8]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float tv = bf2f(raw[i]);
+          tgf[tb][kk][i] = (__bf16)(tv * sg[kk][i]);
+          tbf[tb][kk][i] = (__bf16)(tv * sb8[kk][i]);
+        }
+      }
+  }
+  // bf16 Q rows for the chain, from f32 input, once per q/k head.
+  if (kSplit && h % grp == 0) {
+    uint16_t* dst = ws.Qb + (((int64_t)bb * Hk + kh) * NC + c) * (CK * DH);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      *reinterpret_cast<u16x8*>(dst + (w * 16 + li) * DH + kk * 32 + lg * 8) = frag_bits(qf[kk]);
+  }
+  lds_barrier();
 
   // K^T to the workspace once per q/k head (the first value head of the group).
   if (h % grp == 0) {
     uint16_t* dst = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int idx = i * 64 + lane;  // 16-byte piece: row idx/8, piece idx%8
+    for (int i = 0; i < 4; ++i) {
+      const int idx = i * PREP_THREADS + tid;  // 16-byte piece: row idx/8, piece idx%8
       const int row = idx >> 3, pc = idx & 7;
       *reinterpret_cast<u16x8*>(dst + row * CK + pc * 8) =
           *reinterpret_cast<const u16x8*>(&XT[row * XP + pc * 8]);
     }
   }
 
-  // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T; stored as W[t][dk].
-  // T is lower triangular, so t blocks 0 and 1 need only s < 32.
+  // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T, stored as W[t][dk];
+  // wave w takes dk blocks 2w and 2w+1.  T is lower triangular, so t blocks 0
+  // and 1 need only s < 32.
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
+    if ((db >> 1) != w) continue;
     const bf16x8 kt0 = ld_frag(&XT[(db * 16 + li) * XP + lg * 8]);
     const bf16x8 kt1 = ld_frag(&XT[(db * 16 + li) * XP + 32 + lg * 8]);
 #pragma unroll
@@ -421,27 +444,29 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
       st4<uint16_t>(ws.W + (chunk * CK + t) * DH + dk, acc[0], acc[1], acc[2], acc[3]);
     }
   }
-  wave_lds_fence();
+  lds_barrier();
 
-  // V^T into LDS.
+  // V^T of token block w into LDS.
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
+  for (int kk = 0; kk < 4; ++kk) {
+    const u16x8 bits = frag_bits(vf[kk]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u16x8 bits = frag_bits(vf[rb][kk]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) XT[(kk * 32 + lg * 8 + i) * XP + rb * 16 + li] = bits[i];
-    }
-  wave_lds_fence();
+    for (int i = 0; i < 8; ++i) XT[(kk * 32 + lg * 8 + i) * XP + w * 16 + li] = bits[i];
+  }
+  lds_barrier();
 
-  // Ut tiles [t block][dv block] = (T diag(b)) V; stored transposed, Ut^T[dv][t].
+  // Ut tiles [t block][dv block] = (T diag(b)) V, stored transposed as
+  // Ut^T[dv][t]; wave w takes dv blocks 2w and 2w+1.
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
+  for (int vb = 0; vb < 8; ++vb) {
+    if ((vb >> 1) != w) continue;
+    const bf16x8 v0 = ld_frag(&XT[(vb * 16 + li) * XP + lg * 8]);
+    const bf16x8 v1 = ld_frag(&XT[(vb * 16 + li) * XP + 32 + lg * 8]);
 #pragma unroll
-    for (int vb = 0; vb < 8; ++vb) {
+    for (int tb = 0; tb < 4; ++tb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(tbf[tb][0], ld_frag(&XT[(vb * 16 + li) * XP + lg * 8]), acc);
-      if (tb >= 2) acc = mfma16(tbf[tb][1], ld_frag(&XT[(vb * 16 + li) * XP + 32 + lg * 8]), acc);
+      acc = mfma16(tbf[tb][0], v0, acc);
+      if (tb >= 2) acc = mfma16(tbf[tb][1], v1, acc);
       const int t = tb * 16 + lg * 4, dv = vb * 16 + li;
       st4<uint16_t>(ws.Ut + (chunk * DH + dv) * CK + t, acc[0], acc[1], acc[2], acc[3]);
     }
@@ -450,68 +475,112 @@ __global__ __launch_bounds__(64) void chunk_prep_kernel(
 
 // ---------------------------------------------------------------------------
 // Phase 2: per (batch, value head, slice of NV value columns), sequential
-// over chunks.  Wave w owns token rows [16w, 16w+16) for U and O, and key
-// rows [32w, 32w+32) of the state slice H.
+// over chunks.  Eight waves: waves 0-3 compute, waves 4-7 load.  While the
+// compute waves run chunk c from LDS stage c%2, the loader waves write chunk
+// c+1 from their registers into the other stage and issue the global loads of
+// chunk c+4 (three chunks stay in flight in registers: the workspace comes
+// from memory with about two chunk-steps of latency).  All eight waves pass
+// the same two barriers per chunk.  Compute wave w owns token rows
+// [16w, 16w+16) for U and O and key rows [32w, 32w+32) of the state slice H.
+constexpr int CH_COMPUTE_WAVES = 4;
+constexpr int CH_LOADER_WAVES = 4;
+constexpr int CH_LOADER_LANES = 64 * CH_LOADER_WAVES;
+constexpr int CH_THREADS = 64 * (CH_COMPUTE_WAVES + CH_LOADER_WAVES);
+constexpr int RP = DH + 8;  // pitch (bf16) of [*, 128] LDS tiles: 272-byte rows
+
 template <int NV>
-struct ChainFrags {
-  bf16x8 w[4];        // W rows of this wave's token block, 4 k steps over dk
-  bf16x8 qf[4];       // Q rows, same shape
-  u16x4 ut[NV / 16];  // Ut^T at the wave's U accumulator positions
-  bf16x8 p[2];        // P rows of this wave's token block, 2 k steps over s
-  bf16x8 kt[2][2];    // K^T rows (key block 2w+i), 2 k steps over s
-  float4 gu;          // G at the 4 token rows this lane's U accumulators hold
-  float gt;           // G at token 16w + (lane % 16)
-  float glast;        // G at the last token of the chunk
+struct ChainStage {
+  uint16_t W[CK * RP];   // W [t][dk]
+  uint16_t Q[CK * RP];   // Q [t][dk], bf16
+  uint16_t P[CK * XP];   // P [t][s]
+  uint16_t Kt[DH * XP];  // K^T [dk][s]
+  uint16_t Ut[NV * XP];  // Ut^T [dv][t], this slice's columns
+  float G[2 * CK];       // G_t, then G_last replicated
 };
 
-template <int NV, typename TI>
-__device__ __forceinline__ void load_chain_frags(ChainFrags<NV>& f, const WsLayout& ws,
-                                                 const TI* __restrict__ q, int64_t q_ts, int bb,
-                                                 int bh, int kh, int c, int T, int Hk, int NC,
-                                                 int dv0, int w, int li, int lg) {
+// One chunk as the loader lanes hold it: 16-byte pieces, round-robin over the
+// loader lanes.  Pieces: W 1024, Q 1024 (2048 for f32 input), P 512, K^T 1024,
+// Ut^T slice NV*8, G 32.
+template <int NV>
+struct ChainLoadBase {
+  static constexpr int kUt = (NV * 8 + CH_LOADER_LANES - 1) / CH_LOADER_LANES;
+  u16x8 w[4], p[2], kt[4], ut[kUt];
+  f32x4 g;
+};
+template <int NV>
+struct ChainLoad : ChainLoadBase<NV> {
+  u16x8 qb[4];  // bf16 Q rows
+};
+
+template <int NV>
+__device__ __forceinline__ void chain_load(ChainLoad<NV>& L, const WsLayout& ws, const QRows& Q,
+                                           int bb, int bh, int kh, int c, int T, int Hk, int NC,
+                                           int dv0, int l) {
+  c = min(c, NC - 1);  // past the end: re-read the last chunk (never stored)
   const int64_t chunk = (int64_t)bh * NC + c;
   const int t0 = c * CK;
   const int n = min(CK, T - t0);
-  const int tr = w * 16 + li;
+  constexpr int LL = CH_LOADER_LANES;
+  const uint16_t* wp = ws.W + chunk * (CK * DH);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) f.w[kk] = ld_frag(ws.W + (chunk * CK + tr) * DH + kk * 32 + lg * 8);
-  if (tr < n) {
-    const TI* qp = q + ((int64_t)bb * T + t0 + tr) * q_ts + kh * DH + lg * 8;
+  for (int i = 0; i < 4; ++i) L.w[i] = *reinterpret_cast<const u16x8*>(wp + (i * LL + l) * 8);
+  const uint16_t* pp = ws.P + chunk * (CK * CK);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 unused;
-      load_row8(qp + kk * 32, f.qf[kk], unused);
-    }
-  } else {
+  for (int i = 0; i < 2; ++i) L.p[i] = *reinterpret_cast<const u16x8*>(pp + (i * LL + l) * 8);
+  const uint16_t* kp = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) f.qf[kk] = zero_frag();
+  for (int i = 0; i < 4; ++i) L.kt[i] = *reinterpret_cast<const u16x8*>(kp + (i * LL + l) * 8);
+  const uint16_t* up = ws.Ut + (chunk * DH + dv0) * CK;
+#pragma unroll
+  for (int i = 0; i < ChainLoadBase<NV>::kUt; ++i) {
+    const int pc = i * LL + l;
+    if (pc < NV * 8) L.ut[i] = *reinterpret_cast<const u16x8*>(up + pc * 8);
   }
+  const uint16_t* qp = Q.p + bb * Q.bs + kh * Q.hs + c * Q.cs;
 #pragma unroll
-  for (int vb = 0; vb < NV / 16; ++vb)
-    f.ut[vb] = *reinterpret_cast<const u16x4*>(ws.Ut + (chunk * DH + dv0 + vb * 16 + li) * CK +
-                                               w * 16 + lg * 4);
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) f.p[kk] = ld_frag(ws.P + (chunk * CK + tr) * CK + kk * 32 + lg * 8);
-  const uint16_t* ktp = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      f.kt[i][kk] = ld_frag(ktp + ((2 * w + i) * 16 + li) * CK + kk * 32 + lg * 8);
-  const float* gp = ws.G + chunk * 2 * CK;
-  f.gu = *reinterpret_cast<const float4*>(gp + w * 16 + lg * 4);
-  f.gt = gp[tr];
-  f.glast = gp[CK + (w * 16 + lg * 4 + li) % CK];  // replicated copy: a per-lane (vector) load
+  for (int i = 0; i < 4; ++i) {
+    const int pc = i * LL + l, row = pc >> 4, col = (pc & 15) * 8;
+    const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    L.qb[i] = row < n ? *reinterpret_cast<const u16x8*>(qp + row * Q.ts + col) : z;
+  }
+  if (l < 32) L.g = *reinterpret_cast<const f32x4*>(ws.G + chunk * 2 * CK + l * 4);
 }
 
-template <int NV, typename TI, typename TO>
-__global__ __launch_bounds__(256) void chunk_chain_kernel(
-    const TI* __restrict__ q, int64_t q_ts, WsLayout ws, const float* state_in,
+template <int NV>
+__device__ __forceinline__ void chain_store(const ChainLoad<NV>& L, ChainStage<NV>& S, int l) {
+  constexpr int LL = CH_LOADER_LANES;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pc = i * LL + l;
+    *reinterpret_cast<u16x8*>(&S.W[(pc >> 4) * RP + (pc & 15) * 8]) = L.w[i];
+    *reinterpret_cast<u16x8*>(&S.Kt[(pc >> 3) * XP + (pc & 7) * 8]) = L.kt[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pc = i * LL + l;
+    *reinterpret_cast<u16x8*>(&S.P[(pc >> 3) * XP + (pc & 7) * 8]) = L.p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < ChainLoadBase<NV>::kUt; ++i) {
+    const int pc = i * LL + l;
+    if (pc < NV * 8) *reinterpret_cast<u16x8*>(&S.Ut[(pc >> 3) * XP + (pc & 7) * 8]) = L.ut[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pc = i * LL + l;
+    *reinterpret_cast<u16x8*>(&S.Q[(pc >> 4) * RP + (pc & 15) * 8]) = L.qb[i];
+  }
+  if (l < 32) *reinterpret_cast<f32x4*>(&S.G[l * 4]) = L.g;
+}
+
+template <int NV, typename TO>
+__global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
+    QRows Q, WsLayout ws, const float* state_in,
     float* state_out, TO* __restrict__ o, int B, int T, int Hk, int Hv, int NC, float q_scale) {
   constexpr int NSL = DH / NV;  // slices per head
   constexpr int NVB = NV / 16;  // 16-column blocks per slice
-  constexpr int SP = DH + 8;    // pitch of the bf16 state copy: 272-byte rows
-  __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * SP];   // S slice [dv][dk], bf16
+  __shared__ __attribute__((aligned(16))) ChainStage<NV> stage[2];
+  __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * RP];   // S slice [dv][dk], bf16
   __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
   __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
 
@@ -524,6 +593,39 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
   const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
   const int dv0 = sl * NV;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const bool loader = w >= CH_COMPUTE_WAVES;
+  const int ll = tid - 64 * CH_COMPUTE_WAVES;  // loader lane
+
+  if (loader) {
+    // Loader waves.  Chunk 0 goes straight to stage 0; buffers A, B, C hold
+    // chunks c+1, c+2, c+3 at the top of step c.  Each step stores one
+    // buffer into the free stage and refills it with the chunk three ahead;
+    // the loop is unrolled by three so every buffer stays in place.
+    ChainLoad<NV> A, Bf, Cf;
+    chain_load<NV>(A, ws, Q, bb, bh, kh, 0, T, Hk, NC, dv0, ll);
+    chain_store<NV>(A, stage[0], ll);
+    chain_load<NV>(A, ws, Q, bb, bh, kh, 1, T, Hk, NC, dv0, ll);
+    chain_load<NV>(Bf, ws, Q, bb, bh, kh, 2, T, Hk, NC, dv0, ll);
+    chain_load<NV>(Cf, ws, Q, bb, bh, kh, 3, T, Hk, NC, dv0, ll);
+    lds_barrier();
+    auto step = [&](ChainLoad<NV>& buf, int c) {
+      if (c + 1 < NC) {
+        chain_store<NV>(buf, stage[(c + 1) & 1], ll);
+        chain_load<NV>(buf, ws, Q, bb, bh, kh, c + 4, T, Hk, NC, dv0, ll);
+      }
+      lds_barrier();
+      lds_barrier();
+    };
+    int c = 0;
+    for (; c + 3 <= NC; c += 3) {
+      step(A, c);
+      step(Bf, c + 1);
+      step(Cf, c + 2);
+    }
+    if (c < NC) step(A, c);
+    if (c + 1 < NC) step(Bf, c + 1);
+    return;
+  }
 
   f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
 #pragma unroll
@@ -538,18 +640,17 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
       } else {
         H[i][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      st4<uint16_t>(&Sb[(vb * 16 + li) * SP + dk], H[i][vb][0], H[i][vb][1], H[i][vb][2],
+      st4<uint16_t>(&Sb[(vb * 16 + li) * RP + dk], H[i][vb][0], H[i][vb][1], H[i][vb][2],
                     H[i][vb][3]);
     }
   }
+  lds_barrier();
 
-  // Software pipeline of depth two: chunk c+2's operands are loaded while
-  // chunk c computes.  Three named buffers and a loop unrolled by three keep
-  // every buffer in place, so no register copy forces an early wait; loads
-  // past the last chunk re-read it and are never used.
-  auto step = [&](const ChainFrags<NV>& cur, int c) {
+  for (int c = 0; c < NC; ++c) {
+    const ChainStage<NV>& S = stage[c & 1];
     const int t0 = c * CK;
     const int n = min(CK, T - t0);
+    const int tr = w * 16 + li;
 
     // (1) U = Ut - W H and (Q H)^T, both against the bf16 state copy.
     f32x4 accU[NVB], accQ[NVB];
@@ -560,23 +661,29 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 wf = ld_frag(&S.W[tr * RP + kk * 32 + lg * 8]);
+      const bf16x8 qf = ld_frag(&S.Q[tr * RP + kk * 32 + lg * 8]);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
-        const bf16x8 sf = ld_frag(&Sb[(vb * 16 + li) * SP + kk * 32 + lg * 8]);
-        accU[vb] = mfma16(cur.w[kk], sf, accU[vb]);
-        accQ[vb] = mfma16(sf, cur.qf[kk], accQ[vb]);
+        const bf16x8 sf = ld_frag(&Sb[(vb * 16 + li) * RP + kk * 32 + lg * 8]);
+        accU[vb] = mfma16(wf, sf, accU[vb]);
+        accQ[vb] = mfma16(sf, qf, accQ[vb]);
       }
     }
+    const float glast = S.G[CK + tr];
+    const float4 gu = *reinterpret_cast<const float4*>(&S.G[w * 16 + lg * 4]);
+    const float gt = S.G[tr];
     // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.
     {
-      const float sc[4] = {__expf(cur.glast - cur.gu.x), __expf(cur.glast - cur.gu.y),
-                           __expf(cur.glast - cur.gu.z), __expf(cur.glast - cur.gu.w)};
+      const float sc[4] = {__expf(glast - gu.x), __expf(glast - gu.y), __expf(glast - gu.z),
+                           __expf(glast - gu.w)};
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
+        const int off = (vb * 16 + li) * XP + w * 16 + lg * 4;
+        const u16x4 ut = *reinterpret_cast<const u16x4*>(&S.Ut[off]);
         float u[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = bf2f(cur.ut[vb][r]) - accU[vb][r];
-        const int off = (vb * 16 + li) * XP + w * 16 + lg * 4;
+        for (int r = 0; r < 4; ++r) u[r] = bf2f(ut[r]) - accU[vb][r];
         st4<uint16_t>(&Utl[off], u[0], u[1], u[2], u[3]);
         st4<uint16_t>(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
       }
@@ -586,14 +693,14 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     // (3) O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token
     // blocks 0 and 1 need only s < 32.
     {
-      const float gq = q_scale * __expf(cur.gt);
-      const int tr = w * 16 + li;
+      const float gq = q_scale * __expf(gt);
+      const bf16x8 p0 = ld_frag(&S.P[tr * XP + lg * 8]);
+      const bf16x8 p1 = ld_frag(&S.P[tr * XP + 32 + lg * 8]);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + lg * 8]), cur.p[0], acc);
-        if (w >= 2)
-          acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), cur.p[1], acc);
+        acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + lg * 8]), p0, acc);
+        if (w >= 2) acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), p1, acc);
         if (tr < n) {
           const int dv = dv0 + vb * 16 + lg * 4;
           TO* op = o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv;
@@ -604,7 +711,13 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     }
     // (4) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U.
     {
-      const float gl = __expf(cur.glast);
+      const float gl = __expf(glast);
+      bf16x8 ktf[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          ktf[i][kk] = ld_frag(&S.Kt[((2 * w + i) * 16 + li) * XP + kk * 32 + lg * 8]);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         const bf16x8 u0 = ld_frag(&Usl[(vb * 16 + li) * XP + lg * 8]);
@@ -614,8 +727,8 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
           f32x4 hcur = H[i][vb];
 #pragma unroll
           for (int r = 0; r < 4; ++r) hcur[r] *= gl;
-          hcur = mfma16(cur.kt[i][0], u0, hcur);
-          hcur = mfma16(cur.kt[i][1], u1, hcur);
+          hcur = mfma16(ktf[i][0], u0, hcur);
+          hcur = mfma16(ktf[i][1], u1, hcur);
           H[i][vb] = hcur;
         }
       }
@@ -625,29 +738,10 @@ __global__ __launch_bounds__(256) void chunk_chain_kernel(
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb)
-        st4<uint16_t>(&Sb[(vb * 16 + li) * SP + (2 * w + i) * 16 + lg * 4], H[i][vb][0],
+        st4<uint16_t>(&Sb[(vb * 16 + li) * RP + (2 * w + i) * 16 + lg * 4], H[i][vb][0],
                       H[i][vb][1], H[i][vb][2], H[i][vb][3]);
     lds_barrier();
-  };
-  auto fill = [&](ChainFrags<NV>& f, int c) {
-    load_chain_frags<NV, TI>(f, ws, q, q_ts, bb, bh, kh, min(c, NC - 1), T, Hk, NC, dv0, w, li,
-                             lg);
-  };
-  ChainFrags<NV> f0, f1, f2;
-  fill(f0, 0);
-  fill(f1, 1);
-  lds_barrier();
-  int c = 0;
-  for (; c + 3 <= NC; c += 3) {
-    fill(f2, c + 2);
-    step(f0, c);
-    fill(f0, c + 3);
-    step(f1, c + 1);
-    fill(f1, c + 4);
-    step(f2, c + 2);
   }
-  if (c < NC) step(f0, c);
-  if (c + 1 < NC) step(f1, c + 1);
 
   if (state_out) {
 #pragma unroll
@@ -669,22 +763,23 @@ void launch_prep(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const
                  int64_t v_ts, const void* a, const void* b, const float* A_log,
                  const float* dt_bias, const WsLayout& ws, int B, int T, int Hk, int Hv, int NC,
                  float q_scale, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_prep_kernel<TI, TG>), dim3((unsigned)((int64_t)B * Hv * NC)), dim3(64),
+  hipLaunchKernelGGL((chunk_prep_kernel<TI, TG>), dim3((unsigned)((int64_t)B * Hv * NC)),
+                     dim3(PREP_THREADS),
                      0, stream, (const TI*)q, q_ts, (const TI*)k, k_ts, (const TI*)v, v_ts,
                      (const TG*)a, (const TG*)b, A_log, dt_bias, ws, T, Hk, Hv, NC, q_scale);
 }
 
-template <typename TI, typename TO>
-void launch_chain(const void* q, int64_t q_ts, const WsLayout& ws, const float* state_in,
-                  float* state_out, void* o, int B, int T, int Hk, int Hv, int NC, float q_scale,
+template <typename TO>
+void launch_chain(const QRows& Q, const WsLayout& ws, const float* state_in, float* state_out,
+                  void* o, int B, int T, int Hk, int Hv, int NC, float q_scale,
                   hipStream_t stream) {
   constexpr int NV = 32;
   constexpr int NSL = DH / NV;
   const int64_t heads = (int64_t)B * Hv;
   const int64_t groups = (heads + 7) / 8;  // ids are padded to whole XCD rounds
-  hipLaunchKernelGGL((chunk_chain_kernel<NV, TI, TO>), dim3((unsigned)(groups * 8 * NSL)),
-                     dim3(256), 0, stream, (const TI*)q, q_ts, ws, state_in, state_out, (TO*)o, B,
-                     T, Hk, Hv, NC, q_scale);
+  hipLaunchKernelGGL((chunk_chain_kernel<NV, TO>), dim3((unsigned)(groups * 8 * NSL)),
+                     dim3(CH_THREADS), 0, stream, Q, ws, state_in, state_out, (TO*)o, B, T, Hk, Hv,
+                     NC, q_scale);
 }
 
 }  // namespace
@@ -714,21 +809,16 @@ hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, in
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (qkv_dt == 1) {
-    if (o_dt == 1)
-      launch_chain<uint16_t, uint16_t>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC,
-                                       q_scale, stream);
-    else
-      launch_chain<uint16_t, float>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC,
-                                    q_scale, stream);
-  } else {
-    if (o_dt == 1)
-      launch_chain<float, uint16_t>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC,
-                                    q_scale, stream);
-    else
-      launch_chain<float, float>(q, q_ts, ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale,
-                                 stream);
+  QRows Q;
+  if (qkv_dt == 1) {  // the bf16 input itself
+    Q = QRows{static_cast<const uint16_t*>(q), (int64_t)T * q_ts, DH, (int64_t)CK * q_ts, q_ts};
+  } else {  // the prep kernel's bf16 copy
+    Q = QRows{ws.Qb, (int64_t)Hk * NC * CK * DH, (int64_t)NC * CK * DH, (int64_t)CK * DH, DH};
   }
+  if (o_dt == 1)
+    launch_chain<uint16_t>(Q, ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
+  else
+    launch_chain<float>(Q, ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
   return hipGetLastError();
 }
 
