@@ -24,9 +24,9 @@
 //    bf16 operand precision; no other product does.
 //  * chunk_chain: one workgroup per (batch, value head, 32-column slice of
 //    dv), sequential over chunks.  The f32 state slice lives in MFMA
-//    accumulator registers of four compute waves; its bf16 copy and U^T are
-//    staged in LDS.  Four loader waves keep the next chunk's operands in a
-//    double-buffered LDS stage and the three after it in their registers.
+//    accumulator registers of four waves; each wave loads its own operands
+//    of the next chunk straight into registers while it computes the
+//    current one; the bf16 copy of the state and U^T are exchanged in LDS.
 //    The dv columns of H are independent, which is what allows the slicing.
 //
 // MFMA operand layouts (checked on the device): v_mfma_f32_16x16x32_bf16 --
@@ -60,10 +60,6 @@ __device__ __forceinline__ f32x4 mfma16k16(const s16x4& a, const s16x4& b, const
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-
-// Within one wave LDS operations complete in order; this only stops the
-// compiler from reordering LDS accesses across the point.
-__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 ld_frag(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -131,22 +127,30 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
   return x;
 }
 
+// The chain kernel's operands, per chunk, in the order its lanes load them:
+// "fragment-major", so that each of its 16-byte-per-lane loads reads 1 KB of
+// contiguous memory.  Lane l = li + 16 lg of chain wave w holds, for step kk,
+//   Wf[w][kk][l][j]  = W[16w + li][32kk + 8lg + j]            (t, dk)
+//   Qf[w][kk][l][j]  = Q[16w + li][32kk + 8lg + j]            (t, dk), bf16
+//   Pf[w][kk][l][j]  = P[16w + li][32kk + 8lg + j]            (t, s), kk < 2
+//   Ktf[w][i][kk][l][j] = K[32kk + 8lg + j][32w + 16i + li]   (s, dk), kk < 2
+//   Utf[sl][w][vb][l][r] = Ut[16w + 4lg + r][32sl + 16vb + li] (t, dv), r < 4
 struct WsLayout {
-  uint16_t* W;   // [B*Hv*NC][64 t][128 dk]
-  uint16_t* Ut;  // [B*Hv*NC][128 dv][64 t]
-  uint16_t* P;   // [B*Hv*NC][64 t][64 s]
+  uint16_t* W;   // [B*Hv*NC][8192]  Wf
+  uint16_t* Ut;  // [B*Hv*NC][8192]  Utf
+  uint16_t* P;   // [B*Hv*NC][4096]  Pf
   float* G;      // [B*Hv*NC][128]: G_t (t < 64), then G_last replicated 64 times
-  uint16_t* Kt;  // [B*Hk*NC][128 dk][64 s]
-  uint16_t* Qb;  // [B*Hk*NC][64 t][128 dk]: bf16 Q, written only for f32 input
+  uint16_t* Kt;  // [B*Hk*NC][8192]  Ktf
+  uint16_t* Qb;  // [B*Hk*NC][8192]  Qf
 };
 
-// bf16 Q rows as the chain reads them: element (b, q/k head, chunk, t, i) at
-// p + b*bs + h*hs + c*cs + t*ts + i -- either the bf16 input itself or the
-// workspace copy made from f32 input.
-struct QRows {
-  const uint16_t* p;
-  int64_t bs, hs, cs, ts;
-};
+// Offset of element (t, c) of a 64 x (32 m) tile in the Wf/Qf/Pf order, for a
+// 4-wide run of c starting at a multiple of 4 (what one MFMA result lane holds
+// after the operand swap): m = number of 32-wide k steps.
+__device__ __forceinline__ int frag_off(int t, int col, int m) {
+  const int w = t >> 4, li = t & 15, kk = col >> 5, lg = (col >> 3) & 3, j = col & 7;
+  return ((w * m + kk) * 64 + li + 16 * lg) * 8 + j;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -294,12 +298,14 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         const int sq = sb * 16 + lg * 4 + r;
         pv[r] = (sq <= tq) ? q_scale * __expf(Gs[tq] - Gs[sq]) * pq[r] : 0.0f;
       }
-      st4<uint16_t>(ws.P + (chunk * CK + tq) * CK + sb * 16 + lg * 4, pv[0], pv[1], pv[2], pv[3]);
+      st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tq, sb * 16 + lg * 4, 2), pv[0], pv[1],
+                    pv[2], pv[3]);
     }
     // Blocks above the diagonal of P are zero.
 #pragma unroll
     for (int sb = tb + 1; sb < 4; ++sb)
-      st4<uint16_t>(ws.P + (chunk * CK + tb * 16 + li) * CK + sb * 16 + lg * 4, 0.f, 0.f, 0.f, 0.f);
+      st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tb * 16 + li, sb * 16 + lg * 4, 2), 0.f,
+                    0.f, 0.f, 0.f);
   }
   lds_barrier();
 
@@ -406,12 +412,12 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         }
       }
   }
-  // bf16 Q rows for the chain, from f32 input, once per q/k head.
-  if (kSplit && h % grp == 0) {
+  // bf16 Q for the chain (Qf: the fragments as held here), once per q/k head.
+  if (h % grp == 0) {
     uint16_t* dst = ws.Qb + (((int64_t)bb * Hk + kh) * NC + c) * (CK * DH);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      *reinterpret_cast<u16x8*>(dst + (w * 16 + li) * DH + kk * 32 + lg * 8) = frag_bits(qf[kk]);
+      *reinterpret_cast<u16x8*>(dst + ((w * 4 + kk) * 64 + lane) * 8) = frag_bits(qf[kk]);
   }
   lds_barrier();
 
@@ -420,14 +426,15 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     uint16_t* dst = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = i * PREP_THREADS + tid;  // 16-byte piece: row idx/8, piece idx%8
-      const int row = idx >> 3, pc = idx & 7;
-      *reinterpret_cast<u16x8*>(dst + row * CK + pc * 8) =
-          *reinterpret_cast<const u16x8*>(&XT[row * XP + pc * 8]);
+      // 16-byte piece idx = ((cw * 2 + ci) * 2 + kk) * 64 + cl of Ktf.
+      const int idx = i * PREP_THREADS + tid;
+      const int cl = idx & 63, kk = (idx >> 6) & 1, ci = (idx >> 7) & 1, cw = idx >> 8;
+      const int dk = 32 * cw + 16 * ci + (cl & 15), s = 32 * kk + 8 * (cl >> 4);
+      *reinterpret_cast<u16x8*>(dst + idx * 8) = *reinterpret_cast<const u16x8*>(&XT[dk * XP + s]);
     }
   }
 
-  // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T, stored as W[t][dk];
+  // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T, stored as Wf;
   // wave w takes dk blocks 2w and 2w+1.  T is lower triangular, so t blocks 0
   // and 1 need only s < 32.
 #pragma unroll
@@ -441,7 +448,7 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
       acc = mfma16(kt0, tgf[tb][0], acc);
       if (tb >= 2) acc = mfma16(kt1, tgf[tb][1], acc);
       const int t = tb * 16 + li, dk = db * 16 + lg * 4;
-      st4<uint16_t>(ws.W + (chunk * CK + t) * DH + dk, acc[0], acc[1], acc[2], acc[3]);
+      st4<uint16_t>(ws.W + chunk * (CK * DH) + frag_off(t, dk, 4), acc[0], acc[1], acc[2], acc[3]);
     }
   }
   lds_barrier();
@@ -455,8 +462,8 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
   }
   lds_barrier();
 
-  // Ut tiles [t block][dv block] = (T diag(b)) V, stored transposed as
-  // Ut^T[dv][t]; wave w takes dv blocks 2w and 2w+1.
+  // Ut tiles [t block][dv block] = (T diag(b)) V, stored as Utf; wave w takes
+  // dv blocks 2w and 2w+1.
 #pragma unroll
   for (int vb = 0; vb < 8; ++vb) {
     if ((vb >> 1) != w) continue;
@@ -467,119 +474,76 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mfma16(tbf[tb][0], v0, acc);
       if (tb >= 2) acc = mfma16(tbf[tb][1], v1, acc);
-      const int t = tb * 16 + lg * 4, dv = vb * 16 + li;
-      st4<uint16_t>(ws.Ut + (chunk * DH + dv) * CK + t, acc[0], acc[1], acc[2], acc[3]);
+      // Utf[sl = vb / 2][w = tb][vb % 2][lane][0..3]
+      st4<uint16_t>(ws.Ut + chunk * (CK * DH) + ((vb >> 1) * 4 + tb) * 512 + (vb & 1) * 256 +
+                        lane * 4,
+                    acc[0], acc[1], acc[2], acc[3]);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Phase 2: per (batch, value head, slice of NV value columns), sequential
-// over chunks.  Eight waves: waves 0-3 compute, waves 4-7 load.  While the
-// compute waves run chunk c from LDS stage c%2, the loader waves write chunk
-// c+1 from their registers into the other stage and issue the global loads of
-// chunk c+4 (three chunks stay in flight in registers: the workspace comes
-// from memory with about two chunk-steps of latency).  All eight waves pass
-// the same two barriers per chunk.  Compute wave w owns token rows
-// [16w, 16w+16) for U and O and key rows [32w, 32w+32) of the state slice H.
-constexpr int CH_COMPUTE_WAVES = 4;
-constexpr int CH_LOADER_WAVES = 4;
-constexpr int CH_LOADER_LANES = 64 * CH_LOADER_WAVES;
-constexpr int CH_THREADS = 64 * (CH_COMPUTE_WAVES + CH_LOADER_WAVES);
+// over chunks; four waves.  Wave w owns token rows [16w, 16w+16) for U and O
+// and key rows [32w, 32w+32) of the state slice H.  Every operand a wave
+// multiplies with is its own -- its rows of W, Q and P, its rows of K^T, its
+// block of Ut^T and the gate sums -- so those go from global memory straight
+// into registers, one chunk ahead, in the MFMA operand layouts.  Only the
+// bf16 copy of H and U^T pass through LDS, behind two barriers per chunk.
+constexpr int CH_THREADS = 256;
 constexpr int RP = DH + 8;  // pitch (bf16) of [*, 128] LDS tiles: 272-byte rows
 
 template <int NV>
-struct ChainStage {
-  uint16_t W[CK * RP];   // W [t][dk]
-  uint16_t Q[CK * RP];   // Q [t][dk], bf16
-  uint16_t P[CK * XP];   // P [t][s]
-  uint16_t Kt[DH * XP];  // K^T [dk][s]
-  uint16_t Ut[NV * XP];  // Ut^T [dv][t], this slice's columns
-  float G[2 * CK];       // G_t, then G_last replicated
+struct ChainRegs {
+  bf16x8 w[4];       // W[16w + li][32kk + 8lg ..]
+  bf16x8 q[4];       // Q[16w + li][32kk + 8lg ..]
+  bf16x8 p[2];       // P[16w + li][32kk + 8lg ..]
+  bf16x8 kt[2][2];   // K^T[32w + 16i + li][32kk + 8lg ..]
+  u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + 16vb + li]
+  f32x4 gu;          // G[16w + 4lg ..]
+  float gt, gl;      // G[16w + li], G_last
 };
 
-// One chunk as the loader lanes hold it: 16-byte pieces, round-robin over the
-// loader lanes.  Pieces: W 1024, Q 1024 (2048 for f32 input), P 512, K^T 1024,
-// Ut^T slice NV*8, G 32.
-template <int NV>
-struct ChainLoadBase {
-  static constexpr int kUt = (NV * 8 + CH_LOADER_LANES - 1) / CH_LOADER_LANES;
-  u16x8 w[4], p[2], kt[4], ut[kUt];
-  f32x4 g;
-};
-template <int NV>
-struct ChainLoad : ChainLoadBase<NV> {
-  u16x8 qb[4];  // bf16 Q rows
-};
-
-template <int NV>
-__device__ __forceinline__ void chain_load(ChainLoad<NV>& L, const WsLayout& ws, const QRows& Q,
-                                           int bb, int bh, int kh, int c, int T, int Hk, int NC,
-                                           int dv0, int l) {
-  c = min(c, NC - 1);  // past the end: re-read the last chunk (never stored)
-  const int64_t chunk = (int64_t)bh * NC + c;
-  const int t0 = c * CK;
-  const int n = min(CK, T - t0);
-  constexpr int LL = CH_LOADER_LANES;
-  const uint16_t* wp = ws.W + chunk * (CK * DH);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) L.w[i] = *reinterpret_cast<const u16x8*>(wp + (i * LL + l) * 8);
-  const uint16_t* pp = ws.P + chunk * (CK * CK);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) L.p[i] = *reinterpret_cast<const u16x8*>(pp + (i * LL + l) * 8);
-  const uint16_t* kp = ws.Kt + (((int64_t)bb * Hk + kh) * NC + c) * (DH * CK);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) L.kt[i] = *reinterpret_cast<const u16x8*>(kp + (i * LL + l) * 8);
-  const uint16_t* up = ws.Ut + (chunk * DH + dv0) * CK;
-#pragma unroll
-  for (int i = 0; i < ChainLoadBase<NV>::kUt; ++i) {
-    const int pc = i * LL + l;
-    if (pc < NV * 8) L.ut[i] = *reinterpret_cast<const u16x8*>(up + pc * 8);
-  }
-  const uint16_t* qp = Q.p + bb * Q.bs + kh * Q.hs + c * Q.cs;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pc = i * LL + l, row = pc >> 4, col = (pc & 15) * 8;
-    const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    L.qb[i] = row < n ? *reinterpret_cast<const u16x8*>(qp + row * Q.ts + col) : z;
-  }
-  if (l < 32) L.g = *reinterpret_cast<const f32x4*>(ws.G + chunk * 2 * CK + l * 4);
+__device__ __forceinline__ bf16x8 gld_frag(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
 }
 
 template <int NV>
-__device__ __forceinline__ void chain_store(const ChainLoad<NV>& L, ChainStage<NV>& S, int l) {
-  constexpr int LL = CH_LOADER_LANES;
+__device__ __forceinline__ void chain_fetch(ChainRegs<NV>& R, const WsLayout& ws, int bb, int bh,
+                                            int kh, int c, int Hk, int NC, int sl, int w,
+                                            int lane) {
+  const int64_t chunk = (int64_t)bh * NC + c;
+  const int64_t kchunk = ((int64_t)bb * Hk + kh) * NC + c;
+  const uint16_t* wp = ws.W + chunk * (CK * DH) + (w * 4 * 64 + lane) * 8;
+  const uint16_t* qp = ws.Qb + kchunk * (CK * DH) + (w * 4 * 64 + lane) * 8;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pc = i * LL + l;
-    *reinterpret_cast<u16x8*>(&S.W[(pc >> 4) * RP + (pc & 15) * 8]) = L.w[i];
-    *reinterpret_cast<u16x8*>(&S.Kt[(pc >> 3) * XP + (pc & 7) * 8]) = L.kt[i];
+  for (int kk = 0; kk < 4; ++kk) {
+    R.w[kk] = gld_frag(wp + kk * 512);
+    R.q[kk] = gld_frag(qp + kk * 512);
   }
+  const uint16_t* pp = ws.P + chunk * (CK * CK) + (w * 2 * 64 + lane) * 8;
+  R.p[0] = gld_frag(pp);
+  R.p[1] = gld_frag(pp + 512);
+  const uint16_t* kp = ws.Kt + kchunk * (DH * CK) + (w * 4 * 64 + lane) * 8;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int pc = i * LL + l;
-    *reinterpret_cast<u16x8*>(&S.P[(pc >> 3) * XP + (pc & 7) * 8]) = L.p[i];
-  }
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-  for (int i = 0; i < ChainLoadBase<NV>::kUt; ++i) {
-    const int pc = i * LL + l;
-    if (pc < NV * 8) *reinterpret_cast<u16x8*>(&S.Ut[(pc >> 3) * XP + (pc & 7) * 8]) = L.ut[i];
-  }
+    for (int kk = 0; kk < 2; ++kk) R.kt[i][kk] = gld_frag(kp + (i * 2 + kk) * 512);
+  const uint16_t* up = ws.Ut + chunk * (CK * DH) + (sl * 4 + w) * 512 + lane * 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pc = i * LL + l;
-    *reinterpret_cast<u16x8*>(&S.Q[(pc >> 4) * RP + (pc & 15) * 8]) = L.qb[i];
-  }
-  if (l < 32) *reinterpret_cast<f32x4*>(&S.G[l * 4]) = L.g;
+  for (int vb = 0; vb < NV / 16; ++vb) R.ut[vb] = *reinterpret_cast<const u16x4*>(up + vb * 256);
+  const float* gp = ws.G + chunk * 2 * CK;
+  R.gu = *reinterpret_cast<const f32x4*>(gp + 16 * w + 4 * (lane >> 4));
+  R.gt = gp[16 * w + (lane & 15)];
+  R.gl = gp[CK + (lane & 15)];  // G_last, replicated
 }
 
 template <int NV, typename TO>
 __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
-    QRows Q, WsLayout ws, const float* state_in,
+    WsLayout ws, const float* state_in,
     float* state_out, TO* __restrict__ o, int B, int T, int Hk, int Hv, int NC, float q_scale) {
   constexpr int NSL = DH / NV;  // slices per head
   constexpr int NVB = NV / 16;  // 16-column blocks per slice
-  __shared__ __attribute__((aligned(16))) ChainStage<NV> stage[2];
   __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * RP];   // S slice [dv][dk], bf16
   __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
   __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
@@ -593,39 +557,10 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
   const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
   const int dv0 = sl * NV;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const bool loader = w >= CH_COMPUTE_WAVES;
-  const int ll = tid - 64 * CH_COMPUTE_WAVES;  // loader lane
+  const int tr = w * 16 + li;
 
-  if (loader) {
-    // Loader waves.  Chunk 0 goes straight to stage 0; buffers A, B, C hold
-    // chunks c+1, c+2, c+3 at the top of step c.  Each step stores one
-    // buffer into the free stage and refills it with the chunk three ahead;
-    // the loop is unrolled by three so every buffer stays in place.
-    ChainLoad<NV> A, Bf, Cf;
-    chain_load<NV>(A, ws, Q, bb, bh, kh, 0, T, Hk, NC, dv0, ll);
-    chain_store<NV>(A, stage[0], ll);
-    chain_load<NV>(A, ws, Q, bb, bh, kh, 1, T, Hk, NC, dv0, ll);
-    chain_load<NV>(Bf, ws, Q, bb, bh, kh, 2, T, Hk, NC, dv0, ll);
-    chain_load<NV>(Cf, ws, Q, bb, bh, kh, 3, T, Hk, NC, dv0, ll);
-    lds_barrier();
-    auto step = [&](ChainLoad<NV>& buf, int c) {
-      if (c + 1 < NC) {
-        chain_store<NV>(buf, stage[(c + 1) & 1], ll);
-        chain_load<NV>(buf, ws, Q, bb, bh, kh, c + 4, T, Hk, NC, dv0, ll);
-      }
-      lds_barrier();
-      lds_barrier();
-    };
-    int c = 0;
-    for (; c + 3 <= NC; c += 3) {
-      step(A, c);
-      step(Bf, c + 1);
-      step(Cf, c + 2);
-    }
-    if (c < NC) step(A, c);
-    if (c + 1 < NC) step(Bf, c + 1);
-    return;
-  }
+  ChainRegs<NV> RA, RB;
+  chain_fetch<NV>(RA, ws, bb, bh, kh, 0, Hk, NC, sl, w, lane);
 
   f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
 #pragma unroll
@@ -646,11 +581,13 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
   }
   lds_barrier();
 
-  for (int c = 0; c < NC; ++c) {
-    const ChainStage<NV>& S = stage[c & 1];
+  // Chunk c + 1 is loaded into registers at step c.
+  auto step = [&](const ChainRegs<NV>& R, ChainRegs<NV>& next, int c) {
+    // Past the last chunk the loads repeat it (unconditional loads keep the
+    // compiler's count of loads in flight exact).
+    chain_fetch<NV>(next, ws, bb, bh, kh, min(c + 1, NC - 1), Hk, NC, sl, w, lane);
     const int t0 = c * CK;
     const int n = min(CK, T - t0);
-    const int tr = w * 16 + li;
 
     // (1) U = Ut - W H and (Q H)^T, both against the bf16 state copy.
     f32x4 accU[NVB], accQ[NVB];
@@ -661,63 +598,34 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 wf = ld_frag(&S.W[tr * RP + kk * 32 + lg * 8]);
-      const bf16x8 qf = ld_frag(&S.Q[tr * RP + kk * 32 + lg * 8]);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         const bf16x8 sf = ld_frag(&Sb[(vb * 16 + li) * RP + kk * 32 + lg * 8]);
-        accU[vb] = mfma16(wf, sf, accU[vb]);
-        accQ[vb] = mfma16(sf, qf, accQ[vb]);
+        accU[vb] = mfma16(R.w[kk], sf, accU[vb]);
+        accQ[vb] = mfma16(sf, R.q[kk], accQ[vb]);
       }
     }
-    const float glast = S.G[CK + tr];
-    const float4 gu = *reinterpret_cast<const float4*>(&S.G[w * 16 + lg * 4]);
-    const float gt = S.G[tr];
     // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.
     {
-      const float sc[4] = {__expf(glast - gu.x), __expf(glast - gu.y), __expf(glast - gu.z),
-                           __expf(glast - gu.w)};
+      const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
+                           __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         const int off = (vb * 16 + li) * XP + w * 16 + lg * 4;
-        const u16x4 ut = *reinterpret_cast<const u16x4*>(&S.Ut[off]);
         float u[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = bf2f(ut[r]) - accU[vb][r];
+        for (int r = 0; r < 4; ++r) u[r] = bf2f(R.ut[vb][r]) - accU[vb][r];
         st4<uint16_t>(&Utl[off], u[0], u[1], u[2], u[3]);
         st4<uint16_t>(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
       }
     }
     lds_barrier();
 
-    // (3) O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token
-    // blocks 0 and 1 need only s < 32.
+    // (3) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U, then its bf16
+    // copy for the next chunk (every wave finished reading the old copy
+    // before the barrier above).
     {
-      const float gq = q_scale * __expf(gt);
-      const bf16x8 p0 = ld_frag(&S.P[tr * XP + lg * 8]);
-      const bf16x8 p1 = ld_frag(&S.P[tr * XP + 32 + lg * 8]);
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + lg * 8]), p0, acc);
-        if (w >= 2) acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), p1, acc);
-        if (tr < n) {
-          const int dv = dv0 + vb * 16 + lg * 4;
-          TO* op = o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv;
-          st4<TO>(op, fmaf(gq, accQ[vb][0], acc[0]), fmaf(gq, accQ[vb][1], acc[1]),
-                  fmaf(gq, accQ[vb][2], acc[2]), fmaf(gq, accQ[vb][3], acc[3]));
-        }
-      }
-    }
-    // (4) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U.
-    {
-      const float gl = __expf(glast);
-      bf16x8 ktf[2][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          ktf[i][kk] = ld_frag(&S.Kt[((2 * w + i) * 16 + li) * XP + kk * 32 + lg * 8]);
+      const float gl = __expf(R.gl);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         const bf16x8 u0 = ld_frag(&Usl[(vb * 16 + li) * XP + lg * 8]);
@@ -727,20 +635,42 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
           f32x4 hcur = H[i][vb];
 #pragma unroll
           for (int r = 0; r < 4; ++r) hcur[r] *= gl;
-          hcur = mfma16(ktf[i][0], u0, hcur);
-          hcur = mfma16(ktf[i][1], u1, hcur);
+          hcur = mfma16(R.kt[i][0], u0, hcur);
+          hcur = mfma16(R.kt[i][1], u1, hcur);
           H[i][vb] = hcur;
         }
       }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb)
+          st4<uint16_t>(&Sb[(vb * 16 + li) * RP + (2 * w + i) * 16 + lg * 4], H[i][vb][0],
+                        H[i][vb][1], H[i][vb][2], H[i][vb][3]);
     }
-    // (5) bf16 copy of the new state for the next chunk.
+
+    // (4) O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token
+    // blocks 0 and 1 need only s < 32.
+    {
+      const float gq = q_scale * __expf(R.gt);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb)
-        st4<uint16_t>(&Sb[(vb * 16 + li) * RP + (2 * w + i) * 16 + lg * 4], H[i][vb][0],
-                      H[i][vb][1], H[i][vb][2], H[i][vb][3]);
+      for (int vb = 0; vb < NVB; ++vb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + lg * 8]), R.p[0], acc);
+        if (w >= 2) acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), R.p[1], acc);
+        if (tr < n) {
+          const int dv = dv0 + vb * 16 + lg * 4;
+          TO* op = o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv;
+          st4<TO>(op, fmaf(gq, accQ[vb][0], acc[0]), fmaf(gq, accQ[vb][1], acc[1]),
+                  fmaf(gq, accQ[vb][2], acc[2]), fmaf(gq, accQ[vb][3], acc[3]));
+        }
+      }
+    }
     lds_barrier();
+  };
+
+  for (int c = 0; c < NC; c += 2) {
+    step(RA, RB, c);
+    if (c + 1 < NC) step(RB, RA, c + 1);
   }
 
   if (state_out) {
@@ -770,7 +700,7 @@ void launch_prep(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const
 }
 
 template <typename TO>
-void launch_chain(const QRows& Q, const WsLayout& ws, const float* state_in, float* state_out,
+void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
                   void* o, int B, int T, int Hk, int Hv, int NC, float q_scale,
                   hipStream_t stream) {
   constexpr int NV = 32;
@@ -778,7 +708,7 @@ void launch_chain(const QRows& Q, const WsLayout& ws, const float* state_in, flo
   const int64_t heads = (int64_t)B * Hv;
   const int64_t groups = (heads + 7) / 8;  // ids are padded to whole XCD rounds
   hipLaunchKernelGGL((chunk_chain_kernel<NV, TO>), dim3((unsigned)(groups * 8 * NSL)),
-                     dim3(CH_THREADS), 0, stream, Q, ws, state_in, state_out, (TO*)o, B, T, Hk, Hv,
+                     dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, Hk, Hv,
                      NC, q_scale);
 }
 
@@ -809,16 +739,10 @@ hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, in
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  QRows Q;
-  if (qkv_dt == 1) {  // the bf16 input itself
-    Q = QRows{static_cast<const uint16_t*>(q), (int64_t)T * q_ts, DH, (int64_t)CK * q_ts, q_ts};
-  } else {  // the prep kernel's bf16 copy
-    Q = QRows{ws.Qb, (int64_t)Hk * NC * CK * DH, (int64_t)NC * CK * DH, (int64_t)CK * DH, DH};
-  }
   if (o_dt == 1)
-    launch_chain<uint16_t>(Q, ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
+    launch_chain<uint16_t>(ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
   else
-    launch_chain<float>(Q, ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
+    launch_chain<float>(ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
   return hipGetLastError();
 }
 
