@@ -112,10 +112,6 @@ __device__ __forceinline__ void st4<uint16_t>(uint16_t* p, float a, float b, flo
   v[0] = f2bf(a); v[1] = f2bf(b); v[2] = f2bf(c); v[3] = f2bf(d);
   *reinterpret_cast<u16x4*>(p) = v;
 }
-template <>
-__device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_scan(float x, int lane) {
@@ -134,7 +130,10 @@ __device__ __forceinline__ float wave_scan(float x, int lane) {
 //   Qf[w][kk][l][j]  = Q[16w + li][32kk + 8lg + j]            (t, dk), bf16
 //   Pf[w][kk][l][j]  = P[16w + li][32kk + 8lg + j]            (t, s), kk < 2
 //   Ktf[w][i][kk][l][j] = K[32kk + 8lg + j][32w + 16i + li]   (s, dk), kk < 2
-//   Utf[sl][w][vb][l][r] = Ut[16w + 4lg + r][32sl + 16vb + li] (t, dv), r < 4
+//   Utf[sl][w][vb][l][r] = Ut[16w + 4lg + r][32sl + dvp(vb, li)] (t, dv), r < 4
+// with dvp(vb, m) = 8(m/4) + 4vb + m%4: the chain multiplies the dv rows of a
+// 32-column slice in that order, so that each lane of its output tile ends up
+// with 8 consecutive dv of one token.
 struct WsLayout {
   uint16_t* W;   // [B*Hv*NC][8192]  Wf
   uint16_t* Ut;  // [B*Hv*NC][8192]  Utf
@@ -143,6 +142,9 @@ struct WsLayout {
   uint16_t* Kt;  // [B*Hk*NC][8192]  Ktf
   uint16_t* Qb;  // [B*Hk*NC][8192]  Qf
 };
+
+// Position of dv within a 32-column slice under the chain's row order.
+__device__ __forceinline__ int dvp(int vb, int m) { return 8 * (m >> 2) + 4 * vb + (m & 3); }
 
 // Offset of element (t, c) of a 64 x (32 m) tile in the Wf/Qf/Pf order, for a
 // 4-wide run of c starting at a multiple of 4 (what one MFMA result lane holds
@@ -474,9 +476,12 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mfma16(tbf[tb][0], v0, acc);
       if (tb >= 2) acc = mfma16(tbf[tb][1], v1, acc);
-      // Utf[sl = vb / 2][w = tb][vb % 2][lane][0..3]
-      st4<uint16_t>(ws.Ut + chunk * (CK * DH) + ((vb >> 1) * 4 + tb) * 512 + (vb & 1) * 256 +
-                        lane * 4,
+      // Utf[sl = vb / 2][w = tb][cvb][cli + 16 lg][0..3] with dvp(cvb, cli) = the
+      // column within the slice, 16 (vb % 2) + li.
+      const int col = 16 * (vb & 1) + li;
+      const int cvb = (col >> 2) & 1, cli = 4 * (col >> 3) + (col & 3);
+      st4<uint16_t>(ws.Ut + chunk * (CK * DH) + ((vb >> 1) * 4 + tb) * 512 + cvb * 256 +
+                        (cli + 16 * lg) * 4,
                     acc[0], acc[1], acc[2], acc[3]);
     }
   }
@@ -499,7 +504,7 @@ struct ChainRegs {
   bf16x8 q[4];       // Q[16w + li][32kk + 8lg ..]
   bf16x8 p[2];       // P[16w + li][32kk + 8lg ..]
   bf16x8 kt[2][2];   // K^T[32w + 16i + li][32kk + 8lg ..]
-  u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + 16vb + li]
+  u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + dvp(vb, li)]
   f32x4 gu;          // G[16w + 4lg ..]
   float gt, gl;      // G[16w + li], G_last
 };
@@ -544,6 +549,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     float* state_out, TO* __restrict__ o, int B, int T, int Hk, int Hv, int NC, float q_scale) {
   constexpr int NSL = DH / NV;  // slices per head
   constexpr int NVB = NV / 16;  // 16-column blocks per slice
+  static_assert(NV == 32, "the dvp row order and the 8-wide output stores assume 32 columns");
   __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * RP];   // S slice [dv][dk], bf16
   __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
   __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
@@ -589,7 +595,8 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     const int t0 = c * CK;
     const int n = min(CK, T - t0);
 
-    // (1) U = Ut - W H and (Q H)^T, both against the bf16 state copy.
+    // (1) U = Ut - W H against the bf16 state copy, dv rows in dvp order.
+    bf16x8 sf[4][NVB];
     f32x4 accU[NVB], accQ[NVB];
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
@@ -600,18 +607,18 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
-        const bf16x8 sf = ld_frag(&Sb[(vb * 16 + li) * RP + kk * 32 + lg * 8]);
-        accU[vb] = mfma16(R.w[kk], sf, accU[vb]);
-        accQ[vb] = mfma16(sf, R.q[kk], accQ[vb]);
+        sf[kk][vb] = ld_frag(&Sb[dvp(vb, li) * RP + kk * 32 + lg * 8]);
+        accU[vb] = mfma16(R.w[kk], sf[kk][vb], accU[vb]);
       }
     }
-    // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.
+    // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}; then (Q H)^T,
+    // which only the output needs, while the other waves catch up.
     {
       const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
                            __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
-        const int off = (vb * 16 + li) * XP + w * 16 + lg * 4;
+        const int off = dvp(vb, li) * XP + w * 16 + lg * 4;
         float u[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) u[r] = bf2f(R.ut[vb][r]) - accU[vb][r];
@@ -619,6 +626,10 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
         st4<uint16_t>(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
       }
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) accQ[vb] = mfma16(sf[kk][vb], R.q[kk], accQ[vb]);
     lds_barrier();
 
     // (3) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U, then its bf16
@@ -649,21 +660,20 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     }
 
     // (4) O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token
-    // blocks 0 and 1 need only s < 32.
+    // blocks 0 and 1 need only s < 32.  Lane (li, lg) ends with dv 8lg..8lg+7
+    // of token 16w + li (dvp order), one 8-wide store.
     {
       const float gq = q_scale * __expf(R.gt);
+      float ov[8];
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + lg * 8]), R.p[0], acc);
-        if (w >= 2) acc = mfma16(ld_frag(&Utl[(vb * 16 + li) * XP + 32 + lg * 8]), R.p[1], acc);
-        if (tr < n) {
-          const int dv = dv0 + vb * 16 + lg * 4;
-          TO* op = o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv;
-          st4<TO>(op, fmaf(gq, accQ[vb][0], acc[0]), fmaf(gq, accQ[vb][1], acc[1]),
-                  fmaf(gq, accQ[vb][2], acc[2]), fmaf(gq, accQ[vb][3], acc[3]));
-        }
+        acc = mfma16(ld_frag(&Utl[dvp(vb, li) * XP + lg * 8]), R.p[0], acc);
+        if (w >= 2) acc = mfma16(ld_frag(&Utl[dvp(vb, li) * XP + 32 + lg * 8]), R.p[1], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[4 * vb + r] = fmaf(gq, accQ[vb][r], acc[r]);
       }
+      if (tr < n) store8(o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
     }
     lds_barrier();
   };
