@@ -24,9 +24,9 @@
 //    bf16 operand precision; no other product does.
 //  * chunk_chain: one workgroup per (batch, value head, 32-column slice of
 //    dv), sequential over chunks.  The f32 state slice lives in MFMA
-//    accumulator registers of four waves; each wave loads its own operands
-//    of the next chunk straight into registers while it computes the
-//    current one; the bf16 copy of the state and U^T are exchanged in LDS.
+//    accumulator registers of four state waves; four output waves form O.
+//    Each wave loads its own operands two chunks ahead straight into
+//    registers; the bf16 copy of the state and U^T are exchanged in LDS.
 //    The dv columns of H are independent, which is what allows the slicing.
 //
 // MFMA operand layouts (checked on the device): v_mfma_f32_16x16x32_bf16 --
@@ -489,24 +489,32 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
 
 // ---------------------------------------------------------------------------
 // Phase 2: per (batch, value head, slice of NV value columns), sequential
-// over chunks; four waves.  Wave w owns token rows [16w, 16w+16) for U and O
-// and key rows [32w, 32w+32) of the state slice H.  Every operand a wave
-// multiplies with is its own -- its rows of W, Q and P, its rows of K^T, its
-// block of Ut^T and the gate sums -- so those go from global memory straight
-// into registers, one chunk ahead, in the MFMA operand layouts.  Only the
-// bf16 copy of H and U^T pass through LDS, behind two barriers per chunk.
-constexpr int CH_THREADS = 256;
+// over chunks; eight waves in two roles.  State waves 0-3 carry the
+// recurrence: wave w owns token rows [16w, 16w+16) of U and key rows
+// [32w, 32w+32) of the f32 state slice H.  Output waves 4-7 produce O for
+// token rows [16(w-4), 16(w-4)+16).  Every operand a wave multiplies with is
+// its own (rows of W, K^T and Ut, or of Q and P, and the gate sums), so those
+// go from global memory straight into registers, two chunks ahead, in MFMA
+// operand order.  The bf16 copy of H and U^T are exchanged in LDS behind two
+// barriers per chunk:
+//   state:  U = Ut - W H -> LDS | barrier | H update -> LDS | barrier
+//   output: (Q H)^T          | barrier | O = .. + P U    | barrier
+constexpr int CH_THREADS = 512;
 constexpr int RP = DH + 8;  // pitch (bf16) of [*, 128] LDS tiles: 272-byte rows
 
 template <int NV>
-struct ChainRegs {
+struct StateRegs {
   bf16x8 w[4];       // W[16w + li][32kk + 8lg ..]
-  bf16x8 q[4];       // Q[16w + li][32kk + 8lg ..]
-  bf16x8 p[2];       // P[16w + li][32kk + 8lg ..]
   bf16x8 kt[2][2];   // K^T[32w + 16i + li][32kk + 8lg ..]
   u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + dvp(vb, li)]
   f32x4 gu;          // G[16w + 4lg ..]
-  float gt, gl;      // G[16w + li], G_last
+  float gl;          // G_last
+};
+
+struct OutRegs {
+  bf16x8 q[4];  // Q[16w + li][32kk + 8lg ..]
+  bf16x8 p[2];  // P[16w + li][32kk + 8lg ..]
+  float gt;     // G[16w + li]
 };
 
 __device__ __forceinline__ bf16x8 gld_frag(const uint16_t* p) {
@@ -514,21 +522,14 @@ __device__ __forceinline__ bf16x8 gld_frag(const uint16_t* p) {
 }
 
 template <int NV>
-__device__ __forceinline__ void chain_fetch(ChainRegs<NV>& R, const WsLayout& ws, int bb, int bh,
+__device__ __forceinline__ void state_fetch(StateRegs<NV>& R, const WsLayout& ws, int bb, int bh,
                                             int kh, int c, int Hk, int NC, int sl, int w,
                                             int lane) {
   const int64_t chunk = (int64_t)bh * NC + c;
   const int64_t kchunk = ((int64_t)bb * Hk + kh) * NC + c;
   const uint16_t* wp = ws.W + chunk * (CK * DH) + (w * 4 * 64 + lane) * 8;
-  const uint16_t* qp = ws.Qb + kchunk * (CK * DH) + (w * 4 * 64 + lane) * 8;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    R.w[kk] = gld_frag(wp + kk * 512);
-    R.q[kk] = gld_frag(qp + kk * 512);
-  }
-  const uint16_t* pp = ws.P + chunk * (CK * CK) + (w * 2 * 64 + lane) * 8;
-  R.p[0] = gld_frag(pp);
-  R.p[1] = gld_frag(pp + 512);
+  for (int kk = 0; kk < 4; ++kk) R.w[kk] = gld_frag(wp + kk * 512);
   const uint16_t* kp = ws.Kt + kchunk * (DH * CK) + (w * 4 * 64 + lane) * 8;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -539,8 +540,20 @@ __device__ __forceinline__ void chain_fetch(ChainRegs<NV>& R, const WsLayout& ws
   for (int vb = 0; vb < NV / 16; ++vb) R.ut[vb] = *reinterpret_cast<const u16x4*>(up + vb * 256);
   const float* gp = ws.G + chunk * 2 * CK;
   R.gu = *reinterpret_cast<const f32x4*>(gp + 16 * w + 4 * (lane >> 4));
-  R.gt = gp[16 * w + (lane & 15)];
   R.gl = gp[CK + (lane & 15)];  // G_last, replicated
+}
+
+__device__ __forceinline__ void out_fetch(OutRegs& R, const WsLayout& ws, int bb, int bh, int kh,
+                                          int c, int Hk, int NC, int w, int lane) {
+  const int64_t chunk = (int64_t)bh * NC + c;
+  const int64_t kchunk = ((int64_t)bb * Hk + kh) * NC + c;
+  const uint16_t* qp = ws.Qb + kchunk * (CK * DH) + (w * 4 * 64 + lane) * 8;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) R.q[kk] = gld_frag(qp + kk * 512);
+  const uint16_t* pp = ws.P + chunk * (CK * CK) + (w * 2 * 64 + lane) * 8;
+  R.p[0] = gld_frag(pp);
+  R.p[1] = gld_frag(pp + 512);
+  R.gt = ws.G[chunk * 2 * CK + 16 * w + (lane & 15)];
 }
 
 template <int NV, typename TO>
@@ -562,80 +575,65 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
   if (hs >= B * Hv) return;
   const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
   const int dv0 = sl * NV;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int tr = w * 16 + li;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int w = (tid >> 6) & 3;
+  const bool state_wave = tid < 256;
 
-  ChainRegs<NV> RA, RB;
-  chain_fetch<NV>(RA, ws, bb, bh, kh, 0, Hk, NC, sl, w, lane);
+  if (state_wave) {
+    StateRegs<NV> RA, RB, RC;
+    state_fetch<NV>(RA, ws, bb, bh, kh, 0, Hk, NC, sl, w, lane);
+    state_fetch<NV>(RB, ws, bb, bh, kh, min(1, NC - 1), Hk, NC, sl, w, lane);
 
-  f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
+    f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      const int dk = (2 * w + i) * 16 + lg * 4, dv = dv0 + vb * 16 + li;
-      if (state_in) {
-        const float4 s4 =
-            *reinterpret_cast<const float4*>(state_in + ((int64_t)bh * DH + dv) * DH + dk);
-        H[i][vb] = f32x4{s4.x, s4.y, s4.z, s4.w};
-      } else {
-        H[i][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      st4<uint16_t>(&Sb[(vb * 16 + li) * RP + dk], H[i][vb][0], H[i][vb][1], H[i][vb][2],
-                    H[i][vb][3]);
-    }
-  }
-  lds_barrier();
-
-  // Chunk c + 1 is loaded into registers at step c.
-  auto step = [&](const ChainRegs<NV>& R, ChainRegs<NV>& next, int c) {
-    // Past the last chunk the loads repeat it (unconditional loads keep the
-    // compiler's count of loads in flight exact).
-    chain_fetch<NV>(next, ws, bb, bh, kh, min(c + 1, NC - 1), Hk, NC, sl, w, lane);
-    const int t0 = c * CK;
-    const int n = min(CK, T - t0);
-
-    // (1) U = Ut - W H against the bf16 state copy, dv rows in dvp order.
-    bf16x8 sf[4][NVB];
-    f32x4 accU[NVB], accQ[NVB];
-#pragma unroll
-    for (int vb = 0; vb < NVB; ++vb) {
-      accU[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accQ[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
-        sf[kk][vb] = ld_frag(&Sb[dvp(vb, li) * RP + kk * 32 + lg * 8]);
-        accU[vb] = mfma16(R.w[kk], sf[kk][vb], accU[vb]);
+        const int dk = (2 * w + i) * 16 + lg * 4, dv = dv0 + vb * 16 + li;
+        if (state_in) {
+          const float4 s4 =
+              *reinterpret_cast<const float4*>(state_in + ((int64_t)bh * DH + dv) * DH + dk);
+          H[i][vb] = f32x4{s4.x, s4.y, s4.z, s4.w};
+        } else {
+          H[i][vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        st4<uint16_t>(&Sb[(vb * 16 + li) * RP + dk], H[i][vb][0], H[i][vb][1], H[i][vb][2],
+                      H[i][vb][3]);
       }
     }
-    // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}; then (Q H)^T,
-    // which only the output needs, while the other waves catch up.
-    {
-      const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
-                           __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        const int off = dvp(vb, li) * XP + w * 16 + lg * 4;
-        float u[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) u[r] = bf2f(R.ut[vb][r]) - accU[vb][r];
-        st4<uint16_t>(&Utl[off], u[0], u[1], u[2], u[3]);
-        st4<uint16_t>(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) accQ[vb] = mfma16(sf[kk][vb], R.q[kk], accQ[vb]);
     lds_barrier();
 
-    // (3) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U, then its bf16
-    // copy for the next chunk (every wave finished reading the old copy
-    // before the barrier above).
-    {
+    // Chunk c + 2 is loaded at step c; past the last chunk the loads repeat it
+    // (unconditional loads keep the compiler's count of loads in flight exact).
+    auto step = [&](const StateRegs<NV>& R, StateRegs<NV>& next, int c) {
+      state_fetch<NV>(next, ws, bb, bh, kh, min(c + 2, NC - 1), Hk, NC, sl, w, lane);
+      // (1) U = Ut - W H against the bf16 state copy, dv rows in dvp order.
+      f32x4 accU[NVB];
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) accU[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb)
+          accU[vb] = mfma16(R.w[kk], ld_frag(&Sb[dvp(vb, li) * RP + kk * 32 + lg * 8]), accU[vb]);
+      // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.
+      {
+        const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
+                             __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          const int off = dvp(vb, li) * XP + w * 16 + lg * 4;
+          float u[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) u[r] = bf2f(R.ut[vb][r]) - accU[vb][r];
+          st4<uint16_t>(&Utl[off], u[0], u[1], u[2], u[3]);
+          st4<uint16_t>(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
+        }
+      }
+      lds_barrier();
+      // (3) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U, then its bf16
+      // copy for the next chunk (every wave finished reading the old copy
+      // before the barrier above).
       const float gl = __expf(R.gl);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
@@ -657,12 +655,46 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
         for (int vb = 0; vb < NVB; ++vb)
           st4<uint16_t>(&Sb[(vb * 16 + li) * RP + (2 * w + i) * 16 + lg * 4], H[i][vb][0],
                         H[i][vb][1], H[i][vb][2], H[i][vb][3]);
+      lds_barrier();
+    };
+    for (int c = 0; c < NC; c += 3) {
+      step(RA, RC, c);
+      if (c + 1 < NC) step(RB, RA, c + 1);
+      if (c + 2 < NC) step(RC, RB, c + 2);
     }
 
-    // (4) O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token
-    // blocks 0 and 1 need only s < 32.  Lane (li, lg) ends with dv 8lg..8lg+7
-    // of token 16w + li (dvp order), one 8-wide store.
-    {
+    if (state_out) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          const int dk = (2 * w + i) * 16 + lg * 4, dv = dv0 + vb * 16 + li;
+          *reinterpret_cast<float4*>(state_out + ((int64_t)bh * DH + dv) * DH + dk) =
+              make_float4(H[i][vb][0], H[i][vb][1], H[i][vb][2], H[i][vb][3]);
+        }
+      }
+    }
+  } else {
+    const int tr = w * 16 + li;
+    OutRegs RA, RB, RC;
+    out_fetch(RA, ws, bb, bh, kh, 0, Hk, NC, w, lane);
+    out_fetch(RB, ws, bb, bh, kh, min(1, NC - 1), Hk, NC, w, lane);
+    lds_barrier();
+    auto step = [&](const OutRegs& R, OutRegs& next, int c) {
+      out_fetch(next, ws, bb, bh, kh, min(c + 2, NC - 1), Hk, NC, w, lane);
+      // (Q H)^T against the same state copy as this chunk's U.
+      f32x4 accQ[NVB];
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) accQ[vb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb)
+          accQ[vb] = mfma16(ld_frag(&Sb[dvp(vb, li) * RP + kk * 32 + lg * 8]), R.q[kk], accQ[vb]);
+      lds_barrier();
+      // O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token blocks
+      // 0 and 1 need only s < 32.  Lane (li, lg) ends with dv 8lg..8lg+7 of
+      // token 16w + li (dvp order), one 8-wide store.
       const float gq = q_scale * __expf(R.gt);
       float ov[8];
 #pragma unroll
@@ -673,25 +705,15 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) ov[4 * vb + r] = fmaf(gq, accQ[vb][r], acc[r]);
       }
-      if (tr < n) store8(o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
-    }
-    lds_barrier();
-  };
-
-  for (int c = 0; c < NC; c += 2) {
-    step(RA, RB, c);
-    if (c + 1 < NC) step(RB, RA, c + 1);
-  }
-
-  if (state_out) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int vb = 0; vb < NVB; ++vb) {
-        const int dk = (2 * w + i) * 16 + lg * 4, dv = dv0 + vb * 16 + li;
-        *reinterpret_cast<float4*>(state_out + ((int64_t)bh * DH + dv) * DH + dk) =
-            make_float4(H[i][vb][0], H[i][vb][1], H[i][vb][2], H[i][vb][3]);
-      }
+      const int t0 = c * CK;
+      if (tr < min(CK, T - t0))
+        store8(o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
+      lds_barrier();
+    };
+    for (int c = 0; c < NC; c += 3) {
+      step(RA, RC, c);
+      if (c + 1 < NC) step(RB, RA, c + 1);
+      if (c + 2 < NC) step(RC, RB, c + 2);
     }
   }
 }
