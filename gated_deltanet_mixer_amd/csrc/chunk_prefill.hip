@@ -657,11 +657,14 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
                         H[i][vb][1], H[i][vb][2], H[i][vb][3]);
       lds_barrier();
     };
-    for (int c = 0; c < NC; c += 3) {
+    int c = 0;
+    for (; c + 3 <= NC; c += 3) {
       step(RA, RC, c);
-      if (c + 1 < NC) step(RB, RA, c + 1);
-      if (c + 2 < NC) step(RC, RB, c + 2);
+      step(RB, RA, c + 1);
+      step(RC, RB, c + 2);
     }
+    if (c < NC) step(RA, RC, c);
+    if (c + 1 < NC) step(RB, RA, c + 1);
 
     if (state_out) {
 #pragma unroll
@@ -710,11 +713,14 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
         store8(o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
       lds_barrier();
     };
-    for (int c = 0; c < NC; c += 3) {
+    int c = 0;
+    for (; c + 3 <= NC; c += 3) {
       step(RA, RC, c);
-      if (c + 1 < NC) step(RB, RA, c + 1);
-      if (c + 2 < NC) step(RC, RB, c + 2);
+      step(RB, RA, c + 1);
+      step(RC, RB, c + 2);
     }
+    if (c < NC) step(RA, RC, c);
+    if (c + 1 < NC) step(RB, RA, c + 1);
   }
 }
 
