@@ -41,15 +41,19 @@ def _gpu_prefill(x, state=None, algo="chunked", inplace=False):
     return o, so
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 150])
+CHUNK_ALGOS = ["chunked"]
+
+
+@pytest.mark.parametrize("algo", CHUNK_ALGOS)
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130, 150, 200])
 @pytest.mark.parametrize("A_range,state", [((-1.0, 1.0), 0.05), ((-6.0, -4.0), 0.5),
                                            ((-1.0, 1.0), None)])
-def test_chunked_small(T, A_range, state):
-    banner(f"chunked T={T} A_log~U{A_range} state={state}")
+def test_chunked_small(T, A_range, state, algo):
+    banner(f"{algo} T={T} A_log~U{A_range} state={state}")
     x = recurrence_inputs(2, T, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=T,
                           state_std=state, A_log_range=A_range)
     S0 = None if state is None else to_f64(x["state"])
-    o, S = _gpu_prefill(x, x["state"])
+    o, S = _gpu_prefill(x, x["state"], algo=algo)
     o_ref, S_ref = _ref(x, S0)
     assert max_rel_err(host_f64(o), o_ref) < TOL
     assert max_rel_err(host_f64(S), S_ref) < TOL
@@ -73,34 +77,37 @@ def test_chunked_f32_inputs_and_f32_output(T):
     assert max_rel_err(host_f64(so), S_ref) < TOL
 
 
+@pytest.mark.parametrize("algo", CHUNK_ALGOS)
 @pytest.mark.parametrize("gdt", ["bf16", "f32"])
-def test_chunked_gate_dtypes_and_inplace(gdt):
-    banner(f"chunked in-place state, gates {gdt}")
+def test_chunked_gate_dtypes_and_inplace(gdt, algo):
+    banner(f"{algo} in-place state, gates {gdt}")
     x = recurrence_inputs(1, 200, Hk=2, Hv=6, qkv_dt="bf16", gate_dt=gdt, seed=21, state_std=0.3,
                           A_log_range=(-5.0, -3.0))
-    o, S = _gpu_prefill(x, x["state"], inplace=True)
+    o, S = _gpu_prefill(x, x["state"], inplace=True, algo=algo)
     o_ref, S_ref = _ref(x, to_f64(x["state"]))
     assert max_rel_err(host_f64(o), o_ref) < TOL
     assert max_rel_err(host_f64(S), S_ref) < TOL
 
 
-def test_chunked_head_sharing_16_48():
-    banner("chunked Hk=16 Hv=48 T=100")
+@pytest.mark.parametrize("algo", CHUNK_ALGOS)
+def test_chunked_head_sharing_16_48(algo):
+    banner(f"{algo} Hk=16 Hv=48 T=100")
     x = recurrence_inputs(1, 100, qkv_dt="bf16", gate_dt="f32", seed=22, state_std=0.05)
-    o, S = _gpu_prefill(x, x["state"])
+    o, S = _gpu_prefill(x, x["state"], algo=algo)
     o_ref, S_ref = _ref(x, to_f64(x["state"]))
     assert max_rel_err(host_f64(o), o_ref) < TOL
     assert max_rel_err(host_f64(S), S_ref) < TOL
 
 
-def test_chunked_q_scale():
-    banner("chunked q_scale")
+@pytest.mark.parametrize("algo", CHUNK_ALGOS)
+def test_chunked_q_scale(algo):
+    banner(f"{algo} q_scale")
     x = recurrence_inputs(1, 80, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=23, state_std=0.1)
     si = dev(x["state"])
     so = torch.empty_like(si)
     o = gdn.gdn_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["a"]), dev(x["b"]),
                         dev(x["A_log"]), dev(x["dt_bias"]), si, so, q_scale=128 ** -0.5,
-                        algo="chunked")
+                        algo=algo)
     torch.cuda.synchronize()
     al, be, _ = oracle.gates(to_f64(x["a"]), to_f64(x["b"]), x["A_log"], x["dt_bias"])
     o_ref, S_ref = oracle.recurrence(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), al, be,
@@ -109,20 +116,22 @@ def test_chunked_q_scale():
     assert max_rel_err(host_f64(so), S_ref) < TOL
 
 
-def test_chunked_deterministic_and_matches_sequential():
-    banner("chunked determinism and chunked ~ sequential")
+@pytest.mark.parametrize("algo", CHUNK_ALGOS)
+def test_chunked_deterministic_and_matches_sequential(algo):
+    banner(f"{algo} determinism and ~ sequential")
     x = recurrence_inputs(1, 257, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=24,
                           state_std=0.05)
-    o1, S1 = _gpu_prefill(x, x["state"])
-    o2, S2 = _gpu_prefill(x, x["state"])
+    o1, S1 = _gpu_prefill(x, x["state"], algo=algo)
+    o2, S2 = _gpu_prefill(x, x["state"], algo=algo)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
     o3, S3 = _gpu_prefill(x, x["state"], algo="sequential")
     assert max_rel_err(host_f64(o1), host_f64(o3)) < TOL
     assert max_rel_err(host_f64(S1), host_f64(S3)) < TOL
 
 
-def test_split_calls_with_state_handoff():
-    banner("chunked 3 calls with handoff vs one oracle pass")
+@pytest.mark.parametrize("algo", CHUNK_ALGOS)
+def test_split_calls_with_state_handoff(algo):
+    banner(f"{algo} 3 calls with handoff vs one oracle pass")
     x = recurrence_inputs(1, 300, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=25,
                           state_std=0.05, A_log_range=(-5.0, -2.0))
     S = dev(x["state"])
@@ -131,7 +140,7 @@ def test_split_calls_with_state_handoff():
         part = {n: (x[n][:, t0:t1] if n in ("q", "k", "v", "a", "b") else x[n]) for n in x}
         o = gdn.gdn_prefill(dev(part["q"]), dev(part["k"]), dev(part["v"]), dev(part["a"]),
                             dev(part["b"]), dev(x["A_log"]), dev(x["dt_bias"]), S, S,
-                            algo="chunked")
+                            algo=algo)
         outs.append(o)
     torch.cuda.synchronize()
     o_ref, S_ref = _ref(x, to_f64(x["state"]))
@@ -154,13 +163,38 @@ def test_decode_rows_equals_prefill_of_one_token():
     assert max_rel_err(host_f64(st), host_f64(so)) < 1e-5
 
 
-def test_prefill_bf16_b1_t4096():
+@pytest.mark.parametrize("algo", ["auto"])
+def test_prefill_bf16_b1_t4096(algo):
     """The prefill workload at full size: B=1, T=4096, chunk 64, 16/48 heads,
     bf16 q/k/v, f32 gates, carried state ~N(0, 0.05)."""
-    banner("prefill_bf16_b1_t4096 full")
+    banner(f"prefill_bf16_b1_t4096 full {algo}")
     x = make_workload("prefill_bf16_b1_t4096")
-    o, S = _gpu_prefill(x, x["state"], algo="auto")
+    o, S = _gpu_prefill(x, x["state"], algo=algo)
     o_ref, S_ref = _ref(x, to_f64(x["state"]))
     e_o, e_s = max_rel_err(host_f64(o), o_ref), max_rel_err(host_f64(S), S_ref)
     print(f"prefill_bf16_b1_t4096: o err {e_o:.3e}, state err {e_s:.3e}")
     assert e_o < TOL and e_s < TOL
+
+
+def test_chunked_f32_output_and_strided_views():
+    """bf16 q/k/v read as strided views of one packed [B, T, 2*Hk*d + Hv*d]
+    tensor (how the layer hands them over), with an f32 o."""
+    banner("chunked f32 o, strided q/k/v views")
+    x = recurrence_inputs(2, 150, Hk=2, Hv=6, qkv_dt="bf16", gate_dt="f32", seed=31,
+                          state_std=0.05)
+    B, T = 2, 150
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    packed = torch.cat([q.flatten(2), k.flatten(2), v.flatten(2)], dim=2).contiguous()
+    qv = packed[:, :, :256].unflatten(2, (2, 128))
+    kv = packed[:, :, 256:512].unflatten(2, (2, 128))
+    vv = packed[:, :, 512:].unflatten(2, (6, 128))
+    si = dev(x["state"])
+    so = torch.empty_like(si)
+    o = torch.empty((B, T, 6, 128), dtype=torch.float32, device="cuda")
+    gdn.gdn_prefill(qv, kv, vv, dev(x["a"]), dev(x["b"]), dev(x["A_log"]), dev(x["dt_bias"]),
+                    si, so, o=o, algo="chunked")
+    torch.cuda.synchronize()
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(so), S_ref) < TOL
+
