@@ -195,11 +195,11 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
       st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tq, sb * 16 + lg * 4, 2), pv[0], pv[1],
                     pv[2], pv[3]);
     }
-    // Blocks above the diagonal of P are zero.
-#pragma unroll
-    for (int sb = tb + 1; sb < 4; ++sb)
-      st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tb * 16 + li, sb * 16 + lg * 4, 2), 0.f,
-                    0.f, 0.f, 0.f);
+    // Blocks above the diagonal of P are zero; the chain reads only (0,1)
+    // and (2,3) of them (P is used in 32-column steps).
+    if (tb == 0 || tb == 2)
+      st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tb * 16 + li, (tb + 1) * 16 + lg * 4, 2),
+                    0.f, 0.f, 0.f, 0.f);
   }
   lds_barrier();
 
@@ -434,17 +434,22 @@ __device__ __forceinline__ void state_fetch(StateRegs<NV>& R, const WsLayout& ws
   R.gl = gp[CK + (lane & 15)];  // G_last, replicated
 }
 
+// Q comes from the prep's fragment-order bf16 copy: reading the input rows
+// (16 rows a 64-byte piece each per load, rows a token stride apart) costs
+// the chain more than the copy costs the prep.
 __device__ __forceinline__ void out_fetch(OutRegs& R, const WsLayout& ws, int bb, int bh, int kh,
                                           int c, int Hk, int NC, int w, int lane) {
   const int64_t chunk = (int64_t)bh * NC + c;
+  const int li = lane & 15;
   const int64_t kchunk = ((int64_t)bb * Hk + kh) * NC + c;
   const uint16_t* qp = ws.Qb + kchunk * (CK * DH) + (w * 4 * 64 + lane) * 8;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) R.q[kk] = gld_frag(qp + kk * 512);
+  // P is causal: token blocks 0 and 1 use only its first 32 columns.
   const uint16_t* pp = ws.P + chunk * (CK * CK) + (w * 2 * 64 + lane) * 8;
   R.p[0] = gld_frag(pp);
-  R.p[1] = gld_frag(pp + 512);
-  R.gt = ws.G[chunk * 2 * CK + 16 * w + (lane & 15)];
+  R.p[1] = w >= 2 ? gld_frag(pp + 512) : zero_frag();
+  R.gt = ws.G[chunk * 2 * CK + 16 * w + li];
 }
 
 template <int NV, typename TO>
