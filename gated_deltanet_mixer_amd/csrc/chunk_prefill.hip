@@ -89,7 +89,7 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t R[DH * XP];
   __shared__ __attribute__((aligned(16))) uint16_t Tn[CK * XP];     // T, bf16, row-major
   __shared__ __attribute__((aligned(16))) uint16_t Tdt[4 * 16 * 16];  // diagonal blocks, transposed
-  __shared__ float Gs[CK], Bs[CK];
+  __shared__ __attribute__((aligned(16))) float Gs[CK], Bs[CK], BGs[CK];  // G, b, b e^G
   float* Ad = reinterpret_cast<float*>(R);       // [4][16][ADP]
   uint16_t* Ao = R + 4 * 16 * ADP * 2;           // [64][XP], off-diagonal blocks of A
   uint16_t* XT = R;
@@ -107,25 +107,31 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
   const TI* qbase = q + ((int64_t)bb * T + t0) * q_ts + kh * DH;
   const TI* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
 
-  // Every global load is issued first.  Wave w needs K blocks 0..w (its K K^T
-  // and Q K^T tiles), Q block w and V block w; wave 0 the gate inputs.
+  // Every global load is issued first.  Wave w's K K^T and Q K^T tiles
+  // (t block, s block; see the calls below) need four 16-row operand blocks:
+  //   w 0: K0 K1 Q0 Q1    w 1: K1 K3 Q3 -    w 2: K0 K1 K2 Q2    w 3: K0 K2 K3 Q3
+  // (nibble s of the wave's table: bit 3 used, bit 2 Q, bits 0-1 block), plus
+  // V block w; wave 0 also the gate inputs.
   float a_raw = 0.0f, b_raw = 0.0f;
   if (w == 0 && lane < n) {
     const int64_t gi = ((int64_t)bb * T + t0 + lane) * Hv + h;
     a_raw = load1(a + gi);
     b_raw = load1(b + gi);
   }
-  bf16x8 kf[4][4], kl[4][4], qf[4], ql[4], vf[4];
+  const unsigned slots = w == 0 ? 0xDC98u : w == 1 ? 0x0FB9u : w == 2 ? 0xEA98u : 0xFBA8u;
+  bf16x8 f[4][4], fl[4][4], vf[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int t = rb * 16 + li;
+  for (int sl = 0; sl < 4; ++sl) {
+    const int code = (slots >> (4 * sl)) & 15;
+    const int t = (code & 3) * 16 + li;
+    const TI* row = (code & 4) ? qbase + (int64_t)t * q_ts : kbase + (int64_t)t * k_ts;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      if (rb <= w && t < n) {
-        load_row8(kbase + (int64_t)t * k_ts + kk * 32 + lg * 8, kf[rb][kk], kl[rb][kk]);
+      if ((code & 8) && t < n) {
+        load_row8(row + kk * 32 + lg * 8, f[sl][kk], fl[sl][kk]);
       } else {
-        kf[rb][kk] = zero_frag();
-        kl[rb][kk] = zero_frag();
+        f[sl][kk] = zero_frag();
+        fl[sl][kk] = zero_frag();
       }
     }
   }
@@ -134,12 +140,8 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       bf16x8 unused;
-      if (t < n) {
-        load_row8(qbase + (int64_t)t * q_ts + kk * 32 + lg * 8, qf[kk], ql[kk]);
-        load_row8(vbase + (int64_t)t * v_ts + kk * 32 + lg * 8, vf[kk], unused);
-      } else {
-        qf[kk] = zero_frag(); ql[kk] = zero_frag(); vf[kk] = zero_frag();
-      }
+      if (t < n) load_row8(vbase + (int64_t)t * v_ts + kk * 32 + lg * 8, vf[kk], unused);
+      else vf[kk] = zero_frag();
     }
   }
 
@@ -153,53 +155,69 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     const float Gl = wave_scan(g, lane);
     Gs[lane] = Gl;
     Bs[lane] = be;
+    BGs[lane] = be * __expf(Gl);
     ws.G[chunk * 2 * CK + lane] = Gl;
     ws.G[chunk * 2 * CK + CK + lane] = __shfl(Gl, CK - 1);
   }
   lds_barrier();
 
-  // Token block w: K K^T -> A (lower blocks), (Q K^T)^T -> P rows of block w.
+  // K K^T tile (tb, sb) from slots (st, ss) -> A: D[t][s], lane (li = s, lg)
+  // holds t = 16 tb + 4 lg + r; the diagonal blocks in f32, the others bf16.
+  auto kkt = [&](int st, int ss, int tb, int sb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    if (tb != w) continue;
+    for (int kk = 0; kk < 4; ++kk) acc = mfma16(f[st][kk], f[ss][kk], acc);
+    const int s = sb * 16 + li;
 #pragma unroll
-    for (int sb = 0; sb <= tb; ++sb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma16(kf[tb][kk], kf[sb][kk], acc);
-      const int s = sb * 16 + li;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tb * 16 + lg * 4 + r;
-        const float av = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * acc[r] : 0.0f;
-        if (sb == tb) Ad[(tb * 16 + lg * 4 + r) * ADP + li] = av;
-        else Ao[t * XP + s] = f2bf(av);
-      }
-      // (Q K^T)^T tile [s block sb][t block tb]: C[s][t] = K_s . Q_t.
-      f32x4 pq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        pq = mfma16(kf[sb][kk], qf[kk], pq);
-        if (kSplit) {
-          pq = mfma16(kf[sb][kk], ql[kk], pq);
-          pq = mfma16(kl[sb][kk], qf[kk], pq);
-        }
-      }
-      const int tq = tb * 16 + li;
-      float pv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int sq = sb * 16 + lg * 4 + r;
-        pv[r] = (sq <= tq) ? q_scale * __expf(Gs[tq] - Gs[sq]) * pq[r] : 0.0f;
-      }
-      st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tq, sb * 16 + lg * 4, 2), pv[0], pv[1],
-                    pv[2], pv[3]);
+    for (int r = 0; r < 4; ++r) {
+      const int t = tb * 16 + lg * 4 + r;
+      const float av = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * acc[r] : 0.0f;
+      if (sb == tb) Ad[(tb * 16 + lg * 4 + r) * ADP + li] = av;
+      else Ao[t * XP + s] = f2bf(av);
     }
-    // Blocks above the diagonal of P are zero; the chain reads only (0,1)
-    // and (2,3) of them (P is used in 32-column steps).
-    if (tb == 0 || tb == 2)
-      st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tb * 16 + li, (tb + 1) * 16 + lg * 4, 2),
-                    0.f, 0.f, 0.f, 0.f);
+  };
+  // (Q K^T)^T tile [s block sb][t block tb] from Q slot qs and K slot ks:
+  // C[s][t] = K_s . Q_t -> P in the chain's fragment order.
+  auto qkt = [&](int qs, int ks, int tb, int sb) {
+    f32x4 pq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      pq = mfma16(f[ks][kk], f[qs][kk], pq);
+      if (kSplit) {
+        pq = mfma16(f[ks][kk], fl[qs][kk], pq);
+        pq = mfma16(fl[ks][kk], f[qs][kk], pq);
+      }
+    }
+    const int tq = tb * 16 + li;
+    float pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int sq = sb * 16 + lg * 4 + r;
+      pv[r] = (sq <= tq) ? q_scale * __expf(Gs[tq] - Gs[sq]) * pq[r] : 0.0f;
+    }
+    st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tq, sb * 16 + lg * 4, 2), pv[0], pv[1],
+                  pv[2], pv[3]);
+  };
+  // Zero tile of P above the diagonal at (tb, tb + 1): the chain reads (0,1)
+  // and (2,3) of them (P is used in 32-column steps).
+  auto pzero = [&](int tb) {
+    st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tb * 16 + li, (tb + 1) * 16 + lg * 4, 2),
+                  0.f, 0.f, 0.f, 0.f);
+  };
+  if (w == 0) {
+    kkt(0, 0, 0, 0); kkt(1, 0, 1, 0);
+    qkt(2, 0, 0, 0); qkt(3, 0, 1, 0); qkt(3, 1, 1, 1);
+    pzero(0);
+  } else if (w == 1) {
+    kkt(0, 0, 1, 1); kkt(1, 0, 3, 1);
+    qkt(2, 0, 3, 1); qkt(2, 1, 3, 3);
+  } else if (w == 2) {
+    kkt(2, 2, 2, 2); kkt(2, 0, 2, 0); kkt(2, 1, 2, 1);
+    qkt(3, 0, 2, 0); qkt(3, 1, 2, 1); qkt(3, 2, 2, 2);
+    pzero(2);
+  } else {
+    kkt(2, 2, 3, 3); kkt(2, 0, 3, 0); kkt(2, 1, 3, 2);
+    qkt(3, 0, 3, 0); qkt(3, 1, 3, 2);
   }
   lds_barrier();
 
@@ -269,49 +287,30 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
   }
   lds_barrier();
 
-  // K^T of token block w into LDS (the A blocks are no longer needed).
+  // K^T of token block w into LDS (the A blocks are no longer needed); K
+  // block w is in slot 0 for waves 0 and 1 and in slot 2 for waves 2 and 3.
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    if (rb != w) continue;
+  for (int kk = 0; kk < 4; ++kk) {
+    const u16x8 bits = frag_bits(w < 2 ? f[0][kk] : f[2][kk]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u16x8 bits = frag_bits(kf[rb][kk]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) XT[(kk * 32 + lg * 8 + i) * XP + rb * 16 + li] = bits[i];
-    }
+    for (int i = 0; i < 8; ++i) XT[(kk * 32 + lg * 8 + i) * XP + w * 16 + li] = bits[i];
   }
-  // Rows of T diag(b gamma) and T diag(b), as MFMA operands: [t block][k step].
-  bf16x8 tgf[4][2], tbf[4][2];
-  {
-    float sg[2][8], sb8[2][8];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int s = kk * 32 + lg * 8 + i;
-        sb8[kk][i] = Bs[s];
-        sg[kk][i] = Bs[s] * __expf(Gs[s]);
-      }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const u16x8 raw =
-            *reinterpret_cast<const u16x8*>(&Tn[(tb * 16 + li) * XP + kk * 32 + lg * 8]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float tv = bf2f(raw[i]);
-          tgf[tb][kk][i] = (__bf16)(tv * sg[kk][i]);
-          tbf[tb][kk][i] = (__bf16)(tv * sb8[kk][i]);
-        }
-      }
-  }
-  // bf16 Q for the chain (Qf: the fragments as held here), once per q/k head.
+  // bf16 Q for the chain (Qf: the fragments as held here), once per q/k head:
+  // Q blocks 0 and 1 from wave 0's slots 2 and 3, Q block w from slot 3 of
+  // waves 2 and 3.
   if (h % grp == 0) {
     uint16_t* dst = ws.Qb + (((int64_t)bb * Hk + kh) * NC + c) * (CK * DH);
+    if (w == 0) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      *reinterpret_cast<u16x8*>(dst + ((w * 4 + kk) * 64 + lane) * 8) = frag_bits(qf[kk]);
+      for (int kk = 0; kk < 4; ++kk) {
+        *reinterpret_cast<u16x8*>(dst + ((0 * 4 + kk) * 64 + lane) * 8) = frag_bits(f[2][kk]);
+        *reinterpret_cast<u16x8*>(dst + ((1 * 4 + kk) * 64 + lane) * 8) = frag_bits(f[3][kk]);
+      }
+    } else if (w >= 2) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        *reinterpret_cast<u16x8*>(dst + ((w * 4 + kk) * 64 + lane) * 8) = frag_bits(f[3][kk]);
+    }
   }
   lds_barrier();
 
@@ -328,21 +327,42 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     }
   }
 
+  // Rows of T scaled by a per-column factor (b gamma for W, b for Ut), as an
+  // MFMA operand, read from LDS when needed.
+  auto trow = [&](int tb, int kk, const float* colscale) {
+    const u16x8 raw = *reinterpret_cast<const u16x8*>(&Tn[(tb * 16 + li) * XP + kk * 32 + lg * 8]);
+    const float4 s0 = *reinterpret_cast<const float4*>(&colscale[kk * 32 + lg * 8]);
+    const float4 s1 = *reinterpret_cast<const float4*>(&colscale[kk * 32 + lg * 8 + 4]);
+    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    bf16x8 f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (__bf16)(bf2f(raw[i]) * sc[i]);
+    return f;
+  };
+
   // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T, stored as Wf;
   // wave w takes dk blocks 2w and 2w+1.  T is lower triangular, so t blocks 0
   // and 1 need only s < 32.
+  {
+    bf16x8 kt[2][2];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    if ((db >> 1) != w) continue;
-    const bf16x8 kt0 = ld_frag(&XT[(db * 16 + li) * XP + lg * 8]);
-    const bf16x8 kt1 = ld_frag(&XT[(db * 16 + li) * XP + 32 + lg * 8]);
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        kt[d][kk] = ld_frag(&XT[((2 * w + d) * 16 + li) * XP + kk * 32 + lg * 8]);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(kt0, tgf[tb][0], acc);
-      if (tb >= 2) acc = mfma16(kt1, tgf[tb][1], acc);
-      const int t = tb * 16 + li, dk = db * 16 + lg * 4;
-      st4<uint16_t>(ws.W + chunk * (CK * DH) + frag_off(t, dk, 4), acc[0], acc[1], acc[2], acc[3]);
+      const bf16x8 tg0 = trow(tb, 0, BGs);
+      const bf16x8 tg1 = tb >= 2 ? trow(tb, 1, BGs) : zero_frag();
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(kt[d][0], tg0, acc);
+        if (tb >= 2) acc = mfma16(kt[d][1], tg1, acc);
+        const int t = tb * 16 + li, dk = (2 * w + d) * 16 + lg * 4;
+        st4<uint16_t>(ws.W + chunk * (CK * DH) + frag_off(t, dk, 4), acc[0], acc[1], acc[2],
+                      acc[3]);
+      }
     }
   }
   lds_barrier();
@@ -358,16 +378,22 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
 
   // Ut tiles [t block][dv block] = (T diag(b)) V, stored as Utf; wave w takes
   // dv blocks 2w and 2w+1.
+  bf16x8 vt[2][2];
 #pragma unroll
-  for (int vb = 0; vb < 8; ++vb) {
-    if ((vb >> 1) != w) continue;
-    const bf16x8 v0 = ld_frag(&XT[(vb * 16 + li) * XP + lg * 8]);
-    const bf16x8 v1 = ld_frag(&XT[(vb * 16 + li) * XP + 32 + lg * 8]);
+  for (int d = 0; d < 2; ++d)
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int kk = 0; kk < 2; ++kk)
+      vt[d][kk] = ld_frag(&XT[((2 * w + d) * 16 + li) * XP + kk * 32 + lg * 8]);
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    const bf16x8 tb0 = trow(tb, 0, Bs);
+    const bf16x8 tb1 = tb >= 2 ? trow(tb, 1, Bs) : zero_frag();
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int vb = 2 * w + d;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(tbf[tb][0], v0, acc);
-      if (tb >= 2) acc = mfma16(tbf[tb][1], v1, acc);
+      acc = mfma16(tb0, vt[d][0], acc);
+      if (tb >= 2) acc = mfma16(tb1, vt[d][1], acc);
       // Utf[sl = vb / 2][w = tb][cvb][cli + 16 lg][0..3] with dvp(cvb, cli) = the
       // column within the slice, 16 (vb % 2) + li.
       const int col = 16 * (vb & 1) + li;
