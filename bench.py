@@ -229,7 +229,7 @@ def main():
                 "kernel": "gdn_prefill chunked: chunk_prep_kernel + chunk_chain_kernel (two launches)",
                 "achieved": round(ach_p, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach_p / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": _traffic("prefill_chunked", ["chunk_prefill.hip", "common.hpp"]),
+                "traffic": _traffic("prefill_chunked", ["chunk_prefill.hip", "chunk_common.hpp", "common.hpp"]),
                 "flops_per_launch": pre_flops, "avg_launch_us": round(t_pre * 1e3, 2)}
     roofline, roofline_other = (roof_pre, roof_dec) if t_pre >= t_dec else (roof_dec, roof_pre)
 
