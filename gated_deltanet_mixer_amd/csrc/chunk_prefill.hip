@@ -28,6 +28,8 @@
 //    Each wave loads its own operands two chunks ahead straight into
 //    registers; the bf16 copy of the state and U^T are exchanged in LDS.
 //    The dv columns of H are independent, which is what allows the slicing.
+#include <type_traits>
+
 #include "chunk_common.hpp"
 #include "launch.hpp"
 
@@ -94,8 +96,16 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
   uint16_t* Ao = R + 4 * 16 * ADP * 2;           // [64][XP], off-diagonal blocks of A
   uint16_t* XT = R;
 
-  const int c = blockIdx.x % NC;
-  const int bh = blockIdx.x / NC;
+  // Chunk-major order: the workgroups of one chunk index run together, so the
+  // chain, which reads chunk 0 first, finds every head's data equally recent
+  // in the last-level cache.  Within a round of 8 ids (one per XCD) the value
+  // heads are spread so that each XCD takes a contiguous range of heads, which
+  // keeps the value heads of one q/k group on one XCD when the range is a
+  // whole number of groups (48 heads: 6 per XCD, groups of 3).
+  const int nbh = gridDim.x / NC;
+  const int c = blockIdx.x / nbh;
+  const int r = blockIdx.x % nbh;
+  const int bh = (nbh & 7) == 0 ? (r & 7) * (nbh >> 3) + (r >> 3) : r;
   const int h = bh % Hv, bb = bh / Hv;
   const int grp = Hv / Hk, kh = h / grp;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
@@ -474,7 +484,9 @@ __device__ __forceinline__ void out_fetch(OutRegs& R, const WsLayout& ws, int bb
   // P is causal: token blocks 0 and 1 use only its first 32 columns.
   const uint16_t* pp = ws.P + chunk * (CK * CK) + (w * 2 * 64 + lane) * 8;
   R.p[0] = gld_frag(pp);
-  R.p[1] = w >= 2 ? gld_frag(pp + 512) : zero_frag();
+  // Loaded unconditionally (waves 0 and 1 reload the first tile and ignore
+  // it), so the compiler's count of loads in flight stays exact.
+  R.p[1] = gld_frag(pp + (w >= 2 ? 512 : 0));
   R.gt = ws.G[chunk * 2 * CK + 16 * w + li];
 }
 
@@ -489,16 +501,18 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
   __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
 
-  // Workgroups whose ids agree mod 8 run on the same XCD: keep the NSL slices
-  // of one head there so they share its L2 for W, P, K^T, G and Q.
+  // Workgroups whose ids agree mod 8 run on the same XCD.  Each XCD takes a
+  // contiguous range of (head, slice) units, so the NSL slices of a head, and
+  // the value heads of one q/k group, share its L2 for W, P, K^T, G and Q.
   const int id = blockIdx.x;
-  const int hs = (id >> 3) / NSL * 8 + (id & 7);
-  const int sl = (id >> 3) % NSL;
-  if (hs >= B * Hv) return;
+  const int units = B * Hv * NSL, per_xcd = (units + 7) / 8;
+  const int u = (id & 7) * per_xcd + (id >> 3);
+  if (u >= units) return;
+  const int hs = u / NSL, sl = u % NSL;
   const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
   const int dv0 = sl * NV;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int w = (tid >> 6) & 3;
+  const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
   const bool state_wave = tid < 256;
 
   if (state_wave) {
@@ -528,6 +542,8 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     // Chunk c + 2 is loaded at step c; past the last chunk the loads repeat it
     // (unconditional loads keep the compiler's count of loads in flight exact).
     auto step = [&](const StateRegs<NV>& R, StateRegs<NV>& next, int c) {
+      // Scheduling fence: no work of one chunk step moves into another.
+      __builtin_amdgcn_sched_barrier(0);
       state_fetch<NV>(next, ws, bb, bh, kh, min(c + 2, NC - 1), Hk, NC, sl, w, lane);
       // (1) U = Ut - W H against the bf16 state copy, dv rows in dvp order.
       f32x4 accU[NVB];
@@ -605,8 +621,10 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     out_fetch(RA, ws, bb, bh, kh, 0, Hk, NC, w, lane);
     out_fetch(RB, ws, bb, bh, kh, min(1, NC - 1), Hk, NC, w, lane);
     lds_barrier();
-    auto step = [&](const OutRegs& R, OutRegs& next, int c) {
-      out_fetch(next, ws, bb, bh, kh, min(c + 2, NC - 1), Hk, NC, w, lane);
+    // `full` (std::true_type) marks a chunk of CK tokens, whose store needs no
+    // row check.
+    auto step = [&](const OutRegs& R, OutRegs& next, int c, auto full) {
+      __builtin_amdgcn_sched_barrier(0);
       // (Q H)^T against the same state copy as this chunk's U.
       f32x4 accQ[NVB];
 #pragma unroll
@@ -616,6 +634,12 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb)
           accQ[vb] = mfma16(ld_frag(&Sb[dvp(vb, li) * RP + kk * 32 + lg * 8]), R.q[kk], accQ[vb]);
+      // The loads of chunk c + 2 go out after (Q H)^T: issued at the start of
+      // the step they queue behind the state waves' loads, and (Q H)^T gates
+      // the first barrier.
+      __builtin_amdgcn_sched_barrier(0);
+      out_fetch(next, ws, bb, bh, kh, min(c + 2, NC - 1), Hk, NC, w, lane);
+      __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       // O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token blocks
       // 0 and 1 need only s < 32.  Lane (li, lg) ends with dv 8lg..8lg+7 of
@@ -631,18 +655,20 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
         for (int r = 0; r < 4; ++r) ov[4 * vb + r] = fmaf(gq, accQ[vb][r], acc[r]);
       }
       const int t0 = c * CK;
-      if (tr < min(CK, T - t0))
+      if (decltype(full)::value || tr < min(CK, T - t0))
         store8(o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
       lds_barrier();
     };
     int c = 0;
-    for (; c + 3 <= NC; c += 3) {
-      step(RA, RC, c);
-      step(RB, RA, c + 1);
-      step(RC, RB, c + 2);
+    const int nfull = T / CK;
+    for (; c + 3 <= nfull; c += 3) {
+      step(RA, RC, c, std::true_type{});
+      step(RB, RA, c + 1, std::true_type{});
+      step(RC, RB, c + 2, std::true_type{});
     }
-    if (c < NC) step(RA, RC, c);
-    if (c + 1 < NC) step(RB, RA, c + 1);
+    if (c < NC) step(RA, RC, c, std::false_type{});
+    if (c + 1 < NC) step(RB, RA, c + 1, std::false_type{});
+    if (c + 2 < NC) step(RC, RB, c + 2, std::false_type{});
   }
 }
 
@@ -665,9 +691,9 @@ void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
                   hipStream_t stream) {
   constexpr int NV = 32;
   constexpr int NSL = DH / NV;
-  const int64_t heads = (int64_t)B * Hv;
-  const int64_t groups = (heads + 7) / 8;  // ids are padded to whole XCD rounds
-  hipLaunchKernelGGL((chunk_chain_kernel<NV, TO>), dim3((unsigned)(groups * 8 * NSL)),
+  const int64_t units = (int64_t)B * Hv * NSL;
+  const int64_t per_xcd = (units + 7) / 8;  // ids are padded to whole XCD rounds
+  hipLaunchKernelGGL((chunk_chain_kernel<NV, TO>), dim3((unsigned)(per_xcd * 8)),
                      dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, Hk, Hv,
                      NC, q_scale);
 }
