@@ -80,7 +80,7 @@ size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
 constexpr int PREP_THREADS = 256;
 
 template <typename TI, typename G_T>
-__global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
+__global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     const TI* __restrict__ q, int64_t q_ts, const TI* __restrict__ k, int64_t k_ts,
     const TI* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
     const G_T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
@@ -145,7 +145,11 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
       }
     }
   }
-  {
+  // V block w.  With f32 input it is loaded once the K K^T / Q K^T tiles are
+  // done and the low halves of the split are dead: loaded at entry, its f32
+  // words in flight would push the kernel past the 168 registers that let
+  // three workgroups share a SIMD.
+  auto load_v = [&]() {
     const int t = w * 16 + li;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -153,7 +157,8 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
       if (t < n) load_row8(vbase + (int64_t)t * v_ts + kk * 32 + lg * 8, vf[kk], unused);
       else vf[kk] = zero_frag();
     }
-  }
+  };
+  if (!kSplit) load_v();
 
   // Gates for token `lane` (wave 0); padding tokens get g = 0, b = 0.
   if (w == 0) {
@@ -229,6 +234,7 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     kkt(2, 2, 3, 3); kkt(2, 0, 3, 0); kkt(2, 1, 3, 2);
     qkt(3, 0, 3, 0); qkt(3, 1, 3, 2);
   }
+  if (kSplit) load_v();
   lds_barrier();
 
   // T, diagonal blocks (wave 0): lane (block lg, column li), forward
