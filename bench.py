@@ -2,10 +2,9 @@
 
 One step = one pass of the whole hot path on seeded synthetic inputs shaped
 like the model's layer (16 q/k heads, 48 value heads, width 128):
-  1. the layer prefill at B=1, T=4096: gdn_conv_silu (10240 channels, width 4,
-     silu, L2 of q/k; f32 output) -> gdn_prefill (chunked, state carried in and
-     out, q/k/v read as strided views of the conv output, bf16 o) ->
-     gdn_gated_rmsnorm;
+  1. the layer prefill at B=1, T=4096: one gdn_mixer_prefill call (conv over
+     10240 channels, width 4, silu, L2 of q/k -> chunked prefill with the state
+     carried in and out -> gated RMSNorm with z);
   2. gdn_prefill alone on the prefill workload (B=1, T=4096, bf16 q/k/v, f32
      gates, carried state ~N(0, 0.05), chunk 64);
   3. gdn_decode_rows on 64 fixed rows (state [64,48,128,128] f32, in place).
@@ -145,9 +144,9 @@ def main():
             "conv_w": dev(mx["conv_w"]), "A_log": dev(mx["A_log"]), "dt_bias": dev(mx["dt_bias"]),
             "norm_w": dev(mx["norm_w"]), "state": dev(st_layer),
             "conv_state": torch.zeros((1, 3, C_CONV), dtype=torch.float32, device="cuda"),
-            "y": torch.empty((1, T_PREFILL, C_CONV), dtype=torch.float32, device="cuda"),
-            "o": torch.empty((1, T_PREFILL, HV, D), dtype=torch.bfloat16, device="cuda"),
-            "out": torch.empty((1, T_PREFILL, HV, D), dtype=torch.bfloat16, device="cuda"),
+            "out": torch.empty((1, T_PREFILL, HV * D), dtype=torch.bfloat16, device="cuda"),
+            "ws": torch.empty(gdn.gdn_mixer_prefill_workspace_bytes(1, T_PREFILL, HK, HV),
+                              dtype=torch.uint8, device="cuda"),
         })
     px = make_workload("prefill_bf16_b1_t4096")
     pre = []
@@ -168,33 +167,25 @@ def main():
         L, P, Dd = layer[s], pre[s], dec[s]
         if ev is not None:
             ev[0].record()
-        y = gdn.gdn_conv_silu(L["qkv"], L["conv_w"], L["conv_state"], l2_channels=2 * HK * D,
-                              head_dim=D, y=L["y"])
-        q = y[:, :, :HK * D].unflatten(2, (HK, D))
-        k = y[:, :, HK * D:2 * HK * D].unflatten(2, (HK, D))
-        v = y[:, :, 2 * HK * D:].unflatten(2, (HV, D))
+        gdn.gdn_mixer_prefill(L["qkv"], L["z"], L["conv_w"], L["a"], L["b"], L["A_log"],
+                              L["dt_bias"], L["norm_w"], HK, HV, conv_state=L["conv_state"],
+                              state_in=L["state"], state_out=L["state"], y=L["out"],
+                              workspace=L["ws"])
         if ev is not None:
             ev[1].record()
-        gdn.gdn_prefill(q, k, v, L["a"], L["b"], L["A_log"], L["dt_bias"], L["state"], L["state"],
-                        o=L["o"], algo="chunked", workspace=ws[s])
-        if ev is not None:
-            ev[2].record()
-        gdn.gdn_gated_rmsnorm(L["o"], L["z"].view(1, T_PREFILL, HV, D), L["norm_w"], y=L["out"])
-        if ev is not None:
-            ev[3].record()
         gdn.gdn_prefill(P["q"], P["k"], P["v"], P["a"], P["b"], P["A_log"], P["dt_bias"],
                         P["state"], P["state"], o=P["o"], workspace=ws[s])
         if ev is not None:
-            ev[4].record()
+            ev[2].record()
         gdn.gdn_decode_rows(Dd["q"], Dd["k"], Dd["v"], Dd["a"], Dd["b"], Dd["A_log"],
                             Dd["dt_bias"], Dd["state"], Dd["lengths"], o=Dd["o"])
         if ev is not None:
-            ev[5].record()
+            ev[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -202,14 +193,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
-    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)]
+    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
                       for i in range(args.steps)])  # ms
     mean = parts.mean(axis=0)
-    t_conv, t_lpre, t_norm, t_pre, t_dec = mean
+    t_layer, t_pre, t_dec = mean
     ms_per_step = wall * 1e3 / args.steps
 
     prefill_tps = T_PREFILL / (t_pre * 1e-3)
-    layer_tps = T_PREFILL / ((t_conv + t_lpre + t_norm) * 1e-3)
+    layer_tps = T_PREFILL / (t_layer * 1e-3)
     dec_bytes = decode_bytes_per_launch()
     state_bytes = 2 * R_DECODE * HV * D * D * 4
     dec_gbps = state_bytes / (t_dec * 1e-3) / 1e9
@@ -260,17 +251,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill_bf16_b1_t4096", "B": 1, "T": T_PREFILL, "chunk": 64,
                    "qk_heads": HK, "v_heads": HV, "head_dim": D,
-                   "step": "layer prefill (conv+silu+L2 -> chunked prefill -> gated RMSNorm) "
-                           "at B=1 T=4096, prefill workload at B=1 T=4096, decode_rows at 64 "
-                           "rows"},
+                   "step": "layer prefill (gdn_mixer_prefill: conv+silu+L2 -> chunked prefill "
+                           "-> gated RMSNorm) at B=1 T=4096, prefill workload at B=1 T=4096, "
+                           "decode_rows at 64 rows"},
         "decode_rows": {"value": round(dec_gbps, 1), "unit": "GB/s (state bytes read+written)",
                         "workload": "decode_rows_r64", "avg_launch_us": round(t_dec * 1e3, 2),
                         "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4)},
         "layer_prefill": {"value": round(layer_tps, 1), "unit": "tokens/s",
-                          "workload": "conv+silu+L2 -> chunked prefill -> gated RMSNorm, B=1 "
-                                      "T=4096, 10240 conv channels",
-                          "conv_us": round(t_conv * 1e3, 2), "prefill_us": round(t_lpre * 1e3, 2),
-                          "norm_us": round(t_norm * 1e3, 2)},
+                          "workload": "gdn_mixer_prefill (conv+silu+L2 -> chunked prefill -> "
+                                      "gated RMSNorm), B=1 T=4096, 10240 conv channels",
+                          "call_us": round(t_layer * 1e3, 2)},
         "prefill": {"avg_launch_us": round(t_pre * 1e3, 2),
                     "mfma_tflops": round(pre_flops / (t_pre * 1e-3) / 1e12, 2),
                     "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9,

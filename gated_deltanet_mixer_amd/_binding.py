@@ -56,6 +56,11 @@ def lib():
         L.gdn_decode_rows.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [P, P, P, i32, P, i32, i32, i32, f32, P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn_mixer_prefill_workspace_bytes.argtypes = [i32, i32, gdn_dims]
+        L.gdn_mixer_prefill_workspace_bytes.restype = sz
+        L.gdn_mixer_prefill.argtypes = [P, P, i32, P, P, P, P, i32, P, P, P, P, P, P, i32, i32,
+                                        gdn_dims, f32, f32, f32, P, sz, P]
+        L.gdn_mixer_prefill.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -198,4 +203,40 @@ def gdn_gated_rmsnorm(x, z, w, eps=1e-6, y=None):
     _check(lib().gdn_gated_rmsnorm(_ptr(x), _ptr(z), _ptr(y), _dt(x), _ptr(w), N, H, D, eps,
                                    _stream(x)),
            "gdn_gated_rmsnorm")
+    return y
+
+
+def gdn_mixer_prefill_workspace_bytes(B, T, Hk, Hv, dk=128, dv=128):
+    return int(lib().gdn_mixer_prefill_workspace_bytes(B, T, gdn_dims(Hk, Hv, dk, dv)))
+
+
+def gdn_mixer_prefill(qkv, z, conv_w, a, b, A_log, dt_bias, norm_w, Hk, Hv, conv_state=None,
+                      state_in=None, state_out=None, y=None, q_scale=1.0, l2_eps=1e-6,
+                      norm_eps=1e-6, workspace=None):
+    """Whole mixer between the projections: conv + silu + L2 over qkv [B,T,C],
+    the gated delta rule (state carried in/out) and the gated RMSNorm with z
+    [B,T,Hv*128].  Returns y [B,T,Hv*128] in qkv's dtype."""
+    _need_cuda(qkv, z, conv_w, a, b, A_log, dt_bias, norm_w, conv_state, state_in, state_out, y,
+               workspace)
+    B, T, C = qkv.shape
+    if C != 2 * Hk * 128 + Hv * 128:
+        raise ValueError(f"qkv has {C} channels, expected {2 * Hk * 128 + Hv * 128}")
+    if y is None:
+        y = torch.empty((B, T, Hv * 128), dtype=qkv.dtype, device=qkv.device)
+    for t in (qkv, z, y, conv_w, a, b, norm_w):
+        assert t.is_contiguous()
+    assert z.dtype == qkv.dtype and y.dtype == qkv.dtype and z.shape == y.shape
+    for s in (conv_state, state_in, state_out):
+        if s is not None:
+            assert s.is_contiguous() and s.dtype == torch.float32
+    need = gdn_mixer_prefill_workspace_bytes(B, T, Hk, Hv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_mixer_prefill(_ptr(qkv), _ptr(z), _dt(qkv), _ptr(conv_w), _ptr(conv_state),
+                                   _ptr(a), _ptr(b), _dt(a), _ptr(A_log), _ptr(dt_bias),
+                                   _ptr(norm_w), _ptr(state_in), _ptr(state_out), _ptr(y), B, T,
+                                   gdn_dims(Hk, Hv, 128, 128), q_scale, l2_eps, norm_eps,
+                                   _ptr(workspace), ws_bytes, _stream(qkv)),
+           "gdn_mixer_prefill")
     return y

@@ -8,6 +8,26 @@
 namespace {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+// The whole mixer's workspace: the conv output (q|k in f32, v in bf16), then
+// the chunked prefill's workspace.
+struct MixerWs {
+  size_t qk_bytes, v_bytes, chunk_bytes;
+  size_t total() const { return qk_bytes + v_bytes + chunk_bytes; }
+};
+MixerWs mixer_ws(int32_t B, int32_t T, const gdn_dims& d) {
+  MixerWs w;
+  w.qk_bytes = round256((size_t)B * T * 2 * d.n_qk_heads * d.head_k_dim * 4);
+  w.v_bytes = round256((size_t)B * T * d.n_v_heads * d.head_v_dim * 2);
+  w.chunk_bytes = gdn::prefill_chunked_workspace_bytes(B, T, d.n_qk_heads, d.n_v_heads);
+  return w;
+}
 bool dtype_ok(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
 size_t dsize(int32_t d) { return d == GDN_BF16 ? 2 : 4; }
 
@@ -111,8 +131,8 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
     if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
     return launch_status(gdn::launch_prefill_chunked(
-        q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, a, b, gate_dt, A_log, dt_bias,
-        state_in, state_out, o, o_dt, B, T, Hk, Hv, q_scale, workspace, s));
+        q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, qkv_dt, a, b, gate_dt, A_log,
+        dt_bias, state_in, state_out, o, o_dt, B, T, Hk, Hv, q_scale, workspace, s));
   }
   // Sequential algorithm (also the T == 0 state pass-through).
   return launch_status(gdn::launch_prefill_sequential(
@@ -160,6 +180,61 @@ int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const f
   if (rows == 0) return GDN_OK;
   return launch_status(
       gdn::launch_gated_rmsnorm(x, z, y, dt, w, rows, eps, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims) {
+  if (B <= 0 || T <= 0 || check_dims(dims) != GDN_OK) return 0;
+  return mixer_ws(B, T, dims).total();
+}
+
+int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* conv_w,
+                      float* conv_state, const void* a, const void* b, int32_t gate_dt,
+                      const float* A_log, const float* dt_bias, const float* norm_w,
+                      const float* state_in, float* state_out, void* y, int32_t B, int32_t T,
+                      gdn_dims dims, float q_scale, float l2_eps, float norm_eps,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!conv_w || !A_log || !dt_bias || !norm_w) return GDN_ERR_NULL;
+  if (T != 0 && (!qkv || !z || !a || !b || !y)) return GDN_ERR_NULL;
+  if (!dtype_ok(dt) || !dtype_ok(gate_dt)) return GDN_ERR_DTYPE;
+  int st = check_dims(dims);
+  if (st != GDN_OK) return st;
+  const int Hk = dims.n_qk_heads, Hv = dims.n_v_heads;
+  const int L2C = 2 * Hk * 128, C = L2C + Hv * 128;
+  if (B < 0 || T < 0) return GDN_ERR_SHAPE;
+  if ((int64_t)B * Hv * 8 > INT32_MAX || (int64_t)B * T > INT32_MAX) return GDN_ERR_SHAPE;
+  if (B > 65535 || (T + 7) / 8 > 65535) return GDN_ERR_SHAPE;  // conv grid limits
+  if (!aligned(qkv, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(conv_w, 16) ||
+      (conv_state && !aligned(conv_state, 16)) || !aligned(a, dsize(gate_dt)) ||
+      !aligned(b, dsize(gate_dt)) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
+      !aligned(norm_w, 16) || (state_in && !aligned(state_in, 16)) ||
+      (state_out && !aligned(state_out, 16)))
+    return GDN_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 0) return GDN_OK;
+  if (T == 0)  // no tokens: conv history unchanged, the state passes through
+    return launch_status(gdn::launch_prefill_sequential(
+        nullptr, Hk * 128, nullptr, Hk * 128, nullptr, Hv * 128, dt, nullptr, nullptr, gate_dt,
+        A_log, dt_bias, state_in, state_out, nullptr, dt, B, 0, Hk, Hv, q_scale, s));
+  const MixerWs w = mixer_ws(B, T, dims);
+  if (workspace_bytes < w.total() || !workspace) return GDN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
+  const size_t ybytes = (size_t)B * T * Hv * 128 * dsize(dt);
+  if (overlaps(y, ybytes, workspace, w.total()) || overlaps(y, ybytes, z, ybytes) ||
+      overlaps(y, ybytes, qkv, (size_t)B * T * C * dsize(dt)))
+    return GDN_ERR_SHAPE;
+  char* ws = static_cast<char*>(workspace);
+  float* yqk = reinterpret_cast<float*>(ws);
+  uint16_t* yv = reinterpret_cast<uint16_t*>(ws + w.qk_bytes);
+  void* chunk_ws = ws + w.qk_bytes + w.v_bytes;
+  hipError_t e = gdn::launch_conv_silu_split(qkv, dt, yqk, yv, conv_w, conv_state, B, T, C, L2C,
+                                             l2_eps, s);
+  if (e != hipSuccess) return GDN_ERR_LAUNCH;
+  e = gdn::launch_prefill_chunked(yqk, L2C, yqk + Hk * 128, L2C, yv, Hv * 128, GDN_F32, GDN_BF16,
+                                  a, b, gate_dt, A_log, dt_bias, state_in, state_out, y, dt, B, T,
+                                  Hk, Hv, q_scale, chunk_ws, s);
+  if (e != hipSuccess) return GDN_ERR_LAUNCH;
+  return launch_status(
+      gdn::launch_gated_rmsnorm(y, z, y, dt, norm_w, (int64_t)B * T * Hv, norm_eps, s));
 }
 
 }  // extern "C"

@@ -79,10 +79,10 @@ size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
 // on wave 0 while the others wait at LDS-only barriers.
 constexpr int PREP_THREADS = 256;
 
-template <typename TI, typename G_T>
+template <typename TI, typename TV, typename G_T>
 __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     const TI* __restrict__ q, int64_t q_ts, const TI* __restrict__ k, int64_t k_ts,
-    const TI* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
+    const TV* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
     const G_T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     WsLayout ws, int T, int Hk, int Hv, int NC, float q_scale) {
   constexpr bool kSplit = sizeof(TI) == 4;  // f32 q/k: two-term Q K^T
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
 
   const TI* kbase = k + ((int64_t)bb * T + t0) * k_ts + kh * DH;
   const TI* qbase = q + ((int64_t)bb * T + t0) * q_ts + kh * DH;
-  const TI* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
+  const TV* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
 
   // Every global load is issued first.  Wave w's K K^T and Q K^T tiles
   // (t block, s block; see the calls below) need four 16-row operand blocks:
@@ -680,15 +680,28 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
 
 namespace {
 
-template <typename TI, typename TG>
+template <typename TI, typename TV, typename TG>
 void launch_prep(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const void* v,
                  int64_t v_ts, const void* a, const void* b, const float* A_log,
                  const float* dt_bias, const WsLayout& ws, int B, int T, int Hk, int Hv, int NC,
                  float q_scale, hipStream_t stream) {
-  hipLaunchKernelGGL((chunk_prep_kernel<TI, TG>), dim3((unsigned)((int64_t)B * Hv * NC)),
+  hipLaunchKernelGGL((chunk_prep_kernel<TI, TV, TG>), dim3((unsigned)((int64_t)B * Hv * NC)),
                      dim3(PREP_THREADS),
-                     0, stream, (const TI*)q, q_ts, (const TI*)k, k_ts, (const TI*)v, v_ts,
+                     0, stream, (const TI*)q, q_ts, (const TI*)k, k_ts, (const TV*)v, v_ts,
                      (const TG*)a, (const TG*)b, A_log, dt_bias, ws, T, Hk, Hv, NC, q_scale);
+}
+
+template <typename TI, typename TV>
+void launch_prep_g(int gate_dt, const void* q, int64_t q_ts, const void* k, int64_t k_ts,
+                   const void* v, int64_t v_ts, const void* a, const void* b, const float* A_log,
+                   const float* dt_bias, const WsLayout& ws, int B, int T, int Hk, int Hv,
+                   int NC, float q_scale, hipStream_t stream) {
+  if (gate_dt == 1)
+    launch_prep<TI, TV, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk,
+                                  Hv, NC, q_scale, stream);
+  else
+    launch_prep<TI, TV, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk, Hv,
+                               NC, q_scale, stream);
 }
 
 template <typename TO>
@@ -707,28 +720,24 @@ void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
 }  // namespace
 
 hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
-                                  const void* v, int64_t v_ts, int qkv_dt, const void* a,
+                                  const void* v, int64_t v_ts, int qk_dt, int v_dt, const void* a,
                                   const void* b, int gate_dt, const float* A_log,
                                   const float* dt_bias, const float* state_in, float* state_out,
                                   void* o, int o_dt, int B, int T, int Hk, int Hv, float q_scale,
                                   void* workspace, hipStream_t stream) {
   const int NC = (T + CK - 1) / CK;
   const WsLayout ws = ws_layout(workspace, B, T, Hk, Hv);
-  if (qkv_dt == 1) {
-    if (gate_dt == 1)
-      launch_prep<uint16_t, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T,
-                                      Hk, Hv, NC, q_scale, stream);
-    else
-      launch_prep<uint16_t, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk,
-                                   Hv, NC, q_scale, stream);
-  } else {
-    if (gate_dt == 1)
-      launch_prep<float, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk,
-                                   Hv, NC, q_scale, stream);
-    else
-      launch_prep<float, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk, Hv,
-                                NC, q_scale, stream);
-  }
+  if (qk_dt == 1 && v_dt == 1)
+    launch_prep_g<uint16_t, uint16_t>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias,
+                                      ws, B, T, Hk, Hv, NC, q_scale, stream);
+  else if (qk_dt == 0 && v_dt == 0)
+    launch_prep_g<float, float>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B,
+                                T, Hk, Hv, NC, q_scale, stream);
+  else if (qk_dt == 0 && v_dt == 1)
+    launch_prep_g<float, uint16_t>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws,
+                                   B, T, Hk, Hv, NC, q_scale, stream);
+  else
+    return hipErrorInvalidValue;  // bf16 q/k with f32 v is not instantiated
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (o_dt == 1)

@@ -7,6 +7,12 @@
 // then for c < l2_channels each head_dim group of y is divided by
 // sqrt(sum of squares + l2_eps).  hist_out = the last 3 rows of xhat.
 //
+// Output: channels below l2_channels go to ya (row stride ya_stride), the
+// others to yb at channel c - l2_channels (row stride yb_stride), each in its
+// own dtype.  The plain call points both at one [B, T, C] buffer; the whole
+// mixer keeps q|k in f32 and v in bf16 (the chunked prefill rounds v to bf16
+// anyway, so the bf16 copy changes no result).
+//
 // Mapping: one thread owns 8 consecutive channels (one 16-byte bf16 load per
 // token) and walks CONV_TB consecutive tokens, keeping the previous 3 inputs
 // in registers, so every input element is read once (plus a 3-token halo per
@@ -20,10 +26,11 @@ namespace gdn {
 constexpr int CONV_TB = 8;        // tokens per workgroup (measured best of 8, 16, 32, 64)
 constexpr int CONV_THREADS = 256;  // 8 channels each -> 2048 channels per workgroup
 
-template <typename TX, typename TY>
+template <typename TX, typename TYA, typename TYB>
 __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
-    const TX* __restrict__ x, TY* __restrict__ y, const float* __restrict__ w,
-    float* conv_state, int Tlen, int C, int l2_channels, float l2_eps) {
+    const TX* __restrict__ x, TYA* __restrict__ ya, int64_t ya_stride, TYB* __restrict__ yb,
+    int64_t yb_stride, const float* __restrict__ w, float* conv_state, int Tlen, int C,
+    int l2_channels, float l2_eps) {
   const int b = blockIdx.z;
   const int t0 = blockIdx.y * CONV_TB;
   const int t1 = min(Tlen, t0 + CONV_TB);
@@ -31,7 +38,9 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
   if (c0 >= C) return;  // C % 8 == 0; a 16-lane head group is all in or all out
 
   const TX* xb = x + (int64_t)b * Tlen * C + c0;
-  TY* yb = y + (int64_t)b * Tlen * C + c0;
+  const bool l2 = c0 < l2_channels;  // uniform over a 16-lane head group
+  TYA* yab = l2 ? ya + (int64_t)b * Tlen * ya_stride + c0 : nullptr;
+  TYB* ybb = l2 ? nullptr : yb + (int64_t)b * Tlen * yb_stride + (c0 - l2_channels);
 
   float wt[4][8];
 #pragma unroll
@@ -73,7 +82,6 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
     for (int j = 0; j < 3; ++j) load8(xb + (int64_t)(t0 - 3 + j) * C, h[j]);
   }
 
-  const bool l2 = c0 < l2_channels;
   constexpr int U = 8;  // loads in flight per thread
   for (int t = t0; t < t1; t += U) {
     float xs[U][8];
@@ -100,7 +108,8 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
 #pragma unroll
           for (int i = 0; i < 8; ++i) yv[i] *= r;
         }
-        store8(yb + (int64_t)(t + u) * C, yv);
+        if (l2) store8(yab + (int64_t)(t + u) * ya_stride, yv);
+        else store8(ybb + (int64_t)(t + u) * yb_stride, yv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           h[0][i] = h[1][i];
@@ -112,25 +121,46 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
   }
 }
 
-template <typename TX, typename TY>
-static void launch_conv_t(const void* x, void* y, const float* w, float* conv_state, int B, int T,
-                          int C, int l2_channels, float l2_eps, hipStream_t stream) {
+template <typename TX, typename TYA, typename TYB>
+static void launch_conv_t(const void* x, void* ya, int64_t ya_stride, void* yb, int64_t yb_stride,
+                          const float* w, float* conv_state, int B, int T, int C, int l2_channels,
+                          float l2_eps, hipStream_t stream) {
   dim3 grid((C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8), (T + CONV_TB - 1) / CONV_TB, B);
-  hipLaunchKernelGGL((conv_silu_kernel<TX, TY>), grid, dim3(CONV_THREADS), 0, stream,
-                     (const TX*)x, (TY*)y, w, conv_state, T, C, l2_channels, l2_eps);
+  hipLaunchKernelGGL((conv_silu_kernel<TX, TYA, TYB>), grid, dim3(CONV_THREADS), 0, stream,
+                     (const TX*)x, (TYA*)ya, ya_stride, (TYB*)yb, yb_stride, w, conv_state, T, C,
+                     l2_channels, l2_eps);
 }
 
 hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const float* w,
                             float* conv_state, int B, int T, int C, int l2_channels, float l2_eps,
                             hipStream_t stream) {
+  // One [B, T, C] output: the second part starts l2_channels into each row.
+  const size_t ds = y_dt == 1 ? 2 : 4;
+  void* yb = static_cast<char*>(y) + (size_t)l2_channels * ds;
   if (x_dt == 1 && y_dt == 1)
-    launch_conv_t<uint16_t, uint16_t>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
+    launch_conv_t<uint16_t, uint16_t, uint16_t>(x, y, C, yb, C, w, conv_state, B, T, C,
+                                                l2_channels, l2_eps, stream);
   else if (x_dt == 1)
-    launch_conv_t<uint16_t, float>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
+    launch_conv_t<uint16_t, float, float>(x, y, C, yb, C, w, conv_state, B, T, C, l2_channels,
+                                          l2_eps, stream);
   else if (y_dt == 1)
-    launch_conv_t<float, uint16_t>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
+    launch_conv_t<float, uint16_t, uint16_t>(x, y, C, yb, C, w, conv_state, B, T, C,
+                                             l2_channels, l2_eps, stream);
   else
-    launch_conv_t<float, float>(x, y, w, conv_state, B, T, C, l2_channels, l2_eps, stream);
+    launch_conv_t<float, float, float>(x, y, C, yb, C, w, conv_state, B, T, C, l2_channels,
+                                       l2_eps, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_silu_split(const void* x, int x_dt, float* yqk, uint16_t* yv,
+                                  const float* w, float* conv_state, int B, int T, int C,
+                                  int l2_channels, float l2_eps, hipStream_t stream) {
+  if (x_dt == 1)
+    launch_conv_t<uint16_t, float, uint16_t>(x, yqk, l2_channels, yv, C - l2_channels, w,
+                                             conv_state, B, T, C, l2_channels, l2_eps, stream);
+  else
+    launch_conv_t<float, float, uint16_t>(x, yqk, l2_channels, yv, C - l2_channels, w,
+                                          conv_state, B, T, C, l2_channels, l2_eps, stream);
   return hipGetLastError();
 }
 

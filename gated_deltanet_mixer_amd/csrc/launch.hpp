@@ -11,6 +11,12 @@ hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const fl
                             float* conv_state, int B, int T, int C, int l2_channels, float l2_eps,
                             hipStream_t stream);
 
+// The same conv with two outputs: channels below l2_channels in f32 to yqk
+// [B, T, l2_channels], the others in bf16 to yv [B, T, C - l2_channels].
+hipError_t launch_conv_silu_split(const void* x, int x_dt, float* yqk, uint16_t* yv,
+                                  const float* w, float* conv_state, int B, int T, int C,
+                                  int l2_channels, float l2_eps, hipStream_t stream);
+
 hipError_t launch_gated_rmsnorm(const void* x, const void* z, void* y, int dt, const float* w,
                                 int64_t rows, float eps, hipStream_t stream);
 
@@ -27,11 +33,12 @@ hipError_t launch_prefill_sequential(const void* q, int64_t q_ts, const void* k,
                                      float* state_out, void* o, int o_dt, int B, int T, int Hk,
                                      int Hv, float q_scale, hipStream_t stream);
 
-// Chunked (WY/UT form) prefill on bf16 MFMA.
+// Chunked (WY/UT form) prefill on bf16 MFMA.  q and k share qk_dt; v has
+// its own dtype (f32 q/k with bf16 v is the whole mixer's layout).
 size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv);
 
 hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
-                                  const void* v, int64_t v_ts, int qkv_dt, const void* a,
+                                  const void* v, int64_t v_ts, int qk_dt, int v_dt, const void* a,
                                   const void* b, int gate_dt, const float* A_log,
                                   const float* dt_bias, const float* state_in, float* state_out,
                                   void* o, int o_dt, int B, int T, int Hk, int Hv, float q_scale,

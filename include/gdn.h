@@ -173,6 +173,47 @@ int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t 
 int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const float* w,
                       int32_t N, int32_t H, int32_t D, float eps, void* stream);
 
+/*
+ * Bytes of device workspace gdn_mixer_prefill needs (0 if B or T is 0 or the
+ * dims are invalid).  The caller allocates it; no initialisation is needed.
+ */
+size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims);
+
+/*
+ * gdn_mixer_prefill -- the whole mixer between the projections for T tokens
+ * of B sequences, in the order the "Qwen3.8 27B" model card's Gated DeltaNet
+ * bullet gives: depthwise causal conv (width 4) + silu over the q|k|v
+ * channels, L2 of each q and k head, the gated delta rule with the state
+ * carried in and out, and the per-head RMSNorm (scale 1 + w) gated by
+ * silu(z).  The same result as gdn_conv_silu (f32 output) -> gdn_prefill
+ * (chunked) -> gdn_gated_rmsnorm, without the f32 round trip of v: the conv
+ * writes q|k in f32 and v in bf16 to the workspace (the chunked prefill
+ * rounds v to bf16 anyway).
+ *   qkv    [B, T, C] contiguous in dt, C = 2*Hk*dk + Hv*dv, channels
+ *          [q heads | k heads | v heads].
+ *   z      [B, T, Hv*dv] contiguous in dt (the output gate).
+ *   conv_w [C, 4] f32 (w[c][3] multiplies the current token);
+ *   conv_state [B, 3, C] f32 in/out as in gdn_conv_silu, or NULL (zero
+ *          history, not written).
+ *   a, b   [B, T, Hv] contiguous in gate_dt; A_log, dt_bias [Hv] f32.
+ *   norm_w [dv] f32 (the scale is 1 + norm_w), shared by all heads.
+ *   state_in / state_out  [B, Hv, dv, dk] f32 as in gdn_prefill.
+ *   y      [B, T, Hv*dv] contiguous in dt; must not overlap qkv, z or the
+ *          workspace.
+ *   l2_eps (1e-6) inside the q/k L2 norm; norm_eps (1e-6) of the RMSNorm.
+ *   workspace  at least gdn_mixer_prefill_workspace_bytes(B, T, dims) bytes,
+ *          256-byte aligned; scratch after the call.
+ * With T == 0 the conv history is left as it is and the state passes
+ * through.  Errors as for the three calls it replaces; GDN_ERR_SHAPE if y
+ * overlaps qkv, z or the workspace.
+ */
+int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* conv_w,
+                      float* conv_state, const void* a, const void* b, int32_t gate_dt,
+                      const float* A_log, const float* dt_bias, const float* norm_w,
+                      const float* state_in, float* state_out, void* y, int32_t B, int32_t T,
+                      gdn_dims dims, float q_scale, float l2_eps, float norm_eps,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

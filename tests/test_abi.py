@@ -27,7 +27,8 @@ def test_header_and_exports():
     L = gdn.lib()
     names = declared_functions()
     assert {"gdn_conv_silu", "gdn_prefill", "gdn_decode_rows", "gdn_gated_rmsnorm",
-            "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version"} <= set(names)
+            "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version",
+            "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert gdn.gdn_abi_version() == 1
@@ -123,6 +124,42 @@ def test_norm_validation():
     assert f(N=-2) == SHAPE
     assert f(w=P + 4) == ALIGN
     assert f(N=0) == OK
+
+
+def mixer(qkv=P, z=2 * P, dt=1, cw=3 * P, cs=None, a=4 * P, b=5 * P, gdt=1, Al=6 * P, db=7 * P,
+          nw=8 * P, si=None, so=None, y=9 * P, B=1, T=64, dims=D16, ws=64 * P, wsb=None):
+    L = gdn.lib()
+    if wsb is None:
+        wsb = L.gdn_mixer_prefill_workspace_bytes(B, T, dims)
+    return L.gdn_mixer_prefill(_vp(qkv), _vp(z), dt, _vp(cw), _vp(cs), _vp(a), _vp(b), gdt,
+                               _vp(Al), _vp(db), _vp(nw), _vp(si), _vp(so), _vp(y), B, T, dims,
+                               1.0, 1e-6, 1e-6, _vp(ws), wsb, None)
+
+
+def test_mixer_prefill_validation():
+    L = gdn.lib()
+    need = L.gdn_mixer_prefill_workspace_bytes(1, 64, D16)
+    # q|k f32 + v bf16 conv output, then the chunked workspace
+    assert need >= 64 * 4096 * 4 + 64 * 6144 * 2 + L.gdn_prefill_workspace_bytes(1, 64, D16, 1, 2)
+    assert L.gdn_mixer_prefill_workspace_bytes(0, 64, D16) == 0
+    assert L.gdn_mixer_prefill_workspace_bytes(1, 64, gdn_dims(16, 40, 128, 128)) == 0
+    assert mixer(qkv=0) == NULL
+    assert mixer(cw=0) == NULL
+    assert mixer(nw=0) == NULL
+    assert mixer(dt=2) == DTYPE
+    assert mixer(gdt=9) == DTYPE
+    assert mixer(dims=gdn_dims(16, 40, 128, 128)) == SHAPE
+    assert mixer(dims=gdn_dims(16, 48, 64, 64)) == UNSUP
+    assert mixer(B=-1) == SHAPE
+    assert mixer(qkv=P + 8) == ALIGN
+    assert mixer(nw=P + 4) == ALIGN
+    assert mixer(cs=P + 4) == ALIGN
+    assert mixer(ws=None) == WS
+    assert mixer(wsb=need - 1) == WS
+    assert mixer(ws=64 * P + 128) == ALIGN
+    assert mixer(y=64 * P) == SHAPE      # y inside the workspace
+    assert mixer(y=2 * P) == SHAPE       # y on top of z
+    assert mixer(B=0) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -3,7 +3,9 @@ against the f64 oracle on sampled heads.
 
 Whole mixer, B=4, T=8192 (bf16 in): gdn_conv_silu (10240 channels, width 4,
 silu, L2 of q/k, f32 output) -> gdn_prefill (chunked, q/k/v read as strided
-views of the conv output, bf16 o) -> gdn_gated_rmsnorm (bf16 y).  Long
+views of the conv output, bf16 o) -> gdn_gated_rmsnorm (bf16 y); and the
+one-call gdn_mixer_prefill, which must give the same bits (its conv writes v
+in bf16, the rounding the chunked prefill applies to an f32 v).  Long
 prefill: T=65536 as 16 calls of 4096 with the f32 state handed between them,
 against one oracle pass.  Value heads are independent given their q/k head,
 so the oracle runs only the sampled (batch, head) pairs end to end.
@@ -49,6 +51,19 @@ def run_mixer_gpu(x, B, T, Hk, Hv, d, conv_state=None, S=None):
     return out, S
 
 
+def run_mixer_fused(x, B, T, Hk, Hv, d, conv_state=None, S=None, dtype=None):
+    if S is None:
+        S = torch.zeros((B, Hv, d, d), dtype=torch.float32, device="cuda")
+    qkv, z = dev(x["qkv"]), dev(x["z"])
+    if dtype is not None:
+        qkv, z = qkv.to(dtype), z.to(dtype)
+    y = gdn.gdn_mixer_prefill(qkv, z, dev(x["conv_w"]), dev(x["a"]), dev(x["b"]), dev(x["A_log"]),
+                              dev(x["dt_bias"]), dev(x["norm_w"]), Hk, Hv, conv_state=conv_state,
+                              state_in=S, state_out=S)
+    torch.cuda.synchronize()
+    return y, S
+
+
 def oracle_mixer_heads(x, pairs, Hk, Hv, d):
     """Oracle output of the whole mixer for the listed (batch, value head)
     pairs, stacked along the batch axis (one q/k head per entry)."""
@@ -86,6 +101,62 @@ def test_mixer_small_all_heads():
     assert np.array_equal(host_f64(cs), h_ref)
 
 
+@pytest.mark.parametrize("T", [150, 64, 5, 2])
+def test_mixer_prefill_one_call_small(T):
+    """gdn_mixer_prefill against the oracle, and bitwise against the three
+    calls it replaces (with a carried state and conv history)."""
+    banner(f"mixer_prefill one call B=2 T={T} Hk=2 Hv=6")
+    B, Hk, Hv, d = 2, 2, 6, 128
+    C = 2 * Hk * d + Hv * d
+    x = mixer_inputs(B, T, Hk=Hk, Hv=Hv, d=d, seed=41 + T)
+    rng = np.random.Generator(np.random.PCG64(7 + T))
+    S0 = torch.from_numpy(rng.normal(0.0, 0.05, (B, Hv, d, d)).astype(np.float32)).cuda()
+    h0 = torch.from_numpy(rng.standard_normal((B, 3, C)).astype(np.float32)).cuda()
+    cs1, S1 = h0.clone(), S0.clone()
+    y1, S1 = run_mixer_fused(x, B, T, Hk, Hv, d, conv_state=cs1, S=S1)
+    cs2, S2 = h0.clone(), S0.clone()
+    y2, S2 = run_mixer_gpu(x, B, T, Hk, Hv, d, conv_state=cs2, S=S2)
+    assert torch.equal(y1.view(B, T, Hv, d), y2)
+    assert torch.equal(S1, S2)
+    assert torch.equal(cs1, cs2)
+    y_ref, S_ref, h_ref = oracle.mixer(to_f64(x["qkv"]), to_f64(x["conv_w"]), to_f64(x["z"]),
+                                       to_f64(x["a"]), to_f64(x["b"]), x["A_log"], x["dt_bias"],
+                                       x["norm_w"], Hk, Hv, d, conv_hist=host_f64(h0),
+                                       S0=host_f64(S0))
+    assert max_rel_err(host_f64(y1), y_ref) < TOL
+    assert max_rel_err(host_f64(S1), S_ref) < TOL
+    assert np.array_equal(host_f64(cs1), h_ref)
+
+
+def test_mixer_prefill_f32_inputs_and_edge_cases():
+    """f32 qkv/z/y (the bf16 accuracy class of the chunked path), no conv
+    history (NULL: zeros, not written), and T == 0 (state passes through)."""
+    banner("mixer_prefill f32 B=1 T=100 Hk=2 Hv=6; T=0")
+    B, T, Hk, Hv, d = 1, 100, 2, 6, 128
+    x = mixer_inputs(B, T, Hk=Hk, Hv=Hv, d=d, dt="f32", seed=53)
+    y, S = run_mixer_fused(x, B, T, Hk, Hv, d, conv_state=None)
+    assert y.dtype == torch.float32
+    y_ref, S_ref, _ = oracle.mixer(to_f64(x["qkv"]), to_f64(x["conv_w"]), to_f64(x["z"]),
+                                   to_f64(x["a"]), to_f64(x["b"]), x["A_log"], x["dt_bias"],
+                                   x["norm_w"], Hk, Hv, d)
+    assert max_rel_err(host_f64(y), y_ref) < TOL
+    assert max_rel_err(host_f64(S), S_ref) < TOL
+    # T == 0: nothing but the state pass-through
+    S_in = torch.randn((B, Hv, d, d), dtype=torch.float32, device="cuda")
+    S_out = torch.full_like(S_in, float("nan"))
+    cs = torch.randn((B, 3, 2 * Hk * d + Hv * d), dtype=torch.float32, device="cuda")
+    cs0 = cs.clone()
+    e = torch.empty((B, 0, 2 * Hk * d + Hv * d), dtype=torch.bfloat16, device="cuda")
+    ez = torch.empty((B, 0, Hv * d), dtype=torch.bfloat16, device="cuda")
+    ea = torch.empty((B, 0, Hv), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_mixer_prefill(e, ez, dev(x["conv_w"]), ea, ea, dev(x["A_log"]), dev(x["dt_bias"]),
+                          dev(x["norm_w"]), Hk, Hv, conv_state=cs, state_in=S_in,
+                          state_out=S_out)
+    torch.cuda.synchronize()
+    assert torch.equal(S_out, S_in)
+    assert torch.equal(cs, cs0)
+
+
 @pytest.mark.slow
 def test_mixer_bf16_b4_t8192_sampled_heads():
     """The whole-mixer workload at full size; 6 (batch, head) pairs checked."""
@@ -106,6 +177,12 @@ def test_mixer_bf16_b4_t8192_sampled_heads():
     # Conv history: the last 3 input rows, exactly.
     assert np.array_equal(host_f64(cs), to_f64(x["qkv"][:, -3:, :]))
     assert all(e_y < TOL and e_s < TOL for _, _, e_y, e_s in errs)
+    # The one-call path, in the launch configuration the bench times: the same bits.
+    del S
+    cs2 = torch.zeros_like(cs)
+    y2, S2 = run_mixer_fused(x, B, T, HK, HV, D, conv_state=cs2)
+    assert torch.equal(y2.view(B, T, HV, D), out)
+    assert torch.equal(cs2, cs)
 
 
 @pytest.mark.slow
