@@ -33,6 +33,13 @@ size_t dsize(int32_t d) { return d == GDN_BF16 ? 2 : 4; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
 
+// The conv runs one workgroup per (batch, token block, channel block),
+// numbered in 32 bits.
+bool conv_grid_ok(int64_t B, int64_t T, int64_t C) {
+  const int64_t chans = gdn::CONV_THREADS * 8;
+  return B * ((T + gdn::CONV_TB - 1) / gdn::CONV_TB) * ((C + chans - 1) / chans) + 8 < INT32_MAX;
+}
+
 // Shared checks of the recurrence inputs.
 int check_dims(const gdn_dims& d) {
   if (d.n_qk_heads <= 0 || d.n_v_heads <= 0 || d.head_k_dim <= 0 || d.head_v_dim <= 0)
@@ -75,7 +82,7 @@ int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const floa
     if (head_dim <= 0 || l2_channels % head_dim != 0) return GDN_ERR_SHAPE;
     if (head_dim != 128) return GDN_ERR_UNSUPPORTED;
   }
-  if (B > 65535 || (T + 7) / 8 > 65535) return GDN_ERR_SHAPE;  // grid limits (8-token blocks)
+  if (!conv_grid_ok(B, T, C)) return GDN_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16) ||
       (conv_state && !aligned(conv_state, 16)))
     return GDN_ERR_ALIGN;
@@ -202,7 +209,7 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
   const int L2C = 2 * Hk * 128, C = L2C + Hv * 128;
   if (B < 0 || T < 0) return GDN_ERR_SHAPE;
   if ((int64_t)B * Hv * 8 > INT32_MAX || (int64_t)B * T > INT32_MAX) return GDN_ERR_SHAPE;
-  if (B > 65535 || (T + 7) / 8 > 65535) return GDN_ERR_SHAPE;  // conv grid limits
+  if (!conv_grid_ok(B, T, C)) return GDN_ERR_SHAPE;
   if (!aligned(qkv, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(conv_w, 16) ||
       (conv_state && !aligned(conv_state, 16)) || !aligned(a, dsize(gate_dt)) ||
       !aligned(b, dsize(gate_dt)) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||

@@ -16,31 +16,63 @@
 // Mapping: one thread owns 8 consecutive channels (one 16-byte bf16 load per
 // token) and walks CONV_TB consecutive tokens, keeping the previous 3 inputs
 // in registers, so every input element is read once (plus a 3-token halo per
-// block, mostly served from L2).  A 128-channel head is 16 lanes, so the L2 sum is a DPP row
+// block, served from L2: the block before it ran on the same XCD).  A 128-channel head is 16 lanes, so the L2 sum is a DPP row
 // reduction.  HBM-bound: one read of x and one write of y.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace gdn {
 
-constexpr int CONV_TB = 8;        // tokens per workgroup (measured best of 8, 16, 32, 64)
-constexpr int CONV_THREADS = 256;  // 8 channels each -> 2048 channels per workgroup
+
+// A row piece of 8 inputs as loaded (packed bf16 or two float4), unpacked
+// only when used, which keeps the loads in flight cheap in registers.
+template <typename TX> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  u16x8 v;
+  __device__ void load(const uint16_t* p) { v = *reinterpret_cast<const u16x8*>(p); }
+  __device__ float operator[](int i) const { return bf2f(v[i]); }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ float operator[](int i) const {
+    const float r[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return r[i];
+  }
+};
 
 template <typename TX, typename TYA, typename TYB>
 __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
     const TX* __restrict__ x, TYA* __restrict__ ya, int64_t ya_stride, TYB* __restrict__ yb,
-    int64_t yb_stride, const float* __restrict__ w, float* conv_state, int Tlen, int C,
+    int64_t yb_stride, const float* __restrict__ w, float* conv_state, int nb, int Tlen, int C,
     int l2_channels, float l2_eps) {
-  const int b = blockIdx.z;
-  const int t0 = blockIdx.y * CONV_TB;
+  // Workgroups whose ids agree mod 8 share an XCD; each XCD takes a
+  // contiguous run of (batch, token block, channel block) so a block's 3-row
+  // halo was read into the same L2 by its neighbour.
+  const int nx = (C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8);
+  const int ny = (Tlen + CONV_TB - 1) / CONV_TB;
+  const int total = nx * ny * nb;  // < 2^31 (checked on the host)
+  const int per = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (lin >= total) return;
+  const int bx = lin % nx, by = (lin / nx) % ny;
+  const int b = lin / (nx * ny);
+  const int t0 = by * CONV_TB;
   const int t1 = min(Tlen, t0 + CONV_TB);
-  const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
+  const int c0 = (bx * CONV_THREADS + threadIdx.x) * 8;
   if (c0 >= C) return;  // C % 8 == 0; a 16-lane head group is all in or all out
 
-  const TX* xb = x + (int64_t)b * Tlen * C + c0;
+  // Row bases are uniform; the thread's channel offset is added last, so the
+  // loads and stores take a scalar base and one per-thread offset.
+  const TX* xrows = x + (int64_t)b * Tlen * C;
+  const TX* xb = xrows + (uint32_t)c0;
   const bool l2 = c0 < l2_channels;  // uniform over a 16-lane head group
-  TYA* yab = l2 ? ya + (int64_t)b * Tlen * ya_stride + c0 : nullptr;
-  TYB* ybb = l2 ? nullptr : yb + (int64_t)b * Tlen * yb_stride + (c0 - l2_channels);
+  TYA* yarows = ya + (int64_t)b * Tlen * ya_stride;
+  TYB* ybrows = yb + (int64_t)b * Tlen * yb_stride;
+  const uint32_t ca = (uint32_t)c0, cb = (uint32_t)(c0 - l2_channels);
 
   float wt[4][8];
 #pragma unroll
@@ -84,10 +116,10 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
 
   constexpr int U = 8;  // loads in flight per thread
   for (int t = t0; t < t1; t += U) {
-    float xs[U][8];
+    Raw8<TX> xs[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (t + u < t1) load8(xb + (int64_t)(t + u) * C, xs[u]);
+      if (t + u < t1) xs[u].load(xrows + (int64_t)(t + u) * C + ca);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + u < t1) {
@@ -108,8 +140,8 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
 #pragma unroll
           for (int i = 0; i < 8; ++i) yv[i] *= r;
         }
-        if (l2) store8(yab + (int64_t)(t + u) * ya_stride, yv);
-        else store8(ybb + (int64_t)(t + u) * yb_stride, yv);
+        if (l2) store8(yarows + (int64_t)(t + u) * ya_stride + ca, yv);
+        else store8(ybrows + (int64_t)(t + u) * yb_stride + cb, yv);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           h[0][i] = h[1][i];
@@ -125,10 +157,12 @@ template <typename TX, typename TYA, typename TYB>
 static void launch_conv_t(const void* x, void* ya, int64_t ya_stride, void* yb, int64_t yb_stride,
                           const float* w, float* conv_state, int B, int T, int C, int l2_channels,
                           float l2_eps, hipStream_t stream) {
-  dim3 grid((C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8), (T + CONV_TB - 1) / CONV_TB, B);
+  const int64_t total = (int64_t)((C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8)) *
+                        ((T + CONV_TB - 1) / CONV_TB) * B;
+  dim3 grid((unsigned)(((total + 7) / 8) * 8));
   hipLaunchKernelGGL((conv_silu_kernel<TX, TYA, TYB>), grid, dim3(CONV_THREADS), 0, stream,
-                     (const TX*)x, (TYA*)ya, ya_stride, (TYB*)yb, yb_stride, w, conv_state, T, C,
-                     l2_channels, l2_eps);
+                     (const TX*)x, (TYA*)ya, ya_stride, (TYB*)yb, yb_stride, w, conv_state, B, T,
+                     C, l2_channels, l2_eps);
 }
 
 hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const float* w,

@@ -7,6 +7,11 @@
 
 namespace gdn {
 
+// Conv workgroup shape: CONV_TB tokens (measured best of 8, 16, 32, 64) by
+// CONV_THREADS threads of 8 channels each.
+constexpr int CONV_TB = 8;
+constexpr int CONV_THREADS = 256;
+
 hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const float* w,
                             float* conv_state, int B, int T, int C, int l2_channels, float l2_eps,
                             hipStream_t stream);
