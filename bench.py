@@ -7,7 +7,9 @@ like the model's layer (16 q/k heads, 48 value heads, width 128):
      carried in and out -> gated RMSNorm with z);
   2. gdn_prefill alone on the prefill workload (B=1, T=4096, bf16 q/k/v, f32
      gates, carried state ~N(0, 0.05), chunk 64);
-  3. gdn_decode_rows on 64 fixed rows (state [64,48,128,128] f32, in place).
+  3. gdn_decode_rows on 64 fixed rows (state [64,48,128,128] f32, in place);
+  4. gdn_prefill_slots on a server's ragged batch: 16 fixed rows with
+     U{1..1024} new tokens each, bf16, states carried in place.
 Each part is timed with HIP events on the stream it runs on.  The inputs of
 every part rotate over three independent buffer sets so that the 256 MB
 last-level cache cannot hold a part's working set between its launches.
@@ -51,6 +53,15 @@ def prefill_flops_per_launch(T=T_PREFILL, Hv=HV, d=D, C=64):
     W H, Q H, K^T U (2 C d^2 each) plus P U (2 C^2 d): 2(5 C^2 d + 3 C d^2)."""
     nc = (T + C - 1) // C
     return nc * Hv * 2 * (5 * C * C * d + 3 * C * d * d)
+
+
+def slots_flops(sx, Hv=HV, d=D, C=64):
+    """Dense-tile chunked flops of a ragged batch: each row's chunks (the last
+    one padded to 64 tokens) at 2(5C^2 d + 3C d^2) per chunk and value head."""
+    import numpy as np
+    lens = np.diff(np.asarray(sx["cu_seqlens"], dtype=np.int64))
+    chunks = int(((lens + C - 1) // C).sum())
+    return chunks * Hv * 2 * (5 * C * C * d + 3 * C * d * d)
 
 
 def prefill_bytes_per_launch(T=T_PREFILL, Hk=HK, Hv=HV, d=D):
@@ -159,6 +170,17 @@ def main():
         dec.append({n: dev(dx[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state",
                                             "lengths")})
         dec[-1]["o"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
+    sx = make_workload("prefill_slots_bf16_r16")
+    slot_sets = []
+    for _ in range(ROT):
+        slot_sets.append({n: dev(sx[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias",
+                                                   "state", "cu_seqlens")})
+        slot_sets[-1]["ws"] = torch.empty(
+            gdn.gdn_prefill_slots_workspace_bytes(16, sx["max_len"], HK, HV), dtype=torch.uint8,
+            device="cuda")
+        slot_sets[-1]["o"] = torch.empty((sx["q"].shape[0], HV, D), dtype=torch.bfloat16,
+                                         device="cuda")
+    slot_tokens = int(sx["cu_seqlens"][-1])
     ws_bytes = gdn.gdn_prefill_workspace_bytes(1, T_PREFILL, HK, HV)
     ws = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(ROT)]
 
@@ -181,11 +203,17 @@ def main():
                             Dd["dt_bias"], Dd["state"], Dd["lengths"], o=Dd["o"])
         if ev is not None:
             ev[3].record()
+        Sx = slot_sets[s]
+        gdn.gdn_prefill_slots(Sx["q"], Sx["k"], Sx["v"], Sx["a"], Sx["b"], Sx["A_log"],
+                              Sx["dt_bias"], Sx["cu_seqlens"], Sx["state"], sx["max_len"],
+                              o=Sx["o"], workspace=Sx["ws"])
+        if ev is not None:
+            ev[4].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -193,10 +221,10 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
-    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)]
+    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
                       for i in range(args.steps)])  # ms
     mean = parts.mean(axis=0)
-    t_layer, t_pre, t_dec = mean
+    t_layer, t_pre, t_dec, t_slots = mean
     ms_per_step = wall * 1e3 / args.steps
 
     prefill_tps = T_PREFILL / (t_pre * 1e-3)
@@ -261,6 +289,12 @@ def main():
                           "workload": "gdn_mixer_prefill (conv+silu+L2 -> chunked prefill -> "
                                       "gated RMSNorm), B=1 T=4096, 10240 conv channels",
                           "call_us": round(t_layer * 1e3, 2)},
+        "prefill_slots": {"value": round(slot_tokens / (t_slots * 1e-3), 1), "unit": "tokens/s",
+                          "workload": "prefill_slots_bf16_r16 (16 fixed rows, U{1..1024} new "
+                                      "tokens each, %d tokens, longest %d)" % (slot_tokens,
+                                                                                sx["max_len"]),
+                          "call_us": round(t_slots * 1e3, 2),
+                          "mfma_tflops": round(slots_flops(sx) / (t_slots * 1e-3) / 1e12, 2)},
         "prefill": {"avg_launch_us": round(t_pre * 1e3, 2),
                     "mfma_tflops": round(pre_flops / (t_pre * 1e-3) / 1e12, 2),
                     "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9,

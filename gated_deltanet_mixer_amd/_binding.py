@@ -56,6 +56,11 @@ def lib():
         L.gdn_decode_rows.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [P, P, P, i32, P, i32, i32, i32, f32, P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn_prefill_slots_workspace_bytes.argtypes = [i32, i32, gdn_dims]
+        L.gdn_prefill_slots_workspace_bytes.restype = sz
+        L.gdn_prefill_slots.argtypes = [P, i64, P, i64, P, i64, i32, P, P, i32, P, P, P, P, P,
+                                        i32, i32, i32, i32, gdn_dims, f32, P, sz, P]
+        L.gdn_prefill_slots.restype = ctypes.c_int
         L.gdn_mixer_prefill_workspace_bytes.argtypes = [i32, i32, gdn_dims]
         L.gdn_mixer_prefill_workspace_bytes.restype = sz
         L.gdn_mixer_prefill.argtypes = [P, P, i32, P, P, P, P, i32, P, P, P, P, P, P, i32, i32,
@@ -240,3 +245,44 @@ def gdn_mixer_prefill(qkv, z, conv_w, a, b, A_log, dt_bias, norm_w, Hk, Hv, conv
                                    _ptr(workspace), ws_bytes, _stream(qkv)),
            "gdn_mixer_prefill")
     return y
+
+
+def gdn_prefill_slots_workspace_bytes(R, max_len, Hk, Hv, dk=128, dv=128):
+    return int(lib().gdn_prefill_slots_workspace_bytes(R, max_len, gdn_dims(Hk, Hv, dk, dv)))
+
+
+def _packed_stride(t, heads, d):
+    """Token stride of a packed [N, heads, d] view."""
+    if t.shape[1:] != (heads, d):
+        raise ValueError(f"expected a [N, {heads}, {d}] view")
+    if t.numel() and (t.stride(2) != 1 or t.stride(1) != d):
+        raise ValueError(f"expected a [N, {heads}, {d}] view with packed heads")
+    return t.stride(0) if t.numel() else heads * d
+
+
+def gdn_prefill_slots(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state, max_len, o=None,
+                      q_scale=1.0, workspace=None, o_dtype=None):
+    """Ragged prefill of fixed rows: the rows' new tokens packed as q, k
+    [N,Hk,dk], v [N,Hv,dv], a, b [N,Hv]; cu_seqlens [R+1] int32 on the GPU;
+    state [R,Hv,dv,dk] f32 updated in place; max_len the longest row."""
+    _need_cuda(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state, o, workspace)
+    N, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    R = cu_seqlens.numel() - 1
+    qs, ks, vs = _packed_stride(q, Hk, dk), _packed_stride(k, Hk, dk), _packed_stride(v, Hv, dv)
+    if o is None:
+        o = torch.empty((N, Hv, dv), dtype=o_dtype or v.dtype, device=v.device)
+    assert o.is_contiguous() and a.is_contiguous() and b.is_contiguous()
+    assert cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()
+    assert state.is_contiguous() and state.dtype == torch.float32 and state.shape[0] == R
+    need = gdn_prefill_slots_workspace_bytes(R, max_len, Hk, Hv, dk, dv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().gdn_prefill_slots(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _dt(q), _ptr(a),
+                                   _ptr(b), _dt(a), _ptr(A_log), _ptr(dt_bias), _ptr(cu_seqlens),
+                                   _ptr(state), _ptr(o), _dt(o), R, max_len, N,
+                                   gdn_dims(Hk, Hv, dk, dv), q_scale, _ptr(workspace), ws_bytes,
+                                   _stream(q)),
+           "gdn_prefill_slots")
+    return o

@@ -139,7 +139,7 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
     if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
     return launch_status(gdn::launch_prefill_chunked(
         q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, qkv_dt, a, b, gate_dt, A_log,
-        dt_bias, state_in, state_out, o, o_dt, B, T, Hk, Hv, q_scale, workspace, s));
+        dt_bias, state_in, state_out, o, o_dt, B, T, nullptr, 0, Hk, Hv, q_scale, workspace, s));
   }
   // Sequential algorithm (also the T == 0 state pass-through).
   return launch_status(gdn::launch_prefill_sequential(
@@ -187,6 +187,44 @@ int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const f
   if (rows == 0) return GDN_OK;
   return launch_status(
       gdn::launch_gated_rmsnorm(x, z, y, dt, w, rows, eps, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_prefill_slots_workspace_bytes(int32_t R, int32_t max_len, gdn_dims dims) {
+  if (R <= 0 || max_len <= 0 || check_dims(dims) != GDN_OK) return 0;
+  return gdn::prefill_chunked_workspace_bytes(R, max_len, dims.n_qk_heads, dims.n_v_heads);
+}
+
+int gdn_prefill_slots(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                      const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
+                      const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, float* state, void* o, int32_t o_dt, int32_t R,
+                      int32_t max_len, int32_t total_tokens, gdn_dims dims, float q_scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!A_log || !dt_bias || !cu_seqlens || !state) return GDN_ERR_NULL;
+  if (total_tokens != 0 && (!q || !k || !v || !a || !b || !o)) return GDN_ERR_NULL;
+  if (!dtype_ok(qkv_dt) || !dtype_ok(gate_dt) || !dtype_ok(o_dt)) return GDN_ERR_DTYPE;
+  int st = check_dims(dims);
+  if (st != GDN_OK) return st;
+  const int Hk = dims.n_qk_heads, Hv = dims.n_v_heads;
+  if (R < 0 || max_len < 0 || total_tokens < 0) return GDN_ERR_SHAPE;
+  if (q_tok_stride < (int64_t)Hk * 128 || k_tok_stride < (int64_t)Hk * 128 ||
+      v_tok_stride < (int64_t)Hv * 128)
+    return GDN_ERR_SHAPE;
+  if ((int64_t)R * Hv * 8 > INT32_MAX || (int64_t)R * ((max_len + 63) / 64) * Hv > INT32_MAX)
+    return GDN_ERR_SHAPE;
+  if (q_tok_stride % 8 || k_tok_stride % 8 || v_tok_stride % 8) return GDN_ERR_ALIGN;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(a, dsize(gate_dt)) || !aligned(b, dsize(gate_dt)) || !aligned(A_log, 4) ||
+      !aligned(dt_bias, 4) || !aligned(cu_seqlens, 4) || !aligned(state, 16))
+    return GDN_ERR_ALIGN;
+  if (R == 0 || max_len == 0 || total_tokens == 0) return GDN_OK;  // every row is empty
+  const size_t need = gdn::prefill_chunked_workspace_bytes(R, max_len, Hk, Hv);
+  if (workspace_bytes < need || !workspace) return GDN_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
+  return launch_status(gdn::launch_prefill_chunked(
+      q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, qkv_dt, a, b, gate_dt, A_log,
+      dt_bias, state, state, o, o_dt, R, max_len, cu_seqlens, total_tokens, Hk, Hv, q_scale,
+      workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims) {
@@ -238,7 +276,7 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
   if (e != hipSuccess) return GDN_ERR_LAUNCH;
   e = gdn::launch_prefill_chunked(yqk, L2C, yqk + Hk * 128, L2C, yv, Hv * 128, GDN_F32, GDN_BF16,
                                   a, b, gate_dt, A_log, dt_bias, state_in, state_out, y, dt, B, T,
-                                  Hk, Hv, q_scale, chunk_ws, s);
+                                  nullptr, 0, Hk, Hv, q_scale, chunk_ws, s);
   if (e != hipSuccess) return GDN_ERR_LAUNCH;
   return launch_status(
       gdn::launch_gated_rmsnorm(y, z, y, dt, norm_w, (int64_t)B * T * Hv, norm_eps, s));

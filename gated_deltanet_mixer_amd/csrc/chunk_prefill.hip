@@ -73,6 +73,24 @@ size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
          align256(nch * 2 * CK * 4) + align256(nck * DH * CK * 2) + align256(nck * CK * DH * 2);
 }
 
+// Token span of row bb: rows of T tokens at stride T, or, with cu (device
+// [rows + 1] offsets into a packed token axis of `total` tokens), row bb's
+// tokens [cu[bb], cu[bb+1]), at most T of them (T is then the longest row).
+// The offsets are clamped into [0, total], so bad offsets cannot reach
+// outside the token arrays.
+__device__ __forceinline__ void row_span(const int32_t* cu, int total, int bb, int T,
+                                         int64_t& base, int& len) {
+  if (cu == nullptr) {
+    base = (int64_t)bb * T;
+    len = T;
+    return;
+  }
+  const int s = max(0, min(cu[bb], total));
+  const int e = max(s, min(cu[bb + 1], total));
+  base = s;
+  len = min(e - s, T);
+}
+
 // ---------------------------------------------------------------------------
 // Phase 1: per (batch, value head, chunk), four waves.  Wave w owns token
 // block w (16 tokens) of every tile loop; the serial parts of the inverse run
@@ -84,7 +102,8 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     const TI* __restrict__ q, int64_t q_ts, const TI* __restrict__ k, int64_t k_ts,
     const TV* __restrict__ v, int64_t v_ts, const G_T* __restrict__ a,
     const G_T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
-    WsLayout ws, int T, int Hk, int Hv, int NC, float q_scale) {
+    WsLayout ws, int T, const int32_t* __restrict__ cu, int total, int Hk, int Hv, int NC,
+    float q_scale) {
   constexpr bool kSplit = sizeof(TI) == 4;  // f32 q/k: two-term Q K^T
   // Region R: first the A blocks (diagonal f32, off-diagonal bf16), then K^T,
   // then V^T (bf16 [128][XP]).
@@ -109,13 +128,17 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   const int h = bh % Hv, bb = bh / Hv;
   const int grp = Hv / Hk, kh = h / grp;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
-  const int t0 = c * CK;
-  const int n = min(CK, T - t0);
+  int64_t tbase;
+  int tlen;
+  row_span(cu, total, bb, T, tbase, tlen);
+  const int t0 = c * CK;  // within the row
+  if (t0 >= tlen) return;  // a shorter row of a ragged batch
+  const int n = min(CK, tlen - t0);
   const int64_t chunk = (int64_t)bh * NC + c;
 
-  const TI* kbase = k + ((int64_t)bb * T + t0) * k_ts + kh * DH;
-  const TI* qbase = q + ((int64_t)bb * T + t0) * q_ts + kh * DH;
-  const TV* vbase = v + ((int64_t)bb * T + t0) * v_ts + h * DH;
+  const TI* kbase = k + (tbase + t0) * k_ts + kh * DH;
+  const TI* qbase = q + (tbase + t0) * q_ts + kh * DH;
+  const TV* vbase = v + (tbase + t0) * v_ts + h * DH;
 
   // Every global load is issued first.  Wave w's K K^T and Q K^T tiles
   // (t block, s block; see the calls below) need four 16-row operand blocks:
@@ -124,7 +147,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   // V block w; wave 0 also the gate inputs.
   float a_raw = 0.0f, b_raw = 0.0f;
   if (w == 0 && lane < n) {
-    const int64_t gi = ((int64_t)bb * T + t0 + lane) * Hv + h;
+    const int64_t gi = (tbase + t0 + lane) * Hv + h;
     a_raw = load1(a + gi);
     b_raw = load1(b + gi);
   }
@@ -499,7 +522,8 @@ __device__ __forceinline__ void out_fetch(OutRegs& R, const WsLayout& ws, int bb
 template <int NV, typename TO>
 __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     WsLayout ws, const float* state_in,
-    float* state_out, TO* __restrict__ o, int B, int T, int Hk, int Hv, int NC, float q_scale) {
+    float* state_out, TO* __restrict__ o, int B, int T, const int32_t* __restrict__ cu,
+    int total, int Hk, int Hv, int NC, float q_scale) {
   constexpr int NSL = DH / NV;  // slices per head
   constexpr int NVB = NV / 16;  // 16-column blocks per slice
   static_assert(NV == 32, "the dvp row order and the 8-wide output stores assume 32 columns");
@@ -517,6 +541,13 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
   const int hs = u / NSL, sl = u % NSL;
   const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
   const int dv0 = sl * NV;
+  int64_t tbase;
+  int tlen;
+  row_span(cu, total, bb, T, tbase, tlen);
+  const int ncr = (tlen + CK - 1) / CK;  // this row's chunks (NC is the workspace stride)
+  // Chunk index for a fetch ahead: past the row's last chunk the loads repeat
+  // it (an empty row loads chunk 0 and uses nothing).
+  auto ahead = [&](int cc) { return max(0, min(cc, ncr - 1)); };
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
   const bool state_wave = tid < 256;
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
   if (state_wave) {
     StateRegs<NV> RA, RB, RC;
     state_fetch<NV>(RA, ws, bb, bh, kh, 0, Hk, NC, sl, w, lane);
-    state_fetch<NV>(RB, ws, bb, bh, kh, min(1, NC - 1), Hk, NC, sl, w, lane);
+    state_fetch<NV>(RB, ws, bb, bh, kh, ahead(1), Hk, NC, sl, w, lane);
 
     f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
 #pragma unroll
@@ -550,7 +581,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     auto step = [&](const StateRegs<NV>& R, StateRegs<NV>& next, int c) {
       // Scheduling fence: no work of one chunk step moves into another.
       __builtin_amdgcn_sched_barrier(0);
-      state_fetch<NV>(next, ws, bb, bh, kh, min(c + 2, NC - 1), Hk, NC, sl, w, lane);
+      state_fetch<NV>(next, ws, bb, bh, kh, ahead(c + 2), Hk, NC, sl, w, lane);
       // (1) U = Ut - W H against the bf16 state copy, dv rows in dvp order.
       f32x4 accU[NVB];
 #pragma unroll
@@ -602,13 +633,13 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
       lds_barrier();
     };
     int c = 0;
-    for (; c + 3 <= NC; c += 3) {
+    for (; c + 3 <= ncr; c += 3) {
       step(RA, RC, c);
       step(RB, RA, c + 1);
       step(RC, RB, c + 2);
     }
-    if (c < NC) step(RA, RC, c);
-    if (c + 1 < NC) step(RB, RA, c + 1);
+    if (c < ncr) step(RA, RC, c);
+    if (c + 1 < ncr) step(RB, RA, c + 1);
 
     if (state_out) {
 #pragma unroll
@@ -625,7 +656,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     const int tr = w * 16 + li;
     OutRegs RA, RB, RC;
     out_fetch(RA, ws, bb, bh, kh, 0, Hk, NC, w, lane);
-    out_fetch(RB, ws, bb, bh, kh, min(1, NC - 1), Hk, NC, w, lane);
+    out_fetch(RB, ws, bb, bh, kh, ahead(1), Hk, NC, w, lane);
     lds_barrier();
     // `full` (std::true_type) marks a chunk of CK tokens, whose store needs no
     // row check.
@@ -644,7 +675,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
       // the step they queue behind the state waves' loads, and (Q H)^T gates
       // the first barrier.
       __builtin_amdgcn_sched_barrier(0);
-      out_fetch(next, ws, bb, bh, kh, min(c + 2, NC - 1), Hk, NC, w, lane);
+      out_fetch(next, ws, bb, bh, kh, ahead(c + 2), Hk, NC, w, lane);
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       // O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token blocks
@@ -661,20 +692,20 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
         for (int r = 0; r < 4; ++r) ov[4 * vb + r] = fmaf(gq, accQ[vb][r], acc[r]);
       }
       const int t0 = c * CK;
-      if (decltype(full)::value || tr < min(CK, T - t0))
-        store8(o + (((int64_t)bb * T + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
+      if (decltype(full)::value || tr < min(CK, tlen - t0))
+        store8(o + ((tbase + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
       lds_barrier();
     };
     int c = 0;
-    const int nfull = T / CK;
+    const int nfull = tlen / CK;
     for (; c + 3 <= nfull; c += 3) {
       step(RA, RC, c, std::true_type{});
       step(RB, RA, c + 1, std::true_type{});
       step(RC, RB, c + 2, std::true_type{});
     }
-    if (c < NC) step(RA, RC, c, std::false_type{});
-    if (c + 1 < NC) step(RB, RA, c + 1, std::false_type{});
-    if (c + 2 < NC) step(RC, RB, c + 2, std::false_type{});
+    if (c < ncr) step(RA, RC, c, std::false_type{});
+    if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
+    if (c + 2 < ncr) step(RC, RB, c + 2, std::false_type{});
   }
 }
 
@@ -683,38 +714,39 @@ namespace {
 template <typename TI, typename TV, typename TG>
 void launch_prep(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const void* v,
                  int64_t v_ts, const void* a, const void* b, const float* A_log,
-                 const float* dt_bias, const WsLayout& ws, int B, int T, int Hk, int Hv, int NC,
-                 float q_scale, hipStream_t stream) {
+                 const float* dt_bias, const WsLayout& ws, int B, int T, const int32_t* cu,
+                 int total, int Hk, int Hv, int NC, float q_scale, hipStream_t stream) {
   hipLaunchKernelGGL((chunk_prep_kernel<TI, TV, TG>), dim3((unsigned)((int64_t)B * Hv * NC)),
                      dim3(PREP_THREADS),
                      0, stream, (const TI*)q, q_ts, (const TI*)k, k_ts, (const TV*)v, v_ts,
-                     (const TG*)a, (const TG*)b, A_log, dt_bias, ws, T, Hk, Hv, NC, q_scale);
+                     (const TG*)a, (const TG*)b, A_log, dt_bias, ws, T, cu, total, Hk, Hv, NC,
+                     q_scale);
 }
 
 template <typename TI, typename TV>
 void launch_prep_g(int gate_dt, const void* q, int64_t q_ts, const void* k, int64_t k_ts,
                    const void* v, int64_t v_ts, const void* a, const void* b, const float* A_log,
-                   const float* dt_bias, const WsLayout& ws, int B, int T, int Hk, int Hv,
-                   int NC, float q_scale, hipStream_t stream) {
+                   const float* dt_bias, const WsLayout& ws, int B, int T, const int32_t* cu,
+                   int total, int Hk, int Hv, int NC, float q_scale, hipStream_t stream) {
   if (gate_dt == 1)
-    launch_prep<TI, TV, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk,
-                                  Hv, NC, q_scale, stream);
+    launch_prep<TI, TV, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, cu,
+                                  total, Hk, Hv, NC, q_scale, stream);
   else
-    launch_prep<TI, TV, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, Hk, Hv,
-                               NC, q_scale, stream);
+    launch_prep<TI, TV, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B, T, cu,
+                               total, Hk, Hv, NC, q_scale, stream);
 }
 
 template <typename TO>
 void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
-                  void* o, int B, int T, int Hk, int Hv, int NC, float q_scale,
-                  hipStream_t stream) {
+                  void* o, int B, int T, const int32_t* cu, int total, int Hk, int Hv, int NC,
+                  float q_scale, hipStream_t stream) {
   constexpr int NV = 32;
   constexpr int NSL = DH / NV;
   const int64_t units = (int64_t)B * Hv * NSL;
   const int64_t per_xcd = (units + 7) / 8;  // ids are padded to whole XCD rounds
   hipLaunchKernelGGL((chunk_chain_kernel<NV, TO>), dim3((unsigned)(per_xcd * 8)),
-                     dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, Hk, Hv,
-                     NC, q_scale);
+                     dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, cu, total,
+                     Hk, Hv, NC, q_scale);
 }
 
 }  // namespace
@@ -723,27 +755,29 @@ hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, in
                                   const void* v, int64_t v_ts, int qk_dt, int v_dt, const void* a,
                                   const void* b, int gate_dt, const float* A_log,
                                   const float* dt_bias, const float* state_in, float* state_out,
-                                  void* o, int o_dt, int B, int T, int Hk, int Hv, float q_scale,
-                                  void* workspace, hipStream_t stream) {
+                                  void* o, int o_dt, int B, int T, const int32_t* cu, int total,
+                                  int Hk, int Hv, float q_scale, void* workspace,
+                                  hipStream_t stream) {
   const int NC = (T + CK - 1) / CK;
   const WsLayout ws = ws_layout(workspace, B, T, Hk, Hv);
   if (qk_dt == 1 && v_dt == 1)
     launch_prep_g<uint16_t, uint16_t>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias,
-                                      ws, B, T, Hk, Hv, NC, q_scale, stream);
+                                      ws, B, T, cu, total, Hk, Hv, NC, q_scale, stream);
   else if (qk_dt == 0 && v_dt == 0)
     launch_prep_g<float, float>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B,
-                                T, Hk, Hv, NC, q_scale, stream);
+                                T, cu, total, Hk, Hv, NC, q_scale, stream);
   else if (qk_dt == 0 && v_dt == 1)
     launch_prep_g<float, uint16_t>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws,
-                                   B, T, Hk, Hv, NC, q_scale, stream);
+                                   B, T, cu, total, Hk, Hv, NC, q_scale, stream);
   else
     return hipErrorInvalidValue;  // bf16 q/k with f32 v is not instantiated
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (o_dt == 1)
-    launch_chain<uint16_t>(ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
+    launch_chain<uint16_t>(ws, state_in, state_out, o, B, T, cu, total, Hk, Hv, NC, q_scale,
+                           stream);
   else
-    launch_chain<float>(ws, state_in, state_out, o, B, T, Hk, Hv, NC, q_scale, stream);
+    launch_chain<float>(ws, state_in, state_out, o, B, T, cu, total, Hk, Hv, NC, q_scale, stream);
   return hipGetLastError();
 }
 

@@ -39,14 +39,18 @@ hipError_t launch_prefill_sequential(const void* q, int64_t q_ts, const void* k,
                                      int Hv, float q_scale, hipStream_t stream);
 
 // Chunked (WY/UT form) prefill on bf16 MFMA.  q and k share qk_dt; v has
-// its own dtype (f32 q/k with bf16 v is the whole mixer's layout).
+// its own dtype (f32 q/k with bf16 v is the whole mixer's layout).  With cu
+// NULL the B rows are T tokens each at stride T; with cu (device, [B + 1]
+// offsets into a packed axis of `total` tokens) row b is tokens
+// [cu[b], cu[b+1]), at most T of them.
 size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv);
 
 hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
                                   const void* v, int64_t v_ts, int qk_dt, int v_dt, const void* a,
                                   const void* b, int gate_dt, const float* A_log,
                                   const float* dt_bias, const float* state_in, float* state_out,
-                                  void* o, int o_dt, int B, int T, int Hk, int Hv, float q_scale,
-                                  void* workspace, hipStream_t stream);
+                                  void* o, int o_dt, int B, int T, const int32_t* cu, int total,
+                                  int Hk, int Hv, float q_scale, void* workspace,
+                                  hipStream_t stream);
 
 }  // namespace gdn

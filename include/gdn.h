@@ -174,6 +174,46 @@ int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const f
                       int32_t N, int32_t H, int32_t D, float eps, void* stream);
 
 /*
+ * Bytes of device workspace gdn_prefill_slots needs for R rows of at most
+ * max_len new tokens (0 if R or max_len is 0).
+ */
+size_t gdn_prefill_slots_workspace_bytes(int32_t R, int32_t max_len, gdn_dims dims);
+
+/*
+ * gdn_prefill_slots -- ragged prefill of a server's fixed rows, each row
+ * continuing from its own state with its own number of new tokens (the
+ * "Qwen3.8 27B" model card's state paragraph: prefill_slots and decode_rows
+ * serve a server's rows each at its own length, fixed rows, conv history and
+ * recurrent state in f32).  The rule uses no positions, so a row's length
+ * so far only lives in its state.  Chunks of 64 start at each row's first
+ * new token.
+ *   q, k   [total_tokens, Hk, dk] in qkv_dt, token t at t*tok_stride
+ *          (elements); v [total_tokens, Hv, dv] likewise: the rows' new
+ *          tokens packed one row after another.
+ *   a, b   [total_tokens, Hv] contiguous in gate_dt; A_log, dt_bias [Hv] f32.
+ *   cu_seqlens  [R + 1] int32, DEVICE: row r's tokens are
+ *          [cu_seqlens[r], cu_seqlens[r+1]) of the packed axis, with
+ *          cu_seqlens[0] = 0, non-decreasing, cu_seqlens[R] = total_tokens
+ *          and no row longer than max_len.  The kernels clamp the offsets
+ *          into [0, total_tokens] and a row to max_len tokens, so bad
+ *          offsets give wrong rows, never accesses outside the arrays.
+ *   state  [R, Hv, dv, dk] f32, row r's state at index r, read and written
+ *          in place; a row with no new tokens keeps its state.
+ *   o      [total_tokens, Hv, dv] contiguous in o_dt.
+ *   max_len  the longest row (host value; sizes the launch and workspace).
+ *   workspace  at least gdn_prefill_slots_workspace_bytes(R, max_len, dims)
+ *          bytes, 256-byte aligned.
+ * Runs the chunked algorithm (the bf16 accuracy class for any input dtype).
+ * R == 0, max_len == 0 or total_tokens == 0 is a no-op.
+ */
+int gdn_prefill_slots(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                      const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
+                      const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
+                      const int32_t* cu_seqlens, float* state, void* o, int32_t o_dt, int32_t R,
+                      int32_t max_len, int32_t total_tokens, gdn_dims dims, float q_scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace gdn_mixer_prefill needs (0 if B or T is 0 or the
  * dims are invalid).  The caller allocates it; no initialisation is needed.
  */

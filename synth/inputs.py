@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = ["HK", "HV", "D", "CONV_CH", "CONV_W", "WORKLOADS", "bf16_round", "f32_round",
            "to_f64", "is_bf16", "recurrence_inputs", "decode_inputs", "mixer_inputs",
-           "make_workload", "unit_heads"]
+           "slots_inputs", "make_workload", "unit_heads"]
 
 HK, HV, D = 16, 48, 128
 CONV_CH = 2 * HK * D + HV * D  # 10240
@@ -90,6 +90,33 @@ def recurrence_inputs(B, T, Hk=HK, Hv=HV, d=D, qkv_dt="f32", gate_dt="f32", seed
     }
 
 
+def slots_inputs(lengths, Hk=HK, Hv=HV, d=D, qkv_dt="bf16", gate_dt="f32", seed=5,
+                 state_std=0.05):
+    """Inputs of one ragged prefill of fixed rows: row r brings lengths[r] new
+    tokens.  The tokens are packed row after row: q, k [N,Hk,d]; v [N,Hv,d];
+    a, b [N,Hv]; cu_seqlens [R+1] int32 (row r is tokens cu[r]..cu[r+1]);
+    A_log, dt_bias [Hv] f32; state [R,Hv,d,d] f32 (each row's carried state)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = np.asarray(lengths, dtype=np.int64)
+    R, N = len(lengths), int(lengths.sum())
+    cu = np.zeros(R + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    q = unit_heads(rng.standard_normal((N, Hk, d)))
+    k = unit_heads(rng.standard_normal((N, Hk, d)))
+    v = rng.standard_normal((N, Hv, d))
+    a = rng.standard_normal((N, Hv))
+    b = rng.standard_normal((N, Hv))
+    A_log = rng.uniform(-1.0, 1.0, Hv)
+    dt_bias = rng.normal(0.0, 0.1, Hv)
+    state = rng.standard_normal((R, Hv, d, d), dtype=np.float32) * np.float32(state_std)
+    return {
+        "q": _round(q, qkv_dt), "k": _round(k, qkv_dt), "v": _round(v, qkv_dt),
+        "a": _round(a, gate_dt), "b": _round(b, gate_dt),
+        "A_log": f32_round(A_log), "dt_bias": f32_round(dt_bias),
+        "state": state.astype(np.float32), "cu_seqlens": cu, "max_len": int(lengths.max(initial=0)),
+    }
+
+
 def decode_inputs(R, Hk=HK, Hv=HV, d=D, qkv_dt="bf16", gate_dt="bf16", seed=1,
                   state_std=0.05, max_len=8192):
     """Inputs of one decode_rows call: q, k [R,Hk,d]; v [R,Hv,d]; a, b [R,Hv];
@@ -147,6 +174,10 @@ WORKLOADS = {
     "prefill_bf16_b1_t65536_x16": dict(kind="prefill", B=1, T=65536, qkv_dt="bf16",
                                        gate_dt="f32", state_std=None, seed=1004,
                                        calls=16),
+    # A server's ragged prefill: 16 fixed rows, new-token counts ~ U{1..1024}
+    # drawn from the seed's first integers, states ~ N(0, 0.05).
+    "prefill_slots_bf16_r16": dict(kind="slots", R=16, max_new=1024, qkv_dt="bf16",
+                                   gate_dt="f32", seed=1005),
 }
 
 
@@ -162,4 +193,8 @@ def make_workload(name, **overrides):
         return decode_inputs(**cfg)
     if kind == "mixer":
         return mixer_inputs(**cfg)
+    if kind == "slots":
+        rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
+        lengths = rng.integers(1, cfg.pop("max_new") + 1, cfg.pop("R"))
+        return slots_inputs(lengths, **cfg)
     raise ValueError(kind)

@@ -28,7 +28,8 @@ def test_header_and_exports():
     names = declared_functions()
     assert {"gdn_conv_silu", "gdn_prefill", "gdn_decode_rows", "gdn_gated_rmsnorm",
             "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version",
-            "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes"} <= set(names)
+            "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes", "gdn_prefill_slots",
+            "gdn_prefill_slots_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert gdn.gdn_abi_version() == 1
@@ -160,6 +161,36 @@ def test_mixer_prefill_validation():
     assert mixer(y=64 * P) == SHAPE      # y inside the workspace
     assert mixer(y=2 * P) == SHAPE       # y on top of z
     assert mixer(B=0) == OK
+
+
+def slots(q=P, k=2 * P, v=3 * P, qdt=1, a=4 * P, b=5 * P, gdt=0, cu=6 * P, st=7 * P, o=8 * P,
+          R=4, max_len=100, total=300, dims=D16, ws=64 * P, wsb=None):
+    L = gdn.lib()
+    if wsb is None:
+        wsb = L.gdn_prefill_slots_workspace_bytes(R, max_len, dims)
+    return L.gdn_prefill_slots(_vp(q), 2048, _vp(k), 2048, _vp(v), 6144, qdt, _vp(a), _vp(b), gdt,
+                               _vp(9 * P), _vp(10 * P), _vp(cu), _vp(st), _vp(o), 1, R, max_len,
+                               total, dims, 1.0, _vp(ws), wsb, None)
+
+
+def test_prefill_slots_validation():
+    L = gdn.lib()
+    assert L.gdn_prefill_slots_workspace_bytes(4, 100, D16) == \
+        L.gdn_prefill_workspace_bytes(4, 100, D16, 1, 2)
+    assert L.gdn_prefill_slots_workspace_bytes(0, 100, D16) == 0
+    assert slots(cu=0) == NULL
+    assert slots(st=0) == NULL
+    assert slots(q=0) == NULL
+    assert slots(qdt=3) == DTYPE
+    assert slots(dims=gdn_dims(16, 40, 128, 128)) == SHAPE
+    assert slots(R=-1) == SHAPE
+    assert slots(max_len=-5) == SHAPE
+    assert slots(cu=6 * P + 2) == ALIGN
+    assert slots(st=7 * P + 8) == ALIGN
+    assert slots(ws=None) == WS
+    assert slots(wsb=100) == WS
+    assert slots(R=0) == OK
+    assert slots(total=0, q=0, k=0, v=0, a=0, b=0, o=0) == OK   # no tokens: nothing to do
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
