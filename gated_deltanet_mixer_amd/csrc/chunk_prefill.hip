@@ -519,8 +519,12 @@ __device__ __forceinline__ void out_fetch(OutRegs& R, const WsLayout& ws, int bb
   R.gt = ws.G[chunk * 2 * CK + 16 * w + li];
 }
 
-template <int NV, typename TO>
-__global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
+// DEPTH = chunks loaded ahead.  2 for up to one workgroup per CU (one
+// head's slices per CU, the B = 1 case); 1 with at most 128 VGPRs, so two
+// workgroups share a CU when there are more slices than CUs and each hides
+// the other's latency.
+template <int NV, typename TO, int DEPTH>
+__global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_kernel(
     WsLayout ws, const float* state_in,
     float* state_out, TO* __restrict__ o, int B, int T, const int32_t* __restrict__ cu,
     int total, int Hk, int Hv, int NC, float q_scale) {
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
   if (state_wave) {
     StateRegs<NV> RA, RB, RC;
     state_fetch<NV>(RA, ws, bb, bh, kh, 0, Hk, NC, sl, w, lane);
-    state_fetch<NV>(RB, ws, bb, bh, kh, ahead(1), Hk, NC, sl, w, lane);
+    if constexpr (DEPTH == 2) state_fetch<NV>(RB, ws, bb, bh, kh, ahead(1), Hk, NC, sl, w, lane);
 
     f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
 #pragma unroll
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     auto step = [&](const StateRegs<NV>& R, StateRegs<NV>& next, int c) {
       // Scheduling fence: no work of one chunk step moves into another.
       __builtin_amdgcn_sched_barrier(0);
-      state_fetch<NV>(next, ws, bb, bh, kh, ahead(c + 2), Hk, NC, sl, w, lane);
+      state_fetch<NV>(next, ws, bb, bh, kh, ahead(c + DEPTH), Hk, NC, sl, w, lane);
       // (1) U = Ut - W H against the bf16 state copy, dv rows in dvp order.
       f32x4 accU[NVB];
 #pragma unroll
@@ -633,13 +637,21 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
       lds_barrier();
     };
     int c = 0;
-    for (; c + 3 <= ncr; c += 3) {
-      step(RA, RC, c);
-      step(RB, RA, c + 1);
-      step(RC, RB, c + 2);
+    if constexpr (DEPTH == 2) {
+      for (; c + 3 <= ncr; c += 3) {
+        step(RA, RC, c);
+        step(RB, RA, c + 1);
+        step(RC, RB, c + 2);
+      }
+      if (c < ncr) step(RA, RC, c);
+      if (c + 1 < ncr) step(RB, RA, c + 1);
+    } else {
+      for (; c + 2 <= ncr; c += 2) {
+        step(RA, RB, c);
+        step(RB, RA, c + 1);
+      }
+      if (c < ncr) step(RA, RB, c);
     }
-    if (c < ncr) step(RA, RC, c);
-    if (c + 1 < ncr) step(RB, RA, c + 1);
 
     if (state_out) {
 #pragma unroll
@@ -656,7 +668,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     const int tr = w * 16 + li;
     OutRegs RA, RB, RC;
     out_fetch(RA, ws, bb, bh, kh, 0, Hk, NC, w, lane);
-    out_fetch(RB, ws, bb, bh, kh, ahead(1), Hk, NC, w, lane);
+    if constexpr (DEPTH == 2) out_fetch(RB, ws, bb, bh, kh, ahead(1), Hk, NC, w, lane);
     lds_barrier();
     // `full` (std::true_type) marks a chunk of CK tokens, whose store needs no
     // row check.
@@ -675,7 +687,7 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
       // the step they queue behind the state waves' loads, and (Q H)^T gates
       // the first barrier.
       __builtin_amdgcn_sched_barrier(0);
-      out_fetch(next, ws, bb, bh, kh, ahead(c + 2), Hk, NC, w, lane);
+      out_fetch(next, ws, bb, bh, kh, ahead(c + DEPTH), Hk, NC, w, lane);
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       // O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token blocks
@@ -698,14 +710,23 @@ __global__ __launch_bounds__(CH_THREADS) void chunk_chain_kernel(
     };
     int c = 0;
     const int nfull = tlen / CK;
-    for (; c + 3 <= nfull; c += 3) {
-      step(RA, RC, c, std::true_type{});
-      step(RB, RA, c + 1, std::true_type{});
-      step(RC, RB, c + 2, std::true_type{});
+    if constexpr (DEPTH == 2) {
+      for (; c + 3 <= nfull; c += 3) {
+        step(RA, RC, c, std::true_type{});
+        step(RB, RA, c + 1, std::true_type{});
+        step(RC, RB, c + 2, std::true_type{});
+      }
+      if (c < ncr) step(RA, RC, c, std::false_type{});
+      if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
+      if (c + 2 < ncr) step(RC, RB, c + 2, std::false_type{});
+    } else {
+      for (; c + 2 <= nfull; c += 2) {
+        step(RA, RB, c, std::true_type{});
+        step(RB, RA, c + 1, std::true_type{});
+      }
+      if (c < ncr) step(RA, RB, c, std::false_type{});
+      if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
     }
-    if (c < ncr) step(RA, RC, c, std::false_type{});
-    if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
-    if (c + 2 < ncr) step(RC, RB, c + 2, std::false_type{});
   }
 }
 
@@ -736,6 +757,10 @@ void launch_prep_g(int gate_dt, const void* q, int64_t q_ts, const void* k, int6
                                total, Hk, Hv, NC, q_scale, stream);
 }
 
+// Up to this many (head, slice) units the chain runs two chunks ahead, one
+// workgroup per CU (256 CUs); beyond it, one chunk ahead, two per CU.
+int kChainOneDeep = 256;
+
 template <typename TO>
 void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
                   void* o, int B, int T, const int32_t* cu, int total, int Hk, int Hv, int NC,
@@ -744,9 +769,14 @@ void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
   constexpr int NSL = DH / NV;
   const int64_t units = (int64_t)B * Hv * NSL;
   const int64_t per_xcd = (units + 7) / 8;  // ids are padded to whole XCD rounds
-  hipLaunchKernelGGL((chunk_chain_kernel<NV, TO>), dim3((unsigned)(per_xcd * 8)),
-                     dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, cu, total,
-                     Hk, Hv, NC, q_scale);
+  if (units <= kChainOneDeep)
+    hipLaunchKernelGGL((chunk_chain_kernel<NV, TO, 2>), dim3((unsigned)(per_xcd * 8)),
+                       dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, cu,
+                       total, Hk, Hv, NC, q_scale);
+  else
+    hipLaunchKernelGGL((chunk_chain_kernel<NV, TO, 1>), dim3((unsigned)(per_xcd * 8)),
+                       dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, cu,
+                       total, Hk, Hv, NC, q_scale);
 }
 
 }  // namespace
