@@ -91,6 +91,19 @@ __device__ __forceinline__ void row_span(const int32_t* cu, int total, int bb, i
   len = min(e - s, T);
 }
 
+// Value head (and slice) of the r-th workgroup of a round: workgroups whose
+// ids agree mod 8 run on one XCD, and the XCD's k-th unit (of `per` units per
+// head, grp heads per q/k group) belongs to group (k / (grp per)) * 8 + xcd,
+// so a group's heads and slices share an XCD and its L2, and groups are dealt
+// round-robin over the XCDs.  Needs a whole number of groups per XCD round;
+// otherwise the plain order (heads round-robin).  Returns head * per + slice.
+__device__ __forceinline__ int xcd_head(int r, int ngroups, int grp, int per) {
+  if ((ngroups & 7) != 0) return r;
+  const int x = r & 7, k = r >> 3;
+  const int g = (k / (grp * per)) * 8 + x, rest = k % (grp * per);
+  return (g * grp + rest / per) * per + rest % per;
+}
+
 // ---------------------------------------------------------------------------
 // Phase 1: per (batch, value head, chunk), four waves.  Wave w owns token
 // block w (16 tokens) of every tile loop; the serial parts of the inverse run
@@ -117,14 +130,13 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
 
   // Chunk-major order: the workgroups of one chunk index run together, so the
   // chain, which reads chunk 0 first, finds every head's data equally recent
-  // in the last-level cache.  Within a round of 8 ids (one per XCD) the value
-  // heads are spread so that each XCD takes a contiguous range of heads, which
-  // keeps the value heads of one q/k group on one XCD when the range is a
-  // whole number of groups (48 heads: 6 per XCD, groups of 3).
+  // in the last-level cache.  Ids that agree mod 8 share an XCD; the q/k
+  // groups (the value heads that read one q/k head) are dealt round-robin
+  // over the XCDs with all of a group's value heads on the same one, so they
+  // share its L2 for K and Q, and the rows of a ragged batch spread evenly.
   const int nbh = gridDim.x / NC;
   const int c = blockIdx.x / nbh;
-  const int r = blockIdx.x % nbh;
-  const int bh = (nbh & 7) == 0 ? (r & 7) * (nbh >> 3) + (r >> 3) : r;
+  const int bh = xcd_head(blockIdx.x % nbh, nbh / (Hv / Hk), Hv / Hk, 1);
   const int h = bh % Hv, bb = bh / Hv;
   const int grp = Hv / Hk, kh = h / grp;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
@@ -535,14 +547,20 @@ __global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_ke
   __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
   __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
 
-  // Workgroups whose ids agree mod 8 run on the same XCD.  Each XCD takes a
-  // contiguous range of (head, slice) units, so the NSL slices of a head, and
-  // the value heads of one q/k group, share its L2 for W, P, K^T, G and Q.
+  // The NSL slices of a head, and the heads of a q/k group, run on one XCD
+  // and share its L2 for W, P, K^T, G and Q; groups are dealt round-robin
+  // over the XCDs (rows of a ragged batch spread evenly).
   const int id = blockIdx.x;
-  const int units = B * Hv * NSL, per_xcd = (units + 7) / 8;
-  const int u = (id & 7) * per_xcd + (id >> 3);
-  if (u >= units) return;
-  const int hs = u / NSL, sl = u % NSL;
+  int hs, sl;
+  if (((B * Hk) & 7) == 0) {
+    const int u = xcd_head(id, B * Hk, Hv / Hk, NSL);
+    hs = u / NSL;
+    sl = u % NSL;
+  } else {
+    hs = (id >> 3) / NSL * 8 + (id & 7);
+    sl = (id >> 3) % NSL;
+  }
+  if (hs >= B * Hv) return;
   const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
   const int dv0 = sl * NV;
   int64_t tbase;
@@ -759,7 +777,7 @@ void launch_prep_g(int gate_dt, const void* q, int64_t q_ts, const void* k, int6
 
 // Up to this many (head, slice) units the chain runs two chunks ahead, one
 // workgroup per CU (256 CUs); beyond it, one chunk ahead, two per CU.
-int kChainOneDeep = 256;
+constexpr int kChainOneDeep = 256;
 
 template <typename TO>
 void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
@@ -767,8 +785,8 @@ void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
                   float q_scale, hipStream_t stream) {
   constexpr int NV = 32;
   constexpr int NSL = DH / NV;
-  const int64_t units = (int64_t)B * Hv * NSL;
-  const int64_t per_xcd = (units + 7) / 8;  // ids are padded to whole XCD rounds
+  const int64_t units = ((int64_t)B * Hv + 7) / 8 * 8 * NSL;  // whole XCD rounds of heads
+  const int64_t per_xcd = units / 8;
   if (units <= kChainOneDeep)
     hipLaunchKernelGGL((chunk_chain_kernel<NV, TO, 2>), dim3((unsigned)(per_xcd * 8)),
                        dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, cu,
