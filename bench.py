@@ -9,10 +9,15 @@ like the model's layer (16 q/k heads, 48 value heads, width 128):
      gates, carried state ~N(0, 0.05), chunk 64);
   3. gdn_decode_rows on 64 fixed rows (state [64,48,128,128] f32, in place);
   4. gdn_prefill_slots on a server's ragged batch: 16 fixed rows with
-     U{1..1024} new tokens each, bf16, states carried in place.
-Each part is timed with HIP events on the stream it runs on.  The inputs of
-every part rotate over three independent buffer sets so that the 256 MB
-last-level cache cannot hold a part's working set between its launches.
+     U{1..1024} new tokens each, bf16, states carried in place;
+  5. gdn_decode_rows_multi verifying a 4-token draft on 64 fixed rows, with
+     the state after every token written out as a snapshot.
+Each part is timed with HIP events on the stream it runs on.  The timed
+region runs each part's K iterations back to back, part after part (so a part
+follows its own previous call, not another part's dirty cache lines), and the
+inputs of every part rotate over three independent buffer sets so that the
+256 MB last-level cache cannot hold a part's working set between its
+launches.
 
 Printed: one JSON line.  value = tokens/s of part 2 (the prefill workload);
 decode_rows state GB/s and the layer-prefill tokens/s ride along in the same
@@ -181,50 +186,71 @@ def main():
         slot_sets[-1]["o"] = torch.empty((sx["q"].shape[0], HV, D), dtype=torch.bfloat16,
                                          device="cuda")
     slot_tokens = int(sx["cu_seqlens"][-1])
+    mx4 = make_workload("decode_rows_r64_k4")
+    multi = []
+    for _ in range(ROT):
+        multi.append({n: dev(mx4[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias",
+                                                "state", "lengths")})
+        multi[-1]["snap"] = torch.empty((R_DECODE, 4, HV, D, D), dtype=torch.float32,
+                                        device="cuda")
+        multi[-1]["o"] = torch.empty((R_DECODE, 4, HV, D), dtype=torch.bfloat16, device="cuda")
     ws_bytes = gdn.gdn_prefill_workspace_bytes(1, T_PREFILL, HK, HV)
     ws = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(ROT)]
 
-    def step(i, ev=None):
-        s = i % ROT
-        L, P, Dd = layer[s], pre[s], dec[s]
-        if ev is not None:
-            ev[0].record()
+    # The parts of a step, each one call.  The timed region runs each part's K
+    # iterations back to back (part after part), so a part follows its own
+    # previous call rather than another part that left the last-level cache
+    # full of its dirty lines; the K steps and their total are the same.
+    def layer_part(i):
+        L = layer[i % ROT]
         gdn.gdn_mixer_prefill(L["qkv"], L["z"], L["conv_w"], L["a"], L["b"], L["A_log"],
                               L["dt_bias"], L["norm_w"], HK, HV, conv_state=L["conv_state"],
                               state_in=L["state"], state_out=L["state"], y=L["out"],
                               workspace=L["ws"])
-        if ev is not None:
-            ev[1].record()
+
+    def prefill_part(i):
+        P = pre[i % ROT]
         gdn.gdn_prefill(P["q"], P["k"], P["v"], P["a"], P["b"], P["A_log"], P["dt_bias"],
-                        P["state"], P["state"], o=P["o"], workspace=ws[s])
-        if ev is not None:
-            ev[2].record()
+                        P["state"], P["state"], o=P["o"], workspace=ws[i % ROT])
+
+    def decode_part(i):
+        Dd = dec[i % ROT]
         gdn.gdn_decode_rows(Dd["q"], Dd["k"], Dd["v"], Dd["a"], Dd["b"], Dd["A_log"],
                             Dd["dt_bias"], Dd["state"], Dd["lengths"], o=Dd["o"])
-        if ev is not None:
-            ev[3].record()
-        Sx = slot_sets[s]
+
+    def slots_part(i):
+        Sx = slot_sets[i % ROT]
         gdn.gdn_prefill_slots(Sx["q"], Sx["k"], Sx["v"], Sx["a"], Sx["b"], Sx["A_log"],
                               Sx["dt_bias"], Sx["cu_seqlens"], Sx["state"], sx["max_len"],
                               o=Sx["o"], workspace=Sx["ws"])
-        if ev is not None:
-            ev[4].record()
 
-    for i in range(args.warmup):
-        step(i)
+    def multi_part(i):
+        M = multi[i % ROT]
+        gdn.gdn_decode_rows_multi(M["q"], M["k"], M["v"], M["a"], M["b"], M["A_log"],
+                                  M["dt_bias"], M["state"], M["snap"], M["lengths"], o=M["o"])
+
+    parts_fn = [layer_part, prefill_part, decode_part, slots_part, multi_part]
+    for fn in parts_fn:
+        for i in range(args.warmup):
+            fn(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)] for _ in parts_fn]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    for j, fn in enumerate(parts_fn):
+        for i in range(args.steps):
+            evs[j][i][0].record()
+            fn(args.warmup + i)
+            evs[j][i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
-    parts = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+    parts = np.array([[evs[j][i][0].elapsed_time(evs[j][i][1]) for j in range(len(parts_fn))]
                       for i in range(args.steps)])  # ms
     mean = parts.mean(axis=0)
-    t_layer, t_pre, t_dec, t_slots = mean
+    t_layer, t_pre, t_dec, t_slots, t_multi = mean
+    multi_bytes = (2 + 4) * R_DECODE * HV * D * D * 4  # state in + out, 4 snapshots
     ms_per_step = wall * 1e3 / args.steps
 
     prefill_tps = T_PREFILL / (t_pre * 1e-3)
@@ -295,6 +321,12 @@ def main():
                                                                                 sx["max_len"]),
                           "call_us": round(t_slots * 1e3, 2),
                           "mfma_tflops": round(slots_flops(sx) / (t_slots * 1e-3) / 1e12, 2)},
+        "decode_rows_multi": {"value": round(4 * R_DECODE / (t_multi * 1e-3), 1),
+                              "unit": "tokens/s",
+                              "workload": "decode_rows_r64_k4 (64 rows x 4 draft tokens, state "
+                                          "snapshot after every token)",
+                              "call_us": round(t_multi * 1e3, 2),
+                              "state_gbps": round(multi_bytes / (t_multi * 1e-3) / 1e9, 1)},
         "prefill": {"avg_launch_us": round(t_pre * 1e3, 2),
                     "mfma_tflops": round(pre_flops / (t_pre * 1e-3) / 1e12, 2),
                     "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9,

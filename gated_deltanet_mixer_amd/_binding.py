@@ -54,6 +54,9 @@ def lib():
         L.gdn_decode_rows.argtypes = [P, i64, P, i64, P, i64, i32, P, P, i32, P, P, P, P, P, i32,
                                       gdn_dims, f32, P]
         L.gdn_decode_rows.restype = ctypes.c_int
+        L.gdn_decode_rows_multi.argtypes = [P, i64, i64, P, i64, i64, P, i64, i64, i32, P, P,
+                                            i32, P, P, P, P, P, P, i32, i32, gdn_dims, f32, P]
+        L.gdn_decode_rows_multi.restype = ctypes.c_int
         L.gdn_gated_rmsnorm.argtypes = [P, P, P, i32, P, i32, i32, i32, f32, P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
         L.gdn_prefill_slots_workspace_bytes.argtypes = [i32, i32, gdn_dims]
@@ -285,4 +288,34 @@ def gdn_prefill_slots(q, k, v, a, b, A_log, dt_bias, cu_seqlens, state, max_len,
                                    gdn_dims(Hk, Hv, dk, dv), q_scale, _ptr(workspace), ws_bytes,
                                    _stream(q)),
            "gdn_prefill_slots")
+    return o
+
+
+def gdn_decode_rows_multi(q, k, v, a, b, A_log, dt_bias, state, snapshots=None, lengths=None,
+                          o=None, q_scale=1.0):
+    """K tokens per fixed row: q, k [R,K,Hk,dk], v [R,K,Hv,dv], a, b [R,K,Hv];
+    state [R,Hv,dv,dk] f32 advanced in place through the K tokens; snapshots
+    [R,K,Hv,dv,dk] f32 (optional) gets the state after each token; lengths
+    [R] int32 (<0 = idle row).  Returns o [R,K,Hv,dv]."""
+    _need_cuda(q, k, v, a, b, A_log, dt_bias, state, snapshots, lengths, o)
+    R, K, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    for t, d in ((q, dk), (k, dk), (v, dv)):
+        if t.numel() and (t.stride(3) != 1 or t.stride(2) != d):
+            raise ValueError("heads must be packed")
+    if o is None:
+        o = torch.empty((R, K, Hv, dv), dtype=v.dtype, device=v.device)
+    assert o.is_contiguous() and a.is_contiguous() and b.is_contiguous()
+    assert state.is_contiguous() and state.dtype == torch.float32
+    if snapshots is not None:
+        assert snapshots.is_contiguous() and snapshots.dtype == torch.float32
+        assert snapshots.shape == (R, K, Hv, dv, dk)
+    if lengths is not None:
+        assert lengths.dtype == torch.int32 and lengths.is_contiguous()
+    _check(lib().gdn_decode_rows_multi(_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0),
+                                       k.stride(1), _ptr(v), v.stride(0), v.stride(1), _dt(q),
+                                       _ptr(a), _ptr(b), _dt(a), _ptr(A_log), _ptr(dt_bias),
+                                       _ptr(state), _ptr(snapshots), _ptr(lengths), _ptr(o), R, K,
+                                       gdn_dims(Hk, Hv, dk, dv), q_scale, _stream(q)),
+           "gdn_decode_rows_multi")
     return o

@@ -174,6 +174,41 @@ int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t 
                                                static_cast<hipStream_t>(stream)));
 }
 
+int gdn_decode_rows_multi(const void* q, int64_t q_row_stride, int64_t q_tok_stride,
+                          const void* k, int64_t k_row_stride, int64_t k_tok_stride,
+                          const void* v, int64_t v_row_stride, int64_t v_tok_stride,
+                          int32_t qkv_dt, const void* a, const void* b, int32_t gate_dt,
+                          const float* A_log, const float* dt_bias, float* state,
+                          float* snapshots, const int32_t* lengths, void* o, int32_t R,
+                          int32_t K, gdn_dims dims, float q_scale, void* stream) {
+  if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !state || !o) return GDN_ERR_NULL;
+  if (!dtype_ok(qkv_dt) || !dtype_ok(gate_dt)) return GDN_ERR_DTYPE;
+  int st = check_dims(dims);
+  if (st != GDN_OK) return st;
+  const int Hk = dims.n_qk_heads, Hv = dims.n_v_heads;
+  if (R < 0 || K < 0) return GDN_ERR_SHAPE;
+  if (q_tok_stride < (int64_t)Hk * 128 || k_tok_stride < (int64_t)Hk * 128 ||
+      v_tok_stride < (int64_t)Hv * 128 || q_row_stride < 0 || k_row_stride < 0 ||
+      v_row_stride < 0)
+    return GDN_ERR_SHAPE;
+  if ((int64_t)R * Hv > INT32_MAX || (int64_t)R * K * Hv > INT32_MAX) return GDN_ERR_SHAPE;
+  if (q_row_stride % 8 || k_row_stride % 8 || v_row_stride % 8 || q_tok_stride % 8 ||
+      k_tok_stride % 8 || v_tok_stride % 8)
+    return GDN_ERR_ALIGN;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(state, 16) || (snapshots && !aligned(snapshots, 16)) ||
+      !aligned(a, dsize(gate_dt)) || !aligned(b, dsize(gate_dt)) || !aligned(A_log, 4) ||
+      !aligned(dt_bias, 4) || (lengths && !aligned(lengths, 4)))
+    return GDN_ERR_ALIGN;
+  const size_t sbytes = (size_t)R * Hv * 128 * 128 * 4;
+  if (snapshots && overlaps(snapshots, sbytes * K, state, sbytes)) return GDN_ERR_SHAPE;
+  if (R == 0 || K == 0) return GDN_OK;
+  return launch_status(gdn::launch_decode_rows_multi(
+      q, q_row_stride, q_tok_stride, k, k_row_stride, k_tok_stride, v, v_row_stride,
+      v_tok_stride, qkv_dt, a, b, gate_dt, A_log, dt_bias, state, snapshots, lengths, o, R, K, Hk,
+      Hv, q_scale, static_cast<hipStream_t>(stream)));
+}
+
 int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const float* w,
                       int32_t N, int32_t H, int32_t D, float eps, void* stream) {
   if (!x || !z || !y || !w) return GDN_ERR_NULL;

@@ -31,6 +31,15 @@ hipError_t launch_decode_rows(const void* q, int64_t q_rs, const void* k, int64_
                               const float* dt_bias, float* state, const int32_t* lengths, void* o,
                               int R, int Hk, int Hv, float q_scale, hipStream_t stream);
 
+// K tokens per row; snapshots (may be NULL) [R, K, Hv, 128, 128].
+hipError_t launch_decode_rows_multi(const void* q, int64_t q_rs, int64_t q_ts, const void* k,
+                                    int64_t k_rs, int64_t k_ts, const void* v, int64_t v_rs,
+                                    int64_t v_ts, int qkv_dt, const void* a, const void* b,
+                                    int gate_dt, const float* A_log, const float* dt_bias,
+                                    float* state, float* snapshots, const int32_t* lengths,
+                                    void* o, int R, int K, int Hk, int Hv, float q_scale,
+                                    hipStream_t stream);
+
 hipError_t launch_prefill_sequential(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
                                      const void* v, int64_t v_ts, int qkv_dt, const void* a,
                                      const void* b, int gate_dt, const float* A_log,

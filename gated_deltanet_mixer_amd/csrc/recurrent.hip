@@ -77,6 +77,68 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_rows_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// decode_rows over K tokens per row (a draft of K tokens to verify): the same
+// mapping, the state held in registers across the K tokens, so it is read and
+// written once; optionally the state after each token is written to
+// snapshots[r][t] (the states a verifier rolls back to).  Each token's
+// arithmetic is that of decode_rows_kernel, in the same order, so K tokens
+// here equal K successive decode_rows calls bit for bit.
+template <typename T, typename G>
+__global__ __launch_bounds__(DEC_THREADS) void decode_rows_multi_kernel(
+    const T* __restrict__ q, int64_t q_rs, int64_t q_ts, const T* __restrict__ k, int64_t k_rs,
+    int64_t k_ts, const T* __restrict__ v, int64_t v_rs, int64_t v_ts, const G* __restrict__ a,
+    const G* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
+    float* __restrict__ state, float* __restrict__ snapshots, const int32_t* __restrict__ lengths,
+    T* __restrict__ o, int K, int Hk, int Hv, float q_scale) {
+  const int r = blockIdx.x / Hv;
+  const int h = blockIdx.x - r * Hv;
+  const int kh = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, grp = lane >> 4, l16 = lane & 15;
+  if (lengths && lengths[r] < 0) {  // idle row: state and snapshots untouched, output zero
+    for (int t = 0; t < K; ++t)
+      if (tid < 128) store1(o + (((int64_t)r * K + t) * Hv + h) * 128 + tid, 0.0f);
+    return;
+  }
+  float* Sb = state + ((int64_t)r * Hv + h) * (128 * 128);
+  float s[8][8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) load8(Sb + (32 * wave + 4 * it + grp) * 128 + l16 * 8, s[it]);
+  const float Al = A_log[h], Db = dt_bias[h];
+
+  for (int t = 0; t < K; ++t) {
+    float kv[8], qv[8];
+    load8(k + r * k_rs + t * k_ts + kh * 128 + l16 * 8, kv);
+    load8(q + r * q_rs + t * q_ts + kh * 128 + l16 * 8, qv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] *= q_scale;
+    float vr[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+      vr[it] = load1(v + r * v_rs + t * v_ts + h * 128 + 32 * wave + 4 * it + grp);
+    const int64_t gi = ((int64_t)r * K + t) * Hv + h;
+    const float al = expf(gate_log_alpha(load1(a + gi), Al, Db));
+    const float be = gate_beta(load1(b + gi));
+    const float kq = sum16(dot8(kv, qv));
+    T* ob = o + gi * 128;
+    float* snap = snapshots ? snapshots + (((int64_t)r * K + t) * Hv + h) * (128 * 128) : nullptr;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = 32 * wave + 4 * it + grp;
+      const float su = sum16(dot8(s[it], kv));
+      const float sq = sum16(dot8(s[it], qv));
+      const float d = be * (vr[it] - al * su);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[it][i] = fmaf(al, s[it][i], d * kv[i]);
+      if (snap) store8(snap + row * 128 + l16 * 8, s[it]);
+      if (l16 == 0) store1(ob + row, fmaf(al, sq, d * kq));
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) store8(Sb + (32 * wave + 4 * it + grp) * 128 + l16 * 8, s[it]);
+}
+
+// ---------------------------------------------------------------------------
 // Sequential prefill: state rows live in registers for the whole sequence.
 // One workgroup per (batch, value head, block of 16 value rows); tokens are
 // staged SEQ_TT at a time in LDS (k, q as f32, this block's v, the gates),
@@ -200,6 +262,45 @@ hipError_t launch_decode_rows(const void* q, int64_t q_rs, const void* k, int64_
   else
     launch_decode_t<float, float>(q, q_rs, k, k_rs, v, v_rs, a, b, A_log, dt_bias, state,
                                   lengths, o, R, Hk, Hv, q_scale, stream);
+  return hipGetLastError();
+}
+
+template <typename T, typename G>
+static void launch_decode_multi_t(const void* q, int64_t q_rs, int64_t q_ts, const void* k,
+                                  int64_t k_rs, int64_t k_ts, const void* v, int64_t v_rs,
+                                  int64_t v_ts, const void* a, const void* b, const float* A_log,
+                                  const float* dt_bias, float* state, float* snapshots,
+                                  const int32_t* lengths, void* o, int R, int K, int Hk, int Hv,
+                                  float q_scale, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_rows_multi_kernel<T, G>), dim3(R * Hv), dim3(DEC_THREADS), 0, stream,
+                     (const T*)q, q_rs, q_ts, (const T*)k, k_rs, k_ts, (const T*)v, v_rs, v_ts,
+                     (const G*)a, (const G*)b, A_log, dt_bias, state, snapshots, lengths, (T*)o, K,
+                     Hk, Hv, q_scale);
+}
+
+hipError_t launch_decode_rows_multi(const void* q, int64_t q_rs, int64_t q_ts, const void* k,
+                                    int64_t k_rs, int64_t k_ts, const void* v, int64_t v_rs,
+                                    int64_t v_ts, int qkv_dt, const void* a, const void* b,
+                                    int gate_dt, const float* A_log, const float* dt_bias,
+                                    float* state, float* snapshots, const int32_t* lengths,
+                                    void* o, int R, int K, int Hk, int Hv, float q_scale,
+                                    hipStream_t stream) {
+  if (qkv_dt == 1 && gate_dt == 1)
+    launch_decode_multi_t<uint16_t, uint16_t>(q, q_rs, q_ts, k, k_rs, k_ts, v, v_rs, v_ts, a, b,
+                                              A_log, dt_bias, state, snapshots, lengths, o, R, K,
+                                              Hk, Hv, q_scale, stream);
+  else if (qkv_dt == 1)
+    launch_decode_multi_t<uint16_t, float>(q, q_rs, q_ts, k, k_rs, k_ts, v, v_rs, v_ts, a, b,
+                                           A_log, dt_bias, state, snapshots, lengths, o, R, K, Hk,
+                                           Hv, q_scale, stream);
+  else if (gate_dt == 1)
+    launch_decode_multi_t<float, uint16_t>(q, q_rs, q_ts, k, k_rs, k_ts, v, v_rs, v_ts, a, b,
+                                           A_log, dt_bias, state, snapshots, lengths, o, R, K, Hk,
+                                           Hv, q_scale, stream);
+  else
+    launch_decode_multi_t<float, float>(q, q_rs, q_ts, k, k_rs, k_ts, v, v_rs, v_ts, a, b, A_log,
+                                        dt_bias, state, snapshots, lengths, o, R, K, Hk, Hv,
+                                        q_scale, stream);
   return hipGetLastError();
 }
 

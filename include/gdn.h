@@ -163,6 +163,34 @@ int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t 
                     float q_scale, void* stream);
 
 /*
+ * gdn_decode_rows_multi -- K new tokens for each of R fixed rows (a draft of
+ * K tokens to verify, the shape of the blog's multi-token prediction and
+ * speculative decoding, and the card's decode_rows serving rows each at its
+ * own length).  Each row's state is read once, advanced through its K tokens
+ * in order and written once; K tokens equal K successive gdn_decode_rows
+ * calls, bit for bit.
+ *   q, k   token t of row r at r*row_stride + t*tok_stride (elements), each
+ *          [Hk, dk]; v likewise [Hv, dv].
+ *   a, b   [R, K, Hv] contiguous in gate_dt; A_log, dt_bias [Hv] f32.
+ *   state  [R, Hv, dv, dk] f32, read and written in place (the state after
+ *          all K tokens).
+ *   snapshots  [R, K, Hv, dv, dk] f32 or NULL: snapshots[r][t] receives row
+ *          r's state after its token t, so a verifier that accepts n tokens
+ *          continues from snapshots[r][n-1].  Must not overlap state.
+ *   lengths [R] int32 or NULL, as in gdn_decode_rows: < 0 marks an idle row
+ *          (state and snapshots untouched, outputs zero).
+ *   o      [R, K, Hv, dv] contiguous in qkv_dt.
+ * K == 0 or R == 0 is a no-op.
+ */
+int gdn_decode_rows_multi(const void* q, int64_t q_row_stride, int64_t q_tok_stride,
+                          const void* k, int64_t k_row_stride, int64_t k_tok_stride,
+                          const void* v, int64_t v_row_stride, int64_t v_tok_stride,
+                          int32_t qkv_dt, const void* a, const void* b, int32_t gate_dt,
+                          const float* A_log, const float* dt_bias, float* state,
+                          float* snapshots, const int32_t* lengths, void* o, int32_t R,
+                          int32_t K, gdn_dims dims, float q_scale, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * (1 + w) * silu(z) per
  * row of D ("Qwen3.8 27B" card, Gated DeltaNet and Norms bullets;
  * llm-arch-viz: RMSNormGated of width 128, eps 1e-06).

@@ -19,7 +19,7 @@ import numpy as np
 
 __all__ = ["HK", "HV", "D", "CONV_CH", "CONV_W", "WORKLOADS", "bf16_round", "f32_round",
            "to_f64", "is_bf16", "recurrence_inputs", "decode_inputs", "mixer_inputs",
-           "slots_inputs", "make_workload", "unit_heads"]
+           "slots_inputs", "decode_multi_inputs", "make_workload", "unit_heads"]
 
 HK, HV, D = 16, 48, 128
 CONV_CH = 2 * HK * D + HV * D  # 10240
@@ -117,6 +117,29 @@ def slots_inputs(lengths, Hk=HK, Hv=HV, d=D, qkv_dt="bf16", gate_dt="f32", seed=
     }
 
 
+def decode_multi_inputs(R, K, Hk=HK, Hv=HV, d=D, qkv_dt="bf16", gate_dt="bf16", seed=6,
+                        state_std=0.05, max_len=8192):
+    """Inputs of one multi-token decode_rows call: K draft tokens per fixed row.
+    q, k [R,K,Hk,d]; v [R,K,Hv,d]; a, b [R,K,Hv]; A_log, dt_bias [Hv];
+    state [R,Hv,d,d] f32; lengths [R] int32 ~ U{1..max_len}."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = unit_heads(rng.standard_normal((R, K, Hk, d)))
+    k = unit_heads(rng.standard_normal((R, K, Hk, d)))
+    v = rng.standard_normal((R, K, Hv, d))
+    a = rng.standard_normal((R, K, Hv))
+    b = rng.standard_normal((R, K, Hv))
+    A_log = rng.uniform(-1.0, 1.0, Hv)
+    dt_bias = rng.normal(0.0, 0.1, Hv)
+    lengths = rng.integers(1, max_len + 1, R).astype(np.int32)
+    state = rng.standard_normal((R, Hv, d, d), dtype=np.float32) * np.float32(state_std)
+    return {
+        "q": _round(q, qkv_dt), "k": _round(k, qkv_dt), "v": _round(v, qkv_dt),
+        "a": _round(a, gate_dt), "b": _round(b, gate_dt),
+        "A_log": f32_round(A_log), "dt_bias": f32_round(dt_bias),
+        "state": state.astype(np.float32), "lengths": lengths,
+    }
+
+
 def decode_inputs(R, Hk=HK, Hv=HV, d=D, qkv_dt="bf16", gate_dt="bf16", seed=1,
                   state_std=0.05, max_len=8192):
     """Inputs of one decode_rows call: q, k [R,Hk,d]; v [R,Hv,d]; a, b [R,Hv];
@@ -174,6 +197,9 @@ WORKLOADS = {
     "prefill_bf16_b1_t65536_x16": dict(kind="prefill", B=1, T=65536, qkv_dt="bf16",
                                        gate_dt="f32", state_std=None, seed=1004,
                                        calls=16),
+    # Verifying a 4-token draft on 64 fixed rows (the decode workload's shape).
+    "decode_rows_r64_k4": dict(kind="decode_multi", R=64, K=4, qkv_dt="bf16", gate_dt="bf16",
+                               seed=1006),
     # A server's ragged prefill: 16 fixed rows, new-token counts ~ U{1..1024}
     # drawn from the seed's first integers, states ~ N(0, 0.05).
     "prefill_slots_bf16_r16": dict(kind="slots", R=16, max_new=1024, qkv_dt="bf16",
@@ -193,6 +219,8 @@ def make_workload(name, **overrides):
         return decode_inputs(**cfg)
     if kind == "mixer":
         return mixer_inputs(**cfg)
+    if kind == "decode_multi":
+        return decode_multi_inputs(**cfg)
     if kind == "slots":
         rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
         lengths = rng.integers(1, cfg.pop("max_new") + 1, cfg.pop("R"))

@@ -29,7 +29,7 @@ def test_header_and_exports():
     assert {"gdn_conv_silu", "gdn_prefill", "gdn_decode_rows", "gdn_gated_rmsnorm",
             "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version",
             "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes", "gdn_prefill_slots",
-            "gdn_prefill_slots_workspace_bytes"} <= set(names)
+            "gdn_prefill_slots_workspace_bytes", "gdn_decode_rows_multi"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert gdn.gdn_abi_version() == 1
@@ -113,6 +113,28 @@ def test_decode_validation():
     assert decode(st=P + 4) == ALIGN
     assert decode(lengths=P + 2) == ALIGN
     assert decode(R=0) == OK
+
+
+def decode_multi(q=P, k=2 * P, v=3 * P, qdt=1, st=4 * P, snap=None, o=5 * P, R=4, K=3,
+                 dims=D16, lengths=None, qts=2048, vts=6144):
+    return gdn.lib().gdn_decode_rows_multi(_vp(q), 3 * 2048, qts, _vp(k), 3 * 2048, qts, _vp(v),
+                                           3 * 6144, vts, qdt, _vp(6 * P), _vp(7 * P), 1,
+                                           _vp(8 * P), _vp(9 * P), _vp(st), _vp(snap),
+                                           _vp(lengths), _vp(o), R, K, dims, 1.0, None)
+
+
+def test_decode_multi_validation():
+    assert decode_multi(st=0) == NULL
+    assert decode_multi(qdt=5) == DTYPE
+    assert decode_multi(dims=gdn_dims(16, 48, 96, 128)) == UNSUP
+    assert decode_multi(R=-1) == SHAPE
+    assert decode_multi(K=-2) == SHAPE
+    assert decode_multi(qts=1024) == SHAPE       # token stride shorter than the heads
+    assert decode_multi(qts=2052) == ALIGN
+    assert decode_multi(snap=P + 4) == ALIGN
+    assert decode_multi(snap=4 * P) == SHAPE     # snapshots on top of the state
+    assert decode_multi(R=0) == OK
+    assert decode_multi(K=0) == OK
 
 
 def test_norm_validation():
