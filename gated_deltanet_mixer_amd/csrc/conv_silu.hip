@@ -44,7 +44,21 @@ template <> struct Raw8<float> {
   }
 };
 
-template <typename TX, typename TYA, typename TYB>
+// Streaming (non-temporal) stores of 8 outputs: the whole mixer's conv output
+// is read once by the prep, and keeping it out of the last-level cache leaves
+// that to the prep's workspace, which the chain reads next.
+__device__ __forceinline__ void store8_stream(float* p, const float* in) {
+  __builtin_nontemporal_store(f32x4{in[0], in[1], in[2], in[3]}, reinterpret_cast<f32x4*>(p));
+  __builtin_nontemporal_store(f32x4{in[4], in[5], in[6], in[7]}, reinterpret_cast<f32x4*>(p + 4));
+}
+__device__ __forceinline__ void store8_stream(uint16_t* p, const float* in) {
+  u16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = f2bf(in[i]);
+  __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(p));
+}
+
+template <typename TX, typename TYA, typename TYB, bool kStream>
 __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
     const TX* __restrict__ x, TYA* __restrict__ ya, int64_t ya_stride, TYB* __restrict__ yb,
     int64_t yb_stride, const float* __restrict__ w, float* conv_state, int nb, int Tlen, int C,
@@ -140,8 +154,13 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
 #pragma unroll
           for (int i = 0; i < 8; ++i) yv[i] *= r;
         }
-        if (l2) store8(yarows + (int64_t)(t + u) * ya_stride + ca, yv);
-        else store8(ybrows + (int64_t)(t + u) * yb_stride + cb, yv);
+        if constexpr (kStream) {
+          if (l2) store8_stream(yarows + (int64_t)(t + u) * ya_stride + ca, yv);
+          else store8_stream(ybrows + (int64_t)(t + u) * yb_stride + cb, yv);
+        } else {
+          if (l2) store8(yarows + (int64_t)(t + u) * ya_stride + ca, yv);
+          else store8(ybrows + (int64_t)(t + u) * yb_stride + cb, yv);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           h[0][i] = h[1][i];
@@ -153,14 +172,14 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
   }
 }
 
-template <typename TX, typename TYA, typename TYB>
+template <typename TX, typename TYA, typename TYB, bool kStream = false>
 static void launch_conv_t(const void* x, void* ya, int64_t ya_stride, void* yb, int64_t yb_stride,
                           const float* w, float* conv_state, int B, int T, int C, int l2_channels,
                           float l2_eps, hipStream_t stream) {
   const int64_t total = (int64_t)((C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8)) *
                         ((T + CONV_TB - 1) / CONV_TB) * B;
   dim3 grid((unsigned)(((total + 7) / 8) * 8));
-  hipLaunchKernelGGL((conv_silu_kernel<TX, TYA, TYB>), grid, dim3(CONV_THREADS), 0, stream,
+  hipLaunchKernelGGL((conv_silu_kernel<TX, TYA, TYB, kStream>), grid, dim3(CONV_THREADS), 0, stream,
                      (const TX*)x, (TYA*)ya, ya_stride, (TYB*)yb, yb_stride, w, conv_state, B, T,
                      C, l2_channels, l2_eps);
 }
@@ -190,11 +209,12 @@ hipError_t launch_conv_silu_split(const void* x, int x_dt, float* yqk, uint16_t*
                                   const float* w, float* conv_state, int B, int T, int C,
                                   int l2_channels, float l2_eps, hipStream_t stream) {
   if (x_dt == 1)
-    launch_conv_t<uint16_t, float, uint16_t>(x, yqk, l2_channels, yv, C - l2_channels, w,
-                                             conv_state, B, T, C, l2_channels, l2_eps, stream);
+    launch_conv_t<uint16_t, float, uint16_t, true>(x, yqk, l2_channels, yv, C - l2_channels, w,
+                                                   conv_state, B, T, C, l2_channels, l2_eps,
+                                                   stream);
   else
-    launch_conv_t<float, float, uint16_t>(x, yqk, l2_channels, yv, C - l2_channels, w,
-                                          conv_state, B, T, C, l2_channels, l2_eps, stream);
+    launch_conv_t<float, float, uint16_t, true>(x, yqk, l2_channels, yv, C - l2_channels, w,
+                                                conv_state, B, T, C, l2_channels, l2_eps, stream);
   return hipGetLastError();
 }
 
