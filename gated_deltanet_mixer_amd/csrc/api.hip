@@ -161,7 +161,7 @@ int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t 
   if (q_row_stride < (int64_t)Hk * 128 || k_row_stride < (int64_t)Hk * 128 ||
       v_row_stride < (int64_t)Hv * 128)
     return GDN_ERR_SHAPE;
-  if ((int64_t)R * Hv > INT32_MAX) return GDN_ERR_SHAPE;
+  if ((int64_t)R * Hv * 4 > INT32_MAX) return GDN_ERR_SHAPE;  // four workgroups per (row, head)
   if (q_row_stride % 8 || k_row_stride % 8 || v_row_stride % 8) return GDN_ERR_ALIGN;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(state, 16) || !aligned(a, dsize(gate_dt)) || !aligned(b, dsize(gate_dt)) ||
@@ -191,7 +191,7 @@ int gdn_decode_rows_multi(const void* q, int64_t q_row_stride, int64_t q_tok_str
       v_tok_stride < (int64_t)Hv * 128 || q_row_stride < 0 || k_row_stride < 0 ||
       v_row_stride < 0)
     return GDN_ERR_SHAPE;
-  if ((int64_t)R * Hv > INT32_MAX || (int64_t)R * K * Hv > INT32_MAX) return GDN_ERR_SHAPE;
+  if ((int64_t)R * Hv * 4 > INT32_MAX || (int64_t)R * K * Hv > INT32_MAX) return GDN_ERR_SHAPE;
   if (q_row_stride % 8 || k_row_stride % 8 || v_row_stride % 8 || q_tok_stride % 8 ||
       k_tok_stride % 8 || v_tok_stride % 8)
     return GDN_ERR_ALIGN;
