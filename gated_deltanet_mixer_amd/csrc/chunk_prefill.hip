@@ -22,8 +22,9 @@
 //    is formed from a two-term bf16 split of both operands: q . k is small
 //    next to |q||k| (unit vectors in 128 dimensions), so it needs more than
 //    bf16 operand precision; no other product does.
-//  * chunk_chain: one workgroup per (batch, value head, 32-column slice of
-//    dv), sequential over chunks.  The f32 state slice lives in MFMA
+//  * chunk_chain: one workgroup per (batch, value head, slice of dv: 32
+//    columns, or 64 when the batch has more 32-column slices than CUs),
+//    sequential over chunks.  The f32 state slice lives in MFMA
 //    accumulator registers of four state waves; four output waves form O.
 //    Each wave loads its own operands two chunks ahead straight into
 //    registers; the bf16 copy of the state and U^T are exchanged in LDS.
@@ -470,11 +471,15 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
 //   output: (Q H)^T          | barrier | O = .. + P U    | barrier
 constexpr int CH_THREADS = 512;
 
+// Column u / 2 * 32 + dvp(u % 2, m) of a slice: the 32-column pieces of a
+// slice each keep the dvp row order.
+__device__ __forceinline__ int dvp2(int u, int m) { return 32 * (u >> 1) + dvp(u & 1, m); }
+
 template <int NV>
 struct StateRegs {
   bf16x8 w[4];       // W[16w + li][32kk + 8lg ..]
   bf16x8 kt[2][2];   // K^T[32w + 16i + li][32kk + 8lg ..]
-  u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + dvp(vb, li)]
+  u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + dvp2(u, li)]
   f32x4 gu;          // G[16w + 4lg ..]
   float gl;          // G_last
 };
@@ -503,9 +508,13 @@ __device__ __forceinline__ void state_fetch(StateRegs<NV>& R, const WsLayout& ws
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) R.kt[i][kk] = gld_frag(kp + (i * 2 + kk) * 512);
-  const uint16_t* up = ws.Ut + chunk * (CK * DH) + (sl * 4 + w) * 512 + lane * 4;
+  // Ut is stored per 32-column piece (the prep's Utf[piece][w][vb]).
 #pragma unroll
-  for (int vb = 0; vb < NV / 16; ++vb) R.ut[vb] = *reinterpret_cast<const u16x4*>(up + vb * 256);
+  for (int u = 0; u < NV / 16; ++u) {
+    const uint16_t* up = ws.Ut + chunk * (CK * DH) + ((sl * (NV / 32) + (u >> 1)) * 4 + w) * 512 +
+                         (u & 1) * 256 + lane * 4;
+    R.ut[u] = *reinterpret_cast<const u16x4*>(up);
+  }
   const float* gp = ws.G + chunk * 2 * CK;
   R.gu = *reinterpret_cast<const f32x4*>(gp + 16 * w + 4 * (lane >> 4));
   R.gl = gp[CK + (lane & 15)];  // G_last, replicated
@@ -531,18 +540,19 @@ __device__ __forceinline__ void out_fetch(OutRegs& R, const WsLayout& ws, int bb
   R.gt = ws.G[chunk * 2 * CK + 16 * w + li];
 }
 
-// DEPTH = chunks loaded ahead.  2 for up to one workgroup per CU (one
-// head's slices per CU, the B = 1 case); 1 with at most 128 VGPRs, so two
-// workgroups share a CU when there are more slices than CUs and each hides
-// the other's latency.
-template <int NV, typename TO, int DEPTH>
-__global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_kernel(
+// NV = 32 or 64 value columns per slice.  Each wave loads its operands two
+// chunks ahead (three register sets in rotation), which needs up to 256
+// VGPRs, so one workgroup runs per CU.
+constexpr int DEPTH = 2;
+
+template <int NV, typename TO>
+__global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
     WsLayout ws, const float* state_in,
     float* state_out, TO* __restrict__ o, int B, int T, const int32_t* __restrict__ cu,
     int total, int Hk, int Hv, int NC, float q_scale) {
   constexpr int NSL = DH / NV;  // slices per head
   constexpr int NVB = NV / 16;  // 16-column blocks per slice
-  static_assert(NV == 32, "the dvp row order and the 8-wide output stores assume 32 columns");
+  static_assert(NV == 32 || NV == 64, "slices are one or two 32-column pieces");
   __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * RP];   // S slice [dv][dk], bf16
   __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
   __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
@@ -577,7 +587,7 @@ __global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_ke
   if (state_wave) {
     StateRegs<NV> RA, RB, RC;
     state_fetch<NV>(RA, ws, bb, bh, kh, 0, Hk, NC, sl, w, lane);
-    if constexpr (DEPTH == 2) state_fetch<NV>(RB, ws, bb, bh, kh, ahead(1), Hk, NC, sl, w, lane);
+    state_fetch<NV>(RB, ws, bb, bh, kh, ahead(1), Hk, NC, sl, w, lane);
 
     f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
 #pragma unroll
@@ -612,14 +622,14 @@ __global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_ke
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb)
-          accU[vb] = mfma16(R.w[kk], ld_frag(&Sb[dvp(vb, li) * RP + kk * 32 + lg * 8]), accU[vb]);
+          accU[vb] = mfma16(R.w[kk], ld_frag(&Sb[dvp2(vb, li) * RP + kk * 32 + lg * 8]), accU[vb]);
       // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.
       {
         const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
                              __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) {
-          const int off = dvp(vb, li) * XP + w * 16 + lg * 4;
+          const int off = dvp2(vb, li) * XP + w * 16 + lg * 4;
           float u[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) u[r] = bf2f(R.ut[vb][r]) - accU[vb][r];
@@ -655,21 +665,13 @@ __global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_ke
       lds_barrier();
     };
     int c = 0;
-    if constexpr (DEPTH == 2) {
-      for (; c + 3 <= ncr; c += 3) {
-        step(RA, RC, c);
-        step(RB, RA, c + 1);
-        step(RC, RB, c + 2);
-      }
-      if (c < ncr) step(RA, RC, c);
-      if (c + 1 < ncr) step(RB, RA, c + 1);
-    } else {
-      for (; c + 2 <= ncr; c += 2) {
-        step(RA, RB, c);
-        step(RB, RA, c + 1);
-      }
-      if (c < ncr) step(RA, RB, c);
+    for (; c + 3 <= ncr; c += 3) {
+      step(RA, RC, c);
+      step(RB, RA, c + 1);
+      step(RC, RB, c + 2);
     }
+    if (c < ncr) step(RA, RC, c);
+    if (c + 1 < ncr) step(RB, RA, c + 1);
 
     if (state_out) {
 #pragma unroll
@@ -686,7 +688,7 @@ __global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_ke
     const int tr = w * 16 + li;
     OutRegs RA, RB, RC;
     out_fetch(RA, ws, bb, bh, kh, 0, Hk, NC, w, lane);
-    if constexpr (DEPTH == 2) out_fetch(RB, ws, bb, bh, kh, ahead(1), Hk, NC, w, lane);
+    out_fetch(RB, ws, bb, bh, kh, ahead(1), Hk, NC, w, lane);
     lds_barrier();
     // `full` (std::true_type) marks a chunk of CK tokens, whose store needs no
     // row check.
@@ -700,7 +702,7 @@ __global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_ke
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb)
-          accQ[vb] = mfma16(ld_frag(&Sb[dvp(vb, li) * RP + kk * 32 + lg * 8]), R.q[kk], accQ[vb]);
+          accQ[vb] = mfma16(ld_frag(&Sb[dvp2(vb, li) * RP + kk * 32 + lg * 8]), R.q[kk], accQ[vb]);
       // The loads of chunk c + 2 go out after (Q H)^T: issued at the start of
       // the step they queue behind the state waves' loads, and (Q H)^T gates
       // the first barrier.
@@ -712,39 +714,33 @@ __global__ __launch_bounds__(CH_THREADS, DEPTH == 1 ? 4 : 2) void chunk_chain_ke
       // 0 and 1 need only s < 32.  Lane (li, lg) ends with dv 8lg..8lg+7 of
       // token 16w + li (dvp order), one 8-wide store.
       const float gq = q_scale * __expf(R.gt);
-      float ov[8];
+      float ov[4 * NVB];
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(ld_frag(&Utl[dvp(vb, li) * XP + lg * 8]), R.p[0], acc);
-        if (w >= 2) acc = mfma16(ld_frag(&Utl[dvp(vb, li) * XP + 32 + lg * 8]), R.p[1], acc);
+        acc = mfma16(ld_frag(&Utl[dvp2(vb, li) * XP + lg * 8]), R.p[0], acc);
+        if (w >= 2) acc = mfma16(ld_frag(&Utl[dvp2(vb, li) * XP + 32 + lg * 8]), R.p[1], acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) ov[4 * vb + r] = fmaf(gq, accQ[vb][r], acc[r]);
       }
       const int t0 = c * CK;
-      if (decltype(full)::value || tr < min(CK, tlen - t0))
-        store8(o + ((tbase + t0 + tr) * Hv + h) * DH + dv0 + 8 * lg, ov);
+      if (decltype(full)::value || tr < min(CK, tlen - t0)) {
+#pragma unroll
+        for (int j = 0; j < NV / 32; ++j)
+          store8(o + ((tbase + t0 + tr) * Hv + h) * DH + dv0 + 32 * j + 8 * lg, ov + 8 * j);
+      }
       lds_barrier();
     };
     int c = 0;
     const int nfull = tlen / CK;
-    if constexpr (DEPTH == 2) {
-      for (; c + 3 <= nfull; c += 3) {
-        step(RA, RC, c, std::true_type{});
-        step(RB, RA, c + 1, std::true_type{});
-        step(RC, RB, c + 2, std::true_type{});
-      }
-      if (c < ncr) step(RA, RC, c, std::false_type{});
-      if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
-      if (c + 2 < ncr) step(RC, RB, c + 2, std::false_type{});
-    } else {
-      for (; c + 2 <= nfull; c += 2) {
-        step(RA, RB, c, std::true_type{});
-        step(RB, RA, c + 1, std::true_type{});
-      }
-      if (c < ncr) step(RA, RB, c, std::false_type{});
-      if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
+    for (; c + 3 <= nfull; c += 3) {
+      step(RA, RC, c, std::true_type{});
+      step(RB, RA, c + 1, std::true_type{});
+      step(RC, RB, c + 2, std::true_type{});
     }
+    if (c < ncr) step(RA, RC, c, std::false_type{});
+    if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
+    if (c + 2 < ncr) step(RC, RB, c + 2, std::false_type{});
   }
 }
 
@@ -775,24 +771,26 @@ void launch_prep_g(int gate_dt, const void* q, int64_t q_ts, const void* k, int6
                                total, Hk, Hv, NC, q_scale, stream);
 }
 
-// Up to this many (head, slice) units the chain runs two chunks ahead, one
-// workgroup per CU (256 CUs); beyond it, one chunk ahead, two per CU.
-constexpr int kChainOneDeep = 256;
+// Up to this many 32-column (head, slice) units, one per CU (256 CUs), the
+// chain runs 32-column slices; beyond it 64-column slices, still one
+// workgroup per CU.  At B = 2 (384 narrow units) the wide form takes the
+// chain from 183 to 134 us: a CU runs one wide workgroup about as fast as two
+// narrow ones side by side, and 192 wide units fill 192 CUs where 384 narrow
+// ones crowd two to a CU on the same 192.
+constexpr int kChainNarrow = 256;
 
 template <typename TO>
 void launch_chain(const WsLayout& ws, const float* state_in, float* state_out,
                   void* o, int B, int T, const int32_t* cu, int total, int Hk, int Hv, int NC,
                   float q_scale, hipStream_t stream) {
-  constexpr int NV = 32;
-  constexpr int NSL = DH / NV;
-  const int64_t units = ((int64_t)B * Hv + 7) / 8 * 8 * NSL;  // whole XCD rounds of heads
+  const int64_t units = ((int64_t)B * Hv + 7) / 8 * 8 * (DH / 32);  // whole XCD rounds of heads
   const int64_t per_xcd = units / 8;
-  if (units <= kChainOneDeep)
-    hipLaunchKernelGGL((chunk_chain_kernel<NV, TO, 2>), dim3((unsigned)(per_xcd * 8)),
+  if (units <= kChainNarrow)
+    hipLaunchKernelGGL((chunk_chain_kernel<32, TO>), dim3((unsigned)(per_xcd * 8)),
                        dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, cu,
                        total, Hk, Hv, NC, q_scale);
   else
-    hipLaunchKernelGGL((chunk_chain_kernel<NV, TO, 1>), dim3((unsigned)(per_xcd * 8)),
+    hipLaunchKernelGGL((chunk_chain_kernel<64, TO>), dim3((unsigned)(per_xcd * 8 / 2)),
                        dim3(CH_THREADS), 0, stream, ws, state_in, state_out, (TO*)o, B, T, cu,
                        total, Hk, Hv, NC, q_scale);
 }

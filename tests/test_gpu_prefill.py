@@ -59,6 +59,23 @@ def test_chunked_small(T, A_range, state, algo):
     assert max_rel_err(host_f64(S), S_ref) < TOL
 
 
+@pytest.mark.parametrize("B,Hk,Hv,T", [(3, 4, 24, 150), (6, 4, 12, 65), (6, 4, 12, 1)])
+def test_chunked_wide_slices(B, Hk, Hv, T):
+    """Batches with more 32-column slices than CUs (B*Hv*4 > 256) run the
+    chain on 64-column slices; B*Hk = 12 takes the plain workgroup order, 24
+    the XCD-grouped one."""
+    banner(f"chunked wide slices B={B} Hk={Hk} Hv={Hv} T={T}")
+    assert B * Hv * 4 > 256
+    x = recurrence_inputs(B, T, Hk=Hk, Hv=Hv, qkv_dt="bf16", gate_dt="f32", seed=40 + T,
+                          state_std=0.05)
+    o, S = _gpu_prefill(x, x["state"], algo="chunked")
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(S), S_ref) < TOL
+    o2, S2 = _gpu_prefill(x, x["state"], algo="chunked")
+    assert torch.equal(o, o2) and torch.equal(S, S2)
+
+
 @pytest.mark.parametrize("T", [64, 150])
 def test_chunked_f32_inputs_and_f32_output(T):
     """The chunked algorithm on f32 q/k/v (bf16 MFMA operands, Q K^T from a
