@@ -76,6 +76,22 @@ def test_chunked_wide_slices(B, Hk, Hv, T):
     assert torch.equal(o, o2) and torch.equal(S, S2)
 
 
+def test_chunked_wide_slices_f32_io():
+    """The 64-column chain with f32 q/k/v in and f32 o out."""
+    banner("chunked wide slices, f32 in and out, B=3 Hk=4 Hv=24 T=100")
+    x = recurrence_inputs(3, 100, Hk=4, Hv=24, qkv_dt="f32", gate_dt="f32", seed=47,
+                          state_std=0.05)
+    si = dev(x["state"])
+    so = torch.empty_like(si)
+    o = gdn.gdn_prefill(dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["a"]), dev(x["b"]),
+                        dev(x["A_log"]), dev(x["dt_bias"]), si, so, algo="chunked")
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float32
+    o_ref, S_ref = _ref(x, to_f64(x["state"]))
+    assert max_rel_err(host_f64(o), o_ref) < TOL
+    assert max_rel_err(host_f64(so), S_ref) < TOL
+
+
 @pytest.mark.parametrize("T", [64, 150])
 def test_chunked_f32_inputs_and_f32_output(T):
     """The chunked algorithm on f32 q/k/v (bf16 MFMA operands, Q K^T from a
