@@ -84,6 +84,23 @@ def test_prefill_slots_ragged_small(qkv_dt):
         assert max_rel_err(host_f64(st[r]), S_ref[0]) < TOL, r
 
 
+def test_prefill_slots_wide_chain_ragged():
+    """Enough rows that the chain runs 64-column slices (16 rows x 24 value
+    heads x 4 narrow slices > 256), with empty, one-token and chunk-edge rows."""
+    lengths = [0, 1, 63, 64, 65, 130, 7, 0, 200, 2, 64, 129, 1, 31, 96, 150]
+    banner(f"prefill_slots wide chain lengths={lengths} Hk=4 Hv=24")
+    x = slots_inputs(lengths, Hk=4, Hv=24, qkv_dt="bf16", seed=62)
+    o, st = run_slots(x)
+    cu = x["cu_seqlens"]
+    for r, L in enumerate(lengths):
+        if L == 0:
+            assert torch.equal(st[r], dev(x["state"][r])), "an empty row changed its state"
+            continue
+        o_ref, S_ref = oracle_row(x, r)
+        assert max_rel_err(host_f64(o[cu[r]:cu[r + 1]]), o_ref[0]) < TOL, r
+        assert max_rel_err(host_f64(st[r]), S_ref[0]) < TOL, r
+
+
 def test_prefill_slots_server_batch_full_width():
     """The benchmarked ragged batch (16 rows of the model's layer, 16 q/k and
     48 value heads, U{1..1024} new tokens each): every row bitwise against its
