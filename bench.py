@@ -26,6 +26,7 @@ host cores as a CPU baseline.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -76,10 +77,16 @@ def prefill_bytes_per_launch(T=T_PREFILL, Hk=HK, Hv=HV, d=D):
 
 
 def _src_hash(names):
+    """Hash of the kernel sources with comments and blank lines removed, so a
+    comment-only edit keeps the counters taken on that code valid."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "gated_deltanet_mixer_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gated_deltanet_mixer_amd", "csrc", n)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code.strip():
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -18,7 +18,8 @@
 //    four 16x16 diagonal blocks by forward substitution in f32, the six
 //    off-diagonal blocks by three levels of 16x16x16 MFMA products; then W
 //    and Ut on MFMA.  Writes W, Ut^T, P = q_scale M o QK^T, G and (once per
-//    q/k head) K^T to the workspace, all bf16 except G.  With f32 q/k, Q K^T
+//    q/k head) K^T and Q to the workspace, all bf16 except G, each in the
+//    order the chain's lanes load it.  With f32 q/k, Q K^T
 //    is formed from a two-term bf16 split of both operands: q . k is small
 //    next to |q||k| (unit vectors in 128 dimensions), so it needs more than
 //    bf16 operand precision; no other product does.
