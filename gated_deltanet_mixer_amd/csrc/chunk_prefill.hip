@@ -182,10 +182,11 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
       }
     }
   }
-  // V block w.  With f32 input it is loaded once the K K^T / Q K^T tiles are
-  // done and the low halves of the split are dead: loaded at entry, its f32
-  // words in flight would push the kernel past the 168 registers that let
-  // three workgroups share a SIMD.
+  // V block w, loaded once the K K^T / Q K^T tiles are done (it is first
+  // used for Ut, after the inverse).  In flight from entry, its words would
+  // sit beside the K/Q operand blocks: with f32 input that pushes the kernel
+  // past the 168 registers that let three workgroups share a SIMD, and with
+  // bf16 it costs 17 registers (123 against 106) for no gain.
   auto load_v = [&]() {
     const int t = w * 16 + li;
 #pragma unroll
@@ -195,7 +196,6 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
       else vf[kk] = zero_frag();
     }
   };
-  if (!kSplit) load_v();
 
   // Gates for token `lane` (wave 0); padding tokens get g = 0, b = 0.
   if (w == 0) {
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     kkt(2, 2, 3, 3); kkt(2, 0, 3, 0); kkt(2, 1, 3, 2);
     qkt(3, 0, 3, 0); qkt(3, 1, 3, 2);
   }
-  if (kSplit) load_v();
+  load_v();
   lds_barrier();
 
   // T, diagonal blocks (wave 0): lane (block lg, column li), forward
