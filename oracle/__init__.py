@@ -13,7 +13,9 @@ the passage it follows:
   sigmoid(b), gated delta rule on a [128,128] state per value head, outputs
   RMS-normalised and gated by silu(z); "Norms" bullet -- scale 1+w, f32.
 * llm-arch-viz "Qwen/Qwen3.8-27B" module tree -- conv1d 10240x1x4 without bias,
-  RMSNormGated width 128, eps 1e-06.
+  RMSNormGated width 128, eps 1e-06; the projections in_proj_qkv 5120->10240,
+  in_proj_z 5120->6144, in_proj_a / in_proj_b 5120->48 and out_proj 6144->5120,
+  each the linear map x W^T.
 * The update rule written out: S_t = a_t S_{t-1}(I - b_t k_t k_t^T) + b_t v_t k_t^T,
   o_t = S_t q_t.
 
@@ -46,9 +48,10 @@ def _load():
         lib.gdn_oracle_recurrence.argtypes = [_D, _D, _D, _D, _D, _D, _D, _D,
                                               i32, i32, i32, i32, i32, i32, dbl]
         lib.gdn_oracle_gated_rmsnorm.argtypes = [_D, _D, _D, _D, i64, i32, i32, dbl]
+        lib.gdn_oracle_linear.argtypes = [_D, _D, _D, i64, i32, i32]
         lib.gdn_oracle_num_threads.restype = ctypes.c_int
         for f in ("gdn_oracle_gates", "gdn_oracle_conv_silu", "gdn_oracle_l2norm_heads",
-                  "gdn_oracle_recurrence", "gdn_oracle_gated_rmsnorm"):
+                  "gdn_oracle_recurrence", "gdn_oracle_gated_rmsnorm", "gdn_oracle_linear"):
             getattr(lib, f).restype = None
         _lib = lib
     return _lib
@@ -151,6 +154,21 @@ def gated_rmsnorm(x, z, w, eps=1e-6):
     assert z.shape == x.shape and w.shape == (D,)
     y = np.empty_like(x)
     _load().gdn_oracle_gated_rmsnorm(_p(x), _p(z), _p(w), _p(y), N, H, D, float(eps))
+    return y
+
+
+def linear(x, W):
+    """y = x W^T, the map of every projection around the mixer ("Qwen/Qwen3.8-27B"
+    architecture viewer, module tree: in_proj_qkv, in_proj_z, in_proj_a,
+    in_proj_b, out_proj).  x: [..., K]; W: [N, K]; returns [..., N]."""
+    x = _f64(x)
+    W = _f64(W)
+    N, K = W.shape
+    assert x.shape[-1] == K
+    M = x.size // K if K else 0
+    y = np.empty(x.shape[:-1] + (N,), dtype=np.float64)
+    if M and N:
+        _load().gdn_oracle_linear(_p(x), _p(W), _p(y), M, N, K)
     return y
 
 

@@ -23,6 +23,12 @@
  *   [viz]   "Qwen/Qwen3.8-27B" architecture viewer (llm-arch-viz), module
  *           tree: conv1d 10240x1x4 (41.0K parameters, hence no bias),
  *           Qwen3_5RMSNormGated of width 128; header "RMSNorm eps 1e-06".
+ *   [viz]   module tree, linear layers of the mixer: in_proj_qkv 5120->10240,
+ *           in_proj_z 5120->6144, in_proj_a and in_proj_b 5120->48,
+ *           out_proj 6144->5120 (a Linear maps x to x W^T, W stored
+ *           [out][in]).
+ *   [cuda]  "qwen38" code-generation page (docs.logicaffeine.com), extra
+ *           kernels: the two 48-wide gate projections keep f32 weights.
  *   Update rule as written out in the project statement:
  *           S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
  *           o_t = S_t q_t.
@@ -41,6 +47,9 @@
  *                              form.
  *   gdn_oracle_gated_rmsnorm   pinned: constant-vector closed form, z=0,
  *                              w=-1, scale invariance, logistic library.
+ *   gdn_oracle_linear          pinned: numpy matmul, identity and permutation
+ *                              weights, exact small-integer brute force,
+ *                              linearity.
  */
 #include <math.h>
 #include <stddef.h>
@@ -219,6 +228,25 @@ void gdn_oracle_gated_rmsnorm(const double* x, const double* z, const double* w,
       const double r = 1.0 / sqrt(ss / D + eps);
       for (int32_t d = 0; d < D; ++d)
         y[base + d] = x[base + d] * r * (1.0 + w[d]) * silu(z[base + d]);
+    }
+  }
+}
+
+/*
+ * Linear map of every mixer projection [viz: in_proj_qkv, in_proj_z,
+ * in_proj_a, in_proj_b, out_proj; cuda: gate projections with f32 weights]:
+ *   y[m][n] = sum_k x[m][k] W[n][k]
+ * x : [M, K]; W : [N, K] (the Linear layout, output-major); y : [M, N].
+ * The sum runs over k in order, in double precision.
+ */
+void gdn_oracle_linear(const double* x, const double* W, double* y, int64_t M, int32_t N,
+                       int32_t K) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int32_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int32_t k = 0; k < K; ++k) acc += x[m * K + k] * W[(int64_t)n * K + k];
+      y[m * N + n] = acc;
     }
   }
 }
