@@ -69,6 +69,12 @@ def lib():
         L.gdn_mixer_prefill.argtypes = [P, P, i32, P, P, P, P, i32, P, P, P, P, P, P, i32, i32,
                                         gdn_dims, f32, f32, f32, P, sz, P]
         L.gdn_mixer_prefill.restype = ctypes.c_int
+        L.gdn_gate_proj.argtypes = [P, i64, i32, P, P, P, P, i64, i32, i32, i32, P]
+        L.gdn_gate_proj.restype = ctypes.c_int
+        L.gdn_linear_workspace_bytes.argtypes = []
+        L.gdn_linear_workspace_bytes.restype = sz
+        L.gdn_linear.argtypes = [P, i64, P, i64, P, i64, i32, i32, i32, i32, P, sz, P]
+        L.gdn_linear.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -319,3 +325,63 @@ def gdn_decode_rows_multi(q, k, v, a, b, A_log, dt_bias, state, snapshots=None, 
                                        gdn_dims(Hk, Hv, dk, dv), q_scale, _stream(q)),
            "gdn_decode_rows_multi")
     return o
+
+
+def _row_ld(t, name):
+    """Row stride of a 2-D view whose rows are contiguous."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def gdn_gate_proj(x, W_a, W_b, a=None, b=None):
+    """a = x W_a^T, b = x W_b^T with f32 weights [H, K] (the mixer's in_proj_a
+    and in_proj_b); x [M, K] bf16.  Returns (a, b), each [M, H] f32."""
+    _need_cuda(x, W_a, W_b, a, b)
+    M, K = x.shape
+    H = W_a.shape[0]
+    if W_a.shape != (H, K) or W_b.shape != (H, K):
+        raise ValueError("W_a and W_b must be [H, K]")
+    if not (W_a.is_contiguous() and W_b.is_contiguous()):
+        raise ValueError("W_a and W_b must be contiguous")
+    if a is None:
+        a = torch.empty(M, H, dtype=torch.float32, device=x.device)
+    if b is None:
+        b = torch.empty(M, H, dtype=torch.float32, device=x.device)
+    if a.shape != (M, H) or b.shape != (M, H):
+        raise ValueError("a and b must be [M, H]")
+    ab_ld = _row_ld(a, "a")
+    if _row_ld(b, "b") != ab_ld:
+        raise ValueError("a and b must share a row stride")
+    _check(lib().gdn_gate_proj(_ptr(x), _row_ld(x, "x"), _dt(x), _ptr(W_a), _ptr(W_b), _ptr(a),
+                               _ptr(b), ab_ld, M, K, H, _stream(x)),
+           "gdn_gate_proj")
+    return a, b
+
+
+def gdn_linear_workspace_bytes():
+    return int(lib().gdn_linear_workspace_bytes())
+
+
+def gdn_linear(x, W, y=None, out_dtype=torch.bfloat16, workspace=None):
+    """y = x W^T for bf16 x [M, K] and W [N, K] (a Linear layer's weight),
+    f32 accumulation; y [M, N] in out_dtype (bf16 or f32)."""
+    _need_cuda(x, W, y, workspace)
+    M, K = x.shape
+    N = W.shape[0]
+    if W.shape != (N, K):
+        raise ValueError("W must be [N, K]")
+    if y is None:
+        y = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    if y.shape != (M, N):
+        raise ValueError("y must be [M, N]")
+    if workspace is None:
+        wsb = 0
+    else:
+        wsb = workspace.numel() * workspace.element_size()
+    _check(lib().gdn_linear(_ptr(x), _row_ld(x, "x"), _ptr(W), _row_ld(W, "W"), _ptr(y),
+                            _row_ld(y, "y"), _dt(y), M, N, K, _ptr(workspace), wsb, _stream(x)),
+           "gdn_linear")
+    return y

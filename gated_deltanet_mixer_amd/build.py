@@ -26,6 +26,10 @@ CFLAGS = [
 ]
 
 
+# hipBLASLt runs the plain bf16 linear layers (proj.hip).
+LDFLAGS = ["-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
@@ -46,7 +50,7 @@ def build(verbose: bool = False) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, *LDFLAGS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

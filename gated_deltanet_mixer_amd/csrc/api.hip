@@ -1,5 +1,6 @@
 // The C ABI (include/gdn.h): host-side validation, then one or two launches on
-// the caller's stream.  Nothing here allocates or synchronises.
+// the caller's stream.  Nothing here allocates or synchronises (gdn_linear's
+// first call on a device creates its hipBLASLt handle, in proj.hip).
 #include <hip/hip_runtime.h>
 
 #include "../../include/gdn.h"
@@ -315,6 +316,52 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
   if (e != hipSuccess) return GDN_ERR_LAUNCH;
   return launch_status(
       gdn::launch_gated_rmsnorm(y, z, y, dt, norm_w, (int64_t)B * T * Hv, norm_eps, s));
+}
+
+int gdn_gate_proj(const void* x, int64_t x_ld, int32_t x_dt, const float* W_a,
+                  const float* W_b, float* a, float* b, int64_t ab_ld, int32_t M, int32_t K,
+                  int32_t H, void* stream) {
+  if (M < 0 || K <= 0 || H <= 0) return GDN_ERR_SHAPE;
+  if (!dtype_ok(x_dt)) return GDN_ERR_DTYPE;
+  if (x_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (K % 32 != 0 || H % 16 != 0 || x_ld < K || ab_ld < H) return GDN_ERR_SHAPE;
+  if (M == 0) return GDN_OK;
+  if (!x || !W_a || !W_b || !a || !b) return GDN_ERR_NULL;
+  if (x_ld % 8 != 0 || !aligned(x, 16) || !aligned(W_a, 16) || !aligned(W_b, 16))
+    return GDN_ERR_ALIGN;
+  const size_t xbytes = ((size_t)(M - 1) * x_ld + K) * 2;
+  const size_t abytes = ((size_t)(M - 1) * ab_ld + H) * 4;
+  if (overlaps(a, abytes, x, xbytes) || overlaps(b, abytes, x, xbytes)) return GDN_ERR_SHAPE;
+  return launch_status(gdn::launch_gate_proj(static_cast<const uint16_t*>(x), x_ld, W_a, W_b, a,
+                                             b, ab_ld, M, K, H,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_linear_workspace_bytes(void) { return (size_t)32 << 20; }
+
+int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y, int64_t y_ld,
+               int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return GDN_ERR_SHAPE;
+  if (!dtype_ok(y_dt)) return GDN_ERR_DTYPE;
+  if (x_ld < K || w_ld < K || y_ld < N) return GDN_ERR_SHAPE;
+  if (M == 0) return GDN_OK;
+  if (!x || !W || !y) return GDN_ERR_NULL;
+  if (workspace_bytes > 0 && !workspace) return GDN_ERR_WORKSPACE;
+  if (x_ld % 8 || w_ld % 8 || y_ld % 8) return GDN_ERR_ALIGN;
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, 16)) return GDN_ERR_ALIGN;
+  if (workspace && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
+  const size_t xbytes = ((size_t)(M - 1) * x_ld + K) * 2;
+  const size_t wbytes = ((size_t)(N - 1) * w_ld + K) * 2;
+  const size_t ybytes = ((size_t)(M - 1) * y_ld + N) * dsize(y_dt);
+  if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, W, wbytes)) return GDN_ERR_SHAPE;
+  switch (gdn::launch_linear(static_cast<const uint16_t*>(x), x_ld,
+                             static_cast<const uint16_t*>(W), w_ld, y, y_ld, y_dt, M, N, K,
+                             workspace, workspace_bytes, static_cast<hipStream_t>(stream))) {
+    case gdn::LinearStatus::kOk: return GDN_OK;
+    case gdn::LinearStatus::kNoAlgorithm: return GDN_ERR_UNSUPPORTED;
+    default: return GDN_ERR_LAUNCH;
+  }
 }
 
 }  // extern "C"

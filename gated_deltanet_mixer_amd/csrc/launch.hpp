@@ -62,4 +62,18 @@ hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, in
                                   int Hk, int Hv, float q_scale, void* workspace,
                                   hipStream_t stream);
 
+// Gate projections with f32 weights: a[m][h] = sum_k x[m][k] Wa[h][k], b
+// likewise; x bf16 [M][x_ld], Wa and Wb f32 [H][K], a and b f32 [M][ab_ld].
+// K % 32 == 0, H % 16 == 0.
+hipError_t launch_gate_proj(const uint16_t* x, int64_t x_ld, const float* Wa, const float* Wb,
+                            float* a, float* b, int64_t ab_ld, int M, int K, int H,
+                            hipStream_t stream);
+
+// bf16 linear layer y[M][N] = x[M][K] W[N][K]^T on hipBLASLt, f32 accumulation,
+// y in bf16 (y_dt 1) or f32 (y_dt 0).
+enum class LinearStatus { kOk, kNoAlgorithm, kLaunchFailed };
+LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
+                           void* y, int64_t y_ld, int y_dt, int M, int N, int K, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 }  // namespace gdn

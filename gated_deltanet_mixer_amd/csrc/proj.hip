@@ -1,0 +1,263 @@
+// The projections on either side of the mixer ("Qwen/Qwen3.8-27B" architecture
+// viewer, module tree: in_proj_qkv 5120->10240, in_proj_z 5120->6144,
+// in_proj_a / in_proj_b 5120->48, out_proj 6144->5120; each maps x to x W^T
+// with W stored [out][in]).
+//
+// * The two 48-wide gate projections keep their weights in f32 (the "qwen38"
+//   code-generation page, extra kernels: rounding that [d, 48] matrix would
+//   put the gates at risk for a negligible saving).  gate_proj_kernel runs them
+//   on bf16 MFMA without rounding a weight: each f32 weight w is cut by
+//   truncation into three bf16 parts, hi + lo + lo2 == w exactly (each part
+//   holds 8 of w's 24 significant bits), and a bf16 activation times a bf16
+//   part is exact in f32, so three MFMAs per k-step give the f32-weight
+//   product with f32 accumulation.
+// * in_proj_qkv, in_proj_z and out_proj are plain bf16 GEMMs with f32
+//   accumulation; they go to hipBLASLt.  One handle per device is created on
+//   first use and kept until the process ends; the plan of each shape
+//   (descriptors and the heuristic's best algorithm that fits the workspace)
+//   is cached beside it.  The library links libhipblaslt.so.1 by soname: in a
+//   process that already holds a copy of that library (PyTorch ships one),
+//   that copy serves these calls.
+#include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "chunk_common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+using chunk::mfma16;
+
+// ---------------------------------------------------------------------------
+// Gate projections.  Workgroup = 16*MT tokens x 16 outputs of [a | b], NW
+// waves; wave w takes every token of the workgroup (MT 16-row MFMA tiles) over
+// the w-th of NW contiguous ranges of 32-wide k-steps, loading four k-steps
+// ahead.  The NW partial sums are added in a fixed order through LDS, so
+// results do not depend on timing.  Many tokens: MT = 4, NW = 4 (64 tokens per
+// workgroup); few tokens: MT = 1, NW = 8 (the best of MT 1/2/4 and NW 4/8/16
+// measured at 4096, 1024, 64 and 8 tokens).
+
+// Bits [31:16] of a and of b packed as two bf16 (a in the low half).
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return (b & 0xffff0000u) | (a >> 16);
+}
+
+// Eight f32 weights as three bf16 operands whose sum is exact.
+__device__ __forceinline__ void split3(const float4& w0, const float4& w1, bf16x8& hi, bf16x8& lo,
+                                       bf16x8& lo2) {
+  const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t u0[8], u1[8], u2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u0[i] = __float_as_uint(w[i]);
+    const float r1 = w[i] - __uint_as_float(u0[i] & 0xffff0000u);
+    u1[i] = __float_as_uint(r1);
+    const float r2 = r1 - __uint_as_float(u1[i] & 0xffff0000u);
+    u2[i] = __float_as_uint(r2);
+  }
+  uint32_t h[4], l[4], m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_hi16(u0[2 * i], u0[2 * i + 1]);
+    l[i] = pack_hi16(u1[2 * i], u1[2 * i + 1]);
+    m[i] = pack_hi16(u2[2 * i], u2[2 * i + 1]);
+  }
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+  lo2 = __builtin_bit_cast(bf16x8, u32x4{m[0], m[1], m[2], m[3]});
+}
+
+// One k-step's operands: eight weights of this lane's output and eight x
+// values of each of its MT token rows.
+template <int MT>
+struct GateStep {
+  float4 w0, w1;
+  bf16x8 xf[MT];
+};
+
+template <int MT, int NW>
+__global__ __launch_bounds__(64 * NW) void gate_proj_kernel(
+    const uint16_t* __restrict__ x, int64_t x_ld, const float* __restrict__ Wa,
+    const float* __restrict__ Wb, float* __restrict__ a, float* __restrict__ b, int64_t ab_ld,
+    int M, int K, int H) {
+  __shared__ f32x4 part[NW][MT][64];  // [wave][token tile][lane]
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
+  const int tok0 = blockIdx.x * 16 * MT;
+  const int o = blockIdx.y * 16 + li;  // this lane's output column of [a | b]
+  const float* wrow = (o < H ? Wa + (int64_t)o * K : Wb + (int64_t)(o - H) * K) + lg * 8;
+  // Rows past M read row M-1 (in bounds); their results are not stored.
+  const uint16_t* xr[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+    xr[i] = x + (int64_t)min(tok0 + 16 * i + li, M - 1) * x_ld + lg * 8;
+
+  // Wave w takes k-steps [sb, se) of the K/32, at most `per` of them (the
+  // range may be empty).  Four operand sets in rotation, named statically by
+  // unrolling four steps per trip: a set is reloaded for four steps later as
+  // soon as its step is multiplied, so no register is copied while its load
+  // is in flight.  Loads are unconditional (clamped to the last k-step), so
+  // the compiler's count of loads in flight stays exact; so is every
+  // multiply (a branch around one made the compiler drain all loads at the
+  // top of each trip).
+  const int nsteps = K >> 5, last = nsteps - 1;
+  const int per = (nsteps + NW - 1) / NW;
+  const int sb = min(w * per, nsteps), se = min(sb + per, nsteps);
+  auto load = [&](int st, GateStep<MT>& g) __attribute__((always_inline)) {
+    const int k = min(st, last) * 32;
+    g.w0 = *reinterpret_cast<const float4*>(wrow + k);
+    g.w1 = *reinterpret_cast<const float4*>(wrow + k + 4);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) g.xf[i] = *reinterpret_cast<const bf16x8*>(xr[i] + k);
+  };
+  f32x4 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  GateStep<MT> g[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load(sb + u, g[u]);
+  // The scheduling barriers keep each reload where it is written: left free,
+  // the scheduler sinks the loads next to their use and the prefetch is lost.
+  __builtin_amdgcn_sched_barrier(0);
+  for (int j = sb; j < se; j += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // A step past se multiplies zero weights (a select, not a branch).
+      const bool live = j + u < se;
+      const float4 z4 = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 hi, lo, lo2;
+      split3(live ? g[u].w0 : z4, live ? g[u].w1 : z4, hi, lo, lo2);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        acc[i] = mfma16(g[u].xf[i], hi, acc[i]);
+        acc[i] = mfma16(g[u].xf[i], lo, acc[i]);
+        acc[i] = mfma16(g[u].xf[i], lo2, acc[i]);
+      }
+      load(j + u + 4, g[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i) part[w][i][lane] = acc[i];
+  __syncthreads();
+  // Wave w < MT finishes token tile w: the NW k-ranges summed in order.
+  if (w < MT) {
+    f32x4 s = part[0][w][lane];
+#pragma unroll
+    for (int q = 1; q < NW; ++q) s += part[q][w][lane];
+    float* dst = o < H ? a + o : b + (o - H);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tok0 + 16 * w + 4 * lg + r;  // D[4 lg + r][li]
+      if (t < M) dst[(int64_t)t * ab_ld] = s[r];
+    }
+  }
+}
+
+hipError_t launch_gate_proj(const uint16_t* x, int64_t x_ld, const float* Wa, const float* Wb,
+                            float* a, float* b, int64_t ab_ld, int M, int K, int H,
+                            hipStream_t stream) {
+  const int ntiles = 2 * H / 16;
+  if (M >= 1024) {
+    const dim3 grid((M + 63) / 64, ntiles);
+    hipLaunchKernelGGL((gate_proj_kernel<4, 4>), grid, dim3(256), 0, stream, x, x_ld, Wa, Wb, a,
+                       b, ab_ld, M, K, H);
+  } else {
+    const dim3 grid((M + 15) / 16, ntiles);
+    hipLaunchKernelGGL((gate_proj_kernel<1, 8>), grid, dim3(512), 0, stream, x, x_ld, Wa, Wb, a,
+                       b, ab_ld, M, K, H);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 linear layers on hipBLASLt.  Row-major y[M][N] = x[M][K] W[N][K]^T is
+// the column-major product D (N x M) = op(A) B with A = W viewed as a K x N
+// column-major matrix (op = transpose) and B = x viewed as K x M.
+
+namespace {
+
+struct LtPlan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t A = nullptr, B = nullptr, D = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+  bool ok = false;
+};
+
+using PlanKey = std::tuple<int, int, int, int, int64_t, int64_t, int64_t, int, size_t>;
+
+std::mutex g_lt_mu;
+std::map<int, hipblasLtHandle_t> g_lt_handle;
+std::map<PlanKey, LtPlan> g_lt_plans;
+
+// Builds the plan for one shape; false if hipBLASLt has no algorithm for it.
+bool make_plan(hipblasLtHandle_t h, LtPlan& p, int M, int N, int K, int64_t x_ld, int64_t w_ld,
+               int64_t y_ld, int y_dt, size_t ws_bytes) {
+  const hipblasOperation_t opA = HIPBLAS_OP_T, opB = HIPBLAS_OP_N;
+  const hipDataType dty = y_dt == 1 ? HIP_R_16BF : HIP_R_32F;
+  if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS)
+    return false;
+  hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opA, sizeof(opA));
+  hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opB, sizeof(opB));
+  if (hipblasLtMatrixLayoutCreate(&p.A, HIP_R_16BF, K, N, w_ld) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.B, HIP_R_16BF, K, M, x_ld) != HIPBLAS_STATUS_SUCCESS ||
+      hipblasLtMatrixLayoutCreate(&p.D, dty, N, M, y_ld) != HIPBLAS_STATUS_SUCCESS)
+    return false;
+  hipblasLtMatmulPreference_t pref;
+  if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return false;
+  const uint64_t cap = ws_bytes;
+  hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap,
+                                        sizeof(cap));
+  // Several candidates, best first: some hipBLASLt builds rank first an
+  // algorithm that needs more workspace than the cap allows.
+  constexpr int kCand = 16;
+  hipblasLtMatmulHeuristicResult_t res[kCand];
+  int n = 0;
+  const hipblasStatus_t st =
+      hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.A, p.B, p.D, p.D, pref, kCand, res, &n);
+  hipblasLtMatmulPreferenceDestroy(pref);
+  if (st != HIPBLAS_STATUS_SUCCESS) return false;
+  for (int i = 0; i < n && i < kCand; ++i) {
+    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) {
+      p.algo = res[i].algo;
+      return true;
+    }
+  }
+  return false;
+}
+
+}  // namespace
+
+LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
+                           void* y, int64_t y_ld, int y_dt, int M, int N, int K, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LinearStatus::kLaunchFailed;
+  std::lock_guard<std::mutex> lock(g_lt_mu);
+  auto hit = g_lt_handle.find(dev);
+  if (hit == g_lt_handle.end()) {
+    hipblasLtHandle_t h = nullptr;
+    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return LinearStatus::kLaunchFailed;
+    hit = g_lt_handle.emplace(dev, h).first;
+  }
+  const PlanKey key{dev, M, N, K, x_ld, w_ld, y_ld, y_dt, workspace_bytes};
+  auto pit = g_lt_plans.find(key);
+  if (pit == g_lt_plans.end()) {
+    LtPlan p;
+    p.ok = make_plan(hit->second, p, M, N, K, x_ld, w_ld, y_ld, y_dt, workspace_bytes);
+    pit = g_lt_plans.emplace(key, p).first;
+  }
+  const LtPlan& p = pit->second;
+  if (!p.ok) return LinearStatus::kNoAlgorithm;
+  const float alpha = 1.0f, beta = 0.0f;
+  const hipblasStatus_t st =
+      hipblasLtMatmul(hit->second, p.desc, &alpha, W, p.A, x, p.B, &beta, y, p.D, y, p.D, &p.algo,
+                      workspace, workspace_bytes, stream);
+  return st == HIPBLAS_STATUS_SUCCESS ? LinearStatus::kOk : LinearStatus::kLaunchFailed;
+}
+
+}  // namespace gdn

@@ -18,7 +18,9 @@
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
- *    The library never allocates, frees, synchronises, logs or aborts.
+ *    The library never allocates, frees, synchronises, logs or aborts, with
+ *    one exception: gdn_linear's first call on a device creates the
+ *    hipBLASLt handle it keeps for that device (see there).
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream) and the call returns at once.  Device faults, if
  *    any, surface at the caller's next synchronisation.
@@ -281,6 +283,62 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
                       const float* state_in, float* state_out, void* y, int32_t B, int32_t T,
                       gdn_dims dims, float q_scale, float l2_eps, float norm_eps,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_gate_proj -- the two gate projections of the mixer, with f32 weights.
+ * ("Qwen/Qwen3.8-27B" architecture viewer, module tree: in_proj_a and
+ * in_proj_b, 5120 -> 48 each; the "qwen38" code-generation page, extra
+ * kernels: these two small projections keep f32 weights.)
+ *   a[m][h] = sum_k x[m][k] W_a[h][k],   b[m][h] = sum_k x[m][k] W_b[h][k]
+ *   x         [M, K] bf16 with row stride x_ld (elements); the hidden state.
+ *   W_a, W_b  [H, K] f32, contiguous (the Linear layout, output-major).
+ *   a, b      [M, H] f32 with row stride ab_ld; they feed the gates of
+ *             gdn_prefill / gdn_decode_rows (gate dtype GDN_F32) directly.
+ * The weights are used unrounded: each is split exactly into three bf16
+ * parts on the fly, and every product is exact in f32; sums are f32, in a
+ * fixed order (results do not vary from run to run).
+ * Constraints: x_dt == GDN_BF16 (GDN_ERR_UNSUPPORTED otherwise); K > 0 and
+ * K % 32 == 0; H > 0 and H % 16 == 0; x_ld >= K, x_ld % 8 == 0; ab_ld >= H;
+ * x, W_a, W_b 16-byte aligned; a and b must not overlap x.  M == 0 is a
+ * no-op.
+ */
+int gdn_gate_proj(const void* x, int64_t x_ld, int32_t x_dt, const float* W_a,
+                  const float* W_b, float* a, float* b, int64_t ab_ld, int32_t M, int32_t K,
+                  int32_t H, void* stream);
+
+/*
+ * Bytes of device workspace recommended for gdn_linear (32 MiB).  Smaller
+ * workspaces (including none) are accepted; they limit the algorithms
+ * hipBLASLt may choose.
+ */
+size_t gdn_linear_workspace_bytes(void);
+
+/*
+ * gdn_linear -- a bf16 linear layer, y = x W^T: the mixer's in_proj_qkv
+ * (5120 -> 10240), in_proj_z (5120 -> 6144) and out_proj (6144 -> 5120)
+ * ("Qwen/Qwen3.8-27B" architecture viewer, module tree).
+ *   x  [M, K] bf16, row stride x_ld (elements).
+ *   W  [N, K] bf16, row stride w_ld (the Linear layout, output-major).
+ *   y  [M, N] in y_dt (GDN_BF16 or GDN_F32), row stride y_ld; must not
+ *      overlap x or W.
+ *   y[m][n] = sum_k x[m][k] W[n][k], f32 accumulation, one rounding to y_dt.
+ * Runs on hipBLASLt (the heuristic's best algorithm for the shape that
+ * fits the workspace; whichever libhipblaslt.so.1 the process loaded first
+ * serves the call).  The
+ * first call on a device creates a hipBLASLt handle and keeps it, and the
+ * first call of each shape builds and keeps its plan; those first calls may
+ * allocate and synchronise, so make them before any graph capture.  Calls
+ * from several threads are serialised by a lock while they enqueue.
+ *   workspace  scratch for hipBLASLt, 256-byte aligned, workspace_bytes long
+ *              (gdn_linear_workspace_bytes() recommended), or NULL with 0.
+ * Constraints: M >= 0 (0 is a no-op), N > 0, K > 0; x_ld >= K, w_ld >= K,
+ * y_ld >= N, each a multiple of 8; x, W, y 16-byte aligned.
+ * GDN_ERR_UNSUPPORTED if hipBLASLt has no algorithm for the shape within
+ * the workspace; GDN_ERR_LAUNCH if it fails to enqueue.
+ */
+int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y, int64_t y_ld,
+               int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
+               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

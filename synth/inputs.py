@@ -19,9 +19,11 @@ import numpy as np
 
 __all__ = ["HK", "HV", "D", "CONV_CH", "CONV_W", "WORKLOADS", "bf16_round", "f32_round",
            "to_f64", "is_bf16", "recurrence_inputs", "decode_inputs", "mixer_inputs",
-           "slots_inputs", "decode_multi_inputs", "make_workload", "unit_heads"]
+           "slots_inputs", "decode_multi_inputs", "make_workload", "unit_heads",
+           "proj_inputs", "HIDDEN"]
 
 HK, HV, D = 16, 48, 128
+HIDDEN = 5120  # model width ("Qwen/Qwen3.8-27B" architecture viewer, header)
 CONV_CH = 2 * HK * D + HV * D  # 10240
 CONV_W = 4
 
@@ -183,6 +185,23 @@ def mixer_inputs(B, T, Hk=HK, Hv=HV, d=D, dt="bf16", seed=3, conv_w_std=0.5,
         "A_log": f32_round(A_log), "dt_bias": f32_round(dt_bias),
         "norm_w": f32_round(norm_w),
     }
+
+
+def proj_inputs(M, K=HIDDEN, outs=(("W_qkv", CONV_CH), ("W_z", HV * D)), gate_H=HV, seed=7,
+                x_name="x"):
+    """Inputs of the projections around the mixer: activations x [M, K] ~ N(0,1)
+    in bf16; bf16 weights [N, K] ~ N(0, 1/K) (unit-variance outputs), one per
+    (name, N) in ``outs``; f32 gate weights W_a, W_b [gate_H, K] ~ N(0, 1/K)
+    when gate_H > 0.  Drawn in f32 to bound host memory."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    res = {x_name: bf16_round(rng.standard_normal((M, K), dtype=np.float32))}
+    s = np.float32(1.0 / np.sqrt(K))
+    for name, N in outs:
+        res[name] = bf16_round(rng.standard_normal((N, K), dtype=np.float32) * s)
+    if gate_H:
+        res["W_a"] = rng.standard_normal((gate_H, K), dtype=np.float32) * s
+        res["W_b"] = rng.standard_normal((gate_H, K), dtype=np.float32) * s
+    return res
 
 
 # The five workloads, by name.  Sizes follow the model's layer; the seeds are

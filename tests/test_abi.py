@@ -29,7 +29,8 @@ def test_header_and_exports():
     assert {"gdn_conv_silu", "gdn_prefill", "gdn_decode_rows", "gdn_gated_rmsnorm",
             "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version",
             "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes", "gdn_prefill_slots",
-            "gdn_prefill_slots_workspace_bytes", "gdn_decode_rows_multi"} <= set(names)
+            "gdn_prefill_slots_workspace_bytes", "gdn_decode_rows_multi", "gdn_gate_proj",
+            "gdn_linear", "gdn_linear_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert gdn.gdn_abi_version() == 1
@@ -213,6 +214,51 @@ def test_prefill_slots_validation():
     assert slots(wsb=100) == WS
     assert slots(R=0) == OK
     assert slots(total=0, q=0, k=0, v=0, a=0, b=0, o=0) == OK   # no tokens: nothing to do
+
+
+def test_gate_proj_validation():
+    L = gdn.lib()
+
+    def f(x=P, xld=5120, xdt=1, wa=2 * P, wb=3 * P, a=4 * P, b=5 * P, ld=48, M=8, K=5120, H=48):
+        return L.gdn_gate_proj(_vp(x), xld, xdt, _vp(wa), _vp(wb), _vp(a), _vp(b), ld, M, K, H,
+                               None)
+    assert f(wa=0) == NULL
+    assert f(b=0) == NULL
+    assert f(xdt=5) == DTYPE
+    assert f(xdt=0) == UNSUP           # f32 activations are not implemented
+    assert f(K=5000) == SHAPE          # K % 32
+    assert f(H=40) == SHAPE            # H % 16
+    assert f(xld=4096) == SHAPE        # row stride below K
+    assert f(ld=32) == SHAPE           # output row stride below H
+    assert f(M=-1) == SHAPE
+    assert f(xld=5124) == ALIGN
+    assert f(wa=2 * P + 4) == ALIGN
+    assert f(a=P + 64) == SHAPE        # a overlaps x
+    assert f(M=0, x=0, wa=0, wb=0, a=0, b=0) == OK
+
+
+def test_linear_validation():
+    L = gdn.lib()
+    assert L.gdn_linear_workspace_bytes() == 32 << 20
+
+    def f(x=P, xld=5120, W=64 * P, wld=5120, y=4096 * P, yld=10240, ydt=1, M=8, N=10240,
+          K=5120, ws=None, wsb=0):
+        return L.gdn_linear(_vp(x), xld, _vp(W), wld, _vp(y), yld, ydt, M, N, K, _vp(ws), wsb,
+                            None)
+    assert f(x=0) == NULL
+    assert f(W=0) == NULL
+    assert f(ydt=2) == DTYPE
+    assert f(N=0) == SHAPE
+    assert f(K=0) == SHAPE
+    assert f(M=-3) == SHAPE
+    assert f(xld=100) == SHAPE         # below K
+    assert f(yld=10000) == SHAPE       # below N
+    assert f(xld=5124) == ALIGN
+    assert f(y=4096 * P + 8) == ALIGN
+    assert f(ws=P * 8192 + 64, wsb=1024) == ALIGN
+    assert f(ws=None, wsb=1024) == WS
+    assert f(y=P + 1024) == SHAPE      # y overlaps x
+    assert f(M=0, x=0, W=0, y=0) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,199 @@
+"""GPU parity of the projections around the mixer against the f64 oracle.
+
+The projections ("Qwen/Qwen3.8-27B" architecture viewer, module tree):
+in_proj_qkv 5120->10240, in_proj_z 5120->6144 and out_proj 6144->5120 as bf16
+linear layers (gdn_linear), in_proj_a / in_proj_b 5120->48 with f32 weights
+(gdn_gate_proj; the "qwen38" code-generation page keeps those weights in f32).
+
+Tolerances, as max|y - ref| / max|ref| over the tensor:
+* gdn_gate_proj: every product is exact (bf16 x times an exact three-part bf16
+  split of each f32 weight) and the sum is f32, so the error is f32 summation
+  error, ~1e-7 here; the bound is 2e-6.  A version that rounded the weights to
+  bf16 would sit near 1e-3, which the unrounded-weights test separates
+  explicitly.
+* gdn_linear, f32 output: f32 accumulation of exact bf16 products, bound 2e-5.
+* gdn_linear, bf16 output: one rounding to bf16 (2^-9 relative), bound 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_mixer_amd as gdn
+import oracle
+from synth.inputs import HIDDEN, HV, D, CONV_CH, bf16_round, proj_inputs, to_f64
+from tests.conftest import max_rel_err
+from tests.gpu_util import banner, dev, host_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL_GATE = 2e-6
+TOL_LIN_F32 = 2e-5
+TOL_LIN_BF16 = 5e-3
+
+
+def _gate_ref(x, Wa, Wb):
+    xf = to_f64(x)
+    return oracle.linear(xf, Wa.astype(np.float64)), oracle.linear(xf, Wb.astype(np.float64))
+
+
+@pytest.mark.parametrize("M", [1, 17, 64, 130, 1100])
+def test_gate_proj_parity(M):
+    banner(f"gate_proj M={M} K={HIDDEN} H={HV}")
+    p = proj_inputs(M, outs=(), seed=20 + M)
+    a, b = gdn.gdn_gate_proj(dev(p["x"]), dev(p["W_a"]), dev(p["W_b"]))
+    torch.cuda.synchronize()
+    ra, rb = _gate_ref(p["x"], p["W_a"], p["W_b"])
+    ea, eb = max_rel_err(host_f64(a), ra), max_rel_err(host_f64(b), rb)
+    print(f"gate_proj M={M}: a err {ea:.2e}, b err {eb:.2e}")
+    assert ea <= TOL_GATE and eb <= TOL_GATE
+
+
+def test_gate_proj_uses_weights_unrounded():
+    """Weights with all 24 significant bits set: the result must match the f64
+    product of the f32 weights far more closely than bf16-rounded weights can."""
+    banner("gate_proj unrounded weights")
+    M, K, H = 64, 1024, 16
+    rng = np.random.default_rng(31)
+    x = bf16_round(rng.integers(-3, 4, size=(M, K)).astype(np.float64))
+    mant = rng.integers(1 << 23, 1 << 24, size=(2, H, K)).astype(np.float64)
+    sign = rng.choice([-1.0, 1.0], size=(2, H, K))
+    W = (sign * mant * 2.0 ** -30).astype(np.float32)  # exact in f32, not in bf16
+    a, b = gdn.gdn_gate_proj(dev(x), dev(W[0]), dev(W[1]))
+    torch.cuda.synchronize()
+    ra, rb = _gate_ref(x, W[0], W[1])
+    rounded = oracle.linear(to_f64(x), to_f64(bf16_round(W[0])))
+    e_round = max_rel_err(rounded, ra)
+    ea, eb = max_rel_err(host_f64(a), ra), max_rel_err(host_f64(b), rb)
+    print(f"gate_proj unrounded: a err {ea:.2e}, b err {eb:.2e}; bf16 weights would give {e_round:.2e}")
+    assert e_round > 1e-4
+    assert ea <= TOL_GATE and eb <= TOL_GATE
+    assert ea < e_round / 100
+
+
+@pytest.mark.parametrize("M,K", [(77, 128), (1030, 160)])
+def test_gate_proj_strided_views_small_K_and_determinism(M, K):
+    """x a column slice of a wider buffer, a and b columns of one [M, 2H]
+    buffer (row stride 2H), H = 16, K of 4 or 5 k-steps: most waves get an
+    empty k-range, the others uneven ones."""
+    banner(f"gate_proj strided M={M} K={K} H=16")
+    H = 16
+    p = proj_inputs(M, K=K + 64, outs=(), gate_H=0, seed=32)
+    rng = np.random.default_rng(33)
+    Wa = (rng.standard_normal((H, K)) / np.sqrt(K)).astype(np.float32)
+    Wb = (rng.standard_normal((H, K)) / np.sqrt(K)).astype(np.float32)
+    xw = dev(p["x"])
+    x = xw[:, 32:32 + K]
+    ab = torch.full((M, 2 * H), float("nan"), dtype=torch.float32, device="cuda")
+    gdn.gdn_gate_proj(x, dev(Wa), dev(Wb), a=ab[:, :H], b=ab[:, H:])
+    first = ab.clone()
+    gdn.gdn_gate_proj(x, dev(Wa), dev(Wb), a=ab[:, :H], b=ab[:, H:])
+    torch.cuda.synchronize()
+    assert torch.equal(first, ab)
+    xs = to_f64(p["x"])[:, 32:32 + K]
+    ra = oracle.linear(xs, Wa.astype(np.float64))
+    rb = oracle.linear(xs, Wb.astype(np.float64))
+    got = host_f64(ab)
+    assert max_rel_err(got[:, :H], ra) <= TOL_GATE
+    assert max_rel_err(got[:, H:], rb) <= TOL_GATE
+
+
+def test_gate_proj_feeds_decode_gates():
+    """a and b from gdn_gate_proj drive gdn_decode_rows (f32 gates) exactly as
+    the same values copied from the host do."""
+    banner("gate_proj -> decode_rows")
+    from synth.inputs import decode_inputs
+    R = 8
+    p = proj_inputs(R, outs=(), seed=34)
+    a, b = gdn.gdn_gate_proj(dev(p["x"]), dev(p["W_a"]), dev(p["W_b"]))
+    d = decode_inputs(R, qkv_dt="bf16", gate_dt="f32", seed=35)
+    outs = []
+    for ga, gb in ((a, b), (a.cpu().to("cuda"), b.cpu().to("cuda"))):
+        st = dev(d["state"]).clone()
+        o = gdn.gdn_decode_rows(dev(d["q"]), dev(d["k"]), dev(d["v"]), ga, gb, dev(d["A_log"]),
+                                dev(d["dt_bias"]), st)
+        outs.append((o.clone(), st))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("M,N,K,out", [(1, 48, 128, torch.float32), (33, 96, 256, torch.float32),
+                                       (64, 512, 5120, torch.bfloat16),
+                                       (130, 640, 6144, torch.float32),
+                                       (257, 1024, 5120, torch.bfloat16)])
+def test_linear_parity(M, N, K, out):
+    banner(f"linear M={M} N={N} K={K} out={out}")
+    p = proj_inputs(M, K=K, outs=(("W", N),), gate_H=0, seed=40 + M)
+    ws = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    y = gdn.gdn_linear(dev(p["x"]), dev(p["W"]), out_dtype=out, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.linear(to_f64(p["x"]), to_f64(p["W"]))
+    e = max_rel_err(host_f64(y), ref)
+    print(f"linear {M}x{N}x{K} {out}: err {e:.2e}")
+    assert e <= (TOL_LIN_F32 if out == torch.float32 else TOL_LIN_BF16)
+
+
+def test_linear_without_workspace_and_strided_output():
+    """qkv and z written as column ranges of one [M, 16384] buffer, x a column
+    slice of a wider buffer; no workspace."""
+    banner("linear strided, no workspace")
+    M, K = 96, 512
+    p = proj_inputs(M, K=K + 128, outs=(("W1", 256), ("W2", 128)), gate_H=0, seed=50)
+    W1 = p["W1"][:, :K].copy()
+    W2 = p["W2"][:, :K].copy()
+    xw = dev(p["x"])
+    x = xw[:, 64:64 + K]
+    yb = torch.full((M, 384), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_linear(x, dev(W1), y=yb[:, :256])
+    gdn.gdn_linear(x, dev(W2), y=yb[:, 256:])
+    torch.cuda.synchronize()
+    xs = to_f64(p["x"])[:, 64:64 + K]
+    got = host_f64(yb)
+    assert max_rel_err(got[:, :256], oracle.linear(xs, to_f64(W1))) <= TOL_LIN_BF16
+    assert max_rel_err(got[:, 256:], oracle.linear(xs, to_f64(W2))) <= TOL_LIN_BF16
+
+
+def _sampled_rows(M, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(M, size=n, replace=False))
+
+
+def test_in_proj_full_size_sampled_rows():
+    """in_proj_qkv and in_proj_z at B=1 T=4096 (M=4096, K=5120, N=10240 and
+    6144) into one [4096, 16384] buffer, plus the gate projections; 48 rows
+    checked against the oracle, every column."""
+    banner("in_proj full size M=4096")
+    M = 4096
+    p = proj_inputs(M, seed=60)
+    x = dev(p["x"])
+    ws = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    y = torch.empty(M, CONV_CH + HV * D, dtype=torch.bfloat16, device="cuda")
+    gdn.gdn_linear(x, dev(p["W_qkv"]), y=y[:, :CONV_CH], workspace=ws)
+    gdn.gdn_linear(x, dev(p["W_z"]), y=y[:, CONV_CH:], workspace=ws)
+    a, b = gdn.gdn_gate_proj(x, dev(p["W_a"]), dev(p["W_b"]))
+    torch.cuda.synchronize()
+    rows = _sampled_rows(M, 48, 61)
+    xs = to_f64(p["x"][rows])
+    got = host_f64(y[torch.from_numpy(rows).cuda()])
+    e1 = max_rel_err(got[:, :CONV_CH], oracle.linear(xs, to_f64(p["W_qkv"])))
+    e2 = max_rel_err(got[:, CONV_CH:], oracle.linear(xs, to_f64(p["W_z"])))
+    ra, rb = _gate_ref(p["x"][rows], p["W_a"], p["W_b"])
+    idx = torch.from_numpy(rows).cuda()
+    ea, eb = max_rel_err(host_f64(a[idx]), ra), max_rel_err(host_f64(b[idx]), rb)
+    print(f"in_proj full: qkv {e1:.2e}, z {e2:.2e}, a {ea:.2e}, b {eb:.2e}")
+    assert e1 <= TOL_LIN_BF16 and e2 <= TOL_LIN_BF16
+    assert ea <= TOL_GATE and eb <= TOL_GATE
+
+
+def test_out_proj_full_size_sampled_rows():
+    """out_proj at M=4096, K=6144, N=5120; 48 rows checked, every column."""
+    banner("out_proj full size M=4096")
+    M = 4096
+    p = proj_inputs(M, K=HV * D, outs=(("W_out", HIDDEN),), gate_H=0, seed=62)
+    ws = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    y = gdn.gdn_linear(dev(p["x"]), dev(p["W_out"]), workspace=ws)
+    torch.cuda.synchronize()
+    rows = _sampled_rows(M, 48, 63)
+    got = host_f64(y[torch.from_numpy(rows).cuda()])
+    e = max_rel_err(got, oracle.linear(to_f64(p["x"][rows]), to_f64(p["W_out"])))
+    print(f"out_proj full: {e:.2e}")
+    assert e <= TOL_LIN_BF16
