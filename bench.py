@@ -11,7 +11,11 @@ like the model's layer (16 q/k heads, 48 value heads, width 128):
   4. gdn_prefill_slots on a server's ragged batch: 16 fixed rows with
      U{1..1024} new tokens each, bf16, states carried in place;
   5. gdn_decode_rows_multi verifying a 4-token draft on 64 fixed rows, with
-     the state after every token written out as a snapshot.
+     the state after every token written out as a snapshot;
+  6. the projections around the mixer at 4096 tokens: in_proj_qkv and
+     in_proj_z (gdn_linear, bf16, into one [4096, 16384] buffer), the two
+     gate projections with f32 weights (gdn_gate_proj) and out_proj
+     (gdn_linear, 6144 -> 5120).
 Each part is timed with HIP events on the stream it runs on.  The timed
 region runs each part's K iterations back to back, part after part (so a part
 follows its own previous call, not another part's dirty cache lines), and the
@@ -41,6 +45,7 @@ ROT = 3                       # buffer sets rotated between steps
 
 HK, HV, D, T_PREFILL, R_DECODE = 16, 48, 128, 4096, 64
 C_CONV = 2 * HK * D + HV * D
+HIDDEN = 5120
 
 
 def decode_bytes_per_launch(R=R_DECODE, Hk=HK, Hv=HV, d=D, io_bytes=2, gate_bytes=2):
@@ -151,6 +156,7 @@ def main():
 
     import gated_deltanet_mixer_amd as gdn
     from synth import decode_inputs, make_workload, mixer_inputs, recurrence_inputs
+    from synth.inputs import proj_inputs
     from synth.torch_io import dev
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -201,6 +207,23 @@ def main():
         multi[-1]["snap"] = torch.empty((R_DECODE, 4, HV, D, D), dtype=torch.float32,
                                         device="cuda")
         multi[-1]["o"] = torch.empty((R_DECODE, 4, HV, D), dtype=torch.bfloat16, device="cuda")
+    pin = proj_inputs(T_PREFILL, seed=2007)
+    pout = proj_inputs(T_PREFILL, K=HV * D, outs=(("W_out", HIDDEN),), gate_H=0, seed=2008,
+                       x_name="y")
+    gws_bytes = max(gdn.gdn_gate_proj_workspace_bytes(T_PREFILL, HIDDEN, HV), 256)
+    proj = []
+    for _ in range(ROT):
+        pj = {n: dev(pin[n]) for n in ("x", "W_qkv", "W_z", "W_a", "W_b")}
+        pj.update({"y": dev(pout["y"]), "W_out": dev(pout["W_out"])})
+        pj["yin"] = torch.empty((T_PREFILL, C_CONV + HV * D), dtype=torch.bfloat16, device="cuda")
+        pj["a"] = torch.empty((T_PREFILL, HV), dtype=torch.float32, device="cuda")
+        pj["b"] = torch.empty((T_PREFILL, HV), dtype=torch.float32, device="cuda")
+        pj["out"] = torch.empty((T_PREFILL, HIDDEN), dtype=torch.bfloat16, device="cuda")
+        pj["lws"] = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8,
+                                device="cuda")
+        pj["gws"] = torch.empty(gws_bytes, dtype=torch.uint8, device="cuda")
+        proj.append(pj)
+    del pin, pout
     ws_bytes = gdn.gdn_prefill_workspace_bytes(1, T_PREFILL, HK, HV)
     ws = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(ROT)]
 
@@ -236,13 +259,33 @@ def main():
         gdn.gdn_decode_rows_multi(M["q"], M["k"], M["v"], M["a"], M["b"], M["A_log"],
                                   M["dt_bias"], M["state"], M["snap"], M["lengths"], o=M["o"])
 
-    parts_fn = [layer_part, prefill_part, decode_part, slots_part, multi_part]
+    # Part 6 records an event after each of its four calls as well.
+    proj_ev = {}
+
+    def proj_part(i):
+        Pj = proj[i % ROT]
+        ev = proj_ev.get(i)
+        gdn.gdn_linear(Pj["x"], Pj["W_qkv"], y=Pj["yin"][:, :C_CONV], workspace=Pj["lws"])
+        if ev:
+            ev[0].record()
+        gdn.gdn_linear(Pj["x"], Pj["W_z"], y=Pj["yin"][:, C_CONV:], workspace=Pj["lws"])
+        if ev:
+            ev[1].record()
+        gdn.gdn_gate_proj(Pj["x"], Pj["W_a"], Pj["W_b"], a=Pj["a"], b=Pj["b"],
+                          workspace=Pj["gws"])
+        if ev:
+            ev[2].record()
+        gdn.gdn_linear(Pj["y"], Pj["W_out"], y=Pj["out"], workspace=Pj["lws"])
+
+    parts_fn = [layer_part, prefill_part, decode_part, slots_part, multi_part, proj_part]
     for fn in parts_fn:
         for i in range(args.warmup):
             fn(i)
     torch.cuda.synchronize()
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(args.steps)] for _ in parts_fn]
+    for i in range(args.steps):
+        proj_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for j, fn in enumerate(parts_fn):
@@ -256,7 +299,17 @@ def main():
     parts = np.array([[evs[j][i][0].elapsed_time(evs[j][i][1]) for j in range(len(parts_fn))]
                       for i in range(args.steps)])  # ms
     mean = parts.mean(axis=0)
-    t_layer, t_pre, t_dec, t_slots, t_multi = mean
+    t_layer, t_pre, t_dec, t_slots, t_multi, t_proj = mean
+    # Per call of part 6: in_proj_qkv, in_proj_z, gate projections, out_proj.
+    pc = np.array([[evs[5][i][0].elapsed_time(proj_ev[args.warmup + i][0]),
+                    proj_ev[args.warmup + i][0].elapsed_time(proj_ev[args.warmup + i][1]),
+                    proj_ev[args.warmup + i][1].elapsed_time(proj_ev[args.warmup + i][2]),
+                    proj_ev[args.warmup + i][2].elapsed_time(evs[5][i][1])]
+                   for i in range(args.steps)]).mean(axis=0)  # ms
+    t_qkv, t_z, t_gate, t_out = pc
+    gemm_flops = 2.0 * T_PREFILL * HIDDEN * (C_CONV + HV * D) + 2.0 * T_PREFILL * HV * D * HIDDEN
+    gemm_tflops = gemm_flops / ((t_qkv + t_z + t_out) * 1e-3) / 1e12
+    gate_bytes = T_PREFILL * HIDDEN * 2 + 2 * HV * HIDDEN * 4 + 2 * T_PREFILL * HV * 4
     multi_bytes = (2 + 4) * R_DECODE * HV * D * D * 4  # state in + out, 4 snapshots
     ms_per_step = wall * 1e3 / args.steps
 
@@ -314,7 +367,8 @@ def main():
                    "qk_heads": HK, "v_heads": HV, "head_dim": D,
                    "step": "layer prefill (gdn_mixer_prefill: conv+silu+L2 -> chunked prefill "
                            "-> gated RMSNorm) at B=1 T=4096, prefill workload at B=1 T=4096, "
-                           "decode_rows at 64 rows"},
+                           "decode_rows at 64 rows, prefill_slots (16 rows), decode_rows_multi "
+                           "(64 rows x 4), projections at 4096 tokens"},
         "decode_rows": {"value": round(dec_gbps, 1), "unit": "GB/s (state bytes read+written)",
                         "workload": "decode_rows_r64", "avg_launch_us": round(t_dec * 1e3, 2),
                         "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4)},
@@ -334,6 +388,21 @@ def main():
                                           "snapshot after every token)",
                               "call_us": round(t_multi * 1e3, 2),
                               "state_gbps": round(multi_bytes / (t_multi * 1e-3) / 1e9, 1)},
+        "projections": {
+            "workload": "in_proj_qkv 5120->10240 and in_proj_z 5120->6144 (bf16, hipBLASLt), "
+                        "in_proj_a/b 5120->48 (f32 weights, gdn_gate_proj), out_proj "
+                        "6144->5120 (bf16, hipBLASLt) at 4096 tokens",
+            "call_us": round(t_proj * 1e3, 2),
+            "in_proj_qkv_us": round(t_qkv * 1e3, 2), "in_proj_z_us": round(t_z * 1e3, 2),
+            "gate_proj_us": round(t_gate * 1e3, 2), "out_proj_us": round(t_out * 1e3, 2),
+            "gemm_tflops": round(gemm_tflops, 1),
+            "gemm_frac_of_bf16_peak": round(gemm_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "gate_proj_gbps_algorithmic": round(gate_bytes / (t_gate * 1e-3) / 1e9, 1)},
+        "full_layer_prefill": {
+            "value": round(T_PREFILL / ((t_layer + t_proj) * 1e-3), 1), "unit": "tokens/s",
+            "workload": "projections (part 6) + gdn_mixer_prefill (part 1) at B=1 T=4096, "
+                        "the two parts' times added",
+            "us": round((t_layer + t_proj) * 1e3, 2)},
         "prefill": {"avg_launch_us": round(t_pre * 1e3, 2),
                     "mfma_tflops": round(pre_flops / (t_pre * 1e-3) / 1e12, 2),
                     "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9,

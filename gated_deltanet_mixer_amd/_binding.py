@@ -69,7 +69,9 @@ def lib():
         L.gdn_mixer_prefill.argtypes = [P, P, i32, P, P, P, P, i32, P, P, P, P, P, P, i32, i32,
                                         gdn_dims, f32, f32, f32, P, sz, P]
         L.gdn_mixer_prefill.restype = ctypes.c_int
-        L.gdn_gate_proj.argtypes = [P, i64, i32, P, P, P, P, i64, i32, i32, i32, P]
+        L.gdn_gate_proj_workspace_bytes.argtypes = [i32, i32, i32]
+        L.gdn_gate_proj_workspace_bytes.restype = sz
+        L.gdn_gate_proj.argtypes = [P, i64, i32, P, P, P, P, i64, i32, i32, i32, P, sz, P]
         L.gdn_gate_proj.restype = ctypes.c_int
         L.gdn_linear_workspace_bytes.argtypes = []
         L.gdn_linear_workspace_bytes.restype = sz
@@ -336,10 +338,15 @@ def _row_ld(t, name):
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
-def gdn_gate_proj(x, W_a, W_b, a=None, b=None):
+def gdn_gate_proj_workspace_bytes(M, K, H):
+    return int(lib().gdn_gate_proj_workspace_bytes(M, K, H))
+
+
+def gdn_gate_proj(x, W_a, W_b, a=None, b=None, workspace=None):
     """a = x W_a^T, b = x W_b^T with f32 weights [H, K] (the mixer's in_proj_a
-    and in_proj_b); x [M, K] bf16.  Returns (a, b), each [M, H] f32."""
-    _need_cuda(x, W_a, W_b, a, b)
+    and in_proj_b); x [M, K] bf16.  Returns (a, b), each [M, H] f32.  The
+    workspace (a uint8 tensor) is allocated here when not given."""
+    _need_cuda(x, W_a, W_b, a, b, workspace)
     M, K = x.shape
     H = W_a.shape[0]
     if W_a.shape != (H, K) or W_b.shape != (H, K):
@@ -355,8 +362,12 @@ def gdn_gate_proj(x, W_a, W_b, a=None, b=None):
     ab_ld = _row_ld(a, "a")
     if _row_ld(b, "b") != ab_ld:
         raise ValueError("a and b must share a row stride")
+    need = gdn_gate_proj_workspace_bytes(M, K, H) if M else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().gdn_gate_proj(_ptr(x), _row_ld(x, "x"), _dt(x), _ptr(W_a), _ptr(W_b), _ptr(a),
-                               _ptr(b), ab_ld, M, K, H, _stream(x)),
+                               _ptr(b), ab_ld, M, K, H, _ptr(workspace), wsb, _stream(x)),
            "gdn_gate_proj")
     return a, b
 

@@ -318,22 +318,33 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
       gdn::launch_gated_rmsnorm(y, z, y, dt, norm_w, (int64_t)B * T * Hv, norm_eps, s));
 }
 
+size_t gdn_gate_proj_workspace_bytes(int32_t M, int32_t K, int32_t H) {
+  if (M <= 0 || K <= 0 || K % 32 != 0 || H <= 0 || H % 16 != 0 || H > 64) return 0;
+  return round256(gdn::gate_proj_workspace_bytes(M, K, H));
+}
+
 int gdn_gate_proj(const void* x, int64_t x_ld, int32_t x_dt, const float* W_a,
                   const float* W_b, float* a, float* b, int64_t ab_ld, int32_t M, int32_t K,
-                  int32_t H, void* stream) {
+                  int32_t H, void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || K <= 0 || H <= 0) return GDN_ERR_SHAPE;
   if (!dtype_ok(x_dt)) return GDN_ERR_DTYPE;
-  if (x_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (x_dt != GDN_BF16 || H > 64) return GDN_ERR_UNSUPPORTED;
   if (K % 32 != 0 || H % 16 != 0 || x_ld < K || ab_ld < H) return GDN_ERR_SHAPE;
   if (M == 0) return GDN_OK;
   if (!x || !W_a || !W_b || !a || !b) return GDN_ERR_NULL;
+  if ((int64_t)M * (2 * H / 4) / 256 + 1 > INT32_MAX) return GDN_ERR_SHAPE;
   if (x_ld % 8 != 0 || !aligned(x, 16) || !aligned(W_a, 16) || !aligned(W_b, 16))
     return GDN_ERR_ALIGN;
+  const size_t need = gdn::gate_proj_workspace_bytes(M, K, H);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return GDN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
   const size_t xbytes = ((size_t)(M - 1) * x_ld + K) * 2;
   const size_t abytes = ((size_t)(M - 1) * ab_ld + H) * 4;
   if (overlaps(a, abytes, x, xbytes) || overlaps(b, abytes, x, xbytes)) return GDN_ERR_SHAPE;
+  if (need > 0 && (overlaps(a, abytes, workspace, need) || overlaps(b, abytes, workspace, need)))
+    return GDN_ERR_SHAPE;
   return launch_status(gdn::launch_gate_proj(static_cast<const uint16_t*>(x), x_ld, W_a, W_b, a,
-                                             b, ab_ld, M, K, H,
+                                             b, ab_ld, M, K, H, workspace,
                                              static_cast<hipStream_t>(stream)));
 }
 

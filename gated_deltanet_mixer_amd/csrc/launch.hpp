@@ -64,9 +64,11 @@ hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, in
 
 // Gate projections with f32 weights: a[m][h] = sum_k x[m][k] Wa[h][k], b
 // likewise; x bf16 [M][x_ld], Wa and Wb f32 [H][K], a and b f32 [M][ab_ld].
-// K % 32 == 0, H % 16 == 0.
+// K % 32 == 0, H % 16 == 0, H <= 64.  The workspace (256-byte aligned) holds
+// the partial sums over K ranges; gate_proj_workspace_bytes gives its size.
+size_t gate_proj_workspace_bytes(int M, int K, int H);
 hipError_t launch_gate_proj(const uint16_t* x, int64_t x_ld, const float* Wa, const float* Wb,
-                            float* a, float* b, int64_t ab_ld, int M, int K, int H,
+                            float* a, float* b, int64_t ab_ld, int M, int K, int H, void* workspace,
                             hipStream_t stream);
 
 // bf16 linear layer y[M][N] = x[M][K] W[N][K]^T on hipBLASLt, f32 accumulation,

@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -33,13 +34,14 @@ namespace gdn {
 using chunk::mfma16;
 
 // ---------------------------------------------------------------------------
-// Gate projections.  Workgroup = 16*MT tokens x 16 outputs of [a | b], NW
-// waves; wave w takes every token of the workgroup (MT 16-row MFMA tiles) over
-// the w-th of NW contiguous ranges of 32-wide k-steps, loading four k-steps
-// ahead.  The NW partial sums are added in a fixed order through LDS, so
-// results do not depend on timing.  Many tokens: MT = 4, NW = 4 (64 tokens per
-// workgroup); few tokens: MT = 1, NW = 8 (the best of MT 1/2/4 and NW 4/8/16
-// measured at 4096, 1024, 64 and 8 tokens).
+// Gate projections, split over K.  Pass 1: workgroup = 16*MT tokens x all 2H
+// outputs x one of KS contiguous ranges of 32-wide k-steps; wave w owns output
+// tile w (16 outputs of [a | b]) and multiplies every token of the workgroup
+// (MT 16-row MFMA tiles), so each x value is fetched from memory once per
+// workgroup (the waves share it in L1) and each weight once per token tile.
+// The partial sums go to the workspace, [KS][M][2H] f32; pass 2 adds the KS
+// partials of each output in order 0..KS-1 (results do not depend on timing).
+// With KS == 1, pass 1 writes a and b directly.
 
 // Bits [31:16] of a and of b packed as two bf16 (a in the low half).
 __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
@@ -80,15 +82,26 @@ struct GateStep {
   bf16x8 xf[MT];
 };
 
-template <int MT, int NW>
-__global__ __launch_bounds__(64 * NW) void gate_proj_kernel(
+constexpr int kGateMaxTiles = 8;  // 2H / 16 <= 8 output tiles (H <= 64)
+
+// Number of K ranges for M tokens: about one workgroup per CU (256), at least
+// four k-steps per range.
+int gate_splits(int M, int K) {
+  const int tok = M >= 1024 ? 64 : 16;
+  const int mtiles = (M + tok - 1) / tok;
+  const int nsteps = K / 32;
+  const int want = (256 + mtiles - 1) / mtiles;
+  return std::max(1, std::min(want, nsteps / 4));
+}
+
+template <int MT>
+__global__ __launch_bounds__(64 * kGateMaxTiles) void gate_part_kernel(
     const uint16_t* __restrict__ x, int64_t x_ld, const float* __restrict__ Wa,
-    const float* __restrict__ Wb, float* __restrict__ a, float* __restrict__ b, int64_t ab_ld,
-    int M, int K, int H) {
-  __shared__ f32x4 part[NW][MT][64];  // [wave][token tile][lane]
+    const float* __restrict__ Wb, float* __restrict__ part, float* __restrict__ a,
+    float* __restrict__ b, int64_t ab_ld, int M, int K, int H) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane & 15, lg = lane >> 4;
   const int tok0 = blockIdx.x * 16 * MT;
-  const int o = blockIdx.y * 16 + li;  // this lane's output column of [a | b]
+  const int o = w * 16 + li;  // this lane's output column of [a | b]
   const float* wrow = (o < H ? Wa + (int64_t)o * K : Wb + (int64_t)(o - H) * K) + lg * 8;
   // Rows past M read row M-1 (in bounds); their results are not stored.
   const uint16_t* xr[MT];
@@ -96,17 +109,16 @@ __global__ __launch_bounds__(64 * NW) void gate_proj_kernel(
   for (int i = 0; i < MT; ++i)
     xr[i] = x + (int64_t)min(tok0 + 16 * i + li, M - 1) * x_ld + lg * 8;
 
-  // Wave w takes k-steps [sb, se) of the K/32, at most `per` of them (the
-  // range may be empty).  Four operand sets in rotation, named statically by
-  // unrolling four steps per trip: a set is reloaded for four steps later as
-  // soon as its step is multiplied, so no register is copied while its load
-  // is in flight.  Loads are unconditional (clamped to the last k-step), so
-  // the compiler's count of loads in flight stays exact; so is every
-  // multiply (a branch around one made the compiler drain all loads at the
-  // top of each trip).
-  const int nsteps = K >> 5, last = nsteps - 1;
-  const int per = (nsteps + NW - 1) / NW;
-  const int sb = min(w * per, nsteps), se = min(sb + per, nsteps);
+  // This workgroup's k-steps [sb, se) of the K/32.  Four operand sets in
+  // rotation, named statically by unrolling four steps per trip: a set is
+  // reloaded for four steps later as soon as its step is multiplied, so no
+  // register is copied while its load is in flight.  Loads are unconditional
+  // (clamped to the last k-step), so the compiler's count of loads in flight
+  // stays exact; so is every multiply (a branch around one made the compiler
+  // drain all loads at the top of each trip).
+  const int nsteps = K >> 5, ks = blockIdx.y, KS = gridDim.y;
+  const int sb = (int)((int64_t)ks * nsteps / KS), se = (int)((int64_t)(ks + 1) * nsteps / KS);
+  const int last = se - 1;
   auto load = [&](int st, GateStep<MT>& g) __attribute__((always_inline)) {
     const int k = min(st, last) * 32;
     g.w0 = *reinterpret_cast<const float4*>(wrow + k);
@@ -141,35 +153,74 @@ __global__ __launch_bounds__(64 * NW) void gate_proj_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // D[4 lg + r][li] of token tile i: token tok0 + 16 i + 4 lg + r, output o.
+  const int NO = 2 * H;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) part[w][i][lane] = acc[i];
-  __syncthreads();
-  // Wave w < MT finishes token tile w: the NW k-ranges summed in order.
-  if (w < MT) {
-    f32x4 s = part[0][w][lane];
-#pragma unroll
-    for (int q = 1; q < NW; ++q) s += part[q][w][lane];
-    float* dst = o < H ? a + o : b + (o - H);
+  for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = tok0 + 16 * w + 4 * lg + r;  // D[4 lg + r][li]
-      if (t < M) dst[(int64_t)t * ab_ld] = s[r];
+      const int t = tok0 + 16 * i + 4 * lg + r;
+      if (t >= M) continue;
+      if (part)
+        part[((int64_t)ks * M + t) * NO + o] = acc[i][r];
+      else
+        (o < H ? a + o : b + (o - H))[(int64_t)t * ab_ld] = acc[i][r];
     }
   }
 }
 
+// Pass 2: one thread per four consecutive outputs of one token.
+__global__ __launch_bounds__(256) void gate_sum_kernel(const float* __restrict__ part,
+                                                       float* __restrict__ a,
+                                                       float* __restrict__ b, int64_t ab_ld,
+                                                       int M, int H, int KS) {
+  const int NO = 2 * H, per_tok = NO / 4;
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)M * per_tok) return;
+  const int t = (int)(id / per_tok), o = (int)(id % per_tok) * 4;
+  const int64_t stride = (int64_t)M * NO;
+  const float* p = part + (int64_t)t * NO + o;
+  // Eight partials are loaded before any is added (a load-add chain waits out
+  // the memory latency once per partial); the adds still run in order.
+  float4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < KS; k0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const float4*>(p + (int64_t)min(k0 + j, KS - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (k0 + j < KS) {
+        s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+      }
+    }
+  }
+  // H % 16 == 0, so the four outputs lie all in a or all in b.
+  float* dst = (o < H ? a + o : b + (o - H)) + (int64_t)t * ab_ld;
+  dst[0] = s.x; dst[1] = s.y; dst[2] = s.z; dst[3] = s.w;
+}
+
+size_t gate_proj_workspace_bytes(int M, int K, int H) {
+  const int KS = gate_splits(M, K);
+  return KS > 1 ? (size_t)KS * M * 2 * H * sizeof(float) : 0;
+}
+
 hipError_t launch_gate_proj(const uint16_t* x, int64_t x_ld, const float* Wa, const float* Wb,
-                            float* a, float* b, int64_t ab_ld, int M, int K, int H,
+                            float* a, float* b, int64_t ab_ld, int M, int K, int H, void* workspace,
                             hipStream_t stream) {
-  const int ntiles = 2 * H / 16;
+  const int KS = gate_splits(M, K), NT = 2 * H / 16;
+  float* part = KS > 1 ? static_cast<float*>(workspace) : nullptr;
   if (M >= 1024) {
-    const dim3 grid((M + 63) / 64, ntiles);
-    hipLaunchKernelGGL((gate_proj_kernel<4, 4>), grid, dim3(256), 0, stream, x, x_ld, Wa, Wb, a,
-                       b, ab_ld, M, K, H);
+    hipLaunchKernelGGL(gate_part_kernel<4>, dim3((M + 63) / 64, KS), dim3(64 * NT), 0, stream, x,
+                       x_ld, Wa, Wb, part, a, b, ab_ld, M, K, H);
   } else {
-    const dim3 grid((M + 15) / 16, ntiles);
-    hipLaunchKernelGGL((gate_proj_kernel<1, 8>), grid, dim3(512), 0, stream, x, x_ld, Wa, Wb, a,
-                       b, ab_ld, M, K, H);
+    hipLaunchKernelGGL(gate_part_kernel<1>, dim3((M + 15) / 16, KS), dim3(64 * NT), 0, stream, x,
+                       x_ld, Wa, Wb, part, a, b, ab_ld, M, K, H);
+  }
+  if (KS > 1) {
+    const int64_t threads = (int64_t)M * (2 * H / 4);
+    hipLaunchKernelGGL(gate_sum_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, part, a, b, ab_ld, M, H, KS);
   }
   return hipGetLastError();
 }

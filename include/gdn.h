@@ -285,6 +285,13 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace gdn_gate_proj needs for M tokens (0 when none
+ * is needed or the sizes are invalid).  The caller allocates it; no
+ * initialisation is needed.
+ */
+size_t gdn_gate_proj_workspace_bytes(int32_t M, int32_t K, int32_t H);
+
+/*
  * gdn_gate_proj -- the two gate projections of the mixer, with f32 weights.
  * ("Qwen/Qwen3.8-27B" architecture viewer, module tree: in_proj_a and
  * in_proj_b, 5120 -> 48 each; the "qwen38" code-generation page, extra
@@ -294,17 +301,20 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
  *   W_a, W_b  [H, K] f32, contiguous (the Linear layout, output-major).
  *   a, b      [M, H] f32 with row stride ab_ld; they feed the gates of
  *             gdn_prefill / gdn_decode_rows (gate dtype GDN_F32) directly.
+ *   workspace at least gdn_gate_proj_workspace_bytes(M, K, H) bytes,
+ *             256-byte aligned (NULL when that is 0); scratch after the call.
  * The weights are used unrounded: each is split exactly into three bf16
- * parts on the fly, and every product is exact in f32; sums are f32, in a
- * fixed order (results do not vary from run to run).
- * Constraints: x_dt == GDN_BF16 (GDN_ERR_UNSUPPORTED otherwise); K > 0 and
- * K % 32 == 0; H > 0 and H % 16 == 0; x_ld >= K, x_ld % 8 == 0; ab_ld >= H;
- * x, W_a, W_b 16-byte aligned; a and b must not overlap x.  M == 0 is a
- * no-op.
+ * parts on the fly, and every product is exact in f32.  K is cut into
+ * ranges whose f32 partial sums are added in a fixed order (results do not
+ * vary from run to run).
+ * Constraints: x_dt == GDN_BF16 and H <= 64 (GDN_ERR_UNSUPPORTED
+ * otherwise); K > 0 and K % 32 == 0; H > 0 and H % 16 == 0; x_ld >= K,
+ * x_ld % 8 == 0; ab_ld >= H; x, W_a, W_b 16-byte aligned; a and b must not
+ * overlap x or the workspace.  M == 0 is a no-op.
  */
 int gdn_gate_proj(const void* x, int64_t x_ld, int32_t x_dt, const float* W_a,
                   const float* W_b, float* a, float* b, int64_t ab_ld, int32_t M, int32_t K,
-                  int32_t H, void* stream);
+                  int32_t H, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace recommended for gdn_linear (32 MiB).  Smaller

@@ -30,7 +30,8 @@ def test_header_and_exports():
             "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version",
             "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes", "gdn_prefill_slots",
             "gdn_prefill_slots_workspace_bytes", "gdn_decode_rows_multi", "gdn_gate_proj",
-            "gdn_linear", "gdn_linear_workspace_bytes"} <= set(names)
+            "gdn_linear", "gdn_linear_workspace_bytes",
+            "gdn_gate_proj_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
     assert gdn.gdn_abi_version() == 1
@@ -218,14 +219,22 @@ def test_prefill_slots_validation():
 
 def test_gate_proj_validation():
     L = gdn.lib()
+    need = L.gdn_gate_proj_workspace_bytes(8, 5120, 48)
+    assert need > 0 and need % 256 == 0
+    assert L.gdn_gate_proj_workspace_bytes(8, 5000, 48) == 0
+    assert L.gdn_gate_proj_workspace_bytes(0, 5120, 48) == 0
 
-    def f(x=P, xld=5120, xdt=1, wa=2 * P, wb=3 * P, a=4 * P, b=5 * P, ld=48, M=8, K=5120, H=48):
+    def f(x=P, xld=5120, xdt=1, wa=2 * P, wb=3 * P, a=4 * P, b=5 * P, ld=48, M=8, K=5120, H=48,
+          ws=64 * P, wsb=None):
+        if wsb is None:
+            wsb = need
         return L.gdn_gate_proj(_vp(x), xld, xdt, _vp(wa), _vp(wb), _vp(a), _vp(b), ld, M, K, H,
-                               None)
+                               _vp(ws), wsb, None)
     assert f(wa=0) == NULL
     assert f(b=0) == NULL
     assert f(xdt=5) == DTYPE
     assert f(xdt=0) == UNSUP           # f32 activations are not implemented
+    assert f(H=80, ld=80) == UNSUP     # more than 64 outputs per projection
     assert f(K=5000) == SHAPE          # K % 32
     assert f(H=40) == SHAPE            # H % 16
     assert f(xld=4096) == SHAPE        # row stride below K
@@ -233,8 +242,12 @@ def test_gate_proj_validation():
     assert f(M=-1) == SHAPE
     assert f(xld=5124) == ALIGN
     assert f(wa=2 * P + 4) == ALIGN
+    assert f(ws=None) == WS
+    assert f(wsb=need - 256) == WS
+    assert f(ws=64 * P + 16) == ALIGN
     assert f(a=P + 64) == SHAPE        # a overlaps x
-    assert f(M=0, x=0, wa=0, wb=0, a=0, b=0) == OK
+    assert f(b=64 * P) == SHAPE        # b overlaps the workspace
+    assert f(M=0, x=0, wa=0, wb=0, a=0, b=0, ws=None, wsb=0) == OK
 
 
 def test_linear_validation():
