@@ -14,8 +14,8 @@
 // * in_proj_qkv, in_proj_z and out_proj are plain bf16 GEMMs with f32
 //   accumulation; they go to hipBLASLt.  One handle per device is created on
 //   first use and kept until the process ends; the plan of each shape
-//   (descriptors and the heuristic's best algorithm that fits the workspace)
-//   is cached beside it.  The library links libhipblaslt.so.1 by soname: in a
+//   (descriptors and the fastest of the heuristic's candidates that fit the
+//   workspace, timed on the shape's first call) is cached beside it.  The library links libhipblaslt.so.1 by soname: in a
 //   process that already holds a copy of that library (PyTorch ships one),
 //   that copy serves these calls.
 #include <hip/hip_runtime.h>
@@ -84,8 +84,8 @@ struct GateStep {
 
 constexpr int kGateMaxTiles = 8;  // 2H / 16 <= 8 output tiles (H <= 64)
 
-// Number of K ranges for M tokens: about one workgroup per CU (256), at least
-// four k-steps per range.
+// Number of K ranges for M tokens: about one workgroup per CU (256; 512, 768
+// and 1024 measured slower at 4096 tokens), at least four k-steps per range.
 int gate_splits(int M, int K) {
   const int tok = M >= 1024 ? 64 : 16;
   const int mtiles = (M + tok - 1) / tok;
@@ -246,8 +246,13 @@ std::map<int, hipblasLtHandle_t> g_lt_handle;
 std::map<PlanKey, LtPlan> g_lt_plans;
 
 // Builds the plan for one shape; false if hipBLASLt has no algorithm for it.
-bool make_plan(hipblasLtHandle_t h, LtPlan& p, int M, int N, int K, int64_t x_ld, int64_t w_ld,
-               int64_t y_ld, int y_dt, size_t ws_bytes) {
+// Of the heuristic's candidates that fit the workspace, up to kTune are timed
+// on the caller's own buffers and stream (one warm-up and three timed runs
+// each; they all write y, which the call then writes again) and the fastest
+// is kept.  This is the first call of the shape only.
+bool make_plan(hipblasLtHandle_t h, LtPlan& p, const void* x, int64_t x_ld, const void* W,
+               int64_t w_ld, void* y, int64_t y_ld, int y_dt, int M, int N, int K,
+               void* workspace, size_t ws_bytes, hipStream_t stream) {
   const hipblasOperation_t opA = HIPBLAS_OP_T, opB = HIPBLAS_OP_N;
   const hipDataType dty = y_dt == 1 ? HIP_R_16BF : HIP_R_32F;
   if (hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS)
@@ -265,20 +270,48 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, int M, int N, int K, int64_t x_ld
                                         sizeof(cap));
   // Several candidates, best first: some hipBLASLt builds rank first an
   // algorithm that needs more workspace than the cap allows.
-  constexpr int kCand = 16;
+  constexpr int kCand = 16, kTune = 8;
   hipblasLtMatmulHeuristicResult_t res[kCand];
   int n = 0;
   const hipblasStatus_t st =
       hipblasLtMatmulAlgoGetHeuristic(h, p.desc, p.A, p.B, p.D, p.D, pref, kCand, res, &n);
   hipblasLtMatmulPreferenceDestroy(pref);
   if (st != HIPBLAS_STATUS_SUCCESS) return false;
-  for (int i = 0; i < n && i < kCand; ++i) {
-    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) {
-      p.algo = res[i].algo;
-      return true;
+  int fit[kCand], nfit = 0;
+  for (int i = 0; i < n && i < kCand; ++i)
+    if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes)
+      fit[nfit++] = i;
+  if (nfit == 0) return false;
+  p.algo = res[fit[0]].algo;
+  if (nfit == 1) return true;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return true;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    hipEventDestroy(e0);
+    return true;
+  }
+  const float alpha = 1.0f, beta = 0.0f;
+  float best = 0.0f;
+  for (int c = 0; c < nfit && c < kTune; ++c) {
+    const hipblasLtMatmulAlgo_t* al = &res[fit[c]].algo;
+    auto run = [&]() {
+      return hipblasLtMatmul(h, p.desc, &alpha, W, p.A, x, p.B, &beta, y, p.D, y, p.D, al,
+                             workspace, ws_bytes, stream) == HIPBLAS_STATUS_SUCCESS;
+    };
+    if (!run()) continue;
+    bool ok = hipEventRecord(e0, stream) == hipSuccess;
+    for (int r = 0; r < 3 && ok; ++r) ok = run();
+    ok = ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+    float ms = 0.0f;
+    if (!ok || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) continue;
+    if (best == 0.0f || ms < best) {
+      best = ms;
+      p.algo = *al;
     }
   }
-  return false;
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  return true;
 }
 
 }  // namespace
@@ -299,7 +332,8 @@ LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, i
   auto pit = g_lt_plans.find(key);
   if (pit == g_lt_plans.end()) {
     LtPlan p;
-    p.ok = make_plan(hit->second, p, M, N, K, x_ld, w_ld, y_ld, y_dt, workspace_bytes);
+    p.ok = make_plan(hit->second, p, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace,
+                     workspace_bytes, stream);
     pit = g_lt_plans.emplace(key, p).first;
   }
   const LtPlan& p = pit->second;

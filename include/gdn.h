@@ -332,12 +332,13 @@ size_t gdn_linear_workspace_bytes(void);
  *   y  [M, N] in y_dt (GDN_BF16 or GDN_F32), row stride y_ld; must not
  *      overlap x or W.
  *   y[m][n] = sum_k x[m][k] W[n][k], f32 accumulation, one rounding to y_dt.
- * Runs on hipBLASLt (the heuristic's best algorithm for the shape that
- * fits the workspace; whichever libhipblaslt.so.1 the process loaded first
- * serves the call).  The
- * first call on a device creates a hipBLASLt handle and keeps it, and the
- * first call of each shape builds and keeps its plan; those first calls may
- * allocate and synchronise, so make them before any graph capture.  Calls
+ * Runs on hipBLASLt (whichever libhipblaslt.so.1 the process loaded first
+ * serves the call).  The first call on a device creates a hipBLASLt handle
+ * and keeps it.  The first call of each shape builds and keeps its plan: it
+ * times up to eight of the heuristic's candidates that fit the workspace on
+ * this call's own buffers and stream (each writes y; the call's result is
+ * written last) and keeps the fastest.  Those first calls allocate and
+ * synchronise, so make them before any graph capture.  Calls
  * from several threads are serialised by a lock while they enqueue.
  *   workspace  scratch for hipBLASLt, 256-byte aligned, workspace_bytes long
  *              (gdn_linear_workspace_bytes() recommended), or NULL with 0.
