@@ -15,7 +15,10 @@ like the model's layer (16 q/k heads, 48 value heads, width 128):
   6. the projections around the mixer at 4096 tokens: in_proj_qkv and
      in_proj_z (gdn_linear, bf16, into one [4096, 16384] buffer), the two
      gate projections with f32 weights (gdn_gate_proj) and out_proj
-     (gdn_linear, 6144 -> 5120).
+     (gdn_linear, 6144 -> 5120);
+  7. one decode step of the whole layer for 64 fixed rows: in_proj_qkv,
+     in_proj_z, the gate projections, the conv over one token with each row's
+     conv history, decode_rows, the gated RMSNorm and out_proj.
 Each part is timed with HIP events on the stream it runs on.  The timed
 region runs each part's K iterations back to back, part after part (so a part
 follows its own previous call, not another part's dirty cache lines), and the
@@ -224,6 +227,26 @@ def main():
         pj["gws"] = torch.empty(gws_bytes, dtype=torch.uint8, device="cuda")
         proj.append(pj)
     del pin, pout
+    # Part 7: the layer's decode step for 64 rows (weights shared with part 6).
+    dlx = proj_inputs(R_DECODE, outs=(), gate_H=0, seed=2009)["x"]
+    dly = decode_inputs(R_DECODE, seed=2010)
+    dlayer = []
+    for _ in range(ROT):
+        dl = {"x": dev(dlx), "state": dev(dly["state"]), "A_log": dev(dly["A_log"]),
+              "dt_bias": dev(dly["dt_bias"]), "conv_w": dev(mx["conv_w"]),
+              "norm_w": dev(mx["norm_w"]),
+              "conv_state": torch.zeros((R_DECODE, 3, C_CONV), dtype=torch.float32,
+                                        device="cuda")}
+        dl["qkv"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
+        dl["z"] = torch.empty((R_DECODE, HV * D), dtype=torch.bfloat16, device="cuda")
+        dl["a"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
+        dl["b"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
+        dl["y"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
+        dl["o"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
+        dl["out"] = torch.empty((R_DECODE, HIDDEN), dtype=torch.bfloat16, device="cuda")
+        dl["gws"] = torch.empty(max(gdn.gdn_gate_proj_workspace_bytes(R_DECODE, HIDDEN, HV), 256),
+                                dtype=torch.uint8, device="cuda")
+        dlayer.append(dl)
     ws_bytes = gdn.gdn_prefill_workspace_bytes(1, T_PREFILL, HK, HV)
     ws = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(ROT)]
 
@@ -277,7 +300,35 @@ def main():
             ev[2].record()
         gdn.gdn_linear(Pj["y"], Pj["W_out"], y=Pj["out"], workspace=Pj["lws"])
 
-    parts_fn = [layer_part, prefill_part, decode_part, slots_part, multi_part, proj_part]
+    # Part 7 records an event after each of its first six calls.
+    dl_ev = {}
+
+    def dlayer_part(i):
+        L = dlayer[i % ROT]
+        W = proj[i % ROT]
+        ev = dl_ev.get(i)
+        mark = (lambda j: ev[j].record()) if ev else (lambda j: None)
+        gdn.gdn_linear(L["x"], W["W_qkv"], y=L["qkv"].view(R_DECODE, C_CONV), workspace=W["lws"])
+        mark(0)
+        gdn.gdn_linear(L["x"], W["W_z"], y=L["z"], workspace=W["lws"])
+        mark(1)
+        gdn.gdn_gate_proj(L["x"], W["W_a"], W["W_b"], a=L["a"], b=L["b"], workspace=L["gws"])
+        mark(2)
+        gdn.gdn_conv_silu(L["qkv"], L["conv_w"], L["conv_state"], l2_channels=2 * HK * D,
+                          y=L["y"])
+        mark(3)
+        y = L["y"][:, 0]
+        gdn.gdn_decode_rows(y[:, :HK * D].unflatten(1, (HK, D)),
+                            y[:, HK * D:2 * HK * D].unflatten(1, (HK, D)),
+                            y[:, 2 * HK * D:].unflatten(1, (HV, D)), L["a"], L["b"], L["A_log"],
+                            L["dt_bias"], L["state"], o=L["o"])
+        mark(4)
+        gdn.gdn_gated_rmsnorm(L["o"], L["z"].view(R_DECODE, HV, D), L["norm_w"], y=L["o"])
+        mark(5)
+        gdn.gdn_linear(L["o"].view(R_DECODE, HV * D), W["W_out"], y=L["out"], workspace=W["lws"])
+
+    parts_fn = [layer_part, prefill_part, decode_part, slots_part, multi_part, proj_part,
+                dlayer_part]
     for fn in parts_fn:
         for i in range(args.warmup):
             fn(i)
@@ -286,6 +337,7 @@ def main():
             for _ in range(args.steps)] for _ in parts_fn]
     for i in range(args.steps):
         proj_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        dl_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for j, fn in enumerate(parts_fn):
@@ -299,7 +351,13 @@ def main():
     parts = np.array([[evs[j][i][0].elapsed_time(evs[j][i][1]) for j in range(len(parts_fn))]
                       for i in range(args.steps)])  # ms
     mean = parts.mean(axis=0)
-    t_layer, t_pre, t_dec, t_slots, t_multi, t_proj = mean
+    t_layer, t_pre, t_dec, t_slots, t_multi, t_proj, t_dlayer = mean
+    # Per call of part 7: in_proj_qkv, in_proj_z, gates, conv, decode_rows, norm, out_proj.
+    dlc = []
+    for i in range(args.steps):
+        e = [evs[6][i][0]] + dl_ev[args.warmup + i] + [evs[6][i][1]]
+        dlc.append([e[j].elapsed_time(e[j + 1]) for j in range(7)])
+    dlc = np.array(dlc).mean(axis=0)  # ms
     # Per call of part 6: in_proj_qkv, in_proj_z, gate projections, out_proj.
     pc = np.array([[evs[5][i][0].elapsed_time(proj_ev[args.warmup + i][0]),
                     proj_ev[args.warmup + i][0].elapsed_time(proj_ev[args.warmup + i][1]),
@@ -368,7 +426,8 @@ def main():
                    "step": "layer prefill (gdn_mixer_prefill: conv+silu+L2 -> chunked prefill "
                            "-> gated RMSNorm) at B=1 T=4096, prefill workload at B=1 T=4096, "
                            "decode_rows at 64 rows, prefill_slots (16 rows), decode_rows_multi "
-                           "(64 rows x 4), projections at 4096 tokens"},
+                           "(64 rows x 4), projections at 4096 tokens, a 64-row decode step of "
+                           "the whole layer"},
         "decode_rows": {"value": round(dec_gbps, 1), "unit": "GB/s (state bytes read+written)",
                         "workload": "decode_rows_r64", "avg_launch_us": round(t_dec * 1e3, 2),
                         "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4)},
@@ -403,6 +462,15 @@ def main():
             "workload": "projections (part 6) + gdn_mixer_prefill (part 1) at B=1 T=4096, "
                         "the two parts' times added",
             "us": round((t_layer + t_proj) * 1e3, 2)},
+        "full_layer_decode": {
+            "value": round(R_DECODE / (t_dlayer * 1e-3), 1), "unit": "tokens/s",
+            "workload": "one decode step of the whole layer for 64 fixed rows: in_proj_qkv, "
+                        "in_proj_z, gate projections, conv over one token with the rows' conv "
+                        "history, decode_rows, gated RMSNorm, out_proj",
+            "us": round(t_dlayer * 1e3, 2),
+            "calls_us": dict(zip(["in_proj_qkv", "in_proj_z", "gate_proj", "conv", "decode_rows",
+                                  "gated_rmsnorm", "out_proj"],
+                                 [round(v * 1e3, 2) for v in dlc]))},
         "prefill": {"avg_launch_us": round(t_pre * 1e3, 2),
                     "mfma_tflops": round(pre_flops / (t_pre * 1e-3) / 1e12, 2),
                     "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9,

@@ -152,6 +152,32 @@ def test_linear_without_workspace_and_strided_output():
     assert max_rel_err(got[:, 256:], oracle.linear(xs, to_f64(W2))) <= TOL_LIN_BF16
 
 
+@pytest.mark.parametrize("M,N,K,out,with_ws", [(64, 10240, 5120, torch.bfloat16, True),
+                                                (17, 6144, 5120, torch.float32, False),
+                                                (64, 5120, 6144, torch.bfloat16, False),
+                                                (33, 5120, 6144, torch.float32, True),
+                                                (8, 100, 192, torch.float32, True)])
+def test_linear_few_tokens(M, N, K, out, with_ws):
+    """The decode-step shapes (at most 64 tokens: the weight-streaming kernel),
+    written into columns 32.. of a wider buffer; with a workspace the K range
+    is split and the partials summed, without one it is a single pass.  N = 100
+    leaves a partial block of outputs; K = 192 is three stages."""
+    banner(f"linear few tokens M={M} N={N} K={K} out={out} ws={with_ws}")
+    p = proj_inputs(M, K=K, outs=(("W", N),), gate_H=0, seed=70 + M + N % 97)
+    ws = (torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+          if with_ws else None)
+    width = (N + 64 + 7) // 8 * 8  # row strides are multiples of 8
+    yb = torch.full((M, width), float("nan"), dtype=out, device="cuda")
+    gdn.gdn_linear(dev(p["x"]), dev(p["W"]), y=yb[:, 32:32 + N], workspace=ws)
+    torch.cuda.synchronize()
+    got = host_f64(yb)
+    ref = oracle.linear(to_f64(p["x"]), to_f64(p["W"]))
+    e = max_rel_err(got[:, 32:32 + N], ref)
+    print(f"linear few tokens {M}x{N}x{K}: err {e:.2e}")
+    assert e <= (TOL_LIN_F32 if out == torch.float32 else TOL_LIN_BF16)
+    assert np.isnan(got[:, :32]).all() and np.isnan(got[:, 32 + N:]).all()
+
+
 def _sampled_rows(M, n, seed):
     rng = np.random.default_rng(seed)
     return np.sort(rng.choice(M, size=n, replace=False))
