@@ -169,6 +169,111 @@ __global__ __launch_bounds__(64 * kGateMaxTiles) void gate_part_kernel(
   }
 }
 
+// The same product for many tokens (64 per workgroup), with the token tile
+// staged through LDS: per 64-wide k-stage the workgroup reads the 64 x rows
+// with eight adjacent lanes per 128-byte piece (the MFMA order, lane = row,
+// reads them at about half that rate, and six waves each fetched them
+// through L1), writes them to a double-buffered LDS tile, and the waves read
+// their fragments from there.  x pieces and each wave's weights are loaded
+// four stages ahead in registers; one barrier per stage.  The buffer written
+// at stage s was last read at stage s - 2, before the barrier of stage s - 1.
+constexpr int GL_KC = 64;  // k per stage (two 32-wide k-steps)
+constexpr int GL_XP = 72;  // LDS pitch (bf16): 144-byte rows, conflict-free b128 reads
+
+struct GateLdsStage {
+  float4 w[4];         // this lane's 8 weights of each of the stage's two k-steps
+  uint32_t x0[4], x1[4];  // x pieces tid and tid + 384 (the latter for tid < 128)
+};
+
+__global__ __launch_bounds__(64 * kGateMaxTiles) void gate_part_lds_kernel(
+    const uint16_t* __restrict__ x, int64_t x_ld, const float* __restrict__ Wa,
+    const float* __restrict__ Wb, float* __restrict__ part, float* __restrict__ a,
+    float* __restrict__ b, int64_t ab_ld, int M, int K, int H) {
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][64 * GL_XP];
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int w = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int tok0 = blockIdx.x * 64;
+  const int o = w * 16 + li;  // this lane's output column of [a | b]
+  const float* wrow = (o < H ? Wa + (int64_t)o * K : Wb + (int64_t)(o - H) * K) + lg * 8;
+  // x pieces (row p / 8, 16-byte column p % 8 of a stage): tid, and tid +
+  // nthr while that is below 512 (the launch gives at least 256 threads, so
+  // the two cover all 512).  Rows past M read row M-1.
+  const int p0 = tid, p1 = tid + nthr;
+  const bool two = p1 < 512;
+  const int xr0 = p0 >> 3, xr1 = min(p1, 511) >> 3, xc0 = (p0 & 7) * 8, xc1 = (p1 & 7) * 8;
+  const uint16_t* xp0 = x + (int64_t)min(tok0 + xr0, M - 1) * x_ld + xc0;
+  const uint16_t* xp1 = x + (int64_t)min(tok0 + xr1, M - 1) * x_ld + xc1;
+
+  const int nst = K / GL_KC, ks = blockIdx.y, KS = gridDim.y;
+  const int sb = (int)((int64_t)ks * nst / KS), se = (int)((int64_t)(ks + 1) * nst / KS);
+  const int last = se - 1;
+  auto load = [&](int st, GateLdsStage& g) __attribute__((always_inline)) {
+    const int k = min(st, last) * GL_KC;
+    g.w[0] = *reinterpret_cast<const float4*>(wrow + k);
+    g.w[1] = *reinterpret_cast<const float4*>(wrow + k + 4);
+    g.w[2] = *reinterpret_cast<const float4*>(wrow + k + 32);
+    g.w[3] = *reinterpret_cast<const float4*>(wrow + k + 36);
+    const uint4 v0 = *reinterpret_cast<const uint4*>(xp0 + k);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(xp1 + k);
+    g.x0[0] = v0.x; g.x0[1] = v0.y; g.x0[2] = v0.z; g.x0[3] = v0.w;
+    g.x1[0] = v1.x; g.x1[1] = v1.y; g.x1[2] = v1.z; g.x1[3] = v1.w;
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  GateLdsStage g[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) load(sb + u, g[u]);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int j = sb; j < se; j += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = j + u, bb = s & 1;
+      // A stage past se multiplies zero weights (a select, not a branch).
+      const bool live = s < se;
+      *reinterpret_cast<uint4*>(&Xs[bb][xr0 * GL_XP + xc0]) =
+          uint4{g[u].x0[0], g[u].x0[1], g[u].x0[2], g[u].x0[3]};
+      if (two)
+        *reinterpret_cast<uint4*>(&Xs[bb][xr1 * GL_XP + xc1]) =
+            uint4{g[u].x1[0], g[u].x1[1], g[u].x1[2], g[u].x1[3]};
+      const float4 z4 = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 hi[2], lo[2], lo2[2];
+      split3(live ? g[u].w[0] : z4, live ? g[u].w[1] : z4, hi[0], lo[0], lo2[0]);
+      split3(live ? g[u].w[2] : z4, live ? g[u].w[3] : z4, hi[1], lo[1], lo2[1]);
+      load(s + 4, g[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk::lds_barrier();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 xf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xf[i] = chunk::ld_frag(&Xs[bb][(16 * i + li) * GL_XP + kk * 32 + lg * 8]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] = mfma16(xf[i], hi[kk], acc[i]);
+          acc[i] = mfma16(xf[i], lo[kk], acc[i]);
+          acc[i] = mfma16(xf[i], lo2[kk], acc[i]);
+        }
+      }
+    }
+  }
+  // D[4 lg + r][li] of token tile i: token tok0 + 16 i + 4 lg + r, output o.
+  const int NO = 2 * H;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tok0 + 16 * i + 4 * lg + r;
+      if (t >= M) continue;
+      if (part)
+        part[((int64_t)ks * M + t) * NO + o] = acc[i][r];
+      else
+        (o < H ? a + o : b + (o - H))[(int64_t)t * ab_ld] = acc[i][r];
+    }
+  }
+}
+
 // Pass 2: one thread per four consecutive outputs of one token.
 __global__ __launch_bounds__(256) void gate_sum_kernel(const float* __restrict__ part,
                                                        float* __restrict__ a,
@@ -210,7 +315,10 @@ hipError_t launch_gate_proj(const uint16_t* x, int64_t x_ld, const float* Wa, co
                             hipStream_t stream) {
   const int KS = gate_splits(M, K), NT = 2 * H / 16;
   float* part = KS > 1 ? static_cast<float*>(workspace) : nullptr;
-  if (M >= 1024) {
+  if (M >= 1024 && K % GL_KC == 0 && NT >= 4) {  // >= 256 threads: two x pieces each cover 512
+    hipLaunchKernelGGL(gate_part_lds_kernel, dim3((M + 63) / 64, KS), dim3(64 * NT), 0, stream,
+                       x, x_ld, Wa, Wb, part, a, b, ab_ld, M, K, H);
+  } else if (M >= 1024) {
     hipLaunchKernelGGL(gate_part_kernel<4>, dim3((M + 63) / 64, KS), dim3(64 * NT), 0, stream, x,
                        x_ld, Wa, Wb, part, a, b, ab_ld, M, K, H);
   } else {
