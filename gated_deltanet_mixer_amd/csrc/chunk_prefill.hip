@@ -122,10 +122,16 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   constexpr bool kSplit = sizeof(TI) == 4;  // f32 q/k: two-term Q K^T
   // Region R: first the A blocks (diagonal f32, off-diagonal bf16), then K^T,
   // then V^T (bf16 [128][XP]).
-  __shared__ __attribute__((aligned(16))) uint16_t R[DH * XP];
-  __shared__ __attribute__((aligned(16))) uint16_t Tn[CK * XP];     // T, bf16, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t Tdt[4 * 16 * 16];  // diagonal blocks, transposed
+  // One LDS block holds R, then T (Tn) and its transposed diagonal blocks
+  // (Tdt); with bf16 q/k it first holds the chunk's K and Q rows as loaded
+  // ([64][RP] each), until every wave has its operand fragments.
+  constexpr int kRegion = DH * XP + CK * XP + 4 * 16 * 16;
+  constexpr int kStage = 2 * CK * RP;
+  __shared__ __attribute__((aligned(16))) uint16_t L[kRegion > kStage ? kRegion : kStage];
   __shared__ __attribute__((aligned(16))) float Gs[CK], Bs[CK], BGs[CK];  // G, b, b e^G
+  uint16_t* R = L;
+  uint16_t* Tn = L + DH * XP;              // T, bf16, row-major
+  uint16_t* Tdt = Tn + CK * XP;            // diagonal blocks, transposed
   float* Ad = reinterpret_cast<float*>(R);       // [4][16][ADP]
   uint16_t* Ao = R + 4 * 16 * ADP * 2;           // [64][XP], off-diagonal blocks of A
   uint16_t* XT = R;
@@ -167,8 +173,26 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   }
   const unsigned slots = w == 0 ? 0xDC98u : w == 1 ? 0x0FB9u : w == 2 ? 0xEA98u : 0xFBA8u;
   bf16x8 f[4][4], fl[4][4], vf[4];
+  // bf16 q/k: the chunk's 64 K rows and 64 Q rows are loaded with 16 adjacent
+  // lanes per 256-byte row (the MFMA operand order, lane = row, reads them at
+  // about half that rate, and the waves' operand blocks overlap: 15 block
+  // loads for 8 blocks), staged in LDS, and each wave reads its fragments
+  // from there.  f32 q/k keep the direct loads (their staging would not fit).
+  constexpr bool kStaged = !kSplit;
+  typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+  u32x4s stg[8];
+  if (kStaged) {
 #pragma unroll
-  for (int sl = 0; sl < 4; ++sl) {
+    for (int j = 0; j < 8; ++j) {
+      const int u = (j & 3) * PREP_THREADS + tid;  // 16-byte unit of a [64][128] tile
+      const int t = u >> 4, col = (u & 15) * 8;
+      const TI* src = (j < 4 ? kbase + (int64_t)t * k_ts : qbase + (int64_t)t * q_ts) + col;
+      if (t < n) stg[j] = *reinterpret_cast<const u32x4s*>(src);
+      else stg[j] = u32x4s{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int sl = 0; sl < 4 && !kStaged; ++sl) {
     const int code = (slots >> (4 * sl)) & 15;
     const int t = (code & 3) * 16 + li;
     const TI* row = (code & 4) ? qbase + (int64_t)t * q_ts : kbase + (int64_t)t * k_ts;
@@ -211,7 +235,29 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     ws.G[chunk * 2 * CK + lane] = Gl;
     ws.G[chunk * 2 * CK + CK + lane] = __shfl(Gl, CK - 1);
   }
+  if (kStaged) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int u = (j & 3) * PREP_THREADS + tid;
+      *reinterpret_cast<u32x4s*>(&L[(j >> 2) * CK * RP + (u >> 4) * RP + (u & 15) * 8]) = stg[j];
+    }
+  }
   lds_barrier();
+  if (kStaged) {
+    // Wave w's operand blocks (slot code: bit 3 used, bit 2 Q, bits 0-1 block).
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int code = (slots >> (4 * sl)) & 15;
+      const uint16_t* base = L + ((code >> 2) & 1) * CK * RP + ((code & 3) * 16 + li) * RP + lg * 8;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (code & 8) f[sl][kk] = ld_frag(base + kk * 32);
+        else f[sl][kk] = zero_frag();
+        fl[sl][kk] = zero_frag();
+      }
+    }
+    lds_barrier();  // the block is rewritten by the K K^T tiles below
+  }
 
   // K K^T tile (tb, sb) from slots (st, ss) -> A: D[t][s], lane (li = s, lg)
   // holds t = 16 tb + 4 lg + r; the diagonal blocks in f32, the others bf16.
