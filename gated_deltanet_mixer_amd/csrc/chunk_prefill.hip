@@ -181,6 +181,23 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   constexpr bool kStaged = !kSplit;
   typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
   u32x4s stg[8];
+  // f32 q/k go through the same block in two halves of 64 dims (a [64][68]
+  // f32 tile each for K and Q), both halves' loads issued here.
+  constexpr bool kStagedF = kSplit;
+  constexpr int RPF = 68;  // f32 pitch of a staged half: 272-byte rows
+  u32x4s stgf[2][8];
+  if (kStagedF) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int u = (j & 3) * PREP_THREADS + tid;  // 16-byte unit of a [64][64] f32 half
+        const int t = u >> 4, col = hh * 64 + (u & 15) * 4;
+        const TI* src = (j < 4 ? kbase + (int64_t)t * k_ts : qbase + (int64_t)t * q_ts) + col;
+        if (t < n) stgf[hh][j] = *reinterpret_cast<const u32x4s*>(src);
+        else stgf[hh][j] = u32x4s{0u, 0u, 0u, 0u};
+      }
+  }
   if (kStaged) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -192,7 +209,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     }
   }
 #pragma unroll
-  for (int sl = 0; sl < 4 && !kStaged; ++sl) {
+  for (int sl = 0; sl < 4 && !kStaged && !kStagedF; ++sl) {
     const int code = (slots >> (4 * sl)) & 15;
     const int t = (code & 3) * 16 + li;
     const TI* row = (code & 4) ? qbase + (int64_t)t * q_ts : kbase + (int64_t)t * k_ts;
@@ -254,6 +271,37 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
         if (code & 8) f[sl][kk] = ld_frag(base + kk * 32);
         else f[sl][kk] = zero_frag();
         fl[sl][kk] = zero_frag();
+      }
+    }
+    lds_barrier();  // the block is rewritten by the K K^T tiles below
+  }
+  if (kStagedF) {
+    float* Lf = reinterpret_cast<float*>(L);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 1) lds_barrier();  // every wave has read the first half
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int u = (j & 3) * PREP_THREADS + tid;
+        *reinterpret_cast<u32x4s*>(&Lf[(j >> 2) * CK * RPF + (u >> 4) * RPF + (u & 15) * 4]) =
+            stgf[hh][j];
+      }
+      lds_barrier();
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int code = (slots >> (4 * sl)) & 15;
+        const float* base =
+            Lf + ((code >> 2) & 1) * CK * RPF + ((code & 3) * 16 + li) * RPF + lg * 8;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int kk = hh * 2 + k2;
+          if (code & 8) {
+            load_row8(base + k2 * 32, f[sl][kk], fl[sl][kk]);
+          } else {
+            f[sl][kk] = zero_frag();
+            fl[sl][kk] = zero_frag();
+          }
+        }
       }
     }
     lds_barrier();  // the block is rewritten by the K K^T tiles below
