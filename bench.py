@@ -18,7 +18,9 @@ like the model's layer (16 q/k heads, 48 value heads, width 128):
      (gdn_linear, 6144 -> 5120);
   7. one decode step of the whole layer for 64 fixed rows: in_proj_qkv,
      in_proj_z, the gate projections, the conv over one token with each row's
-     conv history, decode_rows, the gated RMSNorm and out_proj.
+     conv history, decode_rows, the gated RMSNorm and out_proj;
+  8. the same decode step replayed from a HIP graph (captured once per buffer
+     set after the warm-up, so the eight launches go out as one).
 Each part is timed with HIP events on the stream it runs on.  The timed
 region runs each part's K iterations back to back, part after part (so a part
 follows its own previous call, not another part's dirty cache lines), and the
@@ -303,10 +305,10 @@ def main():
     # Part 7 records an event after each of its first six calls.
     dl_ev = {}
 
-    def dlayer_part(i):
+    def dlayer_part(i, events=True):
         L = dlayer[i % ROT]
         W = proj[i % ROT]
-        ev = dl_ev.get(i)
+        ev = dl_ev.get(i) if events else None
         mark = (lambda j: ev[j].record()) if ev else (lambda j: None)
         gdn.gdn_linear(L["x"], W["W_qkv"], y=L["qkv"].view(R_DECODE, C_CONV), workspace=W["lws"])
         mark(0)
@@ -333,6 +335,27 @@ def main():
         for i in range(args.warmup):
             fn(i)
     torch.cuda.synchronize()
+    # Part 8: the decode step of each buffer set captured in a graph (the eager
+    # warm-up above built the hipBLASLt plans, which cannot be made under capture).
+    graphs = []
+    cap = torch.cuda.Stream()
+    for r in range(ROT):
+        gr = torch.cuda.CUDAGraph()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(gr, stream=cap):
+                dlayer_part(r, events=False)
+        torch.cuda.current_stream().wait_stream(cap)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+
+    def dlayer_graph_part(i):
+        graphs[i % ROT].replay()
+
+    parts_fn.append(dlayer_graph_part)
+    for i in range(max(args.warmup, 2)):
+        dlayer_graph_part(i)
+    torch.cuda.synchronize()
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(args.steps)] for _ in parts_fn]
     for i in range(args.steps):
@@ -351,7 +374,7 @@ def main():
     parts = np.array([[evs[j][i][0].elapsed_time(evs[j][i][1]) for j in range(len(parts_fn))]
                       for i in range(args.steps)])  # ms
     mean = parts.mean(axis=0)
-    t_layer, t_pre, t_dec, t_slots, t_multi, t_proj, t_dlayer = mean
+    t_layer, t_pre, t_dec, t_slots, t_multi, t_proj, t_dlayer, t_dgraph = mean
     # Per call of part 7: in_proj_qkv, in_proj_z, gates, conv, decode_rows, norm, out_proj.
     dlc = []
     for i in range(args.steps):
@@ -427,7 +450,7 @@ def main():
                            "-> gated RMSNorm) at B=1 T=4096, prefill workload at B=1 T=4096, "
                            "decode_rows at 64 rows, prefill_slots (16 rows), decode_rows_multi "
                            "(64 rows x 4), projections at 4096 tokens, a 64-row decode step of "
-                           "the whole layer"},
+                           "the whole layer (eager and replayed from a HIP graph)"},
         "decode_rows": {"value": round(dec_gbps, 1), "unit": "GB/s (state bytes read+written)",
                         "workload": "decode_rows_r64", "avg_launch_us": round(t_dec * 1e3, 2),
                         "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4)},
@@ -468,6 +491,8 @@ def main():
                         "in_proj_z, gate projections, conv over one token with the rows' conv "
                         "history, decode_rows, gated RMSNorm, out_proj",
             "us": round(t_dlayer * 1e3, 2),
+            "graph_us": round(t_dgraph * 1e3, 2),
+            "graph_value": round(R_DECODE / (t_dgraph * 1e-3), 1),
             "calls_us": dict(zip(["in_proj_qkv", "in_proj_z", "gate_proj", "conv", "decode_rows",
                                   "gated_rmsnorm", "out_proj"],
                                  [round(v * 1e3, 2) for v in dlc]))},
