@@ -97,6 +97,21 @@ def test_gate_proj_strided_views_small_K_and_determinism(M, K):
     assert max_rel_err(got[:, H:], rb) <= TOL_GATE
 
 
+@pytest.mark.parametrize("M,K,H", [(1024, 512, 32), (1029, 1024, 64), (2050, 5120, 48)])
+def test_gate_proj_many_tokens_lds_path(M, K, H):
+    """From 1024 tokens the token tile is staged through LDS; 2H/16 waves move
+    its 512 pieces (two per thread at H = 32, one at H = 64), with ragged last
+    token tiles."""
+    banner(f"gate_proj many tokens M={M} K={K} H={H}")
+    p = proj_inputs(M, K=K, outs=(), gate_H=H, seed=80 + H)
+    a, b = gdn.gdn_gate_proj(dev(p["x"]), dev(p["W_a"]), dev(p["W_b"]))
+    torch.cuda.synchronize()
+    ra, rb = _gate_ref(p["x"], p["W_a"], p["W_b"])
+    ea, eb = max_rel_err(host_f64(a), ra), max_rel_err(host_f64(b), rb)
+    print(f"gate_proj M={M} K={K} H={H}: a err {ea:.2e}, b err {eb:.2e}")
+    assert ea <= TOL_GATE and eb <= TOL_GATE
+
+
 def test_gate_proj_feeds_decode_gates():
     """a and b from gdn_gate_proj drive gdn_decode_rows (f32 gates) exactly as
     the same values copied from the host do."""
