@@ -30,6 +30,13 @@ MixerWs mixer_ws(int32_t B, int32_t T, const gdn_dims& d) {
   return w;
 }
 bool dtype_ok(int32_t d) { return d == GDN_F32 || d == GDN_BF16; }
+
+// The chunked algorithm runs on bf16 MFMA and serves bf16 q/k/v only: f32
+// inputs go to the sequential f32 kernel (AUTO), and an explicit CHUNKED
+// request with f32 q/k/v is refused.
+bool uses_chunked(int32_t algo, int32_t qkv_dt) {
+  return qkv_dt == GDN_BF16 && (algo == GDN_ALGO_CHUNKED || algo == GDN_ALGO_AUTO);
+}
 size_t dsize(int32_t d) { return d == GDN_BF16 ? 2 : 4; }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
@@ -101,8 +108,7 @@ int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const floa
 size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t qkv_dt,
                                    int32_t algo) {
   if (B <= 0 || T <= 0 || check_dims(dims) != GDN_OK) return 0;
-  const bool chunked = algo == GDN_ALGO_CHUNKED || (algo == GDN_ALGO_AUTO && qkv_dt == GDN_BF16);
-  if (!chunked) return 0;
+  if (!uses_chunked(algo, qkv_dt)) return 0;
   return gdn::prefill_chunked_workspace_bytes(B, T, dims.n_qk_heads, dims.n_v_heads);
 }
 
@@ -131,7 +137,8 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
       !aligned(dt_bias, 4) || (state_in && !aligned(state_in, 16)) ||
       (state_out && !aligned(state_out, 16)))
     return GDN_ERR_ALIGN;
-  const bool chunked = algo == GDN_ALGO_CHUNKED || (algo == GDN_ALGO_AUTO && qkv_dt == GDN_BF16);
+  if (algo == GDN_ALGO_CHUNKED && qkv_dt != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  const bool chunked = uses_chunked(algo, qkv_dt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (B == 0) return GDN_OK;
   if (chunked && T > 0) {
@@ -145,7 +152,7 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
   // Sequential algorithm (also the T == 0 state pass-through).
   return launch_status(gdn::launch_prefill_sequential(
       q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, a, b, gate_dt, A_log, dt_bias,
-      state_in, state_out, o, o_dt, B, T, Hk, Hv, q_scale, s));
+      state_in, state_out, o, o_dt, B, T, nullptr, 0, Hk, Hv, q_scale, s));
 }
 
 int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t k_row_stride,
@@ -254,13 +261,18 @@ int gdn_prefill_slots(const void* q, int64_t q_tok_stride, const void* k, int64_
       !aligned(dt_bias, 4) || !aligned(cu_seqlens, 4) || !aligned(state, 16))
     return GDN_ERR_ALIGN;
   if (R == 0 || max_len == 0 || total_tokens == 0) return GDN_OK;  // every row is empty
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (qkv_dt == GDN_F32)  // f32 inputs: token by token in f32, in place
+    return launch_status(gdn::launch_prefill_sequential(
+        q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, a, b, gate_dt, A_log, dt_bias,
+        state, state, o, o_dt, R, max_len, cu_seqlens, total_tokens, Hk, Hv, q_scale, s));
   const size_t need = gdn::prefill_chunked_workspace_bytes(R, max_len, Hk, Hv);
   if (workspace_bytes < need || !workspace) return GDN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
   return launch_status(gdn::launch_prefill_chunked(
       q, q_tok_stride, k, k_tok_stride, v, v_tok_stride, qkv_dt, qkv_dt, a, b, gate_dt, A_log,
       dt_bias, state, state, o, o_dt, R, max_len, cu_seqlens, total_tokens, Hk, Hv, q_scale,
-      workspace, static_cast<hipStream_t>(stream)));
+      workspace, s));
 }
 
 size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims) {
@@ -295,7 +307,8 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
   if (T == 0)  // no tokens: conv history unchanged, the state passes through
     return launch_status(gdn::launch_prefill_sequential(
         nullptr, Hk * 128, nullptr, Hk * 128, nullptr, Hv * 128, dt, nullptr, nullptr, gate_dt,
-        A_log, dt_bias, state_in, state_out, nullptr, dt, B, 0, Hk, Hv, q_scale, s));
+        A_log, dt_bias, state_in, state_out, nullptr, dt, B, 0, nullptr, 0, Hk, Hv, q_scale,
+        s));
   const MixerWs w = mixer_ws(B, T, dims);
   if (workspace_bytes < w.total() || !workspace) return GDN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
@@ -303,6 +316,22 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
   if (overlaps(y, ybytes, workspace, w.total()) || overlaps(y, ybytes, z, ybytes) ||
       overlaps(y, ybytes, qkv, (size_t)B * T * C * dsize(dt)))
     return GDN_ERR_SHAPE;
+  if (dt == GDN_F32) {
+    // f32 inputs keep f32 accuracy: the conv writes [B, T, C] f32 to the
+    // workspace (B*T*C*4 bytes, less than the chunked layout's total), the
+    // recurrence runs token by token in f32 on views of it, and the norm
+    // runs in place on y.
+    float* yc = static_cast<float*>(workspace);
+    hipError_t e = gdn::launch_conv_silu(qkv, dt, yc, GDN_F32, conv_w, conv_state, B, T, C, L2C,
+                                         l2_eps, s);
+    if (e != hipSuccess) return GDN_ERR_LAUNCH;
+    e = gdn::launch_prefill_sequential(yc, C, yc + Hk * 128, C, yc + L2C, C, GDN_F32, a, b,
+                                       gate_dt, A_log, dt_bias, state_in, state_out, y, dt, B, T,
+                                       nullptr, 0, Hk, Hv, q_scale, s);
+    if (e != hipSuccess) return GDN_ERR_LAUNCH;
+    return launch_status(
+        gdn::launch_gated_rmsnorm(y, z, y, dt, norm_w, (int64_t)B * T * Hv, norm_eps, s));
+  }
   char* ws = static_cast<char*>(workspace);
   float* yqk = reinterpret_cast<float*>(ws);
   uint16_t* yv = reinterpret_cast<uint16_t*>(ws + w.qk_bytes);

@@ -15,7 +15,7 @@ namespace chunk {
 constexpr int CK = 64;   // chunk length
 constexpr int DH = 128;  // head width
 constexpr int XP = 72;   // pitch (bf16) of [*, 64] LDS tiles: 144-byte rows, 16-byte aligned
-constexpr int ADP = 20;  // pitch (f32) of the diagonal A blocks: 80-byte rows
+constexpr int FP = 68;   // pitch (f32) of [64, 64] f32 LDS tiles: 272-byte rows
 constexpr int RP = DH + 8;  // pitch (bf16) of [*, 128] LDS tiles: 272-byte rows
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -84,6 +84,21 @@ __device__ __forceinline__ void st4<uint16_t>(uint16_t* p, float a, float b, flo
   u16x4 v;
   v[0] = f2bf(a); v[1] = f2bf(b); v[2] = f2bf(c); v[3] = f2bf(d);
   *reinterpret_cast<u16x4*>(p) = v;
+}
+
+// Four values as two bf16 parts, hi = bf16(x) and lo = bf16(x - hi), stored
+// at hi_p and lo_p (hi + lo carries ~16 significant bits).
+__device__ __forceinline__ void st4_split(uint16_t* hi_p, uint16_t* lo_p, float a, float b,
+                                          float c, float d) {
+  u16x4 h, l;
+  const float v[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = f2bf(v[i]);
+    l[i] = f2bf(v[i] - bf2f(h[i]));
+  }
+  *reinterpret_cast<u16x4*>(hi_p) = h;
+  *reinterpret_cast<u16x4*>(lo_p) = l;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -43,13 +43,23 @@ using namespace chunk;
 
 namespace {
 
+// Ut and P of a chunk-head flagged by the prep also get a second bf16 part
+// (lo = bf16(x - hi), so hi + lo carries ~16 significant bits).  The chain
+// sums U and P over a chunk's tokens; when a chunk's keys are nearly parallel
+// and its write rates high, those sums cancel (U_t ~ v_t - v_{t-1}) and a
+// one-part bf16 rounding of each term costs ~2% of the result.  The flag
+// (F) marks such chunks: any |T_ts|, s < t, of T = (I + A)^{-1} above
+// kSplitThreshold.  Unflagged chunks leave the lo parts unwritten and unread.
 struct WsLayout {
-  uint16_t* W;   // [B*Hv*NC][8192]  Wf
-  uint16_t* Ut;  // [B*Hv*NC][8192]  Utf
-  uint16_t* P;   // [B*Hv*NC][4096]  Pf
-  float* G;      // [B*Hv*NC][128]: G_t (t < 64), then G_last replicated 64 times
-  uint16_t* Kt;  // [B*Hk*NC][8192]  Ktf
-  uint16_t* Qb;  // [B*Hk*NC][8192]  Qf
+  uint16_t* W;    // [B*Hv*NC][8192]  Wf
+  uint16_t* Ut;   // [B*Hv*NC][8192]  Utf, hi part
+  uint16_t* UtL;  // [B*Hv*NC][8192]  Utf, lo part
+  uint16_t* P;    // [B*Hv*NC][4096]  Pf, hi part
+  uint16_t* PL;   // [B*Hv*NC][4096]  Pf, lo part
+  float* G;       // [B*Hv*NC][128]: G_t (t < 64), then G_last replicated 64 times
+  uint16_t* Kt;   // [B*Hk*NC][8192]  Ktf
+  uint16_t* Qb;   // [B*Hk*NC][8192]  Qf
+  int32_t* F;     // [B*Hv*NC]: 1 if the chunk-head uses the two-part Ut and P
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -59,12 +69,15 @@ WsLayout ws_layout(void* base, int B, int T, int Hk, int Hv) {
   const size_t nch = (size_t)B * Hv * NC, nck = (size_t)B * Hk * NC;
   char* p = static_cast<char*>(base);
   WsLayout L;
-  L.W = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * DH * 2);
-  L.Ut = reinterpret_cast<uint16_t*>(p); p += align256(nch * DH * CK * 2);
-  L.P = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * CK * 2);
+  L.W = reinterpret_cast<uint16_t*>(p);   p += align256(nch * CK * DH * 2);
+  L.Ut = reinterpret_cast<uint16_t*>(p);  p += align256(nch * DH * CK * 2);
+  L.UtL = reinterpret_cast<uint16_t*>(p); p += align256(nch * DH * CK * 2);
+  L.P = reinterpret_cast<uint16_t*>(p);   p += align256(nch * CK * CK * 2);
+  L.PL = reinterpret_cast<uint16_t*>(p);  p += align256(nch * CK * CK * 2);
   L.G = reinterpret_cast<float*>(p);     p += align256(nch * 2 * CK * 4);
   L.Kt = reinterpret_cast<uint16_t*>(p); p += align256(nck * DH * CK * 2);
   L.Qb = reinterpret_cast<uint16_t*>(p); p += align256(nck * CK * DH * 2);
+  L.F = reinterpret_cast<int32_t*>(p);   p += align256(nch * 4);
   return L;
 }
 
@@ -73,8 +86,9 @@ WsLayout ws_layout(void* base, int B, int T, int Hk, int Hv) {
 size_t prefill_chunked_workspace_bytes(int B, int T, int Hk, int Hv) {
   const size_t NC = (size_t)(T + CK - 1) / CK;
   const size_t nch = (size_t)B * Hv * NC, nck = (size_t)B * Hk * NC;
-  return align256(nch * CK * DH * 2) + align256(nch * DH * CK * 2) + align256(nch * CK * CK * 2) +
-         align256(nch * 2 * CK * 4) + align256(nck * DH * CK * 2) + align256(nck * CK * DH * 2);
+  return align256(nch * CK * DH * 2) + 2 * align256(nch * DH * CK * 2) +
+         2 * align256(nch * CK * CK * 2) + align256(nch * 2 * CK * 4) +
+         align256(nck * DH * CK * 2) + align256(nck * CK * DH * 2) + align256(nch * 4);
 }
 
 // Token span of row bb: rows of T tokens at stride T, or, with cu (device
@@ -113,6 +127,18 @@ __device__ __forceinline__ int xcd_head(int r, int ngroups, int grp, int per) {
 // block w (16 tokens) of every tile loop; the serial parts of the inverse run
 // on wave 0 while the others wait at LDS-only barriers.
 constexpr int PREP_THREADS = 256;
+// Floor of a token's log-decay in the chunk form (see the gate computation).
+// e^{-128} is below the smallest f32 subnormal, and a chunk's prefix sums stay
+// within 64 * 128, where f32 differences keep ~1e-3 absolute accuracy.
+constexpr float kLogAlphaFloor = 128.0f;
+// A chunk-head whose T = (I + A)^{-1} has an off-diagonal entry above this in
+// magnitude keeps Ut and P in two bf16 parts.  Measured against the f64
+// definition on CPU emulations of the chunk arithmetic over a grid of key
+// correlations, write rates and decays: with every |T_ts| below 0.4 the
+// one-part form stays within 1e-2; the 1e-2..3e-2 errors start near 0.45
+// (nearly parallel keys, write rates near 1, slow decay).  Random unit keys
+// give 0.1-0.3; the keys of the whole mixer (conv + silu + L2) 0.25-0.47.
+constexpr float kSplitThreshold = 0.4f;
 
 template <typename TI, typename TV, typename G_T>
 __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
@@ -121,22 +147,21 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     const G_T* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     WsLayout ws, int T, const int32_t* __restrict__ cu, int total, int Hk, int Hv, int NC,
     float q_scale) {
-  constexpr bool kSplit = sizeof(TI) == 4;  // f32 q/k: two-term Q K^T
-  // Region R: first the A blocks (diagonal f32, off-diagonal bf16), then K^T,
-  // then V^T (bf16 [128][XP]).
-  // One LDS block holds R, then T (Tn) and its transposed diagonal blocks
-  // (Tdt); with bf16 q/k it first holds the chunk's K and Q rows as loaded
+  constexpr bool kSplit = sizeof(TI) == 4;  // f32 q/k: two-term K K^T and Q K^T
+  // Region R: first A (f32 [64][FP]), then K^T, then V^T (bf16 [128][XP]).
+  // T (f32 [64][FP]) follows R and lives from the inverse to the end.  With
+  // bf16 q/k the block first holds the chunk's K and Q rows as loaded
   // ([64][RP] each), until every wave has its operand fragments.
-  constexpr int kRegion = DH * XP + CK * XP + 4 * 16 * 16;
+  constexpr int kRegion = DH * XP;  // halves; A (CK * FP * 2 halves) fits in it
+  static_assert(CK * FP * 2 <= kRegion, "A fits in region R");
+  constexpr int kTotal = kRegion + CK * FP * 2;
   constexpr int kStage = 2 * CK * RP;
-  __shared__ __attribute__((aligned(16))) uint16_t L[kRegion > kStage ? kRegion : kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t L[kTotal > kStage ? kTotal : kStage];
   __shared__ __attribute__((aligned(16))) float Gs[CK], Bs[CK], BGs[CK];  // G, b, b e^G
-  uint16_t* R = L;
-  uint16_t* Tn = L + DH * XP;              // T, bf16, row-major
-  uint16_t* Tdt = Tn + CK * XP;            // diagonal blocks, transposed
-  float* Ad = reinterpret_cast<float*>(R);       // [4][16][ADP]
-  uint16_t* Ao = R + 4 * 16 * ADP * 2;           // [64][XP], off-diagonal blocks of A
-  uint16_t* XT = R;
+  __shared__ float Tmax;  // max |T_ts|, s < t (the two-part flag)
+  float* Af = reinterpret_cast<float*>(L);            // A, f32, row-major [64][FP]
+  float* Tf = reinterpret_cast<float*>(L + kRegion);  // T, f32, row-major [64][FP]
+  uint16_t* XT = L;
 
   // Chunk-major order: the workgroups of one chunk index run together, so the
   // chain, which reads chunk 0 first, finds every head's data equally recent
@@ -228,10 +253,15 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   };
 
   // Gates for token `lane` (wave 0); padding tokens get g = 0, b = 0.
+  // g is floored at -kLogAlphaFloor: alpha = 0 (a = +inf, or an overflowing
+  // softplus) would give g = -inf and NaN differences G_t - G_s.  Every decay
+  // factor that spans such a token is then e^{<= -128}, which is 0 in f32, as
+  // alpha itself is; a NaN g stays NaN.
   if (w == 0) {
     float g = 0.0f, be = 0.0f;
     if (lane < n) {
       g = gate_log_alpha(a_raw, A_log[h], dt_bias[h]);
+      if (g < -kLogAlphaFloor) g = -kLogAlphaFloor;
       be = gate_beta(b_raw);
     }
     const float Gl = wave_scan(g, lane);
@@ -301,19 +331,27 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   auto kkt = [&](int st, int ss, int tb, int sb) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) acc = mfma16(f[st][kk], f[ss][kk], acc);
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kSplit) {
+        acc = mfma16(f[st][kk], fl[ss][kk], acc);
+        acc = mfma16(fl[st][kk], f[ss][kk], acc);
+      }
+      acc = mfma16(f[st][kk], f[ss][kk], acc);
+    }
     const int s = sb * 16 + li;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = tb * 16 + lg * 4 + r;
-      const float av = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * acc[r] : 0.0f;
-      if (sb == tb) Ad[(tb * 16 + lg * 4 + r) * ADP + li] = av;
-      else Ao[t * XP + s] = f2bf(av);
+      Af[t * FP + s] = (s < t) ? Bs[t] * __expf(Gs[t] - Gs[s]) * acc[r] : 0.0f;
     }
   };
   // (Q K^T)^T tile [s block sb][t block tb] from Q slot qs and K slot ks:
   // C[s][t] = K_s . Q_t -> P in the chain's fragment order.
-  auto qkt = [&](int qs, int ks, int tb, int sb) {
+  // The lo parts of this lane's P values wait in registers (slot = call
+  // number) until the inverse tells whether the chunk needs them.
+  u16x4 plo[4];
+  int poff[4];
+  auto qkt = [&](int qs, int ks, int tb, int sb, int slot) {
     f32x4 pq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -330,44 +368,56 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
       const int sq = sb * 16 + lg * 4 + r;
       pv[r] = (sq <= tq) ? q_scale * __expf(Gs[tq] - Gs[sq]) * pq[r] : 0.0f;
     }
-    st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tq, sb * 16 + lg * 4, 2), pv[0], pv[1],
-                  pv[2], pv[3]);
+    const int off = frag_off(tq, sb * 16 + lg * 4, 2);
+    u16x4 h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      h[r] = f2bf(pv[r]);
+      plo[slot][r] = f2bf(pv[r] - bf2f(h[r]));
+    }
+    *reinterpret_cast<u16x4*>(ws.P + chunk * (CK * CK) + off) = h;
+    poff[slot] = off;
   };
   // Zero tile of P above the diagonal at (tb, tb + 1): the chain reads (0,1)
   // and (2,3) of them (P is used in 32-column steps).
-  auto pzero = [&](int tb) {
-    st4<uint16_t>(ws.P + chunk * (CK * CK) + frag_off(tb * 16 + li, (tb + 1) * 16 + lg * 4, 2),
-                  0.f, 0.f, 0.f, 0.f);
+  auto pzero = [&](int tb, int slot) {
+    const int off = frag_off(tb * 16 + li, (tb + 1) * 16 + lg * 4, 2);
+    const u16x4 z = {0, 0, 0, 0};
+    *reinterpret_cast<u16x4*>(ws.P + chunk * (CK * CK) + off) = z;
+    plo[slot] = z;
+    poff[slot] = off;
   };
   if (w == 0) {
     kkt(0, 0, 0, 0); kkt(1, 0, 1, 0);
-    qkt(2, 0, 0, 0); qkt(3, 0, 1, 0); qkt(3, 1, 1, 1);
-    pzero(0);
+    qkt(2, 0, 0, 0, 0); qkt(3, 0, 1, 0, 1); qkt(3, 1, 1, 1, 2);
+    pzero(0, 3);
   } else if (w == 1) {
     kkt(0, 0, 1, 1); kkt(1, 0, 3, 1);
-    qkt(2, 0, 3, 1); qkt(2, 1, 3, 3);
+    qkt(2, 0, 3, 1, 0); qkt(2, 1, 3, 3, 1);
   } else if (w == 2) {
     kkt(2, 2, 2, 2); kkt(2, 0, 2, 0); kkt(2, 1, 2, 1);
-    qkt(3, 0, 2, 0); qkt(3, 1, 2, 1); qkt(3, 2, 2, 2);
-    pzero(2);
+    qkt(3, 0, 2, 0, 0); qkt(3, 1, 2, 1, 1); qkt(3, 2, 2, 2, 2);
+    pzero(2, 3);
   } else {
     kkt(2, 2, 3, 3); kkt(2, 0, 3, 0); kkt(2, 1, 3, 2);
-    qkt(3, 0, 3, 0); qkt(3, 1, 3, 2);
+    qkt(3, 0, 3, 0, 0); qkt(3, 1, 3, 2, 1);
   }
   load_v();
   lds_barrier();
 
-  // T, diagonal blocks (wave 0): lane (block lg, column li), forward
-  // substitution over the block's 16 rows in f32.
+  // T = (I + A)^{-1} in f32.  Diagonal blocks (wave 0): lane (block lg,
+  // column li), forward substitution over the block's 16 rows.  Waves 1-3
+  // zero the six blocks above the diagonal.
+  float tmax = 0.0f;  // wave 0: max |T_ts|, s < t
   if (w == 0) {
     float x[16];
-    const float* Ab = Ad + lg * 16 * ADP;
+    const float* Ab = Af + lg * 16 * FP + lg * 16;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       float acc = (t == li) ? 1.0f : 0.0f;
 #pragma unroll
       for (int s4 = 0; s4 < t; s4 += 4) {
-        const float4 a4 = *reinterpret_cast<const float4*>(Ab + t * ADP + s4);
+        const float4 a4 = *reinterpret_cast<const float4*>(Ab + t * FP + s4);
         acc = fmaf(-a4.x, x[s4], acc);
         if (s4 + 1 < t) acc = fmaf(-a4.y, x[s4 + 1], acc);
         if (s4 + 2 < t) acc = fmaf(-a4.z, x[s4 + 2], acc);
@@ -375,53 +425,97 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
       }
       x[t] = acc;
     }
-    u16x8 w0, w1;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const uint16_t xb = f2bf(x[t]);
-      Tn[(lg * 16 + t) * XP + lg * 16 + li] = xb;
-      if (t < 8) w0[t] = xb; else w1[t - 8] = xb;
+      Tf[(lg * 16 + t) * FP + lg * 16 + li] = x[t];
+      if (t > li) tmax = fmaxf(tmax, fabsf(x[t]));
     }
-    *reinterpret_cast<u16x8*>(&Tdt[(lg * 16 + li) * 16]) = w0;
-    *reinterpret_cast<u16x8*>(&Tdt[(lg * 16 + li) * 16 + 8]) = w1;
   } else {
-    // Waves 1-3 zero the six blocks above the diagonal (192 16-byte pieces).
-    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int idx = (w - 1) * 64 + lane;  // 0..191
+    const int idx = (w - 1) * 64 + lane;  // 0..191: 6 blocks x 16 rows x 2 halves
     const int blk = idx >> 5, row = (idx & 31) >> 1, half = idx & 1;
     const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
     const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-    *reinterpret_cast<u16x8*>(&Tn[(bi * 16 + row) * XP + bj * 16 + half * 8]) = z8;
+    float* dst = &Tf[(bi * 16 + row) * FP + bj * 16 + half * 8];
+    *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   lds_barrier();
 
   // T, off-diagonal blocks (wave 0): T_ij = -T_ii sum_{j<=m<i} A_im T_mj,
-  // level by level; each product's result feeds the next as a B operand.
+  // level by level, each product on 16x16x16 MFMA with both f32 operands
+  // split into bf16 hi + lo parts (hi*hi + hi*lo + lo*hi: ~16-bit operands,
+  // f32 accumulation).  A result (D layout) is the B layout of the next
+  // product, so the levels chain in registers.
   if (w == 0) {
-    auto Aof = [&](int i, int j) { return ld_frag4(&Ao[(i * 16 + li) * XP + j * 16 + lg * 4]); };
-    auto Tdiag_b = [&](int j) { return ld_frag4(&Tdt[(j * 16 + li) * 16 + lg * 4]); };
-    auto Tdiag_a = [&](int i) { return ld_frag4(&Tn[(i * 16 + li) * XP + i * 16 + lg * 4]); };
-    auto finish = [&](int i, int j, const f32x4& xsum, s16x4& keep) {
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-      y = mfma16k16(Tdiag_a(i), to_s16x4(xsum[0], xsum[1], xsum[2], xsum[3]), y);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Tn[(i * 16 + lg * 4 + r) * XP + j * 16 + li] = f2bf(-y[r]);
-      keep = to_s16x4(-y[0], -y[1], -y[2], -y[3]);
+    auto split_frag = [](float a, float b, float c, float d, s16x4& hi, s16x4& lo) {
+      hi = to_s16x4(a, b, c, d);
+      lo = to_s16x4(a - bf2f((uint16_t)hi[0]), b - bf2f((uint16_t)hi[1]),
+                    c - bf2f((uint16_t)hi[2]), d - bf2f((uint16_t)hi[3]));
+    };
+    struct Frag { s16x4 hi, lo; };
+    // A operand: rows of block (i, j) of an f32 LDS matrix, 4 columns per lane.
+    auto a_op = [&](const float* M, int i, int j) {
+      const float4 v = *reinterpret_cast<const float4*>(&M[(i * 16 + li) * FP + j * 16 + lg * 4]);
+      Frag f;
+      split_frag(v.x, v.y, v.z, v.w, f.hi, f.lo);
+      return f;
+    };
+    // B operand: 4 rows of one column of block (j, j) of T.
+    auto b_diag = [&](int j) {
+      const float* c = &Tf[(j * 16 + lg * 4) * FP + j * 16 + li];
+      Frag f;
+      split_frag(c[0], c[FP], c[2 * FP], c[3 * FP], f.hi, f.lo);
+      return f;
+    };
+    auto b_reg = [&](const f32x4& v) {
+      Frag f;
+      split_frag(v[0], v[1], v[2], v[3], f.hi, f.lo);
+      return f;
+    };
+    auto mul = [&](const Frag& a, const Frag& b, f32x4 acc) {
+      acc = mfma16k16(a.lo, b.hi, acc);
+      acc = mfma16k16(a.hi, b.lo, acc);
+      return mfma16k16(a.hi, b.hi, acc);
     };
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    s16x4 t10, t21, t32, t20, t31, t30;
-    finish(1, 0, mfma16k16(Aof(1, 0), Tdiag_b(0), z), t10);
-    finish(2, 1, mfma16k16(Aof(2, 1), Tdiag_b(1), z), t21);
-    finish(3, 2, mfma16k16(Aof(3, 2), Tdiag_b(2), z), t32);
-    finish(2, 0, mfma16k16(Aof(2, 1), t10, mfma16k16(Aof(2, 0), Tdiag_b(0), z)), t20);
-    finish(3, 1, mfma16k16(Aof(3, 2), t21, mfma16k16(Aof(3, 1), Tdiag_b(1), z)), t31);
+    // T_ij = -T_ii X, stored to LDS; returned for the next levels.
+    auto finish = [&](int i, int j, const f32x4& X) {
+      const f32x4 y = mul(a_op(Tf, i, i), b_reg(X), z);
+      f32x4 t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        t[r] = -y[r];
+        Tf[(i * 16 + lg * 4 + r) * FP + j * 16 + li] = t[r];
+        tmax = fmaxf(tmax, fabsf(t[r]));
+      }
+      return t;
+    };
+    const Frag t00 = b_diag(0), t11 = b_diag(1), t22 = b_diag(2);
+    const f32x4 t10 = finish(1, 0, mul(a_op(Af, 1, 0), t00, z));
+    const f32x4 t21 = finish(2, 1, mul(a_op(Af, 2, 1), t11, z));
+    const f32x4 t32 = finish(3, 2, mul(a_op(Af, 3, 2), t22, z));
+    const f32x4 t20 =
+        finish(2, 0, mul(a_op(Af, 2, 1), b_reg(t10), mul(a_op(Af, 2, 0), t00, z)));
+    const f32x4 t31 =
+        finish(3, 1, mul(a_op(Af, 3, 2), b_reg(t21), mul(a_op(Af, 3, 1), t11, z)));
     finish(3, 0,
-           mfma16k16(Aof(3, 2), t20,
-                     mfma16k16(Aof(3, 1), t10, mfma16k16(Aof(3, 0), Tdiag_b(0), z))),
-           t30);
-    (void)t32; (void)t31; (void)t30;
+           mul(a_op(Af, 3, 2), b_reg(t20),
+               mul(a_op(Af, 3, 1), b_reg(t10), mul(a_op(Af, 3, 0), t00, z))));
+    (void)t32; (void)t31;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+    if (lane == 0) Tmax = tmax;
   }
   lds_barrier();
+  const bool split = Tmax > kSplitThreshold;
+  if (tid == 0) ws.F[chunk] = split ? 1 : 0;
+  if (split) {
+    const int nslots = (w == 0 || w == 2) ? 4 : 2;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+      if (sl < nslots)
+        *reinterpret_cast<u16x4*>(ws.PL + chunk * (CK * CK) + poff[sl]) = plo[sl];
+  }
 
   // K^T of token block w into LDS (the A blocks are no longer needed); K
   // block w is in slot 0 for waves 0 and 1 and in slot 2 for waves 2 and 3.
@@ -464,21 +558,27 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   }
 
   // Rows of T scaled by a per-column factor (b gamma for W, b for Ut), as an
-  // MFMA operand, read from LDS when needed.
-  auto trow = [&](int tb, int kk, const float* colscale) {
-    const u16x8 raw = *reinterpret_cast<const u16x8*>(&Tn[(tb * 16 + li) * XP + kk * 32 + lg * 8]);
+  // MFMA operand in two bf16 parts (hi + lo), read from LDS when needed.
+  auto trow = [&](int tb, int kk, const float* colscale, bf16x8& hi, bf16x8& lo) {
+    const float* row = &Tf[(tb * 16 + li) * FP + kk * 32 + lg * 8];
+    const float4 r0 = *reinterpret_cast<const float4*>(row);
+    const float4 r1 = *reinterpret_cast<const float4*>(row + 4);
     const float4 s0 = *reinterpret_cast<const float4*>(&colscale[kk * 32 + lg * 8]);
     const float4 s1 = *reinterpret_cast<const float4*>(&colscale[kk * 32 + lg * 8 + 4]);
-    const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-    bf16x8 f;
+    const float v[8] = {r0.x * s0.x, r0.y * s0.y, r0.z * s0.z, r0.w * s0.w,
+                        r1.x * s1.x, r1.y * s1.y, r1.z * s1.z, r1.w * s1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (__bf16)(bf2f(raw[i]) * sc[i]);
-    return f;
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)v[i];
+      hi[i] = h;
+      lo[i] = (__bf16)(v[i] - (float)h);
+    }
   };
 
   // W^T tiles [dk block][t block] = K^T (T diag(b gamma))^T, stored as Wf;
   // wave w takes dk blocks 2w and 2w+1.  T is lower triangular, so t blocks 0
-  // and 1 need only s < 32.
+  // and 1 need only s < 32.  K is exact in bf16; T diag(b gamma) takes two
+  // parts.
   {
     bf16x8 kt[2][2];
 #pragma unroll
@@ -488,11 +588,14 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
         kt[d][kk] = ld_frag(&XT[((2 * w + d) * 16 + li) * XP + kk * 32 + lg * 8]);
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const bf16x8 tg0 = trow(tb, 0, BGs);
-      const bf16x8 tg1 = tb >= 2 ? trow(tb, 1, BGs) : zero_frag();
+      bf16x8 tg0, tg0l, tg1, tg1l;
+      trow(tb, 0, BGs, tg0, tg0l);
+      if (tb >= 2) trow(tb, 1, BGs, tg1, tg1l);
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16(kt[d][0], tg0l, acc);
+        if (tb >= 2) acc = mfma16(kt[d][1], tg1l, acc);
         acc = mfma16(kt[d][0], tg0, acc);
         if (tb >= 2) acc = mfma16(kt[d][1], tg1, acc);
         const int t = tb * 16 + li, dk = (2 * w + d) * 16 + lg * 4;
@@ -522,21 +625,25 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
       vt[d][kk] = ld_frag(&XT[((2 * w + d) * 16 + li) * XP + kk * 32 + lg * 8]);
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
-    const bf16x8 tb0 = trow(tb, 0, Bs);
-    const bf16x8 tb1 = tb >= 2 ? trow(tb, 1, Bs) : zero_frag();
+    bf16x8 tb0, tb0l, tb1, tb1l;
+    trow(tb, 0, Bs, tb0, tb0l);
+    if (tb >= 2) trow(tb, 1, Bs, tb1, tb1l);
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const int vb = 2 * w + d;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16(tb0l, vt[d][0], acc);
+      if (tb >= 2) acc = mfma16(tb1l, vt[d][1], acc);
       acc = mfma16(tb0, vt[d][0], acc);
       if (tb >= 2) acc = mfma16(tb1, vt[d][1], acc);
       // Utf[sl = vb / 2][w = tb][cvb][cli + 16 lg][0..3] with dvp(cvb, cli) = the
       // column within the slice, 16 (vb % 2) + li.
       const int col = 16 * (vb & 1) + li;
       const int cvb = (col >> 2) & 1, cli = 4 * (col >> 3) + (col & 3);
-      st4<uint16_t>(ws.Ut + chunk * (CK * DH) + ((vb >> 1) * 4 + tb) * 512 + cvb * 256 +
-                        (cli + 16 * lg) * 4,
-                    acc[0], acc[1], acc[2], acc[3]);
+      const int64_t off =
+          chunk * (CK * DH) + ((vb >> 1) * 4 + tb) * 512 + cvb * 256 + (cli + 16 * lg) * 4;
+      if (split) st4_split(ws.Ut + off, ws.UtL + off, acc[0], acc[1], acc[2], acc[3]);
+      else st4<uint16_t>(ws.Ut + off, acc[0], acc[1], acc[2], acc[3]);
     }
   }
 }
@@ -561,18 +668,29 @@ __device__ __forceinline__ int dvp2(int u, int m) { return 32 * (u >> 1) + dvp(u
 
 template <int NV>
 struct StateRegs {
-  bf16x8 w[4];       // W[16w + li][32kk + 8lg ..]
-  bf16x8 kt[2][2];   // K^T[32w + 16i + li][32kk + 8lg ..]
-  u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + dvp2(u, li)]
-  f32x4 gu;          // G[16w + 4lg ..]
-  float gl;          // G_last
+  bf16x8 w[4];        // W[16w + li][32kk + 8lg ..]
+  bf16x8 kt[2][2];    // K^T[32w + 16i + li][32kk + 8lg ..]
+  u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + dvp2(u, li)], hi part
+  f32x4 gu;           // G[16w + 4lg ..]
+  float gl;           // G_last
+  int split;          // the chunk's two-part flag (read with flag_set)
 };
 
 struct OutRegs {
-  bf16x8 q[4];  // Q[16w + li][32kk + 8lg ..]
-  bf16x8 p[2];  // P[16w + li][32kk + 8lg ..]
-  float gt;     // G[16w + li]
+  bf16x8 q[4];   // Q[16w + li][32kk + 8lg ..]
+  bf16x8 p[2];   // P[16w + li][32kk + 8lg ..], hi part
+  float gt;      // G[16w + li]
+  int split;     // the chunk's two-part flag (read with flag_set)
 };
+
+// The chunk's two-part flag, loaded with the chunk's other operands and
+// read (made wave-uniform) in the chunk's own step.
+__device__ __forceinline__ int chunk_flag(const WsLayout& ws, int64_t chunk) {
+  return ws.F[chunk];
+}
+__device__ __forceinline__ bool flag_set(int raw) {
+  return __builtin_amdgcn_readfirstlane(raw) != 0;
+}
 
 __device__ __forceinline__ bf16x8 gld_frag(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -595,13 +713,29 @@ __device__ __forceinline__ void state_fetch(StateRegs<NV>& R, const WsLayout& ws
   // Ut is stored per 32-column piece (the prep's Utf[piece][w][vb]).
 #pragma unroll
   for (int u = 0; u < NV / 16; ++u) {
-    const uint16_t* up = ws.Ut + chunk * (CK * DH) + ((sl * (NV / 32) + (u >> 1)) * 4 + w) * 512 +
-                         (u & 1) * 256 + lane * 4;
-    R.ut[u] = *reinterpret_cast<const u16x4*>(up);
+    const int64_t off = chunk * (CK * DH) + ((sl * (NV / 32) + (u >> 1)) * 4 + w) * 512 +
+                        (u & 1) * 256 + lane * 4;
+    R.ut[u] = *reinterpret_cast<const u16x4*>(ws.Ut + off);
   }
   const float* gp = ws.G + chunk * 2 * CK;
   R.gu = *reinterpret_cast<const f32x4*>(gp + 16 * w + 4 * (lane >> 4));
   R.gl = gp[CK + (lane & 15)];  // G_last, replicated
+  R.split = chunk_flag(ws, chunk);
+}
+
+// The lo part of Ut for a two-part chunk, loaded in the chunk's own step and
+// used at once: a load for a later step, issued only for some chunks, would
+// leave the compiler's count of loads in flight inexact for every chunk.
+template <int NV>
+__device__ __forceinline__ void state_fetch_lo(u16x4* utl, const WsLayout& ws, int bh, int c,
+                                               int NC, int sl, int w, int lane) {
+  const int64_t chunk = (int64_t)bh * NC + c;
+#pragma unroll
+  for (int u = 0; u < NV / 16; ++u) {
+    const int64_t off = chunk * (CK * DH) + ((sl * (NV / 32) + (u >> 1)) * 4 + w) * 512 +
+                        (u & 1) * 256 + lane * 4;
+    utl[u] = *reinterpret_cast<const u16x4*>(ws.UtL + off);
+  }
 }
 
 // Q comes from the prep's fragment-order bf16 copy: reading the input rows
@@ -616,50 +750,42 @@ __device__ __forceinline__ void out_fetch(OutRegs& R, const WsLayout& ws, int bb
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) R.q[kk] = gld_frag(qp + kk * 512);
   // P is causal: token blocks 0 and 1 use only its first 32 columns.
-  const uint16_t* pp = ws.P + chunk * (CK * CK) + (w * 2 * 64 + lane) * 8;
-  R.p[0] = gld_frag(pp);
+  const int64_t po = chunk * (CK * CK) + (w * 2 * 64 + lane) * 8;
+  R.p[0] = gld_frag(ws.P + po);
   // Loaded unconditionally (waves 0 and 1 reload the first tile and ignore
   // it), so the compiler's count of loads in flight stays exact.
-  R.p[1] = gld_frag(pp + (w >= 2 ? 512 : 0));
+  R.p[1] = gld_frag(ws.P + po + (w >= 2 ? 512 : 0));
   R.gt = ws.G[chunk * 2 * CK + 16 * w + li];
+  R.split = chunk_flag(ws, chunk);
 }
 
-// NV = 32 or 64 value columns per slice.  Each wave loads its operands two
-// chunks ahead (three register sets in rotation), which needs up to 256
-// VGPRs, so one workgroup runs per CU.
-constexpr int DEPTH = 2;
+// The lo part of P for a two-part chunk, loaded in the chunk's own step (as
+// state_fetch_lo).
+__device__ __forceinline__ void out_fetch_lo(bf16x8* pl, const WsLayout& ws, int bh, int c,
+                                             int NC, int w, int lane) {
+  const int64_t po = ((int64_t)bh * NC + c) * (CK * CK) + (w * 2 * 64 + lane) * 8;
+  pl[0] = gld_frag(ws.PL + po);
+  pl[1] = gld_frag(ws.PL + po + (w >= 2 ? 512 : 0));
+}
 
+// NV = 32 or 64 value columns per slice.  Each wave loads its operands
+// kDepth chunks ahead (kDepth + 1 register sets in rotation): two with 32
+// columns, one with 64, whose larger state and U tiles leave no room for a
+// third set in the 256 VGPRs a wave has with one workgroup per CU.
+template <int NV>
+constexpr int chain_depth() { return 2; }
+
+// One row's chain (state and output waves), as the kernel below sets it up.
 template <int NV, typename TO>
-__global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
-    WsLayout ws, const float* state_in,
-    float* state_out, TO* __restrict__ o, int B, int T, const int32_t* __restrict__ cu,
-    int total, int Hk, int Hv, int NC, float q_scale) {
-  constexpr int NSL = DH / NV;  // slices per head
+__device__ __forceinline__ void chain_run(const WsLayout& ws, const float* state_in,
+                                          float* state_out, TO* __restrict__ o, int Hk, int Hv,
+                                          int NC, float q_scale, int bb, int bh, int h, int kh,
+                                          int sl, int64_t tbase, int tlen, uint16_t* Sb,
+                                          uint16_t* Utl, uint16_t* UtlL, uint16_t* Usl,
+                                          uint16_t* UslL) {
   constexpr int NVB = NV / 16;  // 16-column blocks per slice
-  static_assert(NV == 32 || NV == 64, "slices are one or two 32-column pieces");
-  __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * RP];   // S slice [dv][dk], bf16
-  __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];  // U^T [dv][s]
-  __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];  // U^T [dv][s] * e^{G_last - G_s}
-
-  // The NSL slices of a head, and the heads of a q/k group, run on one XCD
-  // and share its L2 for W, P, K^T, G and Q; groups are dealt round-robin
-  // over the XCDs (rows of a ragged batch spread evenly).
-  const int id = blockIdx.x;
-  int hs, sl;
-  if (((B * Hk) & 7) == 0) {
-    const int u = xcd_head(id, B * Hk, Hv / Hk, NSL);
-    hs = u / NSL;
-    sl = u % NSL;
-  } else {
-    hs = (id >> 3) / NSL * 8 + (id & 7);
-    sl = (id >> 3) % NSL;
-  }
-  if (hs >= B * Hv) return;
-  const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
+  constexpr int kDepth = chain_depth<NV>();
   const int dv0 = sl * NV;
-  int64_t tbase;
-  int tlen;
-  row_span(cu, total, bb, T, tbase, tlen);
   const int ncr = (tlen + CK - 1) / CK;  // this row's chunks (NC is the workspace stride)
   // Chunk index for a fetch ahead: past the row's last chunk the loads repeat
   // it (an empty row loads chunk 0 and uses nothing).
@@ -671,7 +797,7 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
   if (state_wave) {
     StateRegs<NV> RA, RB, RC;
     state_fetch<NV>(RA, ws, bb, bh, kh, 0, Hk, NC, sl, w, lane);
-    state_fetch<NV>(RB, ws, bb, bh, kh, ahead(1), Hk, NC, sl, w, lane);
+    if (kDepth == 2) state_fetch<NV>(RB, ws, bb, bh, kh, ahead(1), Hk, NC, sl, w, lane);
 
     f32x4 H[2][NVB];  // H[dk = 16(2w+i) + 4lg + r][dv = dv0 + 16vb + li]
 #pragma unroll
@@ -697,7 +823,8 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
     auto step = [&](const StateRegs<NV>& R, StateRegs<NV>& next, int c) {
       // Scheduling fence: no work of one chunk step moves into another.
       __builtin_amdgcn_sched_barrier(0);
-      state_fetch<NV>(next, ws, bb, bh, kh, ahead(c + DEPTH), Hk, NC, sl, w, lane);
+      const int cn = ahead(c + kDepth);
+      state_fetch<NV>(next, ws, bb, bh, kh, cn, Hk, NC, sl, w, lane);
       // (1) U = Ut - W H against the bf16 state copy, dv rows in dvp order.
       f32x4 accU[NVB];
 #pragma unroll
@@ -707,24 +834,43 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb)
           accU[vb] = mfma16(R.w[kk], ld_frag(&Sb[dvp2(vb, li) * RP + kk * 32 + lg * 8]), accU[vb]);
-      // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.
-      {
-        const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
-                             __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
+      // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.  A two-part
+      // chunk also adds Ut's lo part (loaded here, in its own step) and
+      // writes the lo parts of both copies.
+      const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
+                           __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
+      float u[NVB][4];
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[vb][r] = bf2f(R.ut[vb][r]) - accU[vb][r];
+      const bool two = flag_set(R.split);
+      if (two) {
+        u16x4 utl[NVB];
+        state_fetch_lo<NV>(utl, ws, bh, c, NC, sl, w, lane);
 #pragma unroll
         for (int vb = 0; vb < NVB; ++vb) {
           const int off = dvp2(vb, li) * XP + w * 16 + lg * 4;
-          float u[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) u[r] = bf2f(R.ut[vb][r]) - accU[vb][r];
-          st4<uint16_t>(&Utl[off], u[0], u[1], u[2], u[3]);
-          st4<uint16_t>(&Usl[off], u[0] * sc[0], u[1] * sc[1], u[2] * sc[2], u[3] * sc[3]);
+          for (int r = 0; r < 4; ++r) u[vb][r] += bf2f(utl[vb][r]);
+          st4_split(&Utl[off], &UtlL[off], u[vb][0], u[vb][1], u[vb][2], u[vb][3]);
+          st4_split(&Usl[off], &UslL[off], u[vb][0] * sc[0], u[vb][1] * sc[1], u[vb][2] * sc[2],
+                    u[vb][3] * sc[3]);
+        }
+      } else {
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          const int off = dvp2(vb, li) * XP + w * 16 + lg * 4;
+          st4<uint16_t>(&Utl[off], u[vb][0], u[vb][1], u[vb][2], u[vb][3]);
+          st4<uint16_t>(&Usl[off], u[vb][0] * sc[0], u[vb][1] * sc[1], u[vb][2] * sc[2],
+                        u[vb][3] * sc[3]);
         }
       }
       lds_barrier();
-      // (3) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U, then its bf16
-      // copy for the next chunk (every wave finished reading the old copy
-      // before the barrier above).
+      // (3) H <- gamma_last H + K^T diag(e^{G_last - G_s}) U (for a two-part
+      // chunk also + K^T of U's lo part), then its bf16 copy for the next
+      // chunk (every wave finished reading the old copy before the barrier
+      // above).
       const float gl = __expf(R.gl);
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
@@ -740,6 +886,18 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
           H[i][vb] = hcur;
         }
       }
+      if (two) {
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          const bf16x8 u0l = ld_frag(&UslL[(vb * 16 + li) * XP + lg * 8]);
+          const bf16x8 u1l = ld_frag(&UslL[(vb * 16 + li) * XP + 32 + lg * 8]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            H[i][vb] = mfma16(R.kt[i][0], u0l, H[i][vb]);
+            H[i][vb] = mfma16(R.kt[i][1], u1l, H[i][vb]);
+          }
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -749,13 +907,21 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
       lds_barrier();
     };
     int c = 0;
-    for (; c + 3 <= ncr; c += 3) {
-      step(RA, RC, c);
-      step(RB, RA, c + 1);
-      step(RC, RB, c + 2);
+    if constexpr (kDepth == 2) {
+      for (; c + 3 <= ncr; c += 3) {
+        step(RA, RC, c);
+        step(RB, RA, c + 1);
+        step(RC, RB, c + 2);
+      }
+      if (c < ncr) step(RA, RC, c);
+      if (c + 1 < ncr) step(RB, RA, c + 1);
+    } else {
+      for (; c + 2 <= ncr; c += 2) {
+        step(RA, RB, c);
+        step(RB, RA, c + 1);
+      }
+      if (c < ncr) step(RA, RB, c);
     }
-    if (c < ncr) step(RA, RC, c);
-    if (c + 1 < ncr) step(RB, RA, c + 1);
 
     if (state_out) {
 #pragma unroll
@@ -772,7 +938,7 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
     const int tr = w * 16 + li;
     OutRegs RA, RB, RC;
     out_fetch(RA, ws, bb, bh, kh, 0, Hk, NC, w, lane);
-    out_fetch(RB, ws, bb, bh, kh, ahead(1), Hk, NC, w, lane);
+    if (kDepth == 2) out_fetch(RB, ws, bb, bh, kh, ahead(1), Hk, NC, w, lane);
     lds_barrier();
     // `full` (std::true_type) marks a chunk of CK tokens, whose store needs no
     // row check.
@@ -791,22 +957,42 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
       // the step they queue behind the state waves' loads, and (Q H)^T gates
       // the first barrier.
       __builtin_amdgcn_sched_barrier(0);
-      out_fetch(next, ws, bb, bh, kh, ahead(c + DEPTH), Hk, NC, w, lane);
+      const int cn = ahead(c + kDepth);
+      out_fetch(next, ws, bb, bh, kh, cn, Hk, NC, w, lane);
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       // O^T = q_scale gamma_t (Q H)^T + U^T P^T; P is causal, so token blocks
       // 0 and 1 need only s < 32.  Lane (li, lg) ends with dv 8lg..8lg+7 of
-      // token 16w + li (dvp order), one 8-wide store.
+      // token 16w + li (dvp order), one 8-wide store.  A two-part chunk adds
+      // the lo-part products (loaded here, in its own step): (Uh + Ul)(Ph + Pl)
+      // without Ul Pl.
       const float gq = q_scale * __expf(R.gt);
-      float ov[4 * NVB];
+      f32x4 acc[NVB];
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(ld_frag(&Utl[dvp2(vb, li) * XP + lg * 8]), R.p[0], acc);
-        if (w >= 2) acc = mfma16(ld_frag(&Utl[dvp2(vb, li) * XP + 32 + lg * 8]), R.p[1], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ov[4 * vb + r] = fmaf(gq, accQ[vb][r], acc[r]);
+        const int ro = dvp2(vb, li) * XP + lg * 8;
+        acc[vb] = mfma16(ld_frag(&Utl[ro]), R.p[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        if (w >= 2) acc[vb] = mfma16(ld_frag(&Utl[ro + 32]), R.p[1], acc[vb]);
       }
+      if (flag_set(R.split)) {
+        bf16x8 pl[2];
+        out_fetch_lo(pl, ws, bh, c, NC, w, lane);
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+          const int ro = dvp2(vb, li) * XP + lg * 8;
+          acc[vb] = mfma16(ld_frag(&UtlL[ro]), R.p[0], acc[vb]);
+          acc[vb] = mfma16(ld_frag(&Utl[ro]), pl[0], acc[vb]);
+          if (w >= 2) {
+            acc[vb] = mfma16(ld_frag(&UtlL[ro + 32]), R.p[1], acc[vb]);
+            acc[vb] = mfma16(ld_frag(&Utl[ro + 32]), pl[1], acc[vb]);
+          }
+        }
+      }
+      float ov[4 * NVB];
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[4 * vb + r] = fmaf(gq, accQ[vb][r], acc[vb][r]);
       const int t0 = c * CK;
       if (decltype(full)::value || tr < min(CK, tlen - t0)) {
 #pragma unroll
@@ -817,15 +1003,62 @@ __global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
     };
     int c = 0;
     const int nfull = tlen / CK;
-    for (; c + 3 <= nfull; c += 3) {
-      step(RA, RC, c, std::true_type{});
-      step(RB, RA, c + 1, std::true_type{});
-      step(RC, RB, c + 2, std::true_type{});
+    if constexpr (kDepth == 2) {
+      for (; c + 3 <= nfull; c += 3) {
+        step(RA, RC, c, std::true_type{});
+        step(RB, RA, c + 1, std::true_type{});
+        step(RC, RB, c + 2, std::true_type{});
+      }
+      if (c < ncr) step(RA, RC, c, std::false_type{});
+      if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
+      if (c + 2 < ncr) step(RC, RB, c + 2, std::false_type{});
+    } else {
+      for (; c + 2 <= nfull; c += 2) {
+        step(RA, RB, c, std::true_type{});
+        step(RB, RA, c + 1, std::true_type{});
+      }
+      if (c < ncr) step(RA, RB, c, std::false_type{});
+      if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
     }
-    if (c < ncr) step(RA, RC, c, std::false_type{});
-    if (c + 1 < ncr) step(RB, RA, c + 1, std::false_type{});
-    if (c + 2 < ncr) step(RC, RB, c + 2, std::false_type{});
   }
+}
+
+template <int NV, typename TO>
+__global__ __launch_bounds__(CH_THREADS, 2) void chunk_chain_kernel(
+    WsLayout ws, const float* state_in,
+    float* state_out, TO* __restrict__ o, int B, int T, const int32_t* __restrict__ cu,
+    int total, int Hk, int Hv, int NC, float q_scale) {
+  constexpr int NSL = DH / NV;  // slices per head
+  static_assert(NV == 32 || NV == 64, "slices are one or two 32-column pieces");
+  // U^T goes through LDS as bf16, for two-part chunks with a second bf16
+  // part (lo): the state update and the output sum U over a chunk's tokens,
+  // sums that cancel when keys are nearly parallel.
+  __shared__ __attribute__((aligned(16))) uint16_t Sb[NV * RP];    // S slice [dv][dk], bf16
+  __shared__ __attribute__((aligned(16))) uint16_t Utl[NV * XP];   // U^T [dv][s], hi
+  __shared__ __attribute__((aligned(16))) uint16_t UtlL[NV * XP];  // U^T [dv][s], lo
+  __shared__ __attribute__((aligned(16))) uint16_t Usl[NV * XP];   // U^T e^{G_last - G_s}, hi
+  __shared__ __attribute__((aligned(16))) uint16_t UslL[NV * XP];  // U^T e^{G_last - G_s}, lo
+
+  // The NSL slices of a head, and the heads of a q/k group, run on one XCD
+  // and share its L2 for W, P, K^T, G and Q; groups are dealt round-robin
+  // over the XCDs (rows of a ragged batch spread evenly).
+  const int id = blockIdx.x;
+  int hs, sl;
+  if (((B * Hk) & 7) == 0) {
+    const int u = xcd_head(id, B * Hk, Hv / Hk, NSL);
+    hs = u / NSL;
+    sl = u % NSL;
+  } else {
+    hs = (id >> 3) / NSL * 8 + (id & 7);
+    sl = (id >> 3) % NSL;
+  }
+  if (hs >= B * Hv) return;
+  const int bh = hs, bb = bh / Hv, h = bh % Hv, kh = h / (Hv / Hk);
+  int64_t tbase;
+  int tlen;
+  row_span(cu, total, bb, T, tbase, tlen);
+  chain_run<NV, TO>(ws, state_in, state_out, o, Hk, Hv, NC, q_scale, bb, bh, h, kh, sl, tbase,
+                    tlen, Sb, Utl, UtlL, Usl, UslL);
 }
 
 namespace {
@@ -893,14 +1126,11 @@ hipError_t launch_prefill_chunked(const void* q, int64_t q_ts, const void* k, in
   if (qk_dt == 1 && v_dt == 1)
     launch_prep_g<uint16_t, uint16_t>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias,
                                       ws, B, T, cu, total, Hk, Hv, NC, q_scale, stream);
-  else if (qk_dt == 0 && v_dt == 0)
-    launch_prep_g<float, float>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws, B,
-                                T, cu, total, Hk, Hv, NC, q_scale, stream);
   else if (qk_dt == 0 && v_dt == 1)
     launch_prep_g<float, uint16_t>(gate_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, ws,
                                    B, T, cu, total, Hk, Hv, NC, q_scale, stream);
   else
-    return hipErrorInvalidValue;  // bf16 q/k with f32 v is not instantiated
+    return hipErrorInvalidValue;  // other combinations are not instantiated
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (o_dt == 1)

@@ -6,7 +6,9 @@
 // Mapping: a 128-wide head row is 16 lanes x 8 elements (16-byte bf16 loads);
 // the mean of squares is a DPP row reduction.  Each 16-lane group handles
 // NORM_ROWS rows with all loads issued first.  HBM-bound: read x and z once,
-// write y once.
+// write y once.  y may equal x (the whole mixer normalises its output in
+// place), so x and y are not declared restrict: each lane reads its elements
+// of a row before it writes them, and no lane touches another lane's.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,7 +20,7 @@ constexpr int NORM_ROWS_PER_WG = NORM_THREADS / 16 * NORM_ROWS;
 
 template <typename T>
 __global__ __launch_bounds__(NORM_THREADS) void gated_rmsnorm_kernel(
-    const T* __restrict__ x, const T* __restrict__ z, T* __restrict__ y,
+    const T* x, const T* __restrict__ z, T* y,
     const float* __restrict__ w, int64_t rows, float eps) {
   const int lane16 = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;

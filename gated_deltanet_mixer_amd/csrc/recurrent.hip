@@ -184,8 +184,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void recurrent_prefill_kernel(
     const T* __restrict__ q, int64_t q_ts, const T* __restrict__ k, int64_t k_ts,
     const T* __restrict__ v, int64_t v_ts, const G* __restrict__ a, const G* __restrict__ b,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias,
-    const float* state_in, float* state_out, TO* __restrict__ o, int Tlen, int Hk, int Hv,
-    float q_scale) {
+    const float* state_in, float* state_out, TO* __restrict__ o, int Tlen,
+    const int32_t* __restrict__ cu, int total, int Hk, int Hv, float q_scale) {
   __shared__ float ks[SEQ_TT][128];
   __shared__ float qs[SEQ_TT][128];
   __shared__ float vs[SEQ_TT][16];
@@ -208,15 +208,26 @@ __global__ __launch_bounds__(SEQ_THREADS) void recurrent_prefill_kernel(
     for (int i = 0; i < 8; ++i) s[i] = 0.0f;
   }
 
-  const T* qb = q + (int64_t)bb * Tlen * q_ts + kh * 128;
-  const T* kb = k + (int64_t)bb * Tlen * k_ts + kh * 128;
-  const T* vb = v + (int64_t)bb * Tlen * v_ts + h * 128 + blk * 16;
-  const G* ab = a + (int64_t)bb * Tlen * Hv + h;
-  const G* bbp = b + (int64_t)bb * Tlen * Hv + h;
-  TO* obp = o + ((int64_t)bb * Tlen * Hv + h) * 128 + row;
+  // Row bb's tokens: Tlen at stride Tlen, or with cu (device [B + 1] offsets
+  // into a packed axis of `total` tokens) [cu[bb], cu[bb+1]), at most Tlen of
+  // them; offsets are clamped into [0, total].
+  int64_t tbase = (int64_t)bb * Tlen;
+  int tlen = Tlen;
+  if (cu != nullptr) {
+    const int s0 = max(0, min(cu[bb], total));
+    const int e0 = max(s0, min(cu[bb + 1], total));
+    tbase = s0;
+    tlen = min(e0 - s0, Tlen);
+  }
+  const T* qb = q + tbase * q_ts + kh * 128;
+  const T* kb = k + tbase * k_ts + kh * 128;
+  const T* vb = v + tbase * v_ts + h * 128 + blk * 16;
+  const G* ab = a + tbase * Hv + h;
+  const G* bbp = b + tbase * Hv + h;
+  TO* obp = o + (tbase * Hv + h) * 128 + row;
 
-  for (int t0 = 0; t0 < Tlen; t0 += SEQ_TT) {
-    const int n = min(SEQ_TT, Tlen - t0);
+  for (int t0 = 0; t0 < tlen; t0 += SEQ_TT) {
+    const int n = min(SEQ_TT, tlen - t0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int tt = grp + 16 * half;
@@ -343,45 +354,47 @@ template <typename T, typename G, typename TO>
 static void launch_seq_t(const void* q, int64_t q_ts, const void* k, int64_t k_ts, const void* v,
                          int64_t v_ts, const void* a, const void* b, const float* A_log,
                          const float* dt_bias, const float* state_in, float* state_out, void* o,
-                         int B, int Tlen, int Hk, int Hv, float q_scale, hipStream_t stream) {
+                         int B, int Tlen, const int32_t* cu, int total, int Hk, int Hv,
+                         float q_scale, hipStream_t stream) {
   hipLaunchKernelGGL((recurrent_prefill_kernel<T, G, TO>), dim3(B * Hv * 8), dim3(SEQ_THREADS), 0,
                      stream, (const T*)q, q_ts, (const T*)k, k_ts, (const T*)v, v_ts, (const G*)a,
-                     (const G*)b, A_log, dt_bias, state_in, state_out, (TO*)o, Tlen, Hk, Hv,
-                     q_scale);
+                     (const G*)b, A_log, dt_bias, state_in, state_out, (TO*)o, Tlen, cu, total,
+                     Hk, Hv, q_scale);
 }
 
 template <typename T, typename G>
 static void launch_seq_o(int o_dt, const void* q, int64_t q_ts, const void* k, int64_t k_ts,
                          const void* v, int64_t v_ts, const void* a, const void* b,
                          const float* A_log, const float* dt_bias, const float* state_in,
-                         float* state_out, void* o, int B, int Tlen, int Hk, int Hv, float q_scale,
-                         hipStream_t stream) {
+                         float* state_out, void* o, int B, int Tlen, const int32_t* cu, int total,
+                         int Hk, int Hv, float q_scale, hipStream_t stream) {
   if (o_dt == 1)
     launch_seq_t<T, G, uint16_t>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
-                                 state_out, o, B, Tlen, Hk, Hv, q_scale, stream);
+                                 state_out, o, B, Tlen, cu, total, Hk, Hv, q_scale, stream);
   else
     launch_seq_t<T, G, float>(q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
-                              state_out, o, B, Tlen, Hk, Hv, q_scale, stream);
+                              state_out, o, B, Tlen, cu, total, Hk, Hv, q_scale, stream);
 }
 
 hipError_t launch_prefill_sequential(const void* q, int64_t q_ts, const void* k, int64_t k_ts,
                                      const void* v, int64_t v_ts, int qkv_dt, const void* a,
                                      const void* b, int gate_dt, const float* A_log,
                                      const float* dt_bias, const float* state_in,
-                                     float* state_out, void* o, int o_dt, int B, int T, int Hk,
-                                     int Hv, float q_scale, hipStream_t stream) {
+                                     float* state_out, void* o, int o_dt, int B, int T,
+                                     const int32_t* cu, int total, int Hk, int Hv, float q_scale,
+                                     hipStream_t stream) {
   if (qkv_dt == 1 && gate_dt == 1)
     launch_seq_o<uint16_t, uint16_t>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias,
-                                     state_in, state_out, o, B, T, Hk, Hv, q_scale, stream);
+                                     state_in, state_out, o, B, T, cu, total, Hk, Hv, q_scale, stream);
   else if (qkv_dt == 1)
     launch_seq_o<uint16_t, float>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
-                                  state_out, o, B, T, Hk, Hv, q_scale, stream);
+                                  state_out, o, B, T, cu, total, Hk, Hv, q_scale, stream);
   else if (gate_dt == 1)
     launch_seq_o<float, uint16_t>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
-                                  state_out, o, B, T, Hk, Hv, q_scale, stream);
+                                  state_out, o, B, T, cu, total, Hk, Hv, q_scale, stream);
   else
     launch_seq_o<float, float>(o_dt, q, q_ts, k, k_ts, v, v_ts, a, b, A_log, dt_bias, state_in,
-                               state_out, o, B, T, Hk, Hv, q_scale, stream);
+                               state_out, o, B, T, cu, total, Hk, Hv, q_scale, stream);
   return hipGetLastError();
 }
 

@@ -62,11 +62,11 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 /* Prefill algorithm.  AUTO picks CHUNKED for bf16 q/k/v and SEQUENTIAL for
  * f32 q/k/v.  SEQUENTIAL runs the recurrence token by token in f32 (any
- * dtype; the f32 accuracy class).  CHUNKED uses the chunk-of-64 WY/UT form on
- * bf16 MFMA with f32 accumulation and an f32 state carried between chunks
- * (the bf16 accuracy class whatever the input dtype).  With f32 q/k it keeps
- * them unrounded where it matters: Q K^T is formed from a two-term bf16 split
- * of both operands, because q . k is small next to |q||k|. */
+ * dtype; f32 inputs keep f32 accuracy).  CHUNKED uses the chunk-of-64 WY/UT
+ * form on bf16 MFMA with f32 accumulation and an f32 state carried between
+ * chunks; it accepts bf16 q/k/v only (its bf16 operands cannot give f32
+ * inputs their f32 accuracy): CHUNKED with f32 q/k/v returns
+ * GDN_ERR_UNSUPPORTED. */
 typedef enum gdn_algo { GDN_ALGO_AUTO = 0, GDN_ALGO_SEQUENTIAL = 1, GDN_ALGO_CHUNKED = 2 } gdn_algo;
 
 /* Head counts and widths: 16, 48, 128, 128 for the model's layer. */
@@ -107,16 +107,19 @@ int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const floa
 
 /*
  * Bytes of device workspace gdn_prefill needs for these sizes and algorithm
- * (0 for the sequential algorithm).  The caller allocates it; its contents
- * need no initialisation and are scratch after the call.
+ * (0 for the sequential algorithm, and for f32 q/k/v, which never run
+ * chunked).  The caller allocates it; its contents need no initialisation
+ * and are scratch after the call.
  */
 size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t qkv_dt,
                                    int32_t algo);
 
 /*
  * gdn_prefill -- the gated delta rule over T tokens of B sequences, with the
- * state carried in and out (the card's prefill; the chunk continues "from
- * position pos0" when state_in holds the previous chunk's state_out).
+ * state carried in and out (the card's prefill; a long prompt is continued
+ * from where the previous call stopped when state_in holds that call's
+ * state_out, as the code-generation page's prefill chunks start at a given
+ * position).
  *   q, k   [B, T, Hk, dk] in qkv_dt; element (b,t,h,i) at
  *          b*T*tok_stride + t*tok_stride + h*dk + i (strides in elements),
  *          so q, k and v may be views into the conv output (stride 10240).
@@ -133,7 +136,8 @@ size_t gdn_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims, int32_t 
  *          bytes (may be NULL when that is 0), 256-byte aligned.
  * With T == 0 only the state passes through (state_out = state_in, or
  * zeros); the token pointers may then be NULL.
- * Errors: GDN_ERR_WORKSPACE if the workspace is too small.
+ * Errors: GDN_ERR_WORKSPACE if the workspace is too small;
+ * GDN_ERR_UNSUPPORTED for algo CHUNKED with f32 q/k/v.
  */
 int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
                 const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
@@ -144,8 +148,9 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
 
 /*
  * gdn_decode_rows -- one new token for each of R fixed rows, each row at its
- * own length, the state updated in place (the card's decode_rows: "a
- * server's rows each at its own length (fixed rows)").
+ * own length, the state updated in place (the card's decode_rows, which
+ * serves a server's rows at lengths of their own in fixed slots; "Qwen3.8
+ * 27B" model card, state paragraph).
  *   q, k   [R, Hk, dk] in qkv_dt, row r at r*row_stride (elements).
  *   v      [R, Hv, dv] in qkv_dt, row r at r*v_row_stride.
  *   a, b   [R, Hv] contiguous in gate_dt.
@@ -211,9 +216,9 @@ size_t gdn_prefill_slots_workspace_bytes(int32_t R, int32_t max_len, gdn_dims di
 
 /*
  * gdn_prefill_slots -- ragged prefill of a server's fixed rows, each row
- * continuing from its own state with its own number of new tokens (the
- * "Qwen3.8 27B" model card's state paragraph: prefill_slots and decode_rows
- * serve a server's rows each at its own length, fixed rows, conv history and
+ * continuing from its own state with its own number of new tokens ("Qwen3.8
+ * 27B" model card, state paragraph: the slot calls serve rows that sit in
+ * fixed slots at lengths of their own, each keeping its conv history and
  * recurrent state in f32).  The rule uses no positions, so a row's length
  * so far only lives in its state.  Chunks of 64 start at each row's first
  * new token.
@@ -233,8 +238,9 @@ size_t gdn_prefill_slots_workspace_bytes(int32_t R, int32_t max_len, gdn_dims di
  *   max_len  the longest row (host value; sizes the launch and workspace).
  *   workspace  at least gdn_prefill_slots_workspace_bytes(R, max_len, dims)
  *          bytes, 256-byte aligned.
- * Runs the chunked algorithm (the bf16 accuracy class for any input dtype).
- * R == 0, max_len == 0 or total_tokens == 0 is a no-op.
+ * bf16 q/k/v run the chunked algorithm (bf16 MFMA); f32 q/k/v run token by
+ * token in f32 (the workspace may then be NULL).  R == 0, max_len == 0 or
+ * total_tokens == 0 is a no-op.
  */
 int gdn_prefill_slots(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
                       const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
@@ -245,7 +251,8 @@ int gdn_prefill_slots(const void* q, int64_t q_tok_stride, const void* k, int64_
 
 /*
  * Bytes of device workspace gdn_mixer_prefill needs (0 if B or T is 0 or the
- * dims are invalid).  The caller allocates it; no initialisation is needed.
+ * dims are invalid), enough for either dtype.  The caller allocates it; no
+ * initialisation is needed.
  */
 size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims);
 
@@ -255,10 +262,11 @@ size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims);
  * bullet gives: depthwise causal conv (width 4) + silu over the q|k|v
  * channels, L2 of each q and k head, the gated delta rule with the state
  * carried in and out, and the per-head RMSNorm (scale 1 + w) gated by
- * silu(z).  The same result as gdn_conv_silu (f32 output) -> gdn_prefill
- * (chunked) -> gdn_gated_rmsnorm, without the f32 round trip of v: the conv
- * writes q|k in f32 and v in bf16 to the workspace (the chunked prefill
- * rounds v to bf16 anyway).
+ * silu(z).  bf16 inputs: the same result as gdn_conv_silu (f32 output) ->
+ * gdn_prefill (chunked) -> gdn_gated_rmsnorm, without the f32 round trip of
+ * v: the conv writes q|k in f32 and v in bf16 to the workspace (the chunked
+ * prefill rounds v to bf16 anyway).  f32 inputs: conv (f32 output) ->
+ * sequential f32 recurrence -> norm, f32 throughout.
  *   qkv    [B, T, C] contiguous in dt, C = 2*Hk*dk + Hv*dv, channels
  *          [q heads | k heads | v heads].
  *   z      [B, T, Hv*dv] contiguous in dt (the output gate).

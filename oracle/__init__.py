@@ -50,6 +50,8 @@ def _load():
         lib.gdn_oracle_gated_rmsnorm.argtypes = [_D, _D, _D, _D, i64, i32, i32, dbl]
         lib.gdn_oracle_linear.argtypes = [_D, _D, _D, i64, i32, i32]
         lib.gdn_oracle_num_threads.restype = ctypes.c_int
+        lib.gdn_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.gdn_oracle_set_num_threads.restype = None
         for f in ("gdn_oracle_gates", "gdn_oracle_conv_silu", "gdn_oracle_l2norm_heads",
                   "gdn_oracle_recurrence", "gdn_oracle_gated_rmsnorm", "gdn_oracle_linear"):
             getattr(lib, f).restype = None
@@ -68,6 +70,12 @@ def _p(x):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
     return int(_load().gdn_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's later OpenMP loops (parallel over independent
+    sequences only; the arithmetic does not depend on it)."""
+    _load().gdn_oracle_set_num_threads(int(n))
 
 
 def gates(a, b, A_log, dt_bias):

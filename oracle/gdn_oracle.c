@@ -58,12 +58,15 @@
 #include <string.h>
 
 int gdn_oracle_num_threads(void);
+void gdn_oracle_set_num_threads(int n);
 
 #ifdef _OPENMP
 #include <omp.h>
 int gdn_oracle_num_threads(void) { return omp_get_max_threads(); }
+void gdn_oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int gdn_oracle_num_threads(void) { return 1; }
+void gdn_oracle_set_num_threads(int n) { (void)n; }
 #endif
 
 /* silu(x) = x * logistic(x) = x / (1 + e^-x). */

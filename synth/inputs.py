@@ -20,7 +20,7 @@ import numpy as np
 __all__ = ["HK", "HV", "D", "CONV_CH", "CONV_W", "WORKLOADS", "bf16_round", "f32_round",
            "to_f64", "is_bf16", "recurrence_inputs", "decode_inputs", "mixer_inputs",
            "slots_inputs", "decode_multi_inputs", "make_workload", "unit_heads",
-           "proj_inputs", "HIDDEN"]
+           "proj_inputs", "HIDDEN", "correlated_keys_inputs"]
 
 HK, HV, D = 16, 48, 128
 HIDDEN = 5120  # model width ("Qwen/Qwen3.8-27B" architecture viewer, header)
@@ -83,6 +83,33 @@ def recurrence_inputs(B, T, Hk=HK, Hv=HV, d=D, qkv_dt="f32", gate_dt="f32", seed
     b = rng.standard_normal((B, T, Hv))
     A_log = rng.uniform(A_log_range[0], A_log_range[1], Hv)
     dt_bias = rng.normal(0.0, dt_bias_std, Hv)
+    state = None if state_std is None else rng.normal(0.0, state_std, (B, Hv, d, d))
+    return {
+        "q": _round(q, qkv_dt), "k": _round(k, qkv_dt), "v": _round(v, qkv_dt),
+        "a": _round(a, gate_dt), "b": _round(b, gate_dt),
+        "A_log": f32_round(A_log), "dt_bias": f32_round(dt_bias),
+        "state": None if state is None else f32_round(state),
+    }
+
+
+def correlated_keys_inputs(B, T, Hk=HK, Hv=HV, d=D, spread=0.1, b_mean=6.0,
+                           A_log_range=(-6.0, -4.0), qkv_dt="bf16", gate_dt="f32", seed=9,
+                           state_std=0.05):
+    """Prefill inputs whose keys are nearly parallel within each (batch, q/k
+    head): k_t = unit(u + spread * n_t / sqrt(d)) with one random unit u per
+    (batch, q/k head) and n_t ~ N(0, I); b ~ N(b_mean, 0.5) (write rates near
+    1) and A_log ~ U(A_log_range) (slow decay).  With the defaults, pairs of
+    keys have k.k ~ 0.99.  q: unit random; v, a: N(0,1); dt_bias N(0, 0.1);
+    state N(0, state_std) or None."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = unit_heads(rng.standard_normal((B, 1, Hk, d)))
+    k = unit_heads(u + spread * rng.standard_normal((B, T, Hk, d)) / np.sqrt(d))
+    q = unit_heads(rng.standard_normal((B, T, Hk, d)))
+    v = rng.standard_normal((B, T, Hv, d))
+    a = rng.standard_normal((B, T, Hv))
+    b = rng.normal(b_mean, 0.5, (B, T, Hv))
+    A_log = rng.uniform(A_log_range[0], A_log_range[1], Hv)
+    dt_bias = rng.normal(0.0, 0.1, Hv)
     state = None if state_std is None else rng.normal(0.0, state_std, (B, Hv, d, d))
     return {
         "q": _round(q, qkv_dt), "k": _round(k, qkv_dt), "v": _round(v, qkv_dt),

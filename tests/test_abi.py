@@ -98,7 +98,11 @@ def test_prefill_validation():
         assert prefill(ws=9 * P, wsb=need - 1) == WS
     assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 0, 0) == 0  # f32: sequential
     assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 1, 1) == 0
-    assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 0, 2) > 0   # chunked takes f32 too
+    # the chunked algorithm is bf16-only: f32 q/k/v need no workspace and an
+    # explicit CHUNKED request with them is refused before any launch
+    assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 0, 2) == 0
+    assert prefill(qdt=0, algo=2) == UNSUP
+    assert prefill(qdt=0, algo=2, B=0) == UNSUP
 
 
 def decode(q=P, k=2 * P, v=3 * P, qdt=1, st=4 * P, o=5 * P, R=4, dims=D16, lengths=None):

@@ -1,9 +1,10 @@
 """GPU parity of gdn_prefill_slots: a ragged prefill of fixed rows, each row
 continuing from its own state with its own number of new tokens, packed on
 one token axis.  Checked per row against the f64 oracle (bar 2e-2, bf16
-inputs) and bitwise against a separate gdn_prefill call on that row alone
-(the same chunk boundaries, so the same arithmetic); a row with no tokens
-keeps its state bit for bit."""
+inputs; 1e-4 for f32 inputs, which run token by token in f32) and bitwise
+against a separate gdn_prefill call on that row alone (the same chunk
+boundaries, or the same sequential kernel, so the same arithmetic); a row with
+no tokens keeps its state bit for bit."""
 import numpy as np
 import pytest
 
@@ -17,7 +18,7 @@ from synth import make_workload, slots_inputs, to_f64  # noqa: E402
 from tests.conftest import max_rel_err  # noqa: E402
 from tests.gpu_util import banner, dev, host_f64  # noqa: E402
 
-TOL = 2e-2
+TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -45,7 +46,7 @@ def run_row_alone(x, r):
     o = gdn.gdn_prefill(dev(x["q"][c0:c1])[None], dev(x["k"][c0:c1])[None],
                         dev(x["v"][c0:c1])[None], dev(x["a"][c0:c1])[None],
                         dev(x["b"][c0:c1])[None], dev(x["A_log"]), dev(x["dt_bias"]), S, S,
-                        algo="chunked")
+                        algo="auto")
     torch.cuda.synchronize()
     return o[0], S
 
@@ -80,8 +81,8 @@ def test_prefill_slots_ragged_small(qkv_dt):
         assert torch.equal(o[cu[r]:cu[r + 1]], o_row), f"row {r}: o differs from a lone call"
         assert torch.equal(st[r:r + 1], S_row), f"row {r}: state differs from a lone call"
         o_ref, S_ref = oracle_row(x, r)
-        assert max_rel_err(host_f64(o[cu[r]:cu[r + 1]]), o_ref[0]) < TOL, r
-        assert max_rel_err(host_f64(st[r]), S_ref[0]) < TOL, r
+        assert max_rel_err(host_f64(o[cu[r]:cu[r + 1]]), o_ref[0]) < TOL[qkv_dt], r
+        assert max_rel_err(host_f64(st[r]), S_ref[0]) < TOL[qkv_dt], r
 
 
 def test_prefill_slots_wide_chain_ragged():
@@ -97,8 +98,8 @@ def test_prefill_slots_wide_chain_ragged():
             assert torch.equal(st[r], dev(x["state"][r])), "an empty row changed its state"
             continue
         o_ref, S_ref = oracle_row(x, r)
-        assert max_rel_err(host_f64(o[cu[r]:cu[r + 1]]), o_ref[0]) < TOL, r
-        assert max_rel_err(host_f64(st[r]), S_ref[0]) < TOL, r
+        assert max_rel_err(host_f64(o[cu[r]:cu[r + 1]]), o_ref[0]) < TOL["bf16"], r
+        assert max_rel_err(host_f64(st[r]), S_ref[0]) < TOL["bf16"], r
 
 
 def test_prefill_slots_server_batch_full_width():
@@ -120,4 +121,4 @@ def test_prefill_slots_server_batch_full_width():
         e_o = max_rel_err(host_f64(o[cu[r]:cu[r + 1], heads]), o_ref[0])
         e_s = max_rel_err(host_f64(st[r, heads]), S_ref[0])
         print(f"row {r} (len {lengths[r]}): o err {e_o:.2e}, state err {e_s:.2e}")
-        assert e_o < TOL and e_s < TOL
+        assert e_o < TOL["bf16"] and e_s < TOL["bf16"]
