@@ -1,37 +1,48 @@
 """Benchmark of the Gated DeltaNet mixer hot path on one MI355X.
 
 One step = one pass of the whole hot path on seeded synthetic inputs shaped
-like the model's layer (16 q/k heads, 48 value heads, width 128):
-  1. the layer prefill at B=1, T=4096: one gdn_mixer_prefill call (conv over
-     10240 channels, width 4, silu, L2 of q/k -> chunked prefill with the state
-     carried in and out -> gated RMSNorm with z);
-  2. gdn_prefill alone on the prefill workload (B=1, T=4096, bf16 q/k/v, f32
-     gates, carried state ~N(0, 0.05), chunk 64);
-  3. gdn_decode_rows on 64 fixed rows (state [64,48,128,128] f32, in place);
-  4. gdn_prefill_slots on a server's ragged batch: 16 fixed rows with
-     U{1..1024} new tokens each, bf16, states carried in place;
-  5. gdn_decode_rows_multi verifying a 4-token draft on 64 fixed rows, with
-     the state after every token written out as a snapshot;
-  6. the projections around the mixer at 4096 tokens: in_proj_qkv and
-     in_proj_z (gdn_linear, bf16, into one [4096, 16384] buffer), the two
-     gate projections with f32 weights (gdn_gate_proj) and out_proj
-     (gdn_linear, 6144 -> 5120);
-  7. one decode step of the whole layer for 64 fixed rows: in_proj_qkv,
-     in_proj_z, the gate projections, the conv over one token with each row's
-     conv history, decode_rows, the gated RMSNorm and out_proj;
-  8. the same decode step replayed from a HIP graph (captured once per buffer
-     set after the warm-up, so the eight launches go out as one).
-Each part is timed with HIP events on the stream it runs on.  The timed
-region runs each part's K iterations back to back, part after part (so a part
-follows its own previous call, not another part's dirty cache lines), and the
-inputs of every part rotate over three independent buffer sets so that the
-256 MB last-level cache cannot hold a part's working set between its
-launches.
+like the model's layer (16 q/k heads, 48 value heads, width 128), part by part:
+  layer     the layer prefill at B=1, T=4096: one gdn_mixer_prefill call (conv
+            over 10240 channels, width 4, silu, L2 of q/k -> chunked prefill
+            with the state carried in and out -> gated RMSNorm with z);
+  prefill   gdn_prefill alone on the prefill workload (B=1, T=4096, bf16
+            q/k/v, f32 gates, carried state ~N(0, 0.05), chunk 64): the
+            headline;
+  decode    gdn_decode_rows on 64 fixed rows (state [64,48,128,128] f32, in
+            place);
+  mixer_b4  the whole-mixer workload: one gdn_mixer_prefill call at B=4,
+            T=8192 (bf16, zero initial states);
+  long      the long prefill: T=65536 as 16 gdn_prefill calls of 4096 tokens
+            with the f32 state handed from call to call;
+  slots     gdn_prefill_slots on a server's ragged batch: 16 fixed rows with
+            U{1..1024} new tokens each, bf16, states carried in place;
+  multi     gdn_decode_rows_multi verifying a 4-token draft on 64 fixed rows,
+            with the state after every token written out as a snapshot;
+  proj      the projections around the mixer at 4096 tokens: in_proj_qkv and
+            in_proj_z (gdn_linear, bf16, into one [4096, 16384] buffer), the
+            two gate projections with f32 weights (gdn_gate_proj) and out_proj
+            (gdn_linear, 6144 -> 5120);
+  dlayer    one decode step of the whole layer for 64 fixed rows: in_proj_qkv,
+            in_proj_z, the gate projections, the conv over one token with each
+            row's conv history, decode_rows, the gated RMSNorm and out_proj;
+  dgraph    the same decode step replayed from a HIP graph (captured once per
+            buffer set after the warm-up, so the eight launches go out as one).
+Each part is timed with HIP events on the stream it runs on, per call; the
+JSON reports the median (and min, p90, mean) of the K calls, and every rate
+uses the median.  The timed region runs each part's K iterations back to back,
+part after part (so a part follows its own previous call, not another part's
+dirty cache lines), and the inputs of every part rotate over three
+independent buffer sets so that the 256 MB last-level cache cannot hold a
+part's working set between its launches.
 
-Printed: one JSON line.  value = tokens/s of part 2 (the prefill workload);
-decode_rows state GB/s and the layer-prefill tokens/s ride along in the same
-line, with the roofline of the dominant kernel and the f64 oracle timed on the
-host cores as a CPU baseline.
+Printed: one JSON line.  value = tokens/s of the prefill part (gdn_prefill on
+the B=1 T=4096 prefill workload, the chunked gated delta rule alone); the
+other parts ride in the same line, with the roofline of the dominant kernel
+(the chunked prefill's two launches), the rooflines of the others, a plain
+256 MiB copy as the measured HBM reference, and the f64 oracle timed on the
+host cores (all cores, and one core on a sample of heads) as a CPU baseline.
+--parts selects parts for per-workload profiles (value is then null unless
+the prefill part runs).
 """
 import argparse
 import hashlib
@@ -115,11 +126,37 @@ def _traffic(kernel_key, src_files, launches_bytes_fn=None):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(budget_s=10.0):
+def mixer_bytes(B, T, Hk=HK, Hv=HV, d=D, io=2):
+    """Algorithmic HBM bytes of the whole mixer at B x T (bf16 in and out,
+    zero initial state): the fused minimum reads qkv and z, reads a and b,
+    writes y and the final state; the unfused chain also writes and re-reads
+    the conv output and the recurrence output o.  Returns (fused, unfused)."""
+    C = 2 * Hk * d + Hv * d
+    qkv, z, y = B * T * C * io, B * T * Hv * d * io, B * T * Hv * d * io
+    gates = 2 * B * T * Hv * io
+    state = B * Hv * d * d * 4
+    fused = qkv + z + y + gates + state
+    return fused, fused + 2 * qkv + 2 * y
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(budget_s=10.0, single_budget_s=4.0, sample_heads=12):
     """The f64 oracle (as it stands) on the prefill workload: gates plus the
-    token-by-token recurrence over all 48 value heads of B=1, T=4096, on the
-    host's cores, repeated while the total stays within about budget_s.
-    Returns the JSON object."""
+    token-by-token recurrence over all 48 value heads of B=1, T=4096, on all
+    the host's cores (OpenMP over heads), repeated while the total stays
+    within about budget_s; then on one core over the first sample_heads value
+    heads (sample_heads/3 q/k heads), scaled to the whole workload (the
+    heads are independent and equal work).  Returns the JSON object."""
     import numpy as np
     import oracle
     from synth import make_workload, to_f64
@@ -127,17 +164,49 @@ def cpu_baseline(budget_s=10.0):
     q, k, v = (to_f64(x[n]) for n in "qkv")
     a, b = to_f64(x["a"]), to_f64(x["b"])
     S0 = to_f64(x["state"])
-    times = []
-    while not times or (sum(times) + times[0] < budget_s and len(times) < 50):
-        t0 = time.perf_counter()
-        al, be, _ = oracle.gates(a, b, x["A_log"], x["dt_bias"])
-        oracle.recurrence(q, k, v, al, be, S0)
-        times.append(time.perf_counter() - t0)
-    dt = sum(times) / len(times)
-    return {"value": round(T_PREFILL / dt, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds_per_pass": round(dt, 4), "passes": len(times),
+    cores = oracle.num_threads()
+
+    def run(q, k, v, a, b, Al, db, S0, budget):
+        times = []
+        while not times or (sum(times) + times[0] < budget and len(times) < 50):
+            t0 = time.perf_counter()
+            al, be, _ = oracle.gates(a, b, Al, db)
+            oracle.recurrence(q, k, v, al, be, S0)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times)), len(times)
+
+    dt, n = run(q, k, v, a, b, x["A_log"], x["dt_bias"], S0, budget_s)
+    g = HV // HK
+    nh = sample_heads
+    oracle.set_num_threads(1)
+    try:
+        dt1, n1 = run(q[:, :, :nh // g], k[:, :, :nh // g], v[:, :, :nh], a[:, :, :nh],
+                      b[:, :, :nh], x["A_log"][:nh], x["dt_bias"][:nh], S0[:, :nh],
+                      single_budget_s)
+    finally:
+        oracle.set_num_threads(cores)
+    t1_whole = dt1 * HV / nh
+    return {"value": round(T_PREFILL / dt, 1), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "seconds_per_pass": round(dt, 4), "passes": n,
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"whole prefill workload (B=1, T=4096, 48 value heads: f64 gates + "
-                      f"sequential recurrence, OpenMP over heads), {len(times)} passes"}
+                      f"sequential recurrence, OpenMP over heads), median of {n} passes",
+            "single_core": {"value": round(T_PREFILL / t1_whole, 1), "unit": "tokens/s",
+                            "cores": 1, "seconds_per_pass_sample": round(dt1, 4), "passes": n1,
+                            "sample": f"first {nh} of 48 value heads of the same workload on "
+                                      f"one thread, median of {n1} passes, scaled by 48/{nh}"}}
+
+
+PARTS = ("layer", "prefill", "decode", "mixer_b4", "long", "slots", "multi", "proj", "dlayer",
+         "dgraph")
+
+
+def stats(ms):
+    """median / min / p90 / mean of per-call times (ms in, us out)."""
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median_us": round(float(np.median(a)), 2), "min_us": round(float(a.min()), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "mean_us": round(float(a.mean()), 2)}
 
 
 def main():
@@ -146,15 +215,25 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after the timed steps, run a plain 256 MiB device-to-device copy "
-                         "three times (a kernel of known traffic for scaling HBM counters)")
+    ap.add_argument("--no-copy-calibration", action="store_true",
+                    help="skip the plain 256 MiB device-to-device copy timed after the steps "
+                         "(the measured HBM reference, and a kernel of known traffic for "
+                         "scaling HBM counters)")
+    ap.add_argument("--parts", default=",".join(PARTS),
+                    help="comma-separated parts to run (for per-workload profiles); default all")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the mixer shards "
               "by heads with no exchange inside it, so multi-GPU figures are not measured here.",
               file=sys.stderr)
         sys.exit(2)
+    want = [p.strip() for p in args.parts.split(",") if p.strip()]
+    bad = [p for p in want if p not in PARTS]
+    if bad:
+        print(f"unknown parts {bad}; known: {','.join(PARTS)}", file=sys.stderr)
+        sys.exit(2)
+    if "dgraph" in want and "dlayer" not in want:
+        want.append("dlayer")  # the graph replays the decode step's buffers
 
     import numpy as np
     import torch
@@ -168,282 +247,319 @@ def main():
     torch.cuda.set_device(0)
     gdn.lib()
 
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    fns = {}  # part -> fn(i)
+
     # ---- inputs (seeded; each part's buffers replicated ROT times)
-    mx = mixer_inputs(1, T_PREFILL, seed=2003)
-    st_layer = recurrence_inputs(1, 1, seed=2004, state_std=0.05)["state"]
-    layer = []
-    for _ in range(ROT):
-        layer.append({
-            "qkv": dev(mx["qkv"]), "z": dev(mx["z"]), "a": dev(mx["a"]), "b": dev(mx["b"]),
-            "conv_w": dev(mx["conv_w"]), "A_log": dev(mx["A_log"]), "dt_bias": dev(mx["dt_bias"]),
-            "norm_w": dev(mx["norm_w"]), "state": dev(st_layer),
-            "conv_state": torch.zeros((1, 3, C_CONV), dtype=torch.float32, device="cuda"),
-            "out": torch.empty((1, T_PREFILL, HV * D), dtype=torch.bfloat16, device="cuda"),
-            "ws": torch.empty(gdn.gdn_mixer_prefill_workspace_bytes(1, T_PREFILL, HK, HV),
-                              dtype=torch.uint8, device="cuda"),
-        })
-    px = make_workload("prefill_bf16_b1_t4096")
-    pre = []
-    for _ in range(ROT):
-        pre.append({n: dev(px[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state")})
-        pre[-1]["o"] = torch.empty((1, T_PREFILL, HV, D), dtype=torch.bfloat16, device="cuda")
-    dx = make_workload("decode_rows_r64")
-    dec = []
-    for _ in range(ROT):
-        dec.append({n: dev(dx[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "state",
-                                            "lengths")})
-        dec[-1]["o"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
-    sx = make_workload("prefill_slots_bf16_r16")
-    slot_sets = []
-    for _ in range(ROT):
-        slot_sets.append({n: dev(sx[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias",
-                                                   "state", "cu_seqlens")})
-        slot_sets[-1]["ws"] = torch.empty(
-            gdn.gdn_prefill_slots_workspace_bytes(16, sx["max_len"], HK, HV), dtype=torch.uint8,
-            device="cuda")
-        slot_sets[-1]["o"] = torch.empty((sx["q"].shape[0], HV, D), dtype=torch.bfloat16,
-                                         device="cuda")
-    slot_tokens = int(sx["cu_seqlens"][-1])
-    mx4 = make_workload("decode_rows_r64_k4")
-    multi = []
-    for _ in range(ROT):
-        multi.append({n: dev(mx4[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias",
+    if "layer" in want:
+        mx = mixer_inputs(1, T_PREFILL, seed=2003)
+        st_layer = recurrence_inputs(1, 1, seed=2004, state_std=0.05)["state"]
+        layer = []
+        for _ in range(ROT):
+            layer.append({
+                "qkv": dev(mx["qkv"]), "z": dev(mx["z"]), "a": dev(mx["a"]), "b": dev(mx["b"]),
+                "conv_w": dev(mx["conv_w"]), "A_log": dev(mx["A_log"]),
+                "dt_bias": dev(mx["dt_bias"]), "norm_w": dev(mx["norm_w"]),
+                "state": dev(st_layer),
+                "conv_state": torch.zeros((1, 3, C_CONV), dtype=torch.float32, device="cuda"),
+                "out": torch.empty((1, T_PREFILL, HV * D), dtype=torch.bfloat16, device="cuda"),
+                "ws": torch.empty(gdn.gdn_mixer_prefill_workspace_bytes(1, T_PREFILL, HK, HV),
+                                  dtype=torch.uint8, device="cuda"),
+            })
+
+        def layer_part(i):
+            L = layer[i % ROT]
+            gdn.gdn_mixer_prefill(L["qkv"], L["z"], L["conv_w"], L["a"], L["b"], L["A_log"],
+                                  L["dt_bias"], L["norm_w"], HK, HV, conv_state=L["conv_state"],
+                                  state_in=L["state"], state_out=L["state"], y=L["out"],
+                                  workspace=L["ws"])
+        fns["layer"] = layer_part
+
+    if "prefill" in want:
+        px = make_workload("prefill_bf16_b1_t4096")
+        ws_bytes = gdn.gdn_prefill_workspace_bytes(1, T_PREFILL, HK, HV)
+        pre = []
+        for _ in range(ROT):
+            pre.append({n: dev(px[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias",
+                                                "state")})
+            pre[-1]["o"] = torch.empty((1, T_PREFILL, HV, D), dtype=torch.bfloat16,
+                                       device="cuda")
+            pre[-1]["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+        def prefill_part(i):
+            P = pre[i % ROT]
+            gdn.gdn_prefill(P["q"], P["k"], P["v"], P["a"], P["b"], P["A_log"], P["dt_bias"],
+                            P["state"], P["state"], o=P["o"], workspace=P["ws"])
+        fns["prefill"] = prefill_part
+
+    if "decode" in want:
+        dx = make_workload("decode_rows_r64")
+        dec = []
+        for _ in range(ROT):
+            dec.append({n: dev(dx[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias",
                                                 "state", "lengths")})
-        multi[-1]["snap"] = torch.empty((R_DECODE, 4, HV, D, D), dtype=torch.float32,
-                                        device="cuda")
-        multi[-1]["o"] = torch.empty((R_DECODE, 4, HV, D), dtype=torch.bfloat16, device="cuda")
-    pin = proj_inputs(T_PREFILL, seed=2007)
-    pout = proj_inputs(T_PREFILL, K=HV * D, outs=(("W_out", HIDDEN),), gate_H=0, seed=2008,
-                       x_name="y")
-    gws_bytes = max(gdn.gdn_gate_proj_workspace_bytes(T_PREFILL, HIDDEN, HV), 256)
-    proj = []
-    for _ in range(ROT):
-        pj = {n: dev(pin[n]) for n in ("x", "W_qkv", "W_z", "W_a", "W_b")}
-        pj.update({"y": dev(pout["y"]), "W_out": dev(pout["W_out"])})
-        pj["yin"] = torch.empty((T_PREFILL, C_CONV + HV * D), dtype=torch.bfloat16, device="cuda")
-        pj["a"] = torch.empty((T_PREFILL, HV), dtype=torch.float32, device="cuda")
-        pj["b"] = torch.empty((T_PREFILL, HV), dtype=torch.float32, device="cuda")
-        pj["out"] = torch.empty((T_PREFILL, HIDDEN), dtype=torch.bfloat16, device="cuda")
-        pj["lws"] = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8,
-                                device="cuda")
-        pj["gws"] = torch.empty(gws_bytes, dtype=torch.uint8, device="cuda")
-        proj.append(pj)
-    del pin, pout
-    # Part 7: the layer's decode step for 64 rows (weights shared with part 6).
-    dlx = proj_inputs(R_DECODE, outs=(), gate_H=0, seed=2009)["x"]
-    dly = decode_inputs(R_DECODE, seed=2010)
-    dlayer = []
-    for _ in range(ROT):
-        dl = {"x": dev(dlx), "state": dev(dly["state"]), "A_log": dev(dly["A_log"]),
-              "dt_bias": dev(dly["dt_bias"]), "conv_w": dev(mx["conv_w"]),
-              "norm_w": dev(mx["norm_w"]),
-              "conv_state": torch.zeros((R_DECODE, 3, C_CONV), dtype=torch.float32,
-                                        device="cuda")}
-        dl["qkv"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
-        dl["z"] = torch.empty((R_DECODE, HV * D), dtype=torch.bfloat16, device="cuda")
-        dl["a"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
-        dl["b"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
-        dl["y"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
-        dl["o"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
-        dl["out"] = torch.empty((R_DECODE, HIDDEN), dtype=torch.bfloat16, device="cuda")
-        dl["gws"] = torch.empty(max(gdn.gdn_gate_proj_workspace_bytes(R_DECODE, HIDDEN, HV), 256),
-                                dtype=torch.uint8, device="cuda")
-        dlayer.append(dl)
-    ws_bytes = gdn.gdn_prefill_workspace_bytes(1, T_PREFILL, HK, HV)
-    ws = [torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") for _ in range(ROT)]
+            dec[-1]["o"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
 
-    # The parts of a step, each one call.  The timed region runs each part's K
-    # iterations back to back (part after part), so a part follows its own
-    # previous call rather than another part that left the last-level cache
-    # full of its dirty lines; the K steps and their total are the same.
-    def layer_part(i):
-        L = layer[i % ROT]
-        gdn.gdn_mixer_prefill(L["qkv"], L["z"], L["conv_w"], L["a"], L["b"], L["A_log"],
-                              L["dt_bias"], L["norm_w"], HK, HV, conv_state=L["conv_state"],
-                              state_in=L["state"], state_out=L["state"], y=L["out"],
-                              workspace=L["ws"])
+        def decode_part(i):
+            Dd = dec[i % ROT]
+            gdn.gdn_decode_rows(Dd["q"], Dd["k"], Dd["v"], Dd["a"], Dd["b"], Dd["A_log"],
+                                Dd["dt_bias"], Dd["state"], Dd["lengths"], o=Dd["o"])
+        fns["decode"] = decode_part
 
-    def prefill_part(i):
-        P = pre[i % ROT]
-        gdn.gdn_prefill(P["q"], P["k"], P["v"], P["a"], P["b"], P["A_log"], P["dt_bias"],
-                        P["state"], P["state"], o=P["o"], workspace=ws[i % ROT])
+    B3, T3 = 4, 8192
+    if "mixer_b4" in want:
+        log("inputs: mixer_bf16_b4_t8192")
+        m3 = make_workload("mixer_bf16_b4_t8192")
+        m3d = {n: dev(m3[n]) for n in ("qkv", "z", "a", "b", "conv_w", "A_log", "dt_bias",
+                                       "norm_w")}
+        del m3
+        ws3 = gdn.gdn_mixer_prefill_workspace_bytes(B3, T3, HK, HV)
+        mix4 = []
+        for r in range(ROT):
+            M = {n: (t if r == 0 else t.clone()) for n, t in m3d.items()}
+            M["state"] = torch.zeros((B3, HV, D, D), dtype=torch.float32, device="cuda")
+            M["conv_state"] = torch.zeros((B3, 3, C_CONV), dtype=torch.float32, device="cuda")
+            M["out"] = torch.empty((B3, T3, HV * D), dtype=torch.bfloat16, device="cuda")
+            M["ws"] = torch.empty(ws3, dtype=torch.uint8, device="cuda")
+            mix4.append(M)
 
-    def decode_part(i):
-        Dd = dec[i % ROT]
-        gdn.gdn_decode_rows(Dd["q"], Dd["k"], Dd["v"], Dd["a"], Dd["b"], Dd["A_log"],
-                            Dd["dt_bias"], Dd["state"], Dd["lengths"], o=Dd["o"])
+        def mixer_b4_part(i):
+            M = mix4[i % ROT]
+            # zero initial recurrent state (state_in NULL), as the workload has;
+            # the conv history is read and rewritten (3 rows per batch row),
+            # so a set's later calls start from its previous history: the
+            # same work
+            gdn.gdn_mixer_prefill(M["qkv"], M["z"], M["conv_w"], M["a"], M["b"], M["A_log"],
+                                  M["dt_bias"], M["norm_w"], HK, HV, conv_state=M["conv_state"],
+                                  state_in=None, state_out=M["state"], y=M["out"],
+                                  workspace=M["ws"])
+        fns["mixer_b4"] = mixer_b4_part
 
-    def slots_part(i):
-        Sx = slot_sets[i % ROT]
-        gdn.gdn_prefill_slots(Sx["q"], Sx["k"], Sx["v"], Sx["a"], Sx["b"], Sx["A_log"],
-                              Sx["dt_bias"], Sx["cu_seqlens"], Sx["state"], sx["max_len"],
-                              o=Sx["o"], workspace=Sx["ws"])
+    T4, N4 = 65536, 16
+    L4 = T4 // N4
+    if "long" in want:
+        log("inputs: prefill_bf16_b1_t65536_x16")
+        lx = make_workload("prefill_bf16_b1_t65536_x16")
+        lxd = {n: dev(lx[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias")}
+        del lx
+        ws4 = gdn.gdn_prefill_workspace_bytes(1, L4, HK, HV)
+        longs = []
+        for r in range(ROT):
+            Lg = {n: (t if r == 0 else t.clone()) for n, t in lxd.items()}
+            Lg["state"] = torch.zeros((1, HV, D, D), dtype=torch.float32, device="cuda")
+            Lg["o"] = torch.empty((1, T4, HV, D), dtype=torch.bfloat16, device="cuda")
+            Lg["ws"] = torch.empty(ws4, dtype=torch.uint8, device="cuda")
+            Lg["calls"] = [(Lg["q"][:, c * L4:(c + 1) * L4], Lg["k"][:, c * L4:(c + 1) * L4],
+                            Lg["v"][:, c * L4:(c + 1) * L4], Lg["a"][:, c * L4:(c + 1) * L4],
+                            Lg["b"][:, c * L4:(c + 1) * L4], Lg["o"][:, c * L4:(c + 1) * L4])
+                           for c in range(N4)]
+            longs.append(Lg)
 
-    def multi_part(i):
-        M = multi[i % ROT]
-        gdn.gdn_decode_rows_multi(M["q"], M["k"], M["v"], M["a"], M["b"], M["A_log"],
-                                  M["dt_bias"], M["state"], M["snap"], M["lengths"], o=M["o"])
+        def long_part(i):
+            Lg = longs[i % ROT]
+            for c, (q, k, v, a, b, o) in enumerate(Lg["calls"]):
+                # call 0 starts from the zero state (state_in NULL), the others
+                # continue from the state the previous call left
+                gdn.gdn_prefill(q, k, v, a, b, Lg["A_log"], Lg["dt_bias"],
+                                None if c == 0 else Lg["state"], Lg["state"], o=o,
+                                workspace=Lg["ws"])
+        fns["long"] = long_part
 
-    # Part 6 records an event after each of its four calls as well.
-    proj_ev = {}
+    if "slots" in want:
+        sx = make_workload("prefill_slots_bf16_r16")
+        slot_sets = []
+        for _ in range(ROT):
+            slot_sets.append({n: dev(sx[n]) for n in ("q", "k", "v", "a", "b", "A_log",
+                                                       "dt_bias", "state", "cu_seqlens")})
+            slot_sets[-1]["ws"] = torch.empty(
+                gdn.gdn_prefill_slots_workspace_bytes(16, sx["max_len"], HK, HV),
+                dtype=torch.uint8, device="cuda")
+            slot_sets[-1]["o"] = torch.empty((sx["q"].shape[0], HV, D), dtype=torch.bfloat16,
+                                             device="cuda")
+        slot_tokens = int(sx["cu_seqlens"][-1])
 
-    def proj_part(i):
-        Pj = proj[i % ROT]
-        ev = proj_ev.get(i)
-        gdn.gdn_linear(Pj["x"], Pj["W_qkv"], y=Pj["yin"][:, :C_CONV], workspace=Pj["lws"])
-        if ev:
-            ev[0].record()
-        gdn.gdn_linear(Pj["x"], Pj["W_z"], y=Pj["yin"][:, C_CONV:], workspace=Pj["lws"])
-        if ev:
-            ev[1].record()
-        gdn.gdn_gate_proj(Pj["x"], Pj["W_a"], Pj["W_b"], a=Pj["a"], b=Pj["b"],
-                          workspace=Pj["gws"])
-        if ev:
-            ev[2].record()
-        gdn.gdn_linear(Pj["y"], Pj["W_out"], y=Pj["out"], workspace=Pj["lws"])
+        def slots_part(i):
+            Sx = slot_sets[i % ROT]
+            gdn.gdn_prefill_slots(Sx["q"], Sx["k"], Sx["v"], Sx["a"], Sx["b"], Sx["A_log"],
+                                  Sx["dt_bias"], Sx["cu_seqlens"], Sx["state"], sx["max_len"],
+                                  o=Sx["o"], workspace=Sx["ws"])
+        fns["slots"] = slots_part
 
-    # Part 7 records an event after each of its first six calls.
-    dl_ev = {}
+    if "multi" in want:
+        mx4 = make_workload("decode_rows_r64_k4")
+        multi = []
+        for _ in range(ROT):
+            multi.append({n: dev(mx4[n]) for n in ("q", "k", "v", "a", "b", "A_log", "dt_bias",
+                                                    "state", "lengths")})
+            multi[-1]["snap"] = torch.empty((R_DECODE, 4, HV, D, D), dtype=torch.float32,
+                                            device="cuda")
+            multi[-1]["o"] = torch.empty((R_DECODE, 4, HV, D), dtype=torch.bfloat16,
+                                         device="cuda")
 
-    def dlayer_part(i, events=True):
-        L = dlayer[i % ROT]
-        W = proj[i % ROT]
-        ev = dl_ev.get(i) if events else None
-        mark = (lambda j: ev[j].record()) if ev else (lambda j: None)
-        gdn.gdn_linear(L["x"], W["W_qkv"], y=L["qkv"].view(R_DECODE, C_CONV), workspace=W["lws"])
-        mark(0)
-        gdn.gdn_linear(L["x"], W["W_z"], y=L["z"], workspace=W["lws"])
-        mark(1)
-        gdn.gdn_gate_proj(L["x"], W["W_a"], W["W_b"], a=L["a"], b=L["b"], workspace=L["gws"])
-        mark(2)
-        gdn.gdn_conv_silu(L["qkv"], L["conv_w"], L["conv_state"], l2_channels=2 * HK * D,
-                          y=L["y"])
-        mark(3)
-        y = L["y"][:, 0]
-        gdn.gdn_decode_rows(y[:, :HK * D].unflatten(1, (HK, D)),
-                            y[:, HK * D:2 * HK * D].unflatten(1, (HK, D)),
-                            y[:, 2 * HK * D:].unflatten(1, (HV, D)), L["a"], L["b"], L["A_log"],
-                            L["dt_bias"], L["state"], o=L["o"])
-        mark(4)
-        gdn.gdn_gated_rmsnorm(L["o"], L["z"].view(R_DECODE, HV, D), L["norm_w"], y=L["o"])
-        mark(5)
-        gdn.gdn_linear(L["o"].view(R_DECODE, HV * D), W["W_out"], y=L["out"], workspace=W["lws"])
+        def multi_part(i):
+            M = multi[i % ROT]
+            gdn.gdn_decode_rows_multi(M["q"], M["k"], M["v"], M["a"], M["b"], M["A_log"],
+                                      M["dt_bias"], M["state"], M["snap"], M["lengths"],
+                                      o=M["o"])
+        fns["multi"] = multi_part
 
-    parts_fn = [layer_part, prefill_part, decode_part, slots_part, multi_part, proj_part,
-                dlayer_part]
-    for fn in parts_fn:
+    proj_ev, dl_ev = {}, {}
+    if "proj" in want or "dlayer" in want:
+        mxc = mixer_inputs(1, 1, seed=2003)  # conv and norm weights of the decode step
+        pin = proj_inputs(T_PREFILL, seed=2007)
+        pout = proj_inputs(T_PREFILL, K=HV * D, outs=(("W_out", HIDDEN),), gate_H=0, seed=2008,
+                           x_name="y")
+        gws_bytes = max(gdn.gdn_gate_proj_workspace_bytes(T_PREFILL, HIDDEN, HV), 256)
+        proj = []
+        for _ in range(ROT):
+            pj = {n: dev(pin[n]) for n in ("x", "W_qkv", "W_z", "W_a", "W_b")}
+            pj.update({"y": dev(pout["y"]), "W_out": dev(pout["W_out"])})
+            pj["yin"] = torch.empty((T_PREFILL, C_CONV + HV * D), dtype=torch.bfloat16,
+                                    device="cuda")
+            pj["a"] = torch.empty((T_PREFILL, HV), dtype=torch.float32, device="cuda")
+            pj["b"] = torch.empty((T_PREFILL, HV), dtype=torch.float32, device="cuda")
+            pj["out"] = torch.empty((T_PREFILL, HIDDEN), dtype=torch.bfloat16, device="cuda")
+            pj["lws"] = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8,
+                                    device="cuda")
+            pj["gws"] = torch.empty(gws_bytes, dtype=torch.uint8, device="cuda")
+            proj.append(pj)
+        del pin, pout
+
+    if "proj" in want:
+        # Records an event after each of its first three calls as well.
+        def proj_part(i):
+            Pj = proj[i % ROT]
+            ev = proj_ev.get(i)
+            gdn.gdn_linear(Pj["x"], Pj["W_qkv"], y=Pj["yin"][:, :C_CONV], workspace=Pj["lws"])
+            if ev:
+                ev[0].record()
+            gdn.gdn_linear(Pj["x"], Pj["W_z"], y=Pj["yin"][:, C_CONV:], workspace=Pj["lws"])
+            if ev:
+                ev[1].record()
+            gdn.gdn_gate_proj(Pj["x"], Pj["W_a"], Pj["W_b"], a=Pj["a"], b=Pj["b"],
+                              workspace=Pj["gws"])
+            if ev:
+                ev[2].record()
+            gdn.gdn_linear(Pj["y"], Pj["W_out"], y=Pj["out"], workspace=Pj["lws"])
+        fns["proj"] = proj_part
+
+    if "dlayer" in want:
+        # The layer's decode step for 64 rows (weights shared with the projections).
+        dlx = proj_inputs(R_DECODE, outs=(), gate_H=0, seed=2009)["x"]
+        dly = decode_inputs(R_DECODE, seed=2010)
+        dlayer = []
+        for _ in range(ROT):
+            dl = {"x": dev(dlx), "state": dev(dly["state"]), "A_log": dev(dly["A_log"]),
+                  "dt_bias": dev(dly["dt_bias"]), "conv_w": dev(mxc["conv_w"]),
+                  "norm_w": dev(mxc["norm_w"]),
+                  "conv_state": torch.zeros((R_DECODE, 3, C_CONV), dtype=torch.float32,
+                                            device="cuda")}
+            dl["qkv"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
+            dl["z"] = torch.empty((R_DECODE, HV * D), dtype=torch.bfloat16, device="cuda")
+            dl["a"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
+            dl["b"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
+            dl["y"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
+            dl["o"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
+            dl["o2"] = torch.empty((R_DECODE, HV, D), dtype=torch.bfloat16, device="cuda")
+            dl["out"] = torch.empty((R_DECODE, HIDDEN), dtype=torch.bfloat16, device="cuda")
+            dl["gws"] = torch.empty(
+                max(gdn.gdn_gate_proj_workspace_bytes(R_DECODE, HIDDEN, HV), 256),
+                dtype=torch.uint8, device="cuda")
+            dlayer.append(dl)
+
+        def dlayer_part(i, events=True):
+            L = dlayer[i % ROT]
+            W = proj[i % ROT]
+            ev = dl_ev.get(i) if events else None
+            mark = (lambda j: ev[j].record()) if ev else (lambda j: None)
+            gdn.gdn_linear(L["x"], W["W_qkv"], y=L["qkv"].view(R_DECODE, C_CONV),
+                           workspace=W["lws"])
+            mark(0)
+            gdn.gdn_linear(L["x"], W["W_z"], y=L["z"], workspace=W["lws"])
+            mark(1)
+            gdn.gdn_gate_proj(L["x"], W["W_a"], W["W_b"], a=L["a"], b=L["b"],
+                              workspace=L["gws"])
+            mark(2)
+            gdn.gdn_conv_silu(L["qkv"], L["conv_w"], L["conv_state"], l2_channels=2 * HK * D,
+                              y=L["y"])
+            mark(3)
+            y = L["y"][:, 0]
+            gdn.gdn_decode_rows(y[:, :HK * D].unflatten(1, (HK, D)),
+                                y[:, HK * D:2 * HK * D].unflatten(1, (HK, D)),
+                                y[:, 2 * HK * D:].unflatten(1, (HV, D)), L["a"], L["b"],
+                                L["A_log"], L["dt_bias"], L["state"], o=L["o"])
+            mark(4)
+            gdn.gdn_gated_rmsnorm(L["o"], L["z"].view(R_DECODE, HV, D), L["norm_w"], y=L["o2"])
+            mark(5)
+            gdn.gdn_linear(L["o2"].view(R_DECODE, HV * D), W["W_out"], y=L["out"],
+                           workspace=W["lws"])
+        fns["dlayer"] = dlayer_part
+
+    order = [p for p in PARTS if p in fns]
+    log(f"warm-up: {args.warmup} calls of each part: {','.join(order)}")
+    for p in order:
         for i in range(args.warmup):
-            fn(i)
+            fns[p](i)
     torch.cuda.synchronize()
-    # Part 8: the decode step of each buffer set captured in a graph (the eager
-    # warm-up above built the hipBLASLt plans, which cannot be made under capture).
-    # A capture that fails leaves part 8 out (graph_us is then null); the
+
+    # The decode step of each buffer set captured in a graph (the eager warm-up
+    # above built the hipBLASLt plans, which cannot be made under capture).  A
+    # capture that fails leaves the part out (graph_us is then null); the
     # replays' results are checked against the eager step in the GPU tests.
     graphs = []
-    try:
-        cap = torch.cuda.Stream()
-        for r in range(ROT):
-            gr = torch.cuda.CUDAGraph()
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(gr, stream=cap):
-                    dlayer_part(r, events=False)
-            torch.cuda.current_stream().wait_stream(cap)
-            graphs.append(gr)
-        torch.cuda.synchronize()
-    except RuntimeError as e:
-        print(f"bench.py: graph capture of the decode step failed ({e}); part 8 skipped",
-              file=sys.stderr)
-        graphs = []
-        torch.cuda.synchronize()
+    if "dgraph" in want:
+        try:
+            cap = torch.cuda.Stream()
+            for r in range(ROT):
+                gr = torch.cuda.CUDAGraph()
+                cap.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(cap):
+                    with torch.cuda.graph(gr, stream=cap):
+                        dlayer_part(r, events=False)
+                torch.cuda.current_stream().wait_stream(cap)
+                graphs.append(gr)
+            torch.cuda.synchronize()
+        except RuntimeError as e:
+            print(f"bench.py: graph capture of the decode step failed ({e}); dgraph skipped",
+                  file=sys.stderr)
+            graphs = []
+            torch.cuda.synchronize()
+        if graphs:
+            def dgraph_part(i):
+                graphs[i % ROT].replay()
+            fns["dgraph"] = dgraph_part
+            order.append("dgraph")
+            for i in range(max(args.warmup, 2)):
+                dgraph_part(i)
+            torch.cuda.synchronize()
 
-    def dlayer_graph_part(i):
-        graphs[i % ROT].replay()
-
-    if graphs:
-        parts_fn.append(dlayer_graph_part)
-        for i in range(max(args.warmup, 2)):
-            dlayer_graph_part(i)
-        torch.cuda.synchronize()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)] for _ in parts_fn]
+    evs = {p: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for p in order}
     for i in range(args.steps):
         proj_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         dl_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     torch.cuda.synchronize()
+    log(f"timed: {args.steps} steps")
     t_start = time.perf_counter()
-    for j, fn in enumerate(parts_fn):
+    for p in order:
         for i in range(args.steps):
-            evs[j][i][0].record()
-            fn(args.warmup + i)
-            evs[j][i][1].record()
-    torch.cuda.synchronize()
+            evs[p][i][0].record()
+            fns[p](args.warmup + i)
+            evs[p][i][1].record()
+        torch.cuda.synchronize()
+        log(f"part {p} done")
     wall = time.perf_counter() - t_start
 
-    parts = np.array([[evs[j][i][0].elapsed_time(evs[j][i][1]) for j in range(len(parts_fn))]
-                      for i in range(args.steps)])  # ms
-    mean = parts.mean(axis=0)
-    t_layer, t_pre, t_dec, t_slots, t_multi, t_proj, t_dlayer = mean[:7]
-    t_dgraph = mean[7] if len(mean) > 7 else None
-    # Per call of part 7: in_proj_qkv, in_proj_z, gates, conv, decode_rows, norm, out_proj.
-    dlc = []
-    for i in range(args.steps):
-        e = [evs[6][i][0]] + dl_ev[args.warmup + i] + [evs[6][i][1]]
-        dlc.append([e[j].elapsed_time(e[j + 1]) for j in range(7)])
-    dlc = np.array(dlc).mean(axis=0)  # ms
-    # Per call of part 6: in_proj_qkv, in_proj_z, gate projections, out_proj.
-    pc = np.array([[evs[5][i][0].elapsed_time(proj_ev[args.warmup + i][0]),
-                    proj_ev[args.warmup + i][0].elapsed_time(proj_ev[args.warmup + i][1]),
-                    proj_ev[args.warmup + i][1].elapsed_time(proj_ev[args.warmup + i][2]),
-                    proj_ev[args.warmup + i][2].elapsed_time(evs[5][i][1])]
-                   for i in range(args.steps)]).mean(axis=0)  # ms
-    t_qkv, t_z, t_gate, t_out = pc
-    gemm_flops = 2.0 * T_PREFILL * HIDDEN * (C_CONV + HV * D) + 2.0 * T_PREFILL * HV * D * HIDDEN
-    gemm_tflops = gemm_flops / ((t_qkv + t_z + t_out) * 1e-3) / 1e12
-    gate_bytes = T_PREFILL * HIDDEN * 2 + 2 * HV * HIDDEN * 4 + 2 * T_PREFILL * HV * 4
-    multi_bytes = (2 + 4) * R_DECODE * HV * D * D * 4  # state in + out, 4 snapshots
+    per = {p: [evs[p][i][0].elapsed_time(evs[p][i][1]) for i in range(args.steps)]
+           for p in order}  # ms per call
+    med = {p: float(np.median(v)) for p, v in per.items()}  # ms
     ms_per_step = wall * 1e3 / args.steps
-
-    prefill_tps = T_PREFILL / (t_pre * 1e-3)
-    layer_tps = T_PREFILL / (t_layer * 1e-3)
-    dec_bytes = decode_bytes_per_launch()
-    state_bytes = 2 * R_DECODE * HV * D * D * 4
-    dec_gbps = state_bytes / (t_dec * 1e-3) / 1e9
-
-    # Rooflines.  The prefill call (two launches: chunk_prep, then chunk_chain)
-    # is MFMA work; decode_rows is one HBM-bound launch.  "roofline" is the
-    # one that takes more of the step.
-    pre_flops = prefill_flops_per_launch()
-    ach_d = dec_bytes / (t_dec * 1e-3) / 1e9
-    roof_dec = {"bound": "hbm", "kernel": "decode_rows_kernel<bf16,bf16>",
-                "achieved": round(ach_d, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach_d / HBM_PEAK_GBPS, 4),
-                "traffic": _traffic("decode_rows", ["recurrent.hip", "common.hpp"]),
-                "bytes_per_launch": dec_bytes, "avg_launch_us": round(t_dec * 1e3, 2)}
-    ach_p = pre_flops / (t_pre * 1e-3) / 1e12
-    roof_pre = {"bound": "mfma",
-                "kernel": "gdn_prefill chunked: chunk_prep_kernel + chunk_chain_kernel (two launches)",
-                "achieved": round(ach_p, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach_p / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": _traffic("prefill_chunked", ["chunk_prefill.hip", "chunk_common.hpp", "common.hpp"]),
-                "flops_per_launch": pre_flops, "avg_launch_us": round(t_pre * 1e3, 2)}
-    roofline, roofline_other = (roof_pre, roof_dec) if t_pre >= t_dec else (roof_dec, roof_pre)
-
-    copy_gbps = None
-    if args.copy_calibration:
-        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        ce = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        for i in range(3):
-            ce[i].record()
-            dst.copy_(src)
-        ce[3].record()
-        torch.cuda.synchronize()
-        copy_gbps = round(2 * src.numel() * 4 / (ce[1].elapsed_time(ce[3]) / 2 * 1e-3) / 1e9, 1)
 
     out = {
         "metric": "GDN layer prefill tokens/s (T=4096) + decode_rows state GB/s at 64 rows",
-        "value": round(prefill_tps, 1),
+        "value": round(T_PREFILL / (med["prefill"] * 1e-3), 1) if "prefill" in med else None,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -456,66 +572,178 @@ def main():
         "data": "synthetic",
         "config": {"workload": "prefill_bf16_b1_t4096", "B": 1, "T": T_PREFILL, "chunk": 64,
                    "qk_heads": HK, "v_heads": HV, "head_dim": D,
-                   "step": "layer prefill (gdn_mixer_prefill: conv+silu+L2 -> chunked prefill "
-                           "-> gated RMSNorm) at B=1 T=4096, prefill workload at B=1 T=4096, "
-                           "decode_rows at 64 rows, prefill_slots (16 rows), decode_rows_multi "
-                           "(64 rows x 4), projections at 4096 tokens, a 64-row decode step of "
-                           "the whole layer (eager and replayed from a HIP graph)"},
-        "decode_rows": {"value": round(dec_gbps, 1), "unit": "GB/s (state bytes read+written)",
-                        "workload": "decode_rows_r64", "avg_launch_us": round(t_dec * 1e3, 2),
-                        "frac_of_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4)},
-        "layer_prefill": {"value": round(layer_tps, 1), "unit": "tokens/s",
-                          "workload": "gdn_mixer_prefill (conv+silu+L2 -> chunked prefill -> "
-                                      "gated RMSNorm), B=1 T=4096, 10240 conv channels",
-                          "call_us": round(t_layer * 1e3, 2)},
-        "prefill_slots": {"value": round(slot_tokens / (t_slots * 1e-3), 1), "unit": "tokens/s",
-                          "workload": "prefill_slots_bf16_r16 (16 fixed rows, U{1..1024} new "
-                                      "tokens each, %d tokens, longest %d)" % (slot_tokens,
-                                                                                sx["max_len"]),
-                          "call_us": round(t_slots * 1e3, 2),
-                          "mfma_tflops": round(slots_flops(sx) / (t_slots * 1e-3) / 1e12, 2)},
-        "decode_rows_multi": {"value": round(4 * R_DECODE / (t_multi * 1e-3), 1),
-                              "unit": "tokens/s",
-                              "workload": "decode_rows_r64_k4 (64 rows x 4 draft tokens, state "
-                                          "snapshot after every token)",
-                              "call_us": round(t_multi * 1e3, 2),
-                              "state_gbps": round(multi_bytes / (t_multi * 1e-3) / 1e9, 1)},
-        "projections": {
-            "workload": "in_proj_qkv 5120->10240 and in_proj_z 5120->6144 (bf16, hipBLASLt), "
+                   "value_is": "tokens/s of one gdn_prefill call (the chunked gated delta rule "
+                               "alone: chunk_prep + chunk_chain) on the B=1 T=4096 prefill "
+                               "workload, median over the timed calls; the whole mixer at the "
+                               "same size (conv + rule + gated norm) is layer_prefill",
+                   "step": "one call of each part: " + ", ".join(order)},
+    }
+    parts_out = {p: stats(per[p]) for p in order}
+    out["parts_us"] = parts_out
+    roofs = {}
+
+    if "prefill" in med:
+        t_pre = med["prefill"]
+        pre_flops = prefill_flops_per_launch()
+        ach_p = pre_flops / (t_pre * 1e-3) / 1e12
+        roofs["prefill_b1_t4096"] = {
+            "bound": "mfma",
+            "kernel": "gdn_prefill chunked: chunk_prep_kernel + chunk_chain_kernel (two launches)",
+            "achieved": round(ach_p, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach_p / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": _traffic("prefill_chunked",
+                                ["chunk_prefill.hip", "chunk_common.hpp", "common.hpp"]),
+            "flops_per_launch": pre_flops, "avg_launch_us": round(t_pre * 1e3, 2),
+            "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9, 1)}
+    if "decode" in med:
+        t_dec = med["decode"]
+        dec_bytes = decode_bytes_per_launch()
+        state_bytes = 2 * R_DECODE * HV * D * D * 4
+        ach_d = dec_bytes / (t_dec * 1e-3) / 1e9
+        roofs["decode_rows_r64"] = {
+            "bound": "hbm", "kernel": "decode_rows_kernel<bf16,bf16>",
+            "achieved": round(ach_d, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach_d / HBM_PEAK_GBPS, 4),
+            "traffic": _traffic("decode_rows", ["recurrent.hip", "common.hpp"]),
+            "bytes_per_launch": dec_bytes, "avg_launch_us": round(t_dec * 1e3, 2)}
+        out["decode_rows"] = {"value": round(state_bytes / (t_dec * 1e-3) / 1e9, 1),
+                              "unit": "GB/s (state bytes read+written)",
+                              "workload": "decode_rows_r64", "call_us": round(t_dec * 1e3, 2),
+                              "frac_of_hbm_peak": round(state_bytes / (t_dec * 1e-3) / 1e9
+                                                        / HBM_PEAK_GBPS, 4)}
+    if "layer" in med:
+        t_layer = med["layer"]
+        out["layer_prefill"] = {"value": round(T_PREFILL / (t_layer * 1e-3), 1),
+                                "unit": "tokens/s",
+                                "workload": "gdn_mixer_prefill (conv+silu+L2 -> chunked prefill "
+                                            "-> gated RMSNorm), B=1 T=4096, 10240 conv channels",
+                                "call_us": round(t_layer * 1e3, 2)}
+    if "mixer_b4" in med:
+        t3 = med["mixer_b4"]
+        fused, unfused = mixer_bytes(B3, T3)
+        flops3 = prefill_flops_per_launch(T=T3) * B3
+        ach3 = fused / (t3 * 1e-3) / 1e9
+        out["mixer_b4_t8192"] = {
+            "value": round(B3 * T3 / (t3 * 1e-3), 1), "unit": "tokens/s",
+            "workload": "mixer_bf16_b4_t8192: one gdn_mixer_prefill call, B=4, T=8192, bf16, "
+                        "zero initial states", "call_us": round(t3 * 1e3, 2),
+            "mfma_tflops_chunked_form": round(flops3 / (t3 * 1e-3) / 1e12, 2)}
+        roofs["mixer_b4_t8192"] = {
+            "bound": "hbm", "kernel": "gdn_mixer_prefill (conv, chunk_prep, chunk_chain, norm)",
+            "achieved": round(ach3, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach3 / HBM_PEAK_GBPS, 4), "traffic": None,
+            "bytes_per_launch": fused, "bytes_note": "fused minimum (qkv, z, a, b in; y and "
+                                                     "state out)",
+            "unfused_bytes": unfused,
+            "frac_of_unfused_roof": round(unfused / (t3 * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "avg_launch_us": round(t3 * 1e3, 2)}
+    if "long" in med:
+        t4 = med["long"]
+        flops4 = prefill_flops_per_launch() * N4
+        ach4 = flops4 / (t4 * 1e-3) / 1e12
+        out["long_prefill_t65536"] = {
+            "value": round(T4 / (t4 * 1e-3), 1), "unit": "tokens/s",
+            "workload": "prefill_bf16_b1_t65536_x16: 16 gdn_prefill calls of 4096 tokens, the "
+                        "f32 state handed between them", "us": round(t4 * 1e3, 2)}
+        roofs["long_prefill_t65536_x16"] = {
+            "bound": "mfma", "kernel": "16 x gdn_prefill chunked (chunk_prep + chunk_chain)",
+            "achieved": round(ach4, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach4 / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+            "flops": flops4, "us": round(t4 * 1e3, 2),
+            "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() * N4 / (t4 * 1e-3) / 1e9,
+                                          1)}
+    if "slots" in med:
+        t_slots = med["slots"]
+        out["prefill_slots"] = {
+            "value": round(slot_tokens / (t_slots * 1e-3), 1), "unit": "tokens/s",
+            "workload": "prefill_slots_bf16_r16 (16 fixed rows, U{1..1024} new tokens each, "
+                        "%d tokens, longest %d)" % (slot_tokens, sx["max_len"]),
+            "call_us": round(t_slots * 1e3, 2),
+            "mfma_tflops": round(slots_flops(sx) / (t_slots * 1e-3) / 1e12, 2)}
+    if "multi" in med:
+        t_multi = med["multi"]
+        multi_bytes = (2 + 4) * R_DECODE * HV * D * D * 4  # state in + out, 4 snapshots
+        out["decode_rows_multi"] = {
+            "value": round(4 * R_DECODE / (t_multi * 1e-3), 1), "unit": "tokens/s",
+            "workload": "decode_rows_r64_k4 (64 rows x 4 draft tokens, state snapshot after "
+                        "every token)", "call_us": round(t_multi * 1e3, 2),
+            "state_gbps": round(multi_bytes / (t_multi * 1e-3) / 1e9, 1)}
+    if "proj" in med:
+        t_proj = med["proj"]
+        pc = np.median(np.array(
+            [[evs["proj"][i][0].elapsed_time(proj_ev[args.warmup + i][0]),
+              proj_ev[args.warmup + i][0].elapsed_time(proj_ev[args.warmup + i][1]),
+              proj_ev[args.warmup + i][1].elapsed_time(proj_ev[args.warmup + i][2]),
+              proj_ev[args.warmup + i][2].elapsed_time(evs["proj"][i][1])]
+             for i in range(args.steps)]), axis=0)  # ms
+        t_qkv, t_z, t_gate, t_out = pc
+        gemm_flops = (2.0 * T_PREFILL * HIDDEN * (C_CONV + HV * D)
+                      + 2.0 * T_PREFILL * HV * D * HIDDEN)
+        gemm_tflops = gemm_flops / ((t_qkv + t_z + t_out) * 1e-3) / 1e12
+        gate_bytes = T_PREFILL * HIDDEN * 2 + 2 * HV * HIDDEN * 4 + 2 * T_PREFILL * HV * 4
+        out["projections"] = {
+            "workload": "in_proj_qkv 5120->10240 and in_proj_z 5120->6144 (bf16, gdn_linear), "
                         "in_proj_a/b 5120->48 (f32 weights, gdn_gate_proj), out_proj "
-                        "6144->5120 (bf16, hipBLASLt) at 4096 tokens",
+                        "6144->5120 (bf16, gdn_linear) at 4096 tokens",
             "call_us": round(t_proj * 1e3, 2),
             "in_proj_qkv_us": round(t_qkv * 1e3, 2), "in_proj_z_us": round(t_z * 1e3, 2),
             "gate_proj_us": round(t_gate * 1e3, 2), "out_proj_us": round(t_out * 1e3, 2),
             "gemm_tflops": round(gemm_tflops, 1),
             "gemm_frac_of_bf16_peak": round(gemm_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-            "gate_proj_gbps_algorithmic": round(gate_bytes / (t_gate * 1e-3) / 1e9, 1)},
-        "full_layer_prefill": {
-            "value": round(T_PREFILL / ((t_layer + t_proj) * 1e-3), 1), "unit": "tokens/s",
-            "workload": "projections (part 6) + gdn_mixer_prefill (part 1) at B=1 T=4096, "
-                        "the two parts' times added",
-            "us": round((t_layer + t_proj) * 1e3, 2)},
-        "full_layer_decode": {
-            "value": round(R_DECODE / (t_dlayer * 1e-3), 1), "unit": "tokens/s",
+            "gate_proj_gbps_algorithmic": round(gate_bytes / (t_gate * 1e-3) / 1e9, 1)}
+        if "layer" in med:
+            out["full_layer_prefill"] = {
+                "value": round(T_PREFILL / ((med["layer"] + t_proj) * 1e-3), 1),
+                "unit": "tokens/s",
+                "workload": "projections + gdn_mixer_prefill at B=1 T=4096, the two parts' "
+                            "median times added",
+                "us": round((med["layer"] + t_proj) * 1e3, 2)}
+    if "dlayer" in med:
+        t_dl = med["dlayer"]
+        t_dg = med.get("dgraph")
+        dlc = np.median(np.array(
+            [[e[j].elapsed_time(e[j + 1]) for j in range(7)]
+             for e in ([evs["dlayer"][i][0]] + dl_ev[args.warmup + i] + [evs["dlayer"][i][1]]
+                       for i in range(args.steps))]), axis=0)  # ms
+        out["full_layer_decode"] = {
+            "value": round(R_DECODE / (t_dl * 1e-3), 1), "unit": "tokens/s",
             "workload": "one decode step of the whole layer for 64 fixed rows: in_proj_qkv, "
                         "in_proj_z, gate projections, conv over one token with the rows' conv "
                         "history, decode_rows, gated RMSNorm, out_proj",
-            "us": round(t_dlayer * 1e3, 2),
-            "graph_us": round(t_dgraph * 1e3, 2) if t_dgraph else None,
-            "graph_value": round(R_DECODE / (t_dgraph * 1e-3), 1) if t_dgraph else None,
-            "calls_us": dict(zip(["in_proj_qkv", "in_proj_z", "gate_proj", "conv", "decode_rows",
-                                  "gated_rmsnorm", "out_proj"],
-                                 [round(v * 1e3, 2) for v in dlc]))},
-        "prefill": {"avg_launch_us": round(t_pre * 1e3, 2),
-                    "mfma_tflops": round(pre_flops / (t_pre * 1e-3) / 1e12, 2),
-                    "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() / (t_pre * 1e-3) / 1e9,
-                                                  1)},
-        "roofline": roofline,
-        "roofline_other": roofline_other,
-        "copy_256MiB_GBps": copy_gbps,
-        "cpu_baseline": None,
-    }
-    if not args.no_cpu_baseline:
+            "us": round(t_dl * 1e3, 2),
+            "graph_us": round(t_dg * 1e3, 2) if t_dg else None,
+            "graph_value": round(R_DECODE / (t_dg * 1e-3), 1) if t_dg else None,
+            "calls_us": dict(zip(["in_proj_qkv", "in_proj_z", "gate_proj", "conv",
+                                  "decode_rows", "gated_rmsnorm", "out_proj"],
+                                 [round(v * 1e3, 2) for v in dlc]))}
+
+    # The dominant kernel of the step: the chunked prefill's two launches (they
+    # also carry the long prefill, the ragged batch and the whole mixer's
+    # recurrence); decode_rows and the whole mixer in roofline_other.
+    if "prefill_b1_t4096" in roofs:
+        out["roofline"] = roofs.pop("prefill_b1_t4096")
+    elif roofs:
+        out["roofline"] = roofs.pop(next(iter(roofs)))
+    out["roofline_other"] = roofs
+
+    if not args.no_copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        ce = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for i in range(5):
+            ce[i].record()
+            dst.copy_(src)
+        ce[5].record()
+        torch.cuda.synchronize()
+        ts = [ce[i].elapsed_time(ce[i + 1]) for i in range(1, 5)]
+        out["copy_256MiB"] = {"GBps": round(2 * src.numel() * 4 / (float(np.median(ts)) * 1e-3)
+                                            / 1e9, 1),
+                              "note": "device-to-device copy of 256 MiB (read + write bytes), "
+                                      "median of 4 after one warm-up"}
+        del src, dst
+    out["cpu_baseline"] = None
+    if not args.no_cpu_baseline and "prefill" in want:
+        log("cpu baseline (f64 oracle)")
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
