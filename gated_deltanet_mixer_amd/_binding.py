@@ -73,6 +73,9 @@ def lib():
         L.gdn_gate_proj_workspace_bytes.restype = sz
         L.gdn_gate_proj.argtypes = [P, i64, i32, P, P, P, P, i64, i32, i32, i32, P, sz, P]
         L.gdn_gate_proj.restype = ctypes.c_int
+        L.gdn_prefill_noalloc.argtypes = [P, i64, P, i64, P, i64, i32, P, P, i32, P, P, P, P, P,
+                                          i32, i32, i32, gdn_dims, f32, i32, P]
+        L.gdn_prefill_noalloc.restype = ctypes.c_int
         L.gdn_linear_workspace_bytes.argtypes = []
         L.gdn_linear_workspace_bytes.restype = sz
         L.gdn_linear.argtypes = [P, i64, P, i64, P, i64, i32, i32, i32, i32, P, sz, P]
@@ -180,6 +183,29 @@ def gdn_prefill(q, k, v, a, b, A_log, dt_bias, state_in=None, state_out=None, o=
                              _ALGOS[algo],
                              _ptr(workspace), ws_bytes, _stream(q)),
            "gdn_prefill")
+    return o
+
+
+def gdn_prefill_noalloc(q, k, v, a, b, A_log, dt_bias, state_in=None, state_out=None, o=None,
+                        q_scale=1.0, algo="auto", o_dtype=None):
+    """gdn_prefill with the library's fixed device scratch instead of a
+    workspace (for callers that cannot allocate).  o is allocated here when
+    not given; pass it to allocate nothing."""
+    _need_cuda(q, k, v, a, b, A_log, dt_bias, state_in, state_out, o)
+    B, T, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    qs, ks, vs = _tok_stride(q, Hk, dk), _tok_stride(k, Hk, dk), _tok_stride(v, Hv, dv)
+    if o is None:
+        o = torch.empty((B, T, Hv, dv), dtype=o_dtype or v.dtype, device=v.device)
+    assert o.is_contiguous() and a.is_contiguous() and b.is_contiguous()
+    for s in (state_in, state_out):
+        if s is not None:
+            assert s.is_contiguous() and s.dtype == torch.float32
+    _check(lib().gdn_prefill_noalloc(_ptr(q), qs, _ptr(k), ks, _ptr(v), vs, _dt(q), _ptr(a),
+                                     _ptr(b), _dt(a), _ptr(A_log), _ptr(dt_bias), _ptr(state_in),
+                                     _ptr(state_out), _ptr(o), _dt(o), B, T,
+                                     gdn_dims(Hk, Hv, dk, dv), q_scale, _ALGOS[algo], _stream(q)),
+           "gdn_prefill_noalloc")
     return o
 
 

@@ -71,6 +71,8 @@ const char* gdn_status_str(int status) {
     case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: valid but not implemented";
     case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
     case GDN_ERR_LAUNCH: return "GDN_ERR_LAUNCH: kernel launch failed";
+    case GDN_ERR_SCRATCH:
+      return "GDN_ERR_SCRATCH: larger than the no-allocation entry point's fixed scratch";
     default: return "unknown gdn_status";
   }
 }

@@ -55,7 +55,8 @@ typedef enum gdn_status {
   GDN_ERR_ALIGN = 4,       /* a pointer or stride breaks the alignment rules */
   GDN_ERR_UNSUPPORTED = 5, /* valid but not implemented (e.g. head width != 128) */
   GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
-  GDN_ERR_LAUNCH = 7       /* the HIP runtime refused the launch */
+  GDN_ERR_LAUNCH = 7,      /* the HIP runtime refused the launch */
+  GDN_ERR_SCRATCH = 8      /* larger than the no-allocation entry point's fixed scratch */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -358,6 +359,32 @@ size_t gdn_linear_workspace_bytes(void);
 int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y, int64_t y_ld,
                int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/* Size of the fixed device scratch of gdn_prefill_noalloc: 64 MiB, enough
+ * for the chunked prefill of B*T <= 1152 tokens at 16 q/k and 48 value heads
+ * (gdn_prefill_workspace_bytes gives the need of other sizes). */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * gdn_prefill_noalloc -- gdn_prefill without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The chunked
+ * algorithm's scratch is a fixed device array inside the library
+ * (GDN_NOALLOC_SCRATCH_BYTES; every GPU the library runs on holds its own
+ * copy until the process ends); the call allocates nothing and does not
+ * synchronise.  Its first call on a device looks up the array's device
+ * address.  All calls on one GPU share the array, so calls that overlap on a
+ * GPU (other streams or threads) race: serialise them.  Arguments, results
+ * and errors as gdn_prefill; GDN_ERR_SCRATCH if
+ * gdn_prefill_workspace_bytes(B, T, dims, qkv_dt, algo) exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES (nothing is enqueued).
+ */
+int gdn_prefill_noalloc(const void* q, int64_t q_tok_stride, const void* k, int64_t k_tok_stride,
+                        const void* v, int64_t v_tok_stride, int32_t qkv_dt, const void* a,
+                        const void* b, int32_t gate_dt, const float* A_log, const float* dt_bias,
+                        const float* state_in, float* state_out, void* o, int32_t o_dt,
+                        int32_t B, int32_t T, gdn_dims dims, float q_scale, int32_t algo,
+                        void* stream);
 
 #ifdef __cplusplus
 }

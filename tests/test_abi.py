@@ -35,7 +35,7 @@ def test_header_and_exports():
     for n in names:
         assert hasattr(L, n), n
     assert gdn.gdn_abi_version() == 1
-    for s in range(8):
+    for s in range(9):
         assert gdn.gdn_status_str(s).startswith("GDN_")
     assert gdn.gdn_status_str(99) == "unknown gdn_status"
 
@@ -103,6 +103,23 @@ def test_prefill_validation():
     assert gdn.lib().gdn_prefill_workspace_bytes(1, 64, D16, 0, 2) == 0
     assert prefill(qdt=0, algo=2) == UNSUP
     assert prefill(qdt=0, algo=2, B=0) == UNSUP
+
+
+def test_prefill_noalloc_rejects_sizes_beyond_its_scratch():
+    # The fixed scratch holds the chunked workspace of B*T <= 1152 tokens at
+    # 16/48 heads; larger calls are refused on the host before any launch.
+    L = gdn.lib()
+    assert L.gdn_prefill_workspace_bytes(1, 1152, D16, 1, 0) <= (64 << 20)
+    assert L.gdn_prefill_workspace_bytes(1, 1153, D16, 1, 0) > (64 << 20)
+
+    def na(B, T, qdt=1, algo=0):
+        return L.gdn_prefill_noalloc(_vp(P), 2048, _vp(2 * P), 2048, _vp(3 * P), 6144, qdt,
+                                     _vp(4 * P), _vp(5 * P), 0, _vp(6 * P), _vp(7 * P), None,
+                                     None, _vp(8 * P), 1, B, T, D16, 1.0, algo, None)
+    assert na(1, 1153) == 8            # GDN_ERR_SCRATCH
+    assert na(2, 4096) == 8
+    assert na(1, 64, qdt=0, algo=2) == UNSUP   # validation as gdn_prefill
+    assert na(0, 64) == OK
 
 
 def decode(q=P, k=2 * P, v=3 * P, qdt=1, st=4 * P, o=5 * P, R=4, dims=D16, lengths=None):
