@@ -442,68 +442,72 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
   lds_barrier();
 
   // T, off-diagonal blocks (wave 0): T_ij = -T_ii sum_{j<=m<i} A_im T_mj,
-  // level by level, each product on 16x16x16 MFMA with both f32 operands
-  // split into bf16 hi + lo parts (hi*hi + hi*lo + lo*hi: ~16-bit operands,
-  // f32 accumulation).  A result (D layout) is the B layout of the next
-  // product, so the levels chain in registers.
+  // level by level on 16x16x16 MFMA; a result (D layout) is the B layout of
+  // the next product, so the levels chain in registers.  First with bf16
+  // operands; the largest |T_ts| (s < t) of that T decides whether the chunk
+  // is a two-part one, and a two-part chunk's blocks are then formed again
+  // with both f32 operands split into bf16 hi + lo parts (hi*hi + hi*lo +
+  // lo*hi: ~16-bit operands, f32 accumulation).
   if (w == 0) {
-    auto split_frag = [](float a, float b, float c, float d, s16x4& hi, s16x4& lo) {
-      hi = to_s16x4(a, b, c, d);
-      lo = to_s16x4(a - bf2f((uint16_t)hi[0]), b - bf2f((uint16_t)hi[1]),
-                    c - bf2f((uint16_t)hi[2]), d - bf2f((uint16_t)hi[3]));
-    };
     struct Frag { s16x4 hi, lo; };
-    // A operand: rows of block (i, j) of an f32 LDS matrix, 4 columns per lane.
-    auto a_op = [&](const float* M, int i, int j) {
-      const float4 v = *reinterpret_cast<const float4*>(&M[(i * 16 + li) * FP + j * 16 + lg * 4]);
+    auto make = [](float a, float b, float c, float d, auto two) {
       Frag f;
-      split_frag(v.x, v.y, v.z, v.w, f.hi, f.lo);
+      f.hi = to_s16x4(a, b, c, d);
+      if (decltype(two)::value)
+        f.lo = to_s16x4(a - bf2f((uint16_t)f.hi[0]), b - bf2f((uint16_t)f.hi[1]),
+                        c - bf2f((uint16_t)f.hi[2]), d - bf2f((uint16_t)f.hi[3]));
       return f;
+    };
+    // A operand: rows of block (i, j) of an f32 LDS matrix, 4 columns per lane.
+    auto a_op = [&](const float* M, int i, int j, auto two) {
+      const float4 v = *reinterpret_cast<const float4*>(&M[(i * 16 + li) * FP + j * 16 + lg * 4]);
+      return make(v.x, v.y, v.z, v.w, two);
     };
     // B operand: 4 rows of one column of block (j, j) of T.
-    auto b_diag = [&](int j) {
+    auto b_diag = [&](int j, auto two) {
       const float* c = &Tf[(j * 16 + lg * 4) * FP + j * 16 + li];
-      Frag f;
-      split_frag(c[0], c[FP], c[2 * FP], c[3 * FP], f.hi, f.lo);
-      return f;
+      return make(c[0], c[FP], c[2 * FP], c[3 * FP], two);
     };
-    auto b_reg = [&](const f32x4& v) {
-      Frag f;
-      split_frag(v[0], v[1], v[2], v[3], f.hi, f.lo);
-      return f;
-    };
-    auto mul = [&](const Frag& a, const Frag& b, f32x4 acc) {
-      acc = mfma16k16(a.lo, b.hi, acc);
-      acc = mfma16k16(a.hi, b.lo, acc);
+    auto b_reg = [&](const f32x4& v, auto two) { return make(v[0], v[1], v[2], v[3], two); };
+    auto mul = [&](const Frag& a, const Frag& b, f32x4 acc, auto two) {
+      if (decltype(two)::value) {
+        acc = mfma16k16(a.lo, b.hi, acc);
+        acc = mfma16k16(a.hi, b.lo, acc);
+      }
       return mfma16k16(a.hi, b.hi, acc);
     };
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    // T_ij = -T_ii X, stored to LDS; returned for the next levels.
-    auto finish = [&](int i, int j, const f32x4& X) {
-      const f32x4 y = mul(a_op(Tf, i, i), b_reg(X), z);
-      f32x4 t;
+    auto blocks = [&](auto two) {
+      // T_ij = -T_ii X, stored to LDS; returned for the next levels.
+      auto finish = [&](int i, int j, const f32x4& X) {
+        const f32x4 y = mul(a_op(Tf, i, i, two), b_reg(X, two), z, two);
+        f32x4 t;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        t[r] = -y[r];
-        Tf[(i * 16 + lg * 4 + r) * FP + j * 16 + li] = t[r];
-        tmax = fmaxf(tmax, fabsf(t[r]));
-      }
-      return t;
+        for (int r = 0; r < 4; ++r) {
+          t[r] = -y[r];
+          Tf[(i * 16 + lg * 4 + r) * FP + j * 16 + li] = t[r];
+          tmax = fmaxf(tmax, fabsf(t[r]));
+        }
+        return t;
+      };
+      const Frag t00 = b_diag(0, two), t11 = b_diag(1, two), t22 = b_diag(2, two);
+      const f32x4 t10 = finish(1, 0, mul(a_op(Af, 1, 0, two), t00, z, two));
+      const f32x4 t21 = finish(2, 1, mul(a_op(Af, 2, 1, two), t11, z, two));
+      finish(3, 2, mul(a_op(Af, 3, 2, two), t22, z, two));
+      const f32x4 t20 = finish(
+          2, 0, mul(a_op(Af, 2, 1, two), b_reg(t10, two), mul(a_op(Af, 2, 0, two), t00, z, two), two));
+      finish(3, 1,
+             mul(a_op(Af, 3, 2, two), b_reg(t21, two), mul(a_op(Af, 3, 1, two), t11, z, two), two));
+      finish(3, 0,
+             mul(a_op(Af, 3, 2, two), b_reg(t20, two),
+                 mul(a_op(Af, 3, 1, two), b_reg(t10, two), mul(a_op(Af, 3, 0, two), t00, z, two),
+                     two),
+                 two));
     };
-    const Frag t00 = b_diag(0), t11 = b_diag(1), t22 = b_diag(2);
-    const f32x4 t10 = finish(1, 0, mul(a_op(Af, 1, 0), t00, z));
-    const f32x4 t21 = finish(2, 1, mul(a_op(Af, 2, 1), t11, z));
-    const f32x4 t32 = finish(3, 2, mul(a_op(Af, 3, 2), t22, z));
-    const f32x4 t20 =
-        finish(2, 0, mul(a_op(Af, 2, 1), b_reg(t10), mul(a_op(Af, 2, 0), t00, z)));
-    const f32x4 t31 =
-        finish(3, 1, mul(a_op(Af, 3, 2), b_reg(t21), mul(a_op(Af, 3, 1), t11, z)));
-    finish(3, 0,
-           mul(a_op(Af, 3, 2), b_reg(t20),
-               mul(a_op(Af, 3, 1), b_reg(t10), mul(a_op(Af, 3, 0), t00, z))));
-    (void)t32; (void)t31;
+    blocks(std::false_type{});
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+    if (tmax > kSplitThreshold) blocks(std::true_type{});  // wave-uniform
     if (lane == 0) Tmax = tmax;
   }
   lds_barrier();
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
 
   // Rows of T scaled by a per-column factor (b gamma for W, b for Ut), as an
   // MFMA operand in two bf16 parts (hi + lo), read from LDS when needed.
-  auto trow = [&](int tb, int kk, const float* colscale, bf16x8& hi, bf16x8& lo) {
+  auto trow = [&](int tb, int kk, const float* colscale, bf16x8& hi, bf16x8& lo, bool two) {
     const float* row = &Tf[(tb * 16 + li) * FP + kk * 32 + lg * 8];
     const float4 r0 = *reinterpret_cast<const float4*>(row);
     const float4 r1 = *reinterpret_cast<const float4*>(row + 4);
@@ -568,10 +572,10 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     const float v[8] = {r0.x * s0.x, r0.y * s0.y, r0.z * s0.z, r0.w * s0.w,
                         r1.x * s1.x, r1.y * s1.y, r1.z * s1.z, r1.w * s1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 h = (__bf16)v[i];
-      hi[i] = h;
-      lo[i] = (__bf16)(v[i] - (float)h);
+    for (int i = 0; i < 8; ++i) hi[i] = (__bf16)v[i];
+    if (two) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lo[i] = (__bf16)(v[i] - (float)hi[i]);
     }
   };
 
@@ -589,13 +593,15 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       bf16x8 tg0, tg0l, tg1, tg1l;
-      trow(tb, 0, BGs, tg0, tg0l);
-      if (tb >= 2) trow(tb, 1, BGs, tg1, tg1l);
+      trow(tb, 0, BGs, tg0, tg0l, split);
+      if (tb >= 2) trow(tb, 1, BGs, tg1, tg1l, split);
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16(kt[d][0], tg0l, acc);
-        if (tb >= 2) acc = mfma16(kt[d][1], tg1l, acc);
+        if (split) {
+          acc = mfma16(kt[d][0], tg0l, acc);
+          if (tb >= 2) acc = mfma16(kt[d][1], tg1l, acc);
+        }
         acc = mfma16(kt[d][0], tg0, acc);
         if (tb >= 2) acc = mfma16(kt[d][1], tg1, acc);
         const int t = tb * 16 + li, dk = (2 * w + d) * 16 + lg * 4;
@@ -626,14 +632,16 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     bf16x8 tb0, tb0l, tb1, tb1l;
-    trow(tb, 0, Bs, tb0, tb0l);
-    if (tb >= 2) trow(tb, 1, Bs, tb1, tb1l);
+    trow(tb, 0, Bs, tb0, tb0l, split);
+    if (tb >= 2) trow(tb, 1, Bs, tb1, tb1l, split);
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
       const int vb = 2 * w + d;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(tb0l, vt[d][0], acc);
-      if (tb >= 2) acc = mfma16(tb1l, vt[d][1], acc);
+      if (split) {
+        acc = mfma16(tb0l, vt[d][0], acc);
+        if (tb >= 2) acc = mfma16(tb1l, vt[d][1], acc);
+      }
       acc = mfma16(tb0, vt[d][0], acc);
       if (tb >= 2) acc = mfma16(tb1, vt[d][1], acc);
       // Utf[sl = vb / 2][w = tb][cvb][cli + 16 lg][0..3] with dvp(cvb, cli) = the
