@@ -80,6 +80,8 @@ def lib():
         L.gdn_linear_workspace_bytes.restype = sz
         L.gdn_linear.argtypes = [P, i64, P, i64, P, i64, i32, i32, i32, i32, P, sz, P]
         L.gdn_linear.restype = ctypes.c_int
+        L.gdn_linear_tune.argtypes = L.gdn_linear.argtypes
+        L.gdn_linear_tune.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -402,9 +404,7 @@ def gdn_linear_workspace_bytes():
     return int(lib().gdn_linear_workspace_bytes())
 
 
-def gdn_linear(x, W, y=None, out_dtype=torch.bfloat16, workspace=None):
-    """y = x W^T for bf16 x [M, K] and W [N, K] (a Linear layer's weight),
-    f32 accumulation; y [M, N] in out_dtype (bf16 or f32)."""
+def _linear(fn, name, x, W, y, out_dtype, workspace):
     _need_cuda(x, W, y, workspace)
     M, K = x.shape
     N = W.shape[0]
@@ -418,7 +418,18 @@ def gdn_linear(x, W, y=None, out_dtype=torch.bfloat16, workspace=None):
         wsb = 0
     else:
         wsb = workspace.numel() * workspace.element_size()
-    _check(lib().gdn_linear(_ptr(x), _row_ld(x, "x"), _ptr(W), _row_ld(W, "W"), _ptr(y),
-                            _row_ld(y, "y"), _dt(y), M, N, K, _ptr(workspace), wsb, _stream(x)),
-           "gdn_linear")
+    _check(fn(_ptr(x), _row_ld(x, "x"), _ptr(W), _row_ld(W, "W"), _ptr(y), _row_ld(y, "y"),
+              _dt(y), M, N, K, _ptr(workspace), wsb, _stream(x)), name)
     return y
+
+
+def gdn_linear(x, W, y=None, out_dtype=torch.bfloat16, workspace=None):
+    """y = x W^T for bf16 x [M, K] and W [N, K] (a Linear layer's weight),
+    f32 accumulation; y [M, N] in out_dtype (bf16 or f32)."""
+    return _linear(lib().gdn_linear, "gdn_linear", x, W, y, out_dtype, workspace)
+
+
+def gdn_linear_tune(x, W, y=None, out_dtype=torch.bfloat16, workspace=None):
+    """gdn_linear that also times the shape's candidate algorithms and keeps
+    the fastest for later gdn_linear calls of the same shape (synchronises)."""
+    return _linear(lib().gdn_linear_tune, "gdn_linear_tune", x, W, y, out_dtype, workspace)

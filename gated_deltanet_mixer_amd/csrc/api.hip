@@ -1,6 +1,7 @@
 // The C ABI (include/gdn.h): host-side validation, then one or two launches on
 // the caller's stream.  Nothing here allocates or synchronises (gdn_linear's
-// first call on a device creates its hipBLASLt handle, in proj.hip).
+// first call on a device creates its hipBLASLt handle, and gdn_linear_tune
+// times on the stream; both in proj.hip).
 #include <hip/hip_runtime.h>
 
 #include "../../include/gdn.h"
@@ -381,9 +382,9 @@ int gdn_gate_proj(const void* x, int64_t x_ld, int32_t x_dt, const float* W_a,
 
 size_t gdn_linear_workspace_bytes(void) { return (size_t)32 << 20; }
 
-int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y, int64_t y_ld,
-               int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
-               size_t workspace_bytes, void* stream) {
+static int linear_call(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y,
+                       int64_t y_ld, int32_t y_dt, int32_t M, int32_t N, int32_t K,
+                       void* workspace, size_t workspace_bytes, bool tune, void* stream) {
   if (M < 0 || N <= 0 || K <= 0) return GDN_ERR_SHAPE;
   if (!dtype_ok(y_dt)) return GDN_ERR_DTYPE;
   if (x_ld < K || w_ld < K || y_ld < N) return GDN_ERR_SHAPE;
@@ -399,11 +400,26 @@ int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y
   if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, W, wbytes)) return GDN_ERR_SHAPE;
   switch (gdn::launch_linear(static_cast<const uint16_t*>(x), x_ld,
                              static_cast<const uint16_t*>(W), w_ld, y, y_ld, y_dt, M, N, K,
-                             workspace, workspace_bytes, static_cast<hipStream_t>(stream))) {
+                             workspace, workspace_bytes, tune, static_cast<hipStream_t>(stream))) {
     case gdn::LinearStatus::kOk: return GDN_OK;
-    case gdn::LinearStatus::kNoAlgorithm: return GDN_ERR_UNSUPPORTED;
+    case gdn::LinearStatus::kNoAlgorithm:
+    case gdn::LinearStatus::kBadLibrary: return GDN_ERR_UNSUPPORTED;
     default: return GDN_ERR_LAUNCH;
   }
+}
+
+int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y, int64_t y_ld,
+               int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return linear_call(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace, workspace_bytes, false,
+                     stream);
+}
+
+int gdn_linear_tune(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y,
+                    int64_t y_ld, int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return linear_call(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace, workspace_bytes, true,
+                     stream);
 }
 
 }  // extern "C"

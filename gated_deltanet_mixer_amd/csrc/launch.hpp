@@ -77,10 +77,11 @@ hipError_t launch_gate_proj(const uint16_t* x, int64_t x_ld, const float* Wa, co
                             hipStream_t stream);
 
 // bf16 linear layer y[M][N] = x[M][K] W[N][K]^T on hipBLASLt, f32 accumulation,
-// y in bf16 (y_dt 1) or f32 (y_dt 0).
-enum class LinearStatus { kOk, kNoAlgorithm, kLaunchFailed };
+// y in bf16 (y_dt 1) or f32 (y_dt 0).  `tune` times the shape's candidates
+// (synchronises) and keeps the fastest for later calls of the same shape.
+enum class LinearStatus { kOk, kNoAlgorithm, kBadLibrary, kLaunchFailed };
 LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
                            void* y, int64_t y_ld, int y_dt, int M, int N, int K, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream);
+                           size_t workspace_bytes, bool tune, hipStream_t stream);
 
 }  // namespace gdn

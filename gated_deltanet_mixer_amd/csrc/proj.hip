@@ -13,15 +13,17 @@
 //   product with f32 accumulation.
 // * in_proj_qkv, in_proj_z and out_proj are plain bf16 GEMMs with f32
 //   accumulation; they go to hipBLASLt.  One handle per device is created on
-//   first use and kept until the process ends; the plan of each shape
-//   (descriptors and the fastest of the heuristic's candidates that fit the
-//   workspace, timed on the shape's first call) is cached beside it.  The library links libhipblaslt.so.1 by soname: in a
-//   process that already holds a copy of that library (PyTorch ships one),
+//   first use and kept until the process ends; the plans of recent shapes
+//   (descriptors and the heuristic's first candidate that fits the
+//   workspace, or the fastest of several when the caller asks for timing)
+//   are cached beside it.  The library links libhipblaslt.so.1 by soname: in
+//   a process that already holds a copy of that library (PyTorch ships one),
 //   that copy serves these calls.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
+#include <deque>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -345,21 +347,36 @@ struct LtPlan {
   hipblasLtMatrixLayout_t A = nullptr, B = nullptr, D = nullptr;
   hipblasLtMatmulAlgo_t algo;
   bool ok = false;
+  bool tuned = false;
 };
 
 using PlanKey = std::tuple<int, int, int, int, int64_t, int64_t, int64_t, int, size_t>;
 
+// Plans made without timing are kept for the kMaxPlans most recent shapes
+// (a ragged caller brings a new M on almost every call); timed plans stay.
+constexpr size_t kMaxPlans = 64;
+
 std::mutex g_lt_mu;
 std::map<int, hipblasLtHandle_t> g_lt_handle;
 std::map<PlanKey, LtPlan> g_lt_plans;
+std::deque<PlanKey> g_lt_untimed;  // keys of untimed plans, oldest first
+
+void destroy_plan(LtPlan& p) {
+  if (p.desc) hipblasLtMatmulDescDestroy(p.desc);
+  if (p.A) hipblasLtMatrixLayoutDestroy(p.A);
+  if (p.B) hipblasLtMatrixLayoutDestroy(p.B);
+  if (p.D) hipblasLtMatrixLayoutDestroy(p.D);
+  p = LtPlan{};
+}
 
 // Builds the plan for one shape; false if hipBLASLt has no algorithm for it.
-// Of the heuristic's candidates that fit the workspace, up to kTune are timed
-// on the caller's own buffers and stream (one warm-up and three timed runs
-// each; they all write y, which the call then writes again) and the fastest
-// is kept.  This is the first call of the shape only.
-bool make_plan(hipblasLtHandle_t h, LtPlan& p, const void* x, int64_t x_ld, const void* W,
-               int64_t w_ld, void* y, int64_t y_ld, int y_dt, int M, int N, int K,
+// Without `tune` it takes the heuristic's first candidate that fits the
+// workspace: host work only, nothing enqueued or awaited.  With `tune`, up to
+// kTune of the fitting candidates are timed on the caller's own buffers and
+// stream (one warm-up and three timed runs each, all writing y, which the
+// call then writes again) and the fastest is kept; that synchronises.
+bool make_plan(hipblasLtHandle_t h, LtPlan& p, bool tune, const void* x, int64_t x_ld,
+               const void* W, int64_t w_ld, void* y, int64_t y_ld, int y_dt, int M, int N, int K,
                void* workspace, size_t ws_bytes, hipStream_t stream) {
   const hipblasOperation_t opA = HIPBLAS_OP_T, opB = HIPBLAS_OP_N;
   const hipDataType dty = y_dt == 1 ? HIP_R_16BF : HIP_R_32F;
@@ -391,7 +408,7 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, const void* x, int64_t x_ld, cons
       fit[nfit++] = i;
   if (nfit == 0) return false;
   p.algo = res[fit[0]].algo;
-  if (nfit == 1) return true;
+  if (!tune || nfit == 1) return true;
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return true;
   if (hipEventCreate(&e1) != hipSuccess) {
@@ -426,7 +443,7 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, const void* x, int64_t x_ld, cons
 
 LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
                            void* y, int64_t y_ld, int y_dt, int M, int N, int K, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+                           size_t workspace_bytes, bool tune, hipStream_t stream) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LinearStatus::kLaunchFailed;
   std::lock_guard<std::mutex> lock(g_lt_mu);
@@ -434,15 +451,37 @@ LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, i
   if (hit == g_lt_handle.end()) {
     hipblasLtHandle_t h = nullptr;
     if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return LinearStatus::kLaunchFailed;
+    // The descriptors and results passed here follow this header's major
+    // version (the soname's); a loaded library of another major is refused.
+    int ver = 0;
+    if (hipblasLtGetVersion(h, &ver) != HIPBLAS_STATUS_SUCCESS ||
+        ver / 100000 != HIPBLASLT_VERSION_MAJOR) {
+      hipblasLtDestroy(h);
+      return LinearStatus::kBadLibrary;
+    }
     hit = g_lt_handle.emplace(dev, h).first;
   }
   const PlanKey key{dev, M, N, K, x_ld, w_ld, y_ld, y_dt, workspace_bytes};
   auto pit = g_lt_plans.find(key);
+  if (pit != g_lt_plans.end() && tune && !pit->second.tuned) {
+    g_lt_untimed.erase(std::find(g_lt_untimed.begin(), g_lt_untimed.end(), key));
+    destroy_plan(pit->second);
+    g_lt_plans.erase(pit);
+    pit = g_lt_plans.end();
+  }
   if (pit == g_lt_plans.end()) {
+    if (!tune && g_lt_untimed.size() >= kMaxPlans) {
+      auto old = g_lt_plans.find(g_lt_untimed.front());
+      destroy_plan(old->second);
+      g_lt_plans.erase(old);
+      g_lt_untimed.pop_front();
+    }
     LtPlan p;
-    p.ok = make_plan(hit->second, p, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace,
+    p.ok = make_plan(hit->second, p, tune, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace,
                      workspace_bytes, stream);
+    p.tuned = tune;
     pit = g_lt_plans.emplace(key, p).first;
+    if (!tune) g_lt_untimed.push_back(key);
   }
   const LtPlan& p = pit->second;
   if (!p.ok) return LinearStatus::kNoAlgorithm;

@@ -18,9 +18,10 @@
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
- *    The library never allocates, frees, synchronises, logs or aborts, with
- *    one exception: gdn_linear's first call on a device creates the
- *    hipBLASLt handle it keeps for that device (see there).
+ *    The library never allocates device memory, frees, synchronises, logs
+ *    or aborts, with two exceptions: the first gdn_linear or
+ *    gdn_linear_tune call on a device creates the hipBLASLt handle kept for
+ *    that device, and gdn_linear_tune synchronises (see there).
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream) and the call returns at once.  Device faults, if
  *    any, surface at the caller's next synchronisation.
@@ -342,13 +343,15 @@ size_t gdn_linear_workspace_bytes(void);
  *      overlap x or W.
  *   y[m][n] = sum_k x[m][k] W[n][k], f32 accumulation, one rounding to y_dt.
  * Runs on hipBLASLt (whichever libhipblaslt.so.1 the process loaded first
- * serves the call).  The first call on a device creates a hipBLASLt handle
- * and keeps it.  The first call of each shape builds and keeps its plan: it
- * times up to eight of the heuristic's candidates that fit the workspace on
- * this call's own buffers and stream (each writes y; the call's result is
- * written last) and keeps the fastest.  Those first calls allocate and
- * synchronise, so make them before any graph capture.  Calls
- * from several threads are serialised by a lock while they enqueue.
+ * serves the call; a loaded library of another major version than the
+ * header this library was built with gives GDN_ERR_UNSUPPORTED).  The first
+ * call on a device creates a hipBLASLt handle and keeps it (hipBLASLt may
+ * allocate then; make that call before any graph capture).  A shape's plan
+ * (descriptors and the heuristic's first algorithm that fits the workspace)
+ * is made on the host by its first call, with nothing enqueued or awaited
+ * beyond the product, and kept for the 64 most recent shapes; a shape timed
+ * by gdn_linear_tune keeps its timed plan.  Calls from several threads are
+ * serialised by a lock while they enqueue.
  *   workspace  scratch for hipBLASLt, 256-byte aligned, workspace_bytes long
  *              (gdn_linear_workspace_bytes() recommended), or NULL with 0.
  * Constraints: M >= 0 (0 is a no-op), N > 0, K > 0; x_ld >= K, w_ld >= K,
@@ -359,6 +362,20 @@ size_t gdn_linear_workspace_bytes(void);
 int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y, int64_t y_ld,
                int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_linear_tune -- gdn_linear that also times the shape's algorithms: up
+ * to eight of the heuristic's candidates that fit the workspace run on this
+ * call's own buffers and stream (one warm-up and three timed runs each; each
+ * writes y, and the call's product is written last), the fastest is kept as
+ * the shape's plan for later gdn_linear calls, and the call synchronises the
+ * stream.  For callers with a fixed set of shapes (a model's projections at
+ * a set batch), once per shape, before any graph capture.  Arguments,
+ * result and errors as gdn_linear.
+ */
+int gdn_linear_tune(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y,
+                    int64_t y_ld, int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* Size of the fixed device scratch of gdn_prefill_noalloc: 64 MiB, enough
  * for the chunked prefill of B*T <= 1152 tokens at 16 q/k and 48 value heads

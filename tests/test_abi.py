@@ -30,7 +30,7 @@ def test_header_and_exports():
             "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version",
             "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes", "gdn_prefill_slots",
             "gdn_prefill_slots_workspace_bytes", "gdn_decode_rows_multi", "gdn_gate_proj",
-            "gdn_linear", "gdn_linear_workspace_bytes",
+            "gdn_linear", "gdn_linear_tune", "gdn_linear_workspace_bytes",
             "gdn_gate_proj_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -293,6 +293,11 @@ def test_linear_validation():
     assert f(ws=None, wsb=1024) == WS
     assert f(y=P + 1024) == SHAPE      # y overlaps x
     assert f(M=0, x=0, W=0, y=0) == OK
+    # the timing variant validates the same way, before touching the device
+    assert L.gdn_linear_tune(None, 5120, _vp(64 * P), 5120, _vp(4096 * P), 10240, 1, 8, 10240,
+                             5120, None, 0, None) == NULL
+    assert L.gdn_linear_tune(_vp(P), 100, _vp(64 * P), 5120, _vp(4096 * P), 10240, 1, 8, 10240,
+                             5120, None, 0, None) == SHAPE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -4,8 +4,9 @@ replayed: every replay must give the eager step's results bit for bit.
 The step for R fixed rows: in_proj_qkv and in_proj_z (gdn_linear), the gate
 projections (gdn_gate_proj), the conv over one token with each row's conv
 history (gdn_conv_silu), decode_rows, the gated RMSNorm in place and out_proj.
-The eager calls run first (they also build the hipBLASLt plans, which may
-synchronise and so cannot happen under capture).  The graph is replayed four
+The eager calls run first (they also create the hipBLASLt handle, which may
+allocate, and the shapes' plans, so that the captured calls reuse the same
+plans as the eager step).  The graph is replayed four
 times with eager work and synchronisations in between; before each replay
 the captured buffers are reset to the same inputs, so each replay must equal
 the eager step exactly.

@@ -147,6 +147,39 @@ def test_linear_parity(M, N, K, out):
     assert e <= (TOL_LIN_F32 if out == torch.float32 else TOL_LIN_BF16)
 
 
+def test_linear_tune_then_plain_calls():
+    """gdn_linear_tune gives the oracle's product and leaves its timed plan for
+    the shape: a later gdn_linear call of the same shape repeats it bit for bit."""
+    banner("linear tune M=64 N=512 K=5120")
+    M, N, K = 64, 512, 5120
+    p = proj_inputs(M, K=K, outs=(("W", N),), gate_H=0, seed=45)
+    ws = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    x, W = dev(p["x"]), dev(p["W"])
+    y0 = gdn.gdn_linear(x, W, out_dtype=torch.float32, workspace=ws)
+    y1 = gdn.gdn_linear_tune(x, W, out_dtype=torch.float32, workspace=ws)
+    y2 = gdn.gdn_linear(x, W, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.linear(to_f64(p["x"]), to_f64(p["W"]))
+    for y in (y0, y1, y2):
+        assert max_rel_err(host_f64(y), ref) <= TOL_LIN_F32
+    assert torch.equal(y1, y2)
+
+
+def test_linear_many_row_counts():
+    """A ragged caller's pattern: 80 different M in a row (more shapes than the
+    plan cache keeps), then the first ones again, each against the oracle."""
+    banner("linear 80 row counts")
+    N, K = 96, 256
+    p = proj_inputs(100, K=K, outs=(("W", N),), gate_H=0, seed=46)
+    x, W = dev(p["x"]), dev(p["W"])
+    ref = oracle.linear(to_f64(p["x"]), to_f64(p["W"]))
+    for M in list(range(1, 81)) + [1, 2, 3, 77]:
+        y = gdn.gdn_linear(x[:M], W, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        e = max_rel_err(host_f64(y), ref[:M])
+        assert e <= TOL_LIN_F32, (M, e)
+
+
 def test_linear_without_workspace_and_strided_output():
     """qkv and z written as column ranges of one [M, 16384] buffer, x a column
     slice of a wider buffer; no workspace."""
