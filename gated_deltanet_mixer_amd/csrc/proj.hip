@@ -412,7 +412,7 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, bool tune, const void* x, int64_t
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return true;
   if (hipEventCreate(&e1) != hipSuccess) {
-    hipEventDestroy(e0);
+    (void)hipEventDestroy(e0);
     return true;
   }
   const float alpha = 1.0f, beta = 0.0f;
@@ -434,8 +434,8 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, bool tune, const void* x, int64_t
       p.algo = *al;
     }
   }
-  hipEventDestroy(e0);
-  hipEventDestroy(e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
   return true;
 }
 
