@@ -561,21 +561,35 @@ def main():
     for i in range(args.steps):
         proj_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         dl_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    # The timed region: each part's K calls back to back between one pair of
+    # events on the library's stream; the mean per call is what the rates
+    # below use.  A second pass with events around every call gives each
+    # part's per-call median / min / p90 (an event pair per call adds its own
+    # few microseconds) and the split of the multi-call parts.
+    reg = {p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for p in order}
     torch.cuda.synchronize()
     log(f"timed: {args.steps} steps")
     t_start = time.perf_counter()
+    for p in order:
+        reg[p][0].record()
+        for i in range(args.steps):
+            fns[p](args.warmup + args.steps + i)  # (no per-call events at these indices)
+        reg[p][1].record()
+        torch.cuda.synchronize()
+        log(f"part {p} done")
+    wall = time.perf_counter() - t_start
+    med = {p: reg[p][0].elapsed_time(reg[p][1]) / args.steps for p in order}  # ms per call
+
     for p in order:
         for i in range(args.steps):
             evs[p][i][0].record()
             fns[p](args.warmup + i)
             evs[p][i][1].record()
         torch.cuda.synchronize()
-        log(f"part {p} done")
-    wall = time.perf_counter() - t_start
-
+    log("per-call pass done")
     per = {p: [evs[p][i][0].elapsed_time(evs[p][i][1]) for i in range(args.steps)]
            for p in order}  # ms per call
-    med = {p: float(np.median(v)) for p, v in per.items()}  # ms
     ms_per_step = wall * 1e3 / args.steps
 
     out = {
@@ -595,11 +609,12 @@ def main():
                    "qk_heads": HK, "v_heads": HV, "head_dim": D,
                    "value_is": "tokens/s of one gdn_prefill call (the chunked gated delta rule "
                                "alone: chunk_prep + chunk_chain) on the B=1 T=4096 prefill "
-                               "workload, median over the timed calls; the whole mixer at the "
-                               "same size (conv + rule + gated norm) is layer_prefill",
+                               "workload, mean over the timed calls run back to back; the "
+                               "whole mixer at the same size (conv + rule + gated norm) is "
+                               "layer_prefill",
                    "step": "one call of each part: " + ", ".join(order)},
     }
-    parts_out = {p: stats(per[p]) for p in order}
+    parts_out = {p: dict(region_mean_us=round(med[p] * 1e3, 2), **stats(per[p])) for p in order}
     out["parts_us"] = parts_out
     roofs = {}
 
@@ -717,7 +732,7 @@ def main():
                 "value": round(T_PREFILL / ((med["layer"] + t_proj) * 1e-3), 1),
                 "unit": "tokens/s",
                 "workload": "projections + gdn_mixer_prefill at B=1 T=4096, the two parts' "
-                            "median times added",
+                            "mean times added",
                 "us": round((med["layer"] + t_proj) * 1e3, 2)}
     if "dlayer" in med:
         t_dl = med["dlayer"]

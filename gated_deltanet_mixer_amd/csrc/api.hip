@@ -172,7 +172,7 @@ int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t 
   if (q_row_stride < (int64_t)Hk * 128 || k_row_stride < (int64_t)Hk * 128 ||
       v_row_stride < (int64_t)Hv * 128)
     return GDN_ERR_SHAPE;
-  if ((int64_t)R * Hv * 4 > INT32_MAX) return GDN_ERR_SHAPE;  // four workgroups per (row, head)
+  if ((int64_t)R * Hv * 8 > INT32_MAX) return GDN_ERR_SHAPE;  // eight workgroups per (row, head)
   if (q_row_stride % 8 || k_row_stride % 8 || v_row_stride % 8) return GDN_ERR_ALIGN;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(state, 16) || !aligned(a, dsize(gate_dt)) || !aligned(b, dsize(gate_dt)) ||

@@ -23,17 +23,21 @@ __device__ __forceinline__ float dot8(const float* a, const float* b) {
 // ---------------------------------------------------------------------------
 // decode_rows: one new token per fixed row, state [R, Hv, 128, 128] updated in
 // place.  HBM-bound: 64 KiB read and 64 KiB written per (row, head).
-// DEC_PARTS workgroups per (row, value head), each with 32 value rows: wave w
-// owns rows 32 part + 8w + 4 it + g (it = 0, 1; g = lane / 16), both loaded
-// before any arithmetic.  Lane l of a 16-lane group holds elements 4l..4l+3
-// and 64+4l..64+4l+3 of its row, so each 16-byte load or store instruction
-// covers 256 contiguous bytes of four rows.  Against one workgroup per (row,
-// head) with 8 contiguous elements per lane this runs at 5.5 TB/s instead of
-// 4.8 TB/s: the finer grid (12288 workgroups at 64 rows) leaves no tail of
-// half-empty rounds.  (Non-temporal stores measured no faster.)
+// DEC_PARTS workgroups per (row, value head), each with 16 value rows: wave w
+// owns rows 16 part + 4w + g (g = lane / 16), loaded before any arithmetic.
+// Lane l of a 16-lane group holds elements 4l..4l+3 and 64+4l..64+4l+3 of its
+// row, so each 16-byte load or store instruction covers 256 contiguous bytes
+// of four rows.  Against one workgroup per (row, head) with 8 contiguous
+// elements per lane this runs at 5.5 TB/s instead of 4.8 TB/s: the finer grid
+// leaves no tail of half-empty rounds.  Two parts of 64 rows ran 76.7 us at
+// 64 rows, four of 32 rows 72.6-73.4 us, eight of 16 rows 69.8-71.1 us (rocprof).
+// (Non-temporal stores measured no faster.)  The multi-token kernel keeps
+// four parts of 32 rows (two rows a lane): with eight it went 225 -> 275 us.
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_PARTS = 4;
+constexpr int DEC_PARTS = 8;
 constexpr int DEC_IT = 128 / DEC_PARTS / 16;  // rows per 16-lane group
+constexpr int MULTI_PARTS = 4;
+constexpr int MULTI_IT = 128 / MULTI_PARTS / 16;
 
 // The 8 elements lane l16 of a 16-lane group holds of a 128-wide row.
 __device__ __forceinline__ void load_row_halves(const float* row, int l16, float* out) {
@@ -119,24 +123,24 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_rows_multi_kernel(
     const G* __restrict__ b, const float* __restrict__ A_log, const float* __restrict__ dt_bias,
     float* __restrict__ state, float* __restrict__ snapshots, const int32_t* __restrict__ lengths,
     T* __restrict__ o, int K, int Hk, int Hv, float q_scale) {
-  const int part = blockIdx.x % DEC_PARTS;
-  const int rh = blockIdx.x / DEC_PARTS;
+  const int part = blockIdx.x % MULTI_PARTS;
+  const int rh = blockIdx.x / MULTI_PARTS;
   const int r = rh / Hv;
   const int h = rh - r * Hv;
   const int kh = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, grp = lane >> 4, l16 = lane & 15;
-  const int row0 = part * (128 / DEC_PARTS) + wave * 4 * DEC_IT + grp;  // + 4 it
+  const int row0 = part * (128 / MULTI_PARTS) + wave * 4 * MULTI_IT + grp;  // + 4 it
   if (lengths && lengths[r] < 0) {  // idle row: state and snapshots untouched, output zero
     for (int t = 0; t < K; ++t)
-      if (tid < 128 / DEC_PARTS)
-        store1(o + (((int64_t)r * K + t) * Hv + h) * 128 + part * (128 / DEC_PARTS) + tid, 0.0f);
+      if (tid < 128 / MULTI_PARTS)
+        store1(o + (((int64_t)r * K + t) * Hv + h) * 128 + part * (128 / MULTI_PARTS) + tid, 0.0f);
     return;
   }
   float* Sb = state + ((int64_t)r * Hv + h) * (128 * 128);
-  float s[DEC_IT][8];
+  float s[MULTI_IT][8];
 #pragma unroll
-  for (int it = 0; it < DEC_IT; ++it) load_row_halves(Sb + (row0 + 4 * it) * 128, l16, s[it]);
+  for (int it = 0; it < MULTI_IT; ++it) load_row_halves(Sb + (row0 + 4 * it) * 128, l16, s[it]);
   const float Al = A_log[h], Db = dt_bias[h];
 
   for (int t = 0; t < K; ++t) {
@@ -145,9 +149,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_rows_multi_kernel(
     load_row_halves(q + r * q_rs + t * q_ts + kh * 128, l16, qv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) qv[i] *= q_scale;
-    float vr[DEC_IT];
+    float vr[MULTI_IT];
 #pragma unroll
-    for (int it = 0; it < DEC_IT; ++it)
+    for (int it = 0; it < MULTI_IT; ++it)
       vr[it] = load1(v + r * v_rs + t * v_ts + h * 128 + row0 + 4 * it);
     const int64_t gi = ((int64_t)r * K + t) * Hv + h;
     const float al = expf(gate_log_alpha(load1(a + gi), Al, Db));
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_rows_multi_kernel(
     T* ob = o + gi * 128;
     float* snap = snapshots ? snapshots + (((int64_t)r * K + t) * Hv + h) * (128 * 128) : nullptr;
 #pragma unroll
-    for (int it = 0; it < DEC_IT; ++it) {
+    for (int it = 0; it < MULTI_IT; ++it) {
       const int row = row0 + 4 * it;
       const float su = sum16(dot8(s[it], kv));
       const float sq = sum16(dot8(s[it], qv));
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_rows_multi_kernel(
     }
   }
 #pragma unroll
-  for (int it = 0; it < DEC_IT; ++it) store_row_halves(Sb + (row0 + 4 * it) * 128, l16, s[it]);
+  for (int it = 0; it < MULTI_IT; ++it) store_row_halves(Sb + (row0 + 4 * it) * 128, l16, s[it]);
 }
 
 // ---------------------------------------------------------------------------
@@ -317,7 +321,7 @@ static void launch_decode_multi_t(const void* q, int64_t q_rs, int64_t q_ts, con
                                   const float* dt_bias, float* state, float* snapshots,
                                   const int32_t* lengths, void* o, int R, int K, int Hk, int Hv,
                                   float q_scale, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_rows_multi_kernel<T, G>), dim3(R * Hv * DEC_PARTS), dim3(DEC_THREADS),
+  hipLaunchKernelGGL((decode_rows_multi_kernel<T, G>), dim3(R * Hv * MULTI_PARTS), dim3(DEC_THREADS),
                      0, stream,
                      (const T*)q, q_rs, q_ts, (const T*)k, k_rs, k_ts, (const T*)v, v_rs, v_ts,
                      (const G*)a, (const G*)b, A_log, dt_bias, state, snapshots, lengths, (T*)o, K,
