@@ -82,6 +82,8 @@ def lib():
         L.gdn_linear.restype = ctypes.c_int
         L.gdn_linear_tune.argtypes = L.gdn_linear.argtypes
         L.gdn_linear_tune.restype = ctypes.c_int
+        L.gdn_linear_kernel.argtypes = [i32, i32, i32, i64, i64]
+        L.gdn_linear_kernel.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -433,3 +435,13 @@ def gdn_linear_tune(x, W, y=None, out_dtype=torch.bfloat16, workspace=None):
     """gdn_linear that also times the shape's candidate algorithms and keeps
     the fastest for later gdn_linear calls of the same shape (synchronises)."""
     return _linear(lib().gdn_linear_tune, "gdn_linear_tune", x, W, y, out_dtype, workspace)
+
+
+def gdn_linear_kernel(M, N, K, x_ld=None, w_ld=None):
+    """Which engine an untimed gdn_linear call of this shape uses on the
+    current device: the library GEMM's block width (160, 192, 256 or 320), or
+    0 for hipBLASLt.  x_ld and w_ld default to K."""
+    r = lib().gdn_linear_kernel(M, N, K, K if x_ld is None else x_ld, K if w_ld is None else w_ld)
+    if r < 0:
+        raise GDNError(-r, "gdn_linear_kernel")
+    return r

@@ -1,7 +1,7 @@
 // The C ABI (include/gdn.h): host-side validation, then one or two launches on
 // the caller's stream.  Nothing here allocates or synchronises (gdn_linear's
-// first call on a device creates its hipBLASLt handle, and gdn_linear_tune
-// times on the stream; both in proj.hip).
+// first call on a device that goes to hipBLASLt creates its handle, and
+// gdn_linear_tune times on the stream; both in proj.hip).
 #include <hip/hip_runtime.h>
 
 #include "../../include/gdn.h"
@@ -420,6 +420,16 @@ int gdn_linear_tune(const void* x, int64_t x_ld, const void* W, int64_t w_ld, vo
                     size_t workspace_bytes, void* stream) {
   return linear_call(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace, workspace_bytes, true,
                      stream);
+}
+
+int gdn_linear_kernel(int32_t M, int32_t N, int32_t K, int64_t x_ld, int64_t w_ld) {
+  if (M < 0 || N <= 0 || K <= 0 || x_ld < K || w_ld < K) return -GDN_ERR_SHAPE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -GDN_ERR_LAUNCH;
+  const int width = gdn::gemm_bf16_width(M, N, K, x_ld, w_ld, cus);
+  return width * 32;
 }
 
 }  // extern "C"

@@ -76,9 +76,19 @@ hipError_t launch_gate_proj(const uint16_t* x, int64_t x_ld, const float* Wa, co
                             float* a, float* b, int64_t ab_ld, int M, int K, int H, void* workspace,
                             hipStream_t stream);
 
-// bf16 linear layer y[M][N] = x[M][K] W[N][K]^T on hipBLASLt, f32 accumulation,
-// y in bf16 (y_dt 1) or f32 (y_dt 0).  `tune` times the shape's candidates
-// (synchronises) and keeps the fastest for later calls of the same shape.
+// The library's bf16 GEMM y[M][N] = x[M][K] W[N][K]^T (gemm.hip): the block
+// width code (5, 6, 8 or 10: 160, 192, 256 or 320 outputs) that suits the
+// shape on a GPU of `cus` CUs, or 0 when the shape should go to hipBLASLt.
+int gemm_bf16_width(int M, int N, int K, int64_t x_ld, int64_t w_ld, int cus);
+hipError_t launch_gemm_bf16(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
+                            void* y, int64_t y_ld, int y_dt, int M, int N, int K, int width,
+                            hipStream_t stream);
+
+// bf16 linear layer y[M][N] = x[M][K] W[N][K]^T, f32 accumulation, y in bf16
+// (y_dt 1) or f32 (y_dt 0): the library's GEMM when gemm_bf16_width picks a
+// width, else hipBLASLt.  `tune` times hipBLASLt's candidates and the
+// library's GEMM (synchronises) and keeps the fastest for later calls of the
+// same shape.
 enum class LinearStatus { kOk, kNoAlgorithm, kBadLibrary, kLaunchFailed };
 LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
                            void* y, int64_t y_ld, int y_dt, int M, int N, int K, void* workspace,

@@ -12,13 +12,15 @@
 //   part is exact in f32, so three MFMAs per k-step give the f32-weight
 //   product with f32 accumulation.
 // * in_proj_qkv, in_proj_z and out_proj are plain bf16 GEMMs with f32
-//   accumulation; they go to hipBLASLt.  One handle per device is created on
-//   first use and kept until the process ends; the plans of recent shapes
-//   (descriptors and the heuristic's first candidate that fits the
-//   workspace, or the fastest of several when the caller asks for timing)
-//   are cached beside it.  The library links libhipblaslt.so.1 by soname: in
-//   a process that already holds a copy of that library (PyTorch ships one),
-//   that copy serves these calls.
+//   accumulation.  Shapes that fill the GPU with the library's own GEMM
+//   (gemm.hip) run there; the others go to hipBLASLt.  One hipBLASLt handle
+//   per device is created on its first use and kept until the process ends;
+//   the plans of recent shapes (descriptors and the heuristic's first
+//   candidate that fits the workspace, or the fastest of the library's GEMM
+//   and several candidates when the caller asks for timing) are cached
+//   beside it.  The library links libhipblaslt.so.1 by soname: in a process
+//   that already holds a copy of that library (PyTorch ships one), that copy
+//   serves these calls.
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
@@ -346,8 +348,10 @@ struct LtPlan {
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t A = nullptr, B = nullptr, D = nullptr;
   hipblasLtMatmulAlgo_t algo;
-  bool ok = false;
-  bool tuned = false;
+  bool ok = false;     // hipBLASLt has an algorithm for the shape
+  bool tuned = false;  // made by a timed call
+  float ms = 0.0f;     // the chosen algorithm's time for three runs (timed plans)
+  int own = 0;         // nonzero: the library's GEMM at this width won the timing
 };
 
 using PlanKey = std::tuple<int, int, int, int, int64_t, int64_t, int64_t, int, size_t>;
@@ -358,6 +362,7 @@ constexpr size_t kMaxPlans = 64;
 
 std::mutex g_lt_mu;
 std::map<int, hipblasLtHandle_t> g_lt_handle;
+std::map<int, int> g_cus;  // CUs per device
 std::map<PlanKey, LtPlan> g_lt_plans;
 std::deque<PlanKey> g_lt_untimed;  // keys of untimed plans, oldest first
 
@@ -408,7 +413,7 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, bool tune, const void* x, int64_t
       fit[nfit++] = i;
   if (nfit == 0) return false;
   p.algo = res[fit[0]].algo;
-  if (!tune || nfit == 1) return true;
+  if (!tune) return true;
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return true;
   if (hipEventCreate(&e1) != hipSuccess) {
@@ -436,7 +441,33 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, bool tune, const void* x, int64_t
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
+  p.ms = best;
   return true;
+}
+
+// Times the library's GEMM at `width` the way make_plan times a candidate
+// (one warm-up and three timed runs on the caller's buffers and stream); 0 if
+// it could not be timed.
+float time_own(int width, const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
+               void* y, int64_t y_ld, int y_dt, int M, int N, int K, hipStream_t stream) {
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return 0.0f;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return 0.0f;
+  }
+  auto run = [&]() {
+    return launch_gemm_bf16(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, width, stream) ==
+           hipSuccess;
+  };
+  float ms = 0.0f;
+  bool ok = run() && hipEventRecord(e0, stream) == hipSuccess;
+  for (int r = 0; r < 3 && ok; ++r) ok = run();
+  ok = ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+  if (!ok || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) ms = 0.0f;
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return ms;
 }
 
 }  // namespace
@@ -447,22 +478,42 @@ LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, i
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LinearStatus::kLaunchFailed;
   std::lock_guard<std::mutex> lock(g_lt_mu);
+  auto cit = g_cus.find(dev);
+  if (cit == g_cus.end()) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 0;
+    cit = g_cus.emplace(dev, cus).first;
+  }
+  const int width = gemm_bf16_width(M, N, K, x_ld, w_ld, cit->second);
+  auto own = [&](int wd) {
+    return launch_gemm_bf16(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, wd, stream) == hipSuccess
+               ? LinearStatus::kOk
+               : LinearStatus::kLaunchFailed;
+  };
+  const PlanKey key{dev, M, N, K, x_ld, w_ld, y_ld, y_dt, workspace_bytes};
+  auto pit = g_lt_plans.find(key);
+  // A timed plan decides; without one, a shape the library's GEMM suits
+  // runs there.
+  if (!tune && pit != g_lt_plans.end() && pit->second.tuned && pit->second.own)
+    return own(pit->second.own);
+  if (!tune && (pit == g_lt_plans.end() || !pit->second.tuned) && width) return own(width);
+
   auto hit = g_lt_handle.find(dev);
   if (hit == g_lt_handle.end()) {
     hipblasLtHandle_t h = nullptr;
-    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS) return LinearStatus::kLaunchFailed;
+    if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS)
+      return width ? own(width) : LinearStatus::kLaunchFailed;
     // The descriptors and results passed here follow this header's major
     // version (the soname's); a loaded library of another major is refused.
     int ver = 0;
     if (hipblasLtGetVersion(h, &ver) != HIPBLAS_STATUS_SUCCESS ||
         ver / 100000 != HIPBLASLT_VERSION_MAJOR) {
       hipblasLtDestroy(h);
-      return LinearStatus::kBadLibrary;
+      return width ? own(width) : LinearStatus::kBadLibrary;
     }
     hit = g_lt_handle.emplace(dev, h).first;
   }
-  const PlanKey key{dev, M, N, K, x_ld, w_ld, y_ld, y_dt, workspace_bytes};
-  auto pit = g_lt_plans.find(key);
   if (pit != g_lt_plans.end() && tune && !pit->second.tuned) {
     g_lt_untimed.erase(std::find(g_lt_untimed.begin(), g_lt_untimed.end(), key));
     destroy_plan(pit->second);
@@ -480,10 +531,15 @@ LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, i
     p.ok = make_plan(hit->second, p, tune, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace,
                      workspace_bytes, stream);
     p.tuned = tune;
+    if (tune && width) {
+      const float ms = time_own(width, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, stream);
+      if (ms > 0.0f && (!p.ok || p.ms == 0.0f || ms < p.ms)) p.own = width;
+    }
     pit = g_lt_plans.emplace(key, p).first;
     if (!tune) g_lt_untimed.push_back(key);
   }
   const LtPlan& p = pit->second;
+  if (p.own) return own(p.own);
   if (!p.ok) return LinearStatus::kNoAlgorithm;
   const float alpha = 1.0f, beta = 0.0f;
   const hipblasStatus_t st =

@@ -20,8 +20,9 @@
  *  - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
  *    The library never allocates device memory, frees, synchronises, logs
  *    or aborts, with two exceptions: the first gdn_linear or
- *    gdn_linear_tune call on a device creates the hipBLASLt handle kept for
- *    that device, and gdn_linear_tune synchronises (see there).
+ *    gdn_linear_tune call on a device that goes to hipBLASLt creates the
+ *    handle kept for that device, and gdn_linear_tune synchronises (see
+ *    there).
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream) and the call returns at once.  Device faults, if
  *    any, surface at the caller's next synchronisation.
@@ -342,22 +343,29 @@ size_t gdn_linear_workspace_bytes(void);
  *   y  [M, N] in y_dt (GDN_BF16 or GDN_F32), row stride y_ld; must not
  *      overlap x or W.
  *   y[m][n] = sum_k x[m][k] W[n][k], f32 accumulation, one rounding to y_dt.
- * Runs on hipBLASLt (whichever libhipblaslt.so.1 the process loaded first
- * serves the call; a loaded library of another major version than the
- * header this library was built with gives GDN_ERR_UNSUPPORTED).  The first
- * call on a device creates a hipBLASLt handle and keeps it (hipBLASLt may
- * allocate then; make that call before any graph capture).  A shape's plan
+ * Two engines serve it.  Shapes that fill the GPU with the library's own
+ * MFMA GEMM run there (gdn_linear_kernel says which width; it needs K a
+ * multiple of 64, N a multiple of 160, 192, 256 or 320, and at least one
+ * full round of 256-row by that-width tiles over the GPU's CUs): no
+ * allocation, no handle, nothing but the product enqueued, results
+ * independent of the workspace.  Every other shape runs on hipBLASLt
+ * (whichever libhipblaslt.so.1 the process loaded first serves the call; a
+ * loaded library of another major version than the header this library was
+ * built with gives GDN_ERR_UNSUPPORTED).  The first call on a device that
+ * goes to hipBLASLt creates its handle and keeps it (hipBLASLt may allocate
+ * then; make that call before any graph capture).  A shape's hipBLASLt plan
  * (descriptors and the heuristic's first algorithm that fits the workspace)
  * is made on the host by its first call, with nothing enqueued or awaited
  * beyond the product, and kept for the 64 most recent shapes; a shape timed
- * by gdn_linear_tune keeps its timed plan.  Calls from several threads are
- * serialised by a lock while they enqueue.
+ * by gdn_linear_tune keeps the engine and plan that won.  Calls from several
+ * threads are serialised by a lock while they enqueue.
  *   workspace  scratch for hipBLASLt, 256-byte aligned, workspace_bytes long
  *              (gdn_linear_workspace_bytes() recommended), or NULL with 0.
  * Constraints: M >= 0 (0 is a no-op), N > 0, K > 0; x_ld >= K, w_ld >= K,
  * y_ld >= N, each a multiple of 8; x, W, y 16-byte aligned.
- * GDN_ERR_UNSUPPORTED if hipBLASLt has no algorithm for the shape within
- * the workspace; GDN_ERR_LAUNCH if it fails to enqueue.
+ * GDN_ERR_UNSUPPORTED if the shape goes to hipBLASLt and it has no
+ * algorithm for it within the workspace; GDN_ERR_LAUNCH if the product
+ * fails to enqueue.
  */
 int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y, int64_t y_ld,
                int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
@@ -365,10 +373,11 @@ int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y
 
 /*
  * gdn_linear_tune -- gdn_linear that also times the shape's algorithms: up
- * to eight of the heuristic's candidates that fit the workspace run on this
- * call's own buffers and stream (one warm-up and three timed runs each; each
- * writes y, and the call's product is written last), the fastest is kept as
- * the shape's plan for later gdn_linear calls, and the call synchronises the
+ * to eight of hipBLASLt's candidates that fit the workspace, and the
+ * library's GEMM when gdn_linear_kernel gives it a width, run on this call's
+ * own buffers and stream (one warm-up and three timed runs each; each writes
+ * y, and the call's product is written last), the fastest is kept as the
+ * shape's plan for later gdn_linear calls, and the call synchronises the
  * stream.  For callers with a fixed set of shapes (a model's projections at
  * a set batch), once per shape, before any graph capture.  Arguments,
  * result and errors as gdn_linear.
@@ -376,6 +385,16 @@ int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y
 int gdn_linear_tune(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y,
                     int64_t y_ld, int32_t y_dt, int32_t M, int32_t N, int32_t K, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * gdn_linear_kernel -- which engine an untimed gdn_linear call of this shape
+ * uses on the current device: the block width (160, 192, 256 or 320
+ * outputs) of the library's MFMA GEMM, 0 for hipBLASLt, or a negative
+ * gdn_status if the arguments are invalid or the device cannot be queried.
+ * Host only; enqueues nothing.  (A shape timed by gdn_linear_tune uses the
+ * engine that won, which this does not report.)
+ */
+int gdn_linear_kernel(int32_t M, int32_t N, int32_t K, int64_t x_ld, int64_t w_ld);
 
 /* Size of the fixed device scratch of gdn_prefill_noalloc: 64 MiB, enough
  * for the chunked prefill of B*T <= 1152 tokens at 16 q/k and 48 value heads

@@ -30,7 +30,7 @@ def test_header_and_exports():
             "gdn_prefill_workspace_bytes", "gdn_status_str", "gdn_abi_version",
             "gdn_mixer_prefill", "gdn_mixer_prefill_workspace_bytes", "gdn_prefill_slots",
             "gdn_prefill_slots_workspace_bytes", "gdn_decode_rows_multi", "gdn_gate_proj",
-            "gdn_linear", "gdn_linear_tune", "gdn_linear_workspace_bytes",
+            "gdn_linear", "gdn_linear_tune", "gdn_linear_kernel", "gdn_linear_workspace_bytes",
             "gdn_gate_proj_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -298,6 +298,11 @@ def test_linear_validation():
                              5120, None, 0, None) == NULL
     assert L.gdn_linear_tune(_vp(P), 100, _vp(64 * P), 5120, _vp(4096 * P), 10240, 1, 8, 10240,
                              5120, None, 0, None) == SHAPE
+    # the engine query validates its shape before it asks the device anything
+    assert L.gdn_linear_kernel(8, 0, 64, 64, 64) == -SHAPE
+    assert L.gdn_linear_kernel(-1, 64, 64, 64, 64) == -SHAPE
+    assert L.gdn_linear_kernel(8, 64, 64, 32, 64) == -SHAPE   # x_ld below K
+    assert L.gdn_linear_kernel(8, 64, 64, 64, 0) == -SHAPE    # w_ld below K
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

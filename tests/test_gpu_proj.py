@@ -13,6 +13,8 @@ Tolerances, as max|y - ref| / max|ref| over the tensor:
   explicitly.
 * gdn_linear, f32 output: f32 accumulation of exact bf16 products, bound 2e-5.
 * gdn_linear, bf16 output: one rounding to bf16 (2^-9 relative), bound 5e-3.
+These hold for both engines behind gdn_linear: the library's MFMA GEMM (shapes
+that fill the GPU, reported by gdn_linear_kernel) and hipBLASLt (the rest).
 """
 import numpy as np
 import pytest
@@ -271,3 +273,76 @@ def test_out_proj_full_size_sampled_rows():
     e = max_rel_err(got, oracle.linear(to_f64(p["x"][rows]), to_f64(p["W_out"])))
     print(f"out_proj full: {e:.2e}")
     assert e <= TOL_LIN_BF16
+
+
+# Shapes that the library's GEMM takes on a 256-CU MI355X, one per block width
+# (x rows in blocks of 256: 2048 or 2000 rows give 8 blocks; the width makes
+# N / width * 8 >= 256 tiles), K small enough for the oracle.
+OWN_CASES = [(2048, 10240, 512, torch.float32, 320),
+             (2000, 10240, 256, torch.bfloat16, 320),   # last x block 208 rows
+             (2048, 8192, 256, torch.float32, 256),
+             (2048, 6144, 320, torch.bfloat16, 192),
+             (2048, 5120, 384, torch.float32, 160),
+             (1900, 5120, 128, torch.bfloat16, 160)]    # one k stage pair, ragged M
+
+
+@pytest.mark.parametrize("M,N,K,out,width", OWN_CASES)
+def test_linear_own_gemm_widths(M, N, K, out, width):
+    """Each block width of the library's GEMM against the oracle, with ragged
+    x-row blocks; two calls give the same bits."""
+    banner(f"linear own GEMM M={M} N={N} K={K} out={out} width {width}")
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the width choice below assumes 256 CUs")
+    assert gdn.gdn_linear_kernel(M, N, K) == width
+    p = proj_inputs(M, K=K, outs=(("W", N),), gate_H=0, seed=60 + K)
+    x, W = dev(p["x"]), dev(p["W"])
+    y = gdn.gdn_linear(x, W, out_dtype=out)
+    y2 = gdn.gdn_linear(x, W, out_dtype=out)
+    torch.cuda.synchronize()
+    ref = oracle.linear(to_f64(p["x"]), to_f64(p["W"]))
+    e = max_rel_err(host_f64(y), ref)
+    print(f"linear own {M}x{N}x{K} {out} width {width}: err {e:.2e}")
+    assert e <= (TOL_LIN_F32 if out == torch.float32 else TOL_LIN_BF16)
+    assert torch.equal(y, y2)
+
+
+def test_linear_own_gemm_strided_and_tuned():
+    """The library's GEMM on a column slice of x (x_ld > K) writing columns of a
+    wider y (y_ld > N), canaries around y untouched; then gdn_linear_tune on
+    the same shape, and a plain call after it repeating the tuned result bit
+    for bit, all against the oracle."""
+    M, N, K = 2048, 6144, 256
+    banner(f"linear own GEMM strided M={M} N={N} K={K}")
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the width choice below assumes 256 CUs")
+    p = proj_inputs(M, K=K + 64, outs=(("W", N),), gate_H=0, seed=71)
+    Wk = dev(p["W"][:, :K].copy())
+    xw = dev(p["x"])
+    x = xw[:, 32:32 + K]
+    assert gdn.gdn_linear_kernel(M, N, K, x_ld=K + 64) == 192
+    yb = torch.full((M, N + 64), float("nan"), dtype=torch.float32, device="cuda")
+    gdn.gdn_linear(x, Wk, y=yb[:, 32:32 + N])
+    torch.cuda.synchronize()
+    ref = oracle.linear(to_f64(p["x"])[:, 32:32 + K], to_f64(p["W"][:, :K]))
+    got = host_f64(yb)
+    assert np.isnan(got[:, :32]).all() and np.isnan(got[:, 32 + N:]).all()
+    assert max_rel_err(got[:, 32:32 + N], ref) <= TOL_LIN_F32
+    ws = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    y1 = gdn.gdn_linear_tune(x, Wk, out_dtype=torch.float32, workspace=ws)
+    y2 = gdn.gdn_linear(x, Wk, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    assert max_rel_err(host_f64(y1), ref) <= TOL_LIN_F32
+    assert torch.equal(y1, y2)
+
+
+def test_linear_kernel_choice_for_the_projections():
+    """At 4096 tokens the three projections take the library's GEMM (320, 192
+    and 320 wide); at 64 decode rows they go to hipBLASLt."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the width choice below assumes 256 CUs")
+    assert gdn.gdn_linear_kernel(4096, 10240, 5120) == 320
+    assert gdn.gdn_linear_kernel(4096, 6144, 5120) == 192
+    assert gdn.gdn_linear_kernel(4096, 5120, 6144) == 320
+    for N, K in ((10240, 5120), (6144, 5120), (5120, 6144)):
+        assert gdn.gdn_linear_kernel(64, N, K) == 0
+    assert gdn.gdn_linear_kernel(4096, 10240, 5100) == 0   # K not a multiple of 64
