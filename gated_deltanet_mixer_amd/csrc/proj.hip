@@ -532,8 +532,10 @@ LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, i
                      workspace_bytes, stream);
     p.tuned = tune;
     if (tune && width) {
+      // The library's GEMM wins when it is faster, or when hipBLASLt has
+      // nothing for the shape.
       const float ms = time_own(width, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, stream);
-      if (ms > 0.0f && (!p.ok || p.ms == 0.0f || ms < p.ms)) p.own = width;
+      if (!p.ok || (ms > 0.0f && (p.ms == 0.0f || ms < p.ms))) p.own = width;
     }
     pit = g_lt_plans.emplace(key, p).first;
     if (!tune) g_lt_untimed.push_back(key);
