@@ -12,9 +12,9 @@
  *     o_t = S_t (q_scale * q_t);
  * the head outputs are RMS-normalised (scale 1 + w, f32) and gated by
  * silu(z).  16 q/k heads serve 48 value heads: value head h reads q/k head
- * h / (Hv / Hk).  The card's state paragraph: prefill serves one batch,
- * decode_rows a server's fixed rows each at its own length; every row keeps
- * its conv history and recurrent state in f32.
+ * h / (Hv / Hk).  Per the card's state paragraph, prefill runs one batch
+ * and decode_rows advances persistent rows whose sequence lengths differ;
+ * each row holds its conv history and recurrent state in f32.
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
@@ -150,10 +150,9 @@ int gdn_prefill(const void* q, int64_t q_tok_stride, const void* k, int64_t k_to
                 size_t workspace_bytes, void* stream);
 
 /*
- * gdn_decode_rows -- one new token for each of R fixed rows, each row at its
- * own length, the state updated in place (the card's decode_rows, which
- * serves a server's rows at lengths of their own in fixed slots; "Qwen3.8
- * 27B" model card, state paragraph).
+ * gdn_decode_rows -- one new token for each of R persistent rows whose
+ * lengths differ, the state updated in place (the card's decode_rows;
+ * "Qwen3.8 27B" model card, state paragraph).
  *   q, k   [R, Hk, dk] in qkv_dt, row r at r*row_stride (elements).
  *   v      [R, Hv, dv] in qkv_dt, row r at r*v_row_stride.
  *   a, b   [R, Hv] contiguous in gate_dt.
@@ -173,10 +172,10 @@ int gdn_decode_rows(const void* q, int64_t q_row_stride, const void* k, int64_t 
                     float q_scale, void* stream);
 
 /*
- * gdn_decode_rows_multi -- K new tokens for each of R fixed rows (a draft of
- * K tokens to verify, the shape of the blog's multi-token prediction and
- * speculative decoding, and the card's decode_rows serving rows each at its
- * own length).  Each row's state is read once, advanced through its K tokens
+ * gdn_decode_rows_multi -- K new tokens for each of R persistent rows (a
+ * draft of K tokens to verify, the shape of the blog's multi-token
+ * prediction and speculative decoding, over the card's decode_rows rows of
+ * differing lengths).  Each row's state is read once, advanced through its K tokens
  * in order and written once; K tokens equal K successive gdn_decode_rows
  * calls, bit for bit.
  *   q, k   token t of row r at r*row_stride + t*tok_stride (elements), each
@@ -218,13 +217,12 @@ int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const f
 size_t gdn_prefill_slots_workspace_bytes(int32_t R, int32_t max_len, gdn_dims dims);
 
 /*
- * gdn_prefill_slots -- ragged prefill of a server's fixed rows, each row
+ * gdn_prefill_slots -- ragged prefill of persistent rows, each row
  * continuing from its own state with its own number of new tokens ("Qwen3.8
- * 27B" model card, state paragraph: the slot calls serve rows that sit in
- * fixed slots at lengths of their own, each keeping its conv history and
- * recurrent state in f32).  The rule uses no positions, so a row's length
- * so far only lives in its state.  Chunks of 64 start at each row's first
- * new token.
+ * 27B" model card, state paragraph: rows stay in place between calls, each
+ * with its own length, conv history and f32 recurrent state).  The rule
+ * uses no positions, so a row's length so far only lives in its state.
+ * Chunks of 64 start at each row's first new token.
  *   q, k   [total_tokens, Hk, dk] in qkv_dt, token t at t*tok_stride
  *          (elements); v [total_tokens, Hv, dv] likewise: the rows' new
  *          tokens packed one row after another.
