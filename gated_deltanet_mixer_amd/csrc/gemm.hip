@@ -217,7 +217,7 @@ int gemm_bf16_width(int M, int N, int K, int64_t x_ld, int64_t w_ld, int cus) {
   // Shape limits of the kernel: k in whole stages, N in whole blocks, each
   // operand's block rows addressable by a 32-bit buffer range.
   if (M <= 0 || N <= 0 || K <= 0 || K % GK || cus <= 0) return 0;
-  if (x_ld > (1 << 21) || w_ld > (1 << 21)) return 0;
+  if (x_ld > (1 << 21) || w_ld > (1 << 21) || M > (1 << 30)) return 0;  // 32-bit row indices
   const int64_t tiles_m = (M + GM_ROWS - 1) / GM_ROWS;
   int best = 0;
   float best_cost = 0.0f;
