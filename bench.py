@@ -4,7 +4,9 @@ One step = one pass of the whole hot path on seeded synthetic inputs shaped
 like the model's layer (16 q/k heads, 48 value heads, width 128), part by part:
   layer     the layer prefill at B=1, T=4096: one gdn_mixer_prefill call (conv
             over 10240 channels, width 4, silu, L2 of q/k -> chunked prefill
-            with the state carried in and out -> gated RMSNorm with z);
+            with the state carried in and out -> gated RMSNorm with z), qkv
+            and z read in place as the two column ranges of one [4096, 16384]
+            buffer, the layout the fused in_proj_qkvz product writes;
   prefill   gdn_prefill alone on the prefill workload (B=1, T=4096, bf16
             q/k/v, f32 gates, carried state ~N(0, 0.05), chunk 64): the
             headline;
@@ -19,12 +21,15 @@ like the model's layer (16 q/k heads, 48 value heads, width 128), part by part:
   multi     gdn_decode_rows_multi verifying a 4-token draft on 64 fixed rows,
             with the state after every token written out as a snapshot;
   proj      the projections around the mixer at 4096 tokens: in_proj_qkv and
-            in_proj_z (gdn_linear, bf16, into one [4096, 16384] buffer), the
-            two gate projections with f32 weights (gdn_gate_proj) and out_proj
+            in_proj_z as one product with the stacked [16384, 5120] weight
+            (gdn_linear, bf16, into one [4096, 16384] buffer), the two gate
+            projections with f32 weights (gdn_gate_proj) and out_proj
             (gdn_linear, 6144 -> 5120);
-  dlayer    one decode step of the whole layer for 64 fixed rows: in_proj_qkv,
-            in_proj_z, the gate projections, the conv over one token with each
-            row's conv history, decode_rows, the gated RMSNorm and out_proj;
+  dlayer    one decode step of the whole layer for 64 fixed rows: the fused
+            in_proj_qkvz product, the gate projections, the conv over one
+            token with each row's conv history (reading the q|k|v columns in
+            place), decode_rows, the gated RMSNorm (reading the z columns in
+            place) and out_proj;
   dgraph    the same decode step replayed from a HIP graph (captured once per
             buffer set after the warm-up, so the eight launches go out as one).
 Each part is timed with HIP events on the stream it runs on, per call; the
@@ -258,8 +263,10 @@ def main():
         st_layer = recurrence_inputs(1, 1, seed=2004, state_std=0.05)["state"]
         layer = []
         for _ in range(ROT):
+            qkvz = torch.cat([dev(mx["qkv"]), dev(mx["z"])], dim=2)  # [1, T, 16384]
             layer.append({
-                "qkv": dev(mx["qkv"]), "z": dev(mx["z"]), "a": dev(mx["a"]), "b": dev(mx["b"]),
+                "qkv": qkvz[..., :C_CONV], "z": qkvz[..., C_CONV:], "a": dev(mx["a"]),
+                "b": dev(mx["b"]),
                 "conv_w": dev(mx["conv_w"]), "A_log": dev(mx["A_log"]),
                 "dt_bias": dev(mx["dt_bias"]), "norm_w": dev(mx["norm_w"]),
                 "state": dev(st_layer),
@@ -414,7 +421,9 @@ def main():
         gws_bytes = max(gdn.gdn_gate_proj_workspace_bytes(T_PREFILL, HIDDEN, HV), 256)
         proj = []
         for _ in range(ROT):
-            pj = {n: dev(pin[n]) for n in ("x", "W_qkv", "W_z", "W_a", "W_b")}
+            pj = {n: dev(pin[n]) for n in ("x", "W_a", "W_b")}
+            # in_proj_qkv and in_proj_z stacked: one [16384, 5120] weight
+            pj["W_qkvz"] = torch.cat([dev(pin["W_qkv"]), dev(pin["W_z"])], dim=0)
             pj.update({"y": dev(pout["y"]), "W_out": dev(pout["W_out"])})
             pj["yin"] = torch.empty((T_PREFILL, C_CONV + HV * D), dtype=torch.bfloat16,
                                     device="cuda")
@@ -428,20 +437,17 @@ def main():
         del pin, pout
 
     if "proj" in want:
-        # Records an event after each of its first three calls as well.
+        # Records an event after each of its first two calls as well.
         def proj_part(i):
             Pj = proj[i % ROT]
             ev = proj_ev.get(i)
-            gdn.gdn_linear(Pj["x"], Pj["W_qkv"], y=Pj["yin"][:, :C_CONV], workspace=Pj["lws"])
+            gdn.gdn_linear(Pj["x"], Pj["W_qkvz"], y=Pj["yin"], workspace=Pj["lws"])
             if ev:
                 ev[0].record()
-            gdn.gdn_linear(Pj["x"], Pj["W_z"], y=Pj["yin"][:, C_CONV:], workspace=Pj["lws"])
-            if ev:
-                ev[1].record()
             gdn.gdn_gate_proj(Pj["x"], Pj["W_a"], Pj["W_b"], a=Pj["a"], b=Pj["b"],
                               workspace=Pj["gws"])
             if ev:
-                ev[2].record()
+                ev[1].record()
             gdn.gdn_linear(Pj["y"], Pj["W_out"], y=Pj["out"], workspace=Pj["lws"])
         fns["proj"] = proj_part
 
@@ -456,8 +462,10 @@ def main():
                   "norm_w": dev(mxc["norm_w"]),
                   "conv_state": torch.zeros((R_DECODE, 3, C_CONV), dtype=torch.float32,
                                             device="cuda")}
-            dl["qkv"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
-            dl["z"] = torch.empty((R_DECODE, HV * D), dtype=torch.bfloat16, device="cuda")
+            dl["qkvz"] = torch.empty((R_DECODE, C_CONV + HV * D), dtype=torch.bfloat16,
+                                     device="cuda")
+            dl["qkv"] = dl["qkvz"][:, :C_CONV].unsqueeze(1)      # [R, 1, 10240], in place
+            dl["z"] = dl["qkvz"][:, C_CONV:].unflatten(1, (HV, D))  # [R, 48, 128], in place
             dl["a"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
             dl["b"] = torch.empty((R_DECODE, HV), dtype=torch.float32, device="cuda")
             dl["y"] = torch.empty((R_DECODE, 1, C_CONV), dtype=torch.bfloat16, device="cuda")
@@ -474,25 +482,22 @@ def main():
             W = proj[i % ROT]
             ev = dl_ev.get(i) if events else None
             mark = (lambda j: ev[j].record()) if ev else (lambda j: None)
-            gdn.gdn_linear(L["x"], W["W_qkv"], y=L["qkv"].view(R_DECODE, C_CONV),
-                           workspace=W["lws"])
+            gdn.gdn_linear(L["x"], W["W_qkvz"], y=L["qkvz"], workspace=W["lws"])
             mark(0)
-            gdn.gdn_linear(L["x"], W["W_z"], y=L["z"], workspace=W["lws"])
-            mark(1)
             gdn.gdn_gate_proj(L["x"], W["W_a"], W["W_b"], a=L["a"], b=L["b"],
                               workspace=L["gws"])
-            mark(2)
+            mark(1)
             gdn.gdn_conv_silu(L["qkv"], L["conv_w"], L["conv_state"], l2_channels=2 * HK * D,
                               y=L["y"])
-            mark(3)
+            mark(2)
             y = L["y"][:, 0]
             gdn.gdn_decode_rows(y[:, :HK * D].unflatten(1, (HK, D)),
                                 y[:, HK * D:2 * HK * D].unflatten(1, (HK, D)),
                                 y[:, 2 * HK * D:].unflatten(1, (HV, D)), L["a"], L["b"],
                                 L["A_log"], L["dt_bias"], L["state"], o=L["o"])
+            mark(3)
+            gdn.gdn_gated_rmsnorm(L["o"], L["z"], L["norm_w"], y=L["o2"])
             mark(4)
-            gdn.gdn_gated_rmsnorm(L["o"], L["z"].view(R_DECODE, HV, D), L["norm_w"], y=L["o2"])
-            mark(5)
             gdn.gdn_linear(L["o2"].view(R_DECODE, HV * D), W["W_out"], y=L["out"],
                            workspace=W["lws"])
         fns["dlayer"] = dlayer_part
@@ -509,14 +514,11 @@ def main():
     # that fits), then the parts that use them are warmed up again.
     if "proj" in want or "dlayer" in want:
         Pj = proj[0]
-        gdn.gdn_linear_tune(Pj["x"], Pj["W_qkv"], y=Pj["yin"][:, :C_CONV], workspace=Pj["lws"])
-        gdn.gdn_linear_tune(Pj["x"], Pj["W_z"], y=Pj["yin"][:, C_CONV:], workspace=Pj["lws"])
+        gdn.gdn_linear_tune(Pj["x"], Pj["W_qkvz"], y=Pj["yin"], workspace=Pj["lws"])
         gdn.gdn_linear_tune(Pj["y"], Pj["W_out"], y=Pj["out"], workspace=Pj["lws"])
     if "dlayer" in want:
         L, W = dlayer[0], proj[0]
-        gdn.gdn_linear_tune(L["x"], W["W_qkv"], y=L["qkv"].view(R_DECODE, C_CONV),
-                            workspace=W["lws"])
-        gdn.gdn_linear_tune(L["x"], W["W_z"], y=L["z"], workspace=W["lws"])
+        gdn.gdn_linear_tune(L["x"], W["W_qkvz"], y=L["qkvz"], workspace=W["lws"])
         gdn.gdn_linear_tune(L["o2"].view(R_DECODE, HV * D), W["W_out"], y=L["out"],
                             workspace=W["lws"])
     for p in ("proj", "dlayer"):
@@ -559,8 +561,8 @@ def main():
     evs = {p: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)] for p in order}
     for i in range(args.steps):
-        proj_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        dl_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        proj_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        dl_ev[args.warmup + i] = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     # The timed region: each part's K calls back to back between one pair of
     # events on the library's stream; the mean per call is what the rates
     # below use.  A second pass with events around every call gives each
@@ -652,7 +654,9 @@ def main():
         out["layer_prefill"] = {"value": round(T_PREFILL / (t_layer * 1e-3), 1),
                                 "unit": "tokens/s",
                                 "workload": "gdn_mixer_prefill (conv+silu+L2 -> chunked prefill "
-                                            "-> gated RMSNorm), B=1 T=4096, 10240 conv channels",
+                                            "-> gated RMSNorm), B=1 T=4096, 10240 conv channels, "
+                                            "qkv and z read in place from one [4096, 16384] "
+                                            "buffer",
                                 "call_us": round(t_layer * 1e3, 2)}
     if "mixer_b4" in med:
         t3 = med["mixer_b4"]
@@ -709,20 +713,20 @@ def main():
         pc = np.median(np.array(
             [[evs["proj"][i][0].elapsed_time(proj_ev[args.warmup + i][0]),
               proj_ev[args.warmup + i][0].elapsed_time(proj_ev[args.warmup + i][1]),
-              proj_ev[args.warmup + i][1].elapsed_time(proj_ev[args.warmup + i][2]),
-              proj_ev[args.warmup + i][2].elapsed_time(evs["proj"][i][1])]
+              proj_ev[args.warmup + i][1].elapsed_time(evs["proj"][i][1])]
              for i in range(args.steps)]), axis=0)  # ms
-        t_qkv, t_z, t_gate, t_out = pc
+        t_qkvz, t_gate, t_out = pc
         gemm_flops = (2.0 * T_PREFILL * HIDDEN * (C_CONV + HV * D)
                       + 2.0 * T_PREFILL * HV * D * HIDDEN)
-        gemm_tflops = gemm_flops / ((t_qkv + t_z + t_out) * 1e-3) / 1e12
+        gemm_tflops = gemm_flops / ((t_qkvz + t_out) * 1e-3) / 1e12
         gate_bytes = T_PREFILL * HIDDEN * 2 + 2 * HV * HIDDEN * 4 + 2 * T_PREFILL * HV * 4
         out["projections"] = {
-            "workload": "in_proj_qkv 5120->10240 and in_proj_z 5120->6144 (bf16, gdn_linear), "
-                        "in_proj_a/b 5120->48 (f32 weights, gdn_gate_proj), out_proj "
-                        "6144->5120 (bf16, gdn_linear) at 4096 tokens",
+            "workload": "in_proj_qkv 5120->10240 and in_proj_z 5120->6144 as one product "
+                        "with the stacked [16384, 5120] weight (bf16, gdn_linear), in_proj_a/b "
+                        "5120->48 (f32 weights, gdn_gate_proj), out_proj 6144->5120 (bf16, "
+                        "gdn_linear) at 4096 tokens",
             "call_us": round(t_proj * 1e3, 2),
-            "in_proj_qkv_us": round(t_qkv * 1e3, 2), "in_proj_z_us": round(t_z * 1e3, 2),
+            "in_proj_qkvz_us": round(t_qkvz * 1e3, 2),
             "gate_proj_us": round(t_gate * 1e3, 2), "out_proj_us": round(t_out * 1e3, 2),
             "gemm_tflops": round(gemm_tflops, 1),
             "gemm_frac_of_bf16_peak": round(gemm_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -738,18 +742,18 @@ def main():
         t_dl = med["dlayer"]
         t_dg = med.get("dgraph")
         dlc = np.median(np.array(
-            [[e[j].elapsed_time(e[j + 1]) for j in range(7)]
+            [[e[j].elapsed_time(e[j + 1]) for j in range(6)]
              for e in ([evs["dlayer"][i][0]] + dl_ev[args.warmup + i] + [evs["dlayer"][i][1]]
                        for i in range(args.steps))]), axis=0)  # ms
         out["full_layer_decode"] = {
             "value": round(R_DECODE / (t_dl * 1e-3), 1), "unit": "tokens/s",
-            "workload": "one decode step of the whole layer for 64 fixed rows: in_proj_qkv, "
-                        "in_proj_z, gate projections, conv over one token with the rows' conv "
-                        "history, decode_rows, gated RMSNorm, out_proj",
+            "workload": "one decode step of the whole layer for 64 fixed rows: in_proj_qkvz "
+                        "(one product), gate projections, conv over one token with the rows' "
+                        "conv history, decode_rows, gated RMSNorm, out_proj",
             "us": round(t_dl * 1e3, 2),
             "graph_us": round(t_dg * 1e3, 2) if t_dg else None,
             "graph_value": round(R_DECODE / (t_dg * 1e-3), 1) if t_dg else None,
-            "calls_us": dict(zip(["in_proj_qkv", "in_proj_z", "gate_proj", "conv",
+            "calls_us": dict(zip(["in_proj_qkvz", "gate_proj", "conv",
                                   "decode_rows", "gated_rmsnorm", "out_proj"],
                                  [round(v * 1e3, 2) for v in dlc]))}
 

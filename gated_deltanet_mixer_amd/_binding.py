@@ -44,7 +44,8 @@ def lib():
         L.gdn_status_str.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
         L.gdn_abi_version.restype = ctypes.c_int
-        L.gdn_conv_silu.argtypes = [P, i32, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, P]
+        L.gdn_conv_silu.argtypes = [P, i64, i32, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32,
+                                    P]
         L.gdn_conv_silu.restype = ctypes.c_int
         L.gdn_prefill_workspace_bytes.argtypes = [i32, i32, gdn_dims, i32, i32]
         L.gdn_prefill_workspace_bytes.restype = sz
@@ -57,7 +58,7 @@ def lib():
         L.gdn_decode_rows_multi.argtypes = [P, i64, i64, P, i64, i64, P, i64, i64, i32, P, P,
                                             i32, P, P, P, P, P, P, i32, i32, gdn_dims, f32, P]
         L.gdn_decode_rows_multi.restype = ctypes.c_int
-        L.gdn_gated_rmsnorm.argtypes = [P, P, P, i32, P, i32, i32, i32, f32, P]
+        L.gdn_gated_rmsnorm.argtypes = [P, P, i64, P, i32, P, i32, i32, i32, f32, P]
         L.gdn_gated_rmsnorm.restype = ctypes.c_int
         L.gdn_prefill_slots_workspace_bytes.argtypes = [i32, i32, gdn_dims]
         L.gdn_prefill_slots_workspace_bytes.restype = sz
@@ -66,8 +67,8 @@ def lib():
         L.gdn_prefill_slots.restype = ctypes.c_int
         L.gdn_mixer_prefill_workspace_bytes.argtypes = [i32, i32, gdn_dims]
         L.gdn_mixer_prefill_workspace_bytes.restype = sz
-        L.gdn_mixer_prefill.argtypes = [P, P, i32, P, P, P, P, i32, P, P, P, P, P, P, i32, i32,
-                                        gdn_dims, f32, f32, f32, P, sz, P]
+        L.gdn_mixer_prefill.argtypes = [P, i64, P, i64, i32, P, P, P, P, i32, P, P, P, P, P, P,
+                                        i32, i32, gdn_dims, f32, f32, f32, P, sz, P]
         L.gdn_mixer_prefill.restype = ctypes.c_int
         L.gdn_gate_proj_workspace_bytes.argtypes = [i32, i32, i32]
         L.gdn_gate_proj_workspace_bytes.restype = sz
@@ -137,20 +138,38 @@ def _tok_stride(t, heads, d):
     return t.stride(1)
 
 
+def _seq_stride(t, name):
+    """Token stride of a [B, T, C] view with contiguous channels, whose tokens
+    lie at (b*T + t) * stride (a column range of a wider buffer is fine)."""
+    B, T, C = t.shape
+    if t.numel() == 0 or B * T == 1:
+        return C
+    if C > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have contiguous channels")
+    if T > 1:
+        ts = t.stride(1)
+        if B > 1 and t.stride(0) != T * ts:
+            raise ValueError(f"{name}: batch stride must be T * token stride")
+        return ts
+    return t.stride(0)
+
+
 def gdn_conv_silu(x, w, conv_state=None, l2_channels=0, head_dim=128, l2_eps=1e-6, y=None,
                   y_dtype=None):
-    """Depthwise causal conv (width 4) + silu over x [B, T, C], optional L2 of
-    the first l2_channels channels per head; conv_state [B, 3, C] f32 in/out.
-    y_dtype (default x.dtype) selects the output dtype when y is not given."""
+    """Depthwise causal conv (width 4) + silu over x [B, T, C] (a view with a
+    token stride is accepted), optional L2 of the first l2_channels channels
+    per head; conv_state [B, 3, C] f32 in/out.  y_dtype (default x.dtype)
+    selects the output dtype when y is not given."""
     _need_cuda(x, w, conv_state, y)
     B, T, C = x.shape
     if y is None:
         y = torch.empty(x.shape, dtype=y_dtype or x.dtype, device=x.device)
-    assert x.is_contiguous() and y.is_contiguous() and w.is_contiguous()
+    assert y.is_contiguous() and w.is_contiguous()
     if conv_state is not None:
         assert conv_state.is_contiguous() and conv_state.dtype == torch.float32
-    _check(lib().gdn_conv_silu(_ptr(x), _dt(x), _ptr(y), _dt(y), _ptr(w), _ptr(conv_state), B, T,
-                               C, w.shape[1], l2_channels, head_dim, l2_eps, _stream(x)),
+    _check(lib().gdn_conv_silu(_ptr(x), _seq_stride(x, "x"), _dt(x), _ptr(y), _dt(y), _ptr(w),
+                               _ptr(conv_state), B, T, C, w.shape[1], l2_channels, head_dim,
+                               l2_eps, _stream(x)),
            "gdn_conv_silu")
     return y
 
@@ -237,19 +256,42 @@ def gdn_decode_rows(q, k, v, a, b, A_log, dt_bias, state, lengths=None, o=None, 
 
 def gdn_gated_rmsnorm(x, z, w, eps=1e-6, y=None):
     """y = x / sqrt(mean(x^2) + eps) * (1 + w) * silu(z) over the last axis
-    (width 128); x, z viewed as [N, H, 128]."""
+    (width 128); x viewed as [N, H, 128]; z of x's shape, contiguous or a view
+    whose tokens (all but the last two axes) lie one token stride apart."""
     _need_cuda(x, z, w, y)
     D = x.shape[-1]
     H = x.shape[-2]
     N = x.numel() // (H * D) if x.numel() else 0
     if y is None:
         y = torch.empty_like(x)
-    assert x.is_contiguous() and z.is_contiguous() and y.is_contiguous()
-    assert z.numel() == x.numel() and y.numel() == x.numel()
-    _check(lib().gdn_gated_rmsnorm(_ptr(x), _ptr(z), _ptr(y), _dt(x), _ptr(w), N, H, D, eps,
-                                   _stream(x)),
+    assert x.is_contiguous() and y.is_contiguous() and y.numel() == x.numel()
+    if z.is_contiguous():
+        assert z.numel() == x.numel()
+        zts = H * D
+    else:
+        assert z.shape == x.shape
+        zts = _head_tok_stride(z, H, D)
+    _check(lib().gdn_gated_rmsnorm(_ptr(x), _ptr(z), zts, _ptr(y), _dt(x),
+                                   _ptr(w), N, H, D, eps, _stream(x)),
            "gdn_gated_rmsnorm")
     return y
+
+
+def _head_tok_stride(t, H, D):
+    """Token stride of a [..., H, D] view with packed heads whose leading axes
+    collapse to one token stride."""
+    if t.numel() == 0 or t.numel() == H * D:
+        return H * D
+    if (D > 1 and t.stride(-1) != 1) or (H > 1 and t.stride(-2) != D):
+        raise ValueError("expected packed heads of contiguous channels")
+    lead = [(n, st) for n, st in zip(t.shape[:-2], t.stride()[:-2]) if n > 1]
+    ts = lead[-1][1]
+    expect = ts
+    for (_, st), (n_inner, _) in zip(reversed(lead[:-1]), reversed(lead[1:])):
+        expect *= n_inner
+        if st != expect:
+            raise ValueError("leading axes must collapse to one token stride")
+    return ts
 
 
 def gdn_mixer_prefill_workspace_bytes(B, T, Hk, Hv, dk=128, dv=128):
@@ -261,7 +303,9 @@ def gdn_mixer_prefill(qkv, z, conv_w, a, b, A_log, dt_bias, norm_w, Hk, Hv, conv
                       norm_eps=1e-6, workspace=None):
     """Whole mixer between the projections: conv + silu + L2 over qkv [B,T,C],
     the gated delta rule (state carried in/out) and the gated RMSNorm with z
-    [B,T,Hv*128].  Returns y [B,T,Hv*128] in qkv's dtype."""
+    [B,T,Hv*128].  qkv and z may be views with a token stride (the two column
+    ranges of one in_proj_qkvz output).  Returns y [B,T,Hv*128] in qkv's
+    dtype."""
     _need_cuda(qkv, z, conv_w, a, b, A_log, dt_bias, norm_w, conv_state, state_in, state_out, y,
                workspace)
     B, T, C = qkv.shape
@@ -269,7 +313,7 @@ def gdn_mixer_prefill(qkv, z, conv_w, a, b, A_log, dt_bias, norm_w, Hk, Hv, conv
         raise ValueError(f"qkv has {C} channels, expected {2 * Hk * 128 + Hv * 128}")
     if y is None:
         y = torch.empty((B, T, Hv * 128), dtype=qkv.dtype, device=qkv.device)
-    for t in (qkv, z, y, conv_w, a, b, norm_w):
+    for t in (y, conv_w, a, b, norm_w):
         assert t.is_contiguous()
     assert z.dtype == qkv.dtype and y.dtype == qkv.dtype and z.shape == y.shape
     for s in (conv_state, state_in, state_out):
@@ -279,7 +323,8 @@ def gdn_mixer_prefill(qkv, z, conv_w, a, b, A_log, dt_bias, norm_w, Hk, Hv, conv
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=qkv.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().gdn_mixer_prefill(_ptr(qkv), _ptr(z), _dt(qkv), _ptr(conv_w), _ptr(conv_state),
+    _check(lib().gdn_mixer_prefill(_ptr(qkv), _seq_stride(qkv, "qkv"), _ptr(z),
+                                   _seq_stride(z, "z"), _dt(qkv), _ptr(conv_w), _ptr(conv_state),
                                    _ptr(a), _ptr(b), _dt(a), _ptr(A_log), _ptr(dt_bias),
                                    _ptr(norm_w), _ptr(state_in), _ptr(state_out), _ptr(y), B, T,
                                    gdn_dims(Hk, Hv, 128, 128), q_scale, l2_eps, norm_eps,

@@ -80,15 +80,16 @@ const char* gdn_status_str(int status) {
 
 int gdn_abi_version(void) { return GDN_ABI_VERSION; }
 
-int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const float* w,
-                  float* conv_state, int32_t B, int32_t T, int32_t C, int32_t W,
+int gdn_conv_silu(const void* x, int64_t x_tok_stride, int32_t x_dt, void* y, int32_t y_dt,
+                  const float* w, float* conv_state, int32_t B, int32_t T, int32_t C, int32_t W,
                   int32_t l2_channels, int32_t head_dim, float l2_eps, void* stream) {
   if (!x || !y || !w) return GDN_ERR_NULL;
   if (!dtype_ok(x_dt) || !dtype_ok(y_dt)) return GDN_ERR_DTYPE;
   if (B < 0 || T < 0 || C <= 0 || W < 1 || l2_channels < 0 || l2_channels > C)
     return GDN_ERR_SHAPE;
   if (W != 4) return GDN_ERR_UNSUPPORTED;
-  if (C % 8 != 0) return GDN_ERR_SHAPE;
+  if (C % 8 != 0 || x_tok_stride < C) return GDN_ERR_SHAPE;
+  if (x_tok_stride % 8 != 0) return GDN_ERR_ALIGN;
   if (l2_channels > 0) {
     if (head_dim <= 0 || l2_channels % head_dim != 0) return GDN_ERR_SHAPE;
     if (head_dim != 128) return GDN_ERR_UNSUPPORTED;
@@ -97,14 +98,12 @@ int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const floa
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(w, 16) ||
       (conv_state && !aligned(conv_state, 16)))
     return GDN_ERR_ALIGN;
-  const size_t xbytes = (size_t)B * T * C * dsize(x_dt);
-  const size_t ybytes = (size_t)B * T * C * dsize(y_dt);
-  const char* xs = static_cast<const char*>(x);
-  const char* ys = static_cast<const char*>(y);
-  if (xbytes > 0 && xs < ys + ybytes && ys < xs + xbytes) return GDN_ERR_SHAPE;  // y overlaps x
   if (B == 0 || T == 0) return GDN_OK;
-  return launch_status(gdn::launch_conv_silu(x, x_dt, y, y_dt, w, conv_state, B, T, C,
-                                             l2_channels, l2_eps,
+  const size_t xbytes = ((size_t)((int64_t)B * T - 1) * x_tok_stride + C) * dsize(x_dt);
+  const size_t ybytes = (size_t)B * T * C * dsize(y_dt);
+  if (overlaps(y, ybytes, x, xbytes)) return GDN_ERR_SHAPE;  // y overlaps x
+  return launch_status(gdn::launch_conv_silu(x, x_tok_stride, x_dt, y, y_dt, w, conv_state, B,
+                                             T, C, l2_channels, l2_eps,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -220,19 +219,21 @@ int gdn_decode_rows_multi(const void* q, int64_t q_row_stride, int64_t q_tok_str
       Hv, q_scale, static_cast<hipStream_t>(stream)));
 }
 
-int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const float* w,
-                      int32_t N, int32_t H, int32_t D, float eps, void* stream) {
+int gdn_gated_rmsnorm(const void* x, const void* z, int64_t z_tok_stride, void* y, int32_t dt,
+                      const float* w, int32_t N, int32_t H, int32_t D, float eps, void* stream) {
   if (!x || !z || !y || !w) return GDN_ERR_NULL;
   if (!dtype_ok(dt)) return GDN_ERR_DTYPE;
   if (N < 0 || H < 0 || D <= 0) return GDN_ERR_SHAPE;
   if (D != 128) return GDN_ERR_UNSUPPORTED;
+  if (z_tok_stride < (int64_t)H * D) return GDN_ERR_SHAPE;
+  if (z_tok_stride % 8 != 0) return GDN_ERR_ALIGN;
   const int64_t rows = (int64_t)N * H;
   if ((rows + 63) / 64 > INT32_MAX) return GDN_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(w, 16))
     return GDN_ERR_ALIGN;
   if (rows == 0) return GDN_OK;
-  return launch_status(
-      gdn::launch_gated_rmsnorm(x, z, y, dt, w, rows, eps, static_cast<hipStream_t>(stream)));
+  return launch_status(gdn::launch_gated_rmsnorm(x, z, z_tok_stride, y, dt, w, N, H, eps,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 size_t gdn_prefill_slots_workspace_bytes(int32_t R, int32_t max_len, gdn_dims dims) {
@@ -283,7 +284,8 @@ size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims) {
   return mixer_ws(B, T, dims).total();
 }
 
-int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* conv_w,
+int gdn_mixer_prefill(const void* qkv, int64_t qkv_tok_stride, const void* z,
+                      int64_t z_tok_stride, int32_t dt, const float* conv_w,
                       float* conv_state, const void* a, const void* b, int32_t gate_dt,
                       const float* A_log, const float* dt_bias, const float* norm_w,
                       const float* state_in, float* state_out, void* y, int32_t B, int32_t T,
@@ -299,6 +301,8 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
   if (B < 0 || T < 0) return GDN_ERR_SHAPE;
   if ((int64_t)B * Hv * 8 > INT32_MAX || (int64_t)B * T > INT32_MAX) return GDN_ERR_SHAPE;
   if (!conv_grid_ok(B, T, C)) return GDN_ERR_SHAPE;
+  if (T != 0 && (qkv_tok_stride < C || z_tok_stride < (int64_t)Hv * 128)) return GDN_ERR_SHAPE;
+  if (qkv_tok_stride % 8 != 0 || z_tok_stride % 8 != 0) return GDN_ERR_ALIGN;
   if (!aligned(qkv, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(conv_w, 16) ||
       (conv_state && !aligned(conv_state, 16)) || !aligned(a, dsize(gate_dt)) ||
       !aligned(b, dsize(gate_dt)) || !aligned(A_log, 4) || !aligned(dt_bias, 4) ||
@@ -316,8 +320,11 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
   if (workspace_bytes < w.total() || !workspace) return GDN_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return GDN_ERR_ALIGN;
   const size_t ybytes = (size_t)B * T * Hv * 128 * dsize(dt);
-  if (overlaps(y, ybytes, workspace, w.total()) || overlaps(y, ybytes, z, ybytes) ||
-      overlaps(y, ybytes, qkv, (size_t)B * T * C * dsize(dt)))
+  const size_t tokens = (size_t)B * T;
+  const size_t zbytes = ((tokens - 1) * z_tok_stride + Hv * 128) * dsize(dt);
+  const size_t qkvbytes = ((tokens - 1) * qkv_tok_stride + C) * dsize(dt);
+  if (overlaps(y, ybytes, workspace, w.total()) || overlaps(y, ybytes, z, zbytes) ||
+      overlaps(y, ybytes, qkv, qkvbytes))
     return GDN_ERR_SHAPE;
   if (dt == GDN_F32) {
     // f32 inputs keep f32 accuracy: the conv writes [B, T, C] f32 to the
@@ -325,29 +332,29 @@ int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* c
     // recurrence runs token by token in f32 on views of it, and the norm
     // runs in place on y.
     float* yc = static_cast<float*>(workspace);
-    hipError_t e = gdn::launch_conv_silu(qkv, dt, yc, GDN_F32, conv_w, conv_state, B, T, C, L2C,
-                                         l2_eps, s);
+    hipError_t e = gdn::launch_conv_silu(qkv, qkv_tok_stride, dt, yc, GDN_F32, conv_w,
+                                         conv_state, B, T, C, L2C, l2_eps, s);
     if (e != hipSuccess) return GDN_ERR_LAUNCH;
     e = gdn::launch_prefill_sequential(yc, C, yc + Hk * 128, C, yc + L2C, C, GDN_F32, a, b,
                                        gate_dt, A_log, dt_bias, state_in, state_out, y, dt, B, T,
                                        nullptr, 0, Hk, Hv, q_scale, s);
     if (e != hipSuccess) return GDN_ERR_LAUNCH;
-    return launch_status(
-        gdn::launch_gated_rmsnorm(y, z, y, dt, norm_w, (int64_t)B * T * Hv, norm_eps, s));
+    return launch_status(gdn::launch_gated_rmsnorm(y, z, z_tok_stride, y, dt, norm_w,
+                                                   (int64_t)B * T, Hv, norm_eps, s));
   }
   char* ws = static_cast<char*>(workspace);
   float* yqk = reinterpret_cast<float*>(ws);
   uint16_t* yv = reinterpret_cast<uint16_t*>(ws + w.qk_bytes);
   void* chunk_ws = ws + w.qk_bytes + w.v_bytes;
-  hipError_t e = gdn::launch_conv_silu_split(qkv, dt, yqk, yv, conv_w, conv_state, B, T, C, L2C,
-                                             l2_eps, s);
+  hipError_t e = gdn::launch_conv_silu_split(qkv, qkv_tok_stride, dt, yqk, yv, conv_w,
+                                             conv_state, B, T, C, L2C, l2_eps, s);
   if (e != hipSuccess) return GDN_ERR_LAUNCH;
   e = gdn::launch_prefill_chunked(yqk, L2C, yqk + Hk * 128, L2C, yv, Hv * 128, GDN_F32, GDN_BF16,
                                   a, b, gate_dt, A_log, dt_bias, state_in, state_out, y, dt, B, T,
                                   nullptr, 0, Hk, Hv, q_scale, chunk_ws, s);
   if (e != hipSuccess) return GDN_ERR_LAUNCH;
-  return launch_status(
-      gdn::launch_gated_rmsnorm(y, z, y, dt, norm_w, (int64_t)B * T * Hv, norm_eps, s));
+  return launch_status(gdn::launch_gated_rmsnorm(y, z, z_tok_stride, y, dt, norm_w,
+                                                 (int64_t)B * T, Hv, norm_eps, s));
 }
 
 size_t gdn_gate_proj_workspace_bytes(int32_t M, int32_t K, int32_t H) {

@@ -7,17 +7,20 @@
 // then for c < l2_channels each head_dim group of y is divided by
 // sqrt(sum of squares + l2_eps).  hist_out = the last 3 rows of xhat.
 //
-// Output: channels below l2_channels go to ya (row stride ya_stride), the
-// others to yb at channel c - l2_channels (row stride yb_stride), each in its
-// own dtype.  The plain call points both at one [B, T, C] buffer; the whole
-// mixer keeps q|k in f32 and v in bf16 (the chunked prefill rounds v to bf16
-// anyway, so the bf16 copy changes no result).
+// Input: token (b, t) of x starts at (b*T + t) * x_ts (a view into a wider
+// buffer, such as the [T, 16384] output of one in_proj_qkvz product, is
+// read in place).  Output: channels below l2_channels go to ya (row stride
+// ya_stride), the others to yb at channel c - l2_channels (row stride
+// yb_stride), each in its own dtype.  The plain call points both at one
+// [B, T, C] buffer; the whole mixer keeps q|k in f32 and v in bf16 (the
+// chunked prefill rounds v to bf16 anyway, so the bf16 copy changes no
+// result).
 //
 // Mapping: one thread owns 8 consecutive channels (one 16-byte bf16 load per
 // token) and walks CONV_TB consecutive tokens, keeping the previous 3 inputs
 // in registers, so every input element is read once (plus a 3-token halo per
-// block, served from L2: the block before it ran on the same XCD).  A 128-channel head is 16 lanes, so the L2 sum is a DPP row
-// reduction.  HBM-bound: one read of x and one write of y.
+// block, served from L2: the block before it ran on the same XCD).  A
+// 128-channel head is 16 lanes, so the L2 sum is a DPP row reduction.  HBM-bound: one read of x and one write of y.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -60,9 +63,9 @@ __device__ __forceinline__ void store8_stream(uint16_t* p, const float* in) {
 
 template <typename TX, typename TYA, typename TYB, bool kStream>
 __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
-    const TX* __restrict__ x, TYA* __restrict__ ya, int64_t ya_stride, TYB* __restrict__ yb,
-    int64_t yb_stride, const float* __restrict__ w, float* conv_state, int nb, int Tlen, int C,
-    int l2_channels, float l2_eps) {
+    const TX* __restrict__ x, int64_t x_ts, TYA* __restrict__ ya, int64_t ya_stride,
+    TYB* __restrict__ yb, int64_t yb_stride, const float* __restrict__ w, float* conv_state,
+    int nb, int Tlen, int C, int l2_channels, float l2_eps) {
   // Workgroups whose ids agree mod 8 share an XCD; each XCD takes a
   // contiguous run of (batch, token block, channel block) so a block's 3-row
   // halo was read into the same L2 by its neighbour.
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
 
   // Row bases are uniform; the thread's channel offset is added last, so the
   // loads and stores take a scalar base and one per-thread offset.
-  const TX* xrows = x + (int64_t)b * Tlen * C;
+  const TX* xrows = x + (int64_t)b * Tlen * x_ts;
   const TX* xb = xrows + (uint32_t)c0;
   const bool l2 = c0 < l2_channels;  // uniform over a 16-lane head group
   TYA* yarows = ya + (int64_t)b * Tlen * ya_stride;
@@ -118,14 +121,14 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
 #pragma unroll
           for (int i = 0; i < 8; ++i) nv[i] = h[r][i];
         } else {
-          load8(xb + (int64_t)(r - 3) * C, nv);
+          load8(xb + (int64_t)(r - 3) * x_ts, nv);
         }
         store8(cs + (int64_t)j * C, nv);
       }
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) load8(xb + (int64_t)(t0 - 3 + j) * C, h[j]);
+    for (int j = 0; j < 3; ++j) load8(xb + (int64_t)(t0 - 3 + j) * x_ts, h[j]);
   }
 
   constexpr int U = 8;  // loads in flight per thread
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
     Raw8<TX> xs[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (t + u < t1) xs[u].load(xrows + (int64_t)(t + u) * C + ca);
+      if (t + u < t1) xs[u].load(xrows + (int64_t)(t + u) * x_ts + ca);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + u < t1) {
@@ -173,48 +176,49 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_silu_kernel(
 }
 
 template <typename TX, typename TYA, typename TYB, bool kStream = false>
-static void launch_conv_t(const void* x, void* ya, int64_t ya_stride, void* yb, int64_t yb_stride,
-                          const float* w, float* conv_state, int B, int T, int C, int l2_channels,
-                          float l2_eps, hipStream_t stream) {
+static void launch_conv_t(const void* x, int64_t x_ts, void* ya, int64_t ya_stride, void* yb,
+                          int64_t yb_stride, const float* w, float* conv_state, int B, int T,
+                          int C, int l2_channels, float l2_eps, hipStream_t stream) {
   const int64_t total = (int64_t)((C + CONV_THREADS * 8 - 1) / (CONV_THREADS * 8)) *
                         ((T + CONV_TB - 1) / CONV_TB) * B;
   dim3 grid((unsigned)(((total + 7) / 8) * 8));
   hipLaunchKernelGGL((conv_silu_kernel<TX, TYA, TYB, kStream>), grid, dim3(CONV_THREADS), 0, stream,
-                     (const TX*)x, (TYA*)ya, ya_stride, (TYB*)yb, yb_stride, w, conv_state, B, T,
-                     C, l2_channels, l2_eps);
+                     (const TX*)x, x_ts, (TYA*)ya, ya_stride, (TYB*)yb, yb_stride, w,
+                     conv_state, B, T, C, l2_channels, l2_eps);
 }
 
-hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const float* w,
-                            float* conv_state, int B, int T, int C, int l2_channels, float l2_eps,
-                            hipStream_t stream) {
+hipError_t launch_conv_silu(const void* x, int64_t x_ts, int x_dt, void* y, int y_dt,
+                            const float* w, float* conv_state, int B, int T, int C,
+                            int l2_channels, float l2_eps, hipStream_t stream) {
   // One [B, T, C] output: the second part starts l2_channels into each row.
   const size_t ds = y_dt == 1 ? 2 : 4;
   void* yb = static_cast<char*>(y) + (size_t)l2_channels * ds;
   if (x_dt == 1 && y_dt == 1)
-    launch_conv_t<uint16_t, uint16_t, uint16_t>(x, y, C, yb, C, w, conv_state, B, T, C,
+    launch_conv_t<uint16_t, uint16_t, uint16_t>(x, x_ts, y, C, yb, C, w, conv_state, B, T, C,
                                                 l2_channels, l2_eps, stream);
   else if (x_dt == 1)
-    launch_conv_t<uint16_t, float, float>(x, y, C, yb, C, w, conv_state, B, T, C, l2_channels,
-                                          l2_eps, stream);
+    launch_conv_t<uint16_t, float, float>(x, x_ts, y, C, yb, C, w, conv_state, B, T, C,
+                                          l2_channels, l2_eps, stream);
   else if (y_dt == 1)
-    launch_conv_t<float, uint16_t, uint16_t>(x, y, C, yb, C, w, conv_state, B, T, C,
+    launch_conv_t<float, uint16_t, uint16_t>(x, x_ts, y, C, yb, C, w, conv_state, B, T, C,
                                              l2_channels, l2_eps, stream);
   else
-    launch_conv_t<float, float, float>(x, y, C, yb, C, w, conv_state, B, T, C, l2_channels,
-                                       l2_eps, stream);
+    launch_conv_t<float, float, float>(x, x_ts, y, C, yb, C, w, conv_state, B, T, C,
+                                       l2_channels, l2_eps, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_conv_silu_split(const void* x, int x_dt, float* yqk, uint16_t* yv,
-                                  const float* w, float* conv_state, int B, int T, int C,
-                                  int l2_channels, float l2_eps, hipStream_t stream) {
+hipError_t launch_conv_silu_split(const void* x, int64_t x_ts, int x_dt, float* yqk,
+                                  uint16_t* yv, const float* w, float* conv_state, int B, int T,
+                                  int C, int l2_channels, float l2_eps, hipStream_t stream) {
   if (x_dt == 1)
-    launch_conv_t<uint16_t, float, uint16_t, true>(x, yqk, l2_channels, yv, C - l2_channels, w,
-                                                   conv_state, B, T, C, l2_channels, l2_eps,
-                                                   stream);
+    launch_conv_t<uint16_t, float, uint16_t, true>(x, x_ts, yqk, l2_channels, yv,
+                                                   C - l2_channels, w, conv_state, B, T, C,
+                                                   l2_channels, l2_eps, stream);
   else
-    launch_conv_t<float, float, uint16_t, true>(x, yqk, l2_channels, yv, C - l2_channels, w,
-                                                conv_state, B, T, C, l2_channels, l2_eps, stream);
+    launch_conv_t<float, float, uint16_t, true>(x, x_ts, yqk, l2_channels, yv, C - l2_channels,
+                                                w, conv_state, B, T, C, l2_channels, l2_eps,
+                                                stream);
   return hipGetLastError();
 }
 

@@ -8,7 +8,10 @@
 // NORM_ROWS rows with all loads issued first.  HBM-bound: read x and z once,
 // write y once.  y may equal x (the whole mixer normalises its output in
 // place), so x and y are not declared restrict: each lane reads its elements
-// of a row before it writes them, and no lane touches another lane's.
+// of a row before it writes them, and no lane touches another lane's.  x and
+// y are [N, H, 128] contiguous; z's token n starts at n * z_ts (a view into
+// a wider buffer, such as one in_proj_qkvz product's output, is read in
+// place).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,7 +23,7 @@ constexpr int NORM_ROWS_PER_WG = NORM_THREADS / 16 * NORM_ROWS;
 
 template <typename T>
 __global__ __launch_bounds__(NORM_THREADS) void gated_rmsnorm_kernel(
-    const T* x, const T* __restrict__ z, T* y,
+    const T* x, const T* __restrict__ z, int64_t z_ts, int H, T* y,
     const float* __restrict__ w, int64_t rows, float eps) {
   const int lane16 = threadIdx.x & 15;
   const int grp = threadIdx.x >> 4;
@@ -35,7 +38,8 @@ __global__ __launch_bounds__(NORM_THREADS) void gated_rmsnorm_kernel(
   for (int r = 0; r < NORM_ROWS; ++r) {
     if (row0 + r < rows) {
       load8(x + (row0 + r) * 128 + lane16 * 8, xv[r]);
-      load8(z + (row0 + r) * 128 + lane16 * 8, zv[r]);
+      const int64_t n = (row0 + r) / H;
+      load8(z + n * z_ts + (row0 + r - n * H) * 128 + lane16 * 8, zv[r]);
     }
   }
 #pragma unroll
@@ -54,15 +58,18 @@ __global__ __launch_bounds__(NORM_THREADS) void gated_rmsnorm_kernel(
   }
 }
 
-hipError_t launch_gated_rmsnorm(const void* x, const void* z, void* y, int dt, const float* w,
-                                int64_t rows, float eps, hipStream_t stream) {
+hipError_t launch_gated_rmsnorm(const void* x, const void* z, int64_t z_ts, void* y, int dt,
+                                const float* w, int64_t N, int H, float eps, hipStream_t stream) {
+  const int64_t rows = N * H;
   const int64_t nwg = (rows + NORM_ROWS_PER_WG - 1) / NORM_ROWS_PER_WG;
   if (dt == 1) {
     hipLaunchKernelGGL(gated_rmsnorm_kernel<uint16_t>, dim3((unsigned)nwg), dim3(NORM_THREADS), 0,
-                       stream, (const uint16_t*)x, (const uint16_t*)z, (uint16_t*)y, w, rows, eps);
+                       stream, (const uint16_t*)x, (const uint16_t*)z, z_ts, H, (uint16_t*)y, w,
+                       rows, eps);
   } else {
     hipLaunchKernelGGL(gated_rmsnorm_kernel<float>, dim3((unsigned)nwg), dim3(NORM_THREADS), 0,
-                       stream, (const float*)x, (const float*)z, (float*)y, w, rows, eps);
+                       stream, (const float*)x, (const float*)z, z_ts, H, (float*)y, w, rows,
+                       eps);
   }
   return hipGetLastError();
 }

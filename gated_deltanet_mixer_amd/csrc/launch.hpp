@@ -12,18 +12,20 @@ namespace gdn {
 constexpr int CONV_TB = 8;
 constexpr int CONV_THREADS = 256;
 
-hipError_t launch_conv_silu(const void* x, int x_dt, void* y, int y_dt, const float* w,
-                            float* conv_state, int B, int T, int C, int l2_channels, float l2_eps,
-                            hipStream_t stream);
+// x's token (b, t) starts at (b*T + t) * x_ts elements; y is [B, T, C].
+hipError_t launch_conv_silu(const void* x, int64_t x_ts, int x_dt, void* y, int y_dt,
+                            const float* w, float* conv_state, int B, int T, int C,
+                            int l2_channels, float l2_eps, hipStream_t stream);
 
 // The same conv with two outputs: channels below l2_channels in f32 to yqk
 // [B, T, l2_channels], the others in bf16 to yv [B, T, C - l2_channels].
-hipError_t launch_conv_silu_split(const void* x, int x_dt, float* yqk, uint16_t* yv,
-                                  const float* w, float* conv_state, int B, int T, int C,
-                                  int l2_channels, float l2_eps, hipStream_t stream);
+hipError_t launch_conv_silu_split(const void* x, int64_t x_ts, int x_dt, float* yqk,
+                                  uint16_t* yv, const float* w, float* conv_state, int B, int T,
+                                  int C, int l2_channels, float l2_eps, hipStream_t stream);
 
-hipError_t launch_gated_rmsnorm(const void* x, const void* z, void* y, int dt, const float* w,
-                                int64_t rows, float eps, hipStream_t stream);
+// x, y [N, H, 128] contiguous; z's token n starts at n * z_ts elements.
+hipError_t launch_gated_rmsnorm(const void* x, const void* z, int64_t z_ts, void* y, int dt,
+                                const float* w, int64_t N, int H, float eps, hipStream_t stream);
 
 hipError_t launch_decode_rows(const void* q, int64_t q_rs, const void* k, int64_t k_rs,
                               const void* v, int64_t v_rs, int qkv_dt, const void* a,

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -90,9 +90,13 @@ int gdn_abi_version(void);
  * gdn_conv_silu -- depthwise causal conv + silu, optional per-head L2.
  * ("Qwen3.8 27B" card, Gated DeltaNet bullet; llm-arch-viz module tree:
  * conv1d 10240x1x4 without bias.)
- *   x           [B, T, C] in dtype x_dt.
- *   y           [B, T, C] in dtype y_dt (f32 output keeps the normalised q/k
- *               unrounded for the recurrence); y must not overlap x.
+ *   x           [B, T, C] in dtype x_dt, token (b, t) at (b*T + t)*x_tok_stride
+ *               elements (x_tok_stride >= C, a multiple of 8; C for a
+ *               contiguous x, wider for the q|k|v columns of a buffer that
+ *               also holds z, as one in_proj_qkvz product writes them).
+ *   y           [B, T, C] contiguous in dtype y_dt (f32 output keeps the
+ *               normalised q/k unrounded for the recurrence); y must not
+ *               overlap x.
  *   w           [C, W] f32; w[c][W-1] multiplies the current token,
  *               w[c][0] the input W-1 tokens back (cross-correlation).
  *   conv_state  [B, W-1, C] f32, in/out: the last W-1 inputs before this
@@ -104,8 +108,8 @@ int gdn_abi_version(void);
  * Constraints: W == 4; C % 8 == 0; l2_channels % head_dim == 0 and
  * l2_channels <= C; head_dim == 128 when l2_channels > 0; T == 0 is a no-op.
  */
-int gdn_conv_silu(const void* x, int32_t x_dt, void* y, int32_t y_dt, const float* w,
-                  float* conv_state, int32_t B, int32_t T, int32_t C, int32_t W,
+int gdn_conv_silu(const void* x, int64_t x_tok_stride, int32_t x_dt, void* y, int32_t y_dt,
+                  const float* w, float* conv_state, int32_t B, int32_t T, int32_t C, int32_t W,
                   int32_t l2_channels, int32_t head_dim, float l2_eps, void* stream);
 
 /*
@@ -203,12 +207,14 @@ int gdn_decode_rows_multi(const void* q, int64_t q_row_stride, int64_t q_tok_str
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * (1 + w) * silu(z) per
  * row of D ("Qwen3.8 27B" card, Gated DeltaNet and Norms bullets;
  * llm-arch-viz: RMSNormGated of width 128, eps 1e-06).
- *   x, z, y  [N, H, D] contiguous in dtype `dt`; y may equal x.
+ *   x, y     [N, H, D] contiguous in dtype `dt`; y may equal x.
+ *   z        [N, H, D] in dtype `dt`, token n at n*z_tok_stride elements
+ *            (z_tok_stride >= H*D, a multiple of 8; H*D when contiguous).
  *   w        [D] f32, shared by all heads.
  * Constraints: D == 128.
  */
-int gdn_gated_rmsnorm(const void* x, const void* z, void* y, int32_t dt, const float* w,
-                      int32_t N, int32_t H, int32_t D, float eps, void* stream);
+int gdn_gated_rmsnorm(const void* x, const void* z, int64_t z_tok_stride, void* y, int32_t dt,
+                      const float* w, int32_t N, int32_t H, int32_t D, float eps, void* stream);
 
 /*
  * Bytes of device workspace gdn_prefill_slots needs for R rows of at most
@@ -268,9 +274,13 @@ size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims);
  * v: the conv writes q|k in f32 and v in bf16 to the workspace (the chunked
  * prefill rounds v to bf16 anyway).  f32 inputs: conv (f32 output) ->
  * sequential f32 recurrence -> norm, f32 throughout.
- *   qkv    [B, T, C] contiguous in dt, C = 2*Hk*dk + Hv*dv, channels
- *          [q heads | k heads | v heads].
- *   z      [B, T, Hv*dv] contiguous in dt (the output gate).
+ *   qkv    [B, T, C] in dt, C = 2*Hk*dk + Hv*dv, channels [q heads | k heads |
+ *          v heads]; token (b, t) at (b*T + t)*qkv_tok_stride elements.
+ *   z      [B, T, Hv*dv] in dt (the output gate); token (b, t) at
+ *          (b*T + t)*z_tok_stride.  The strides (>= C and >= Hv*dv, multiples
+ *          of 8) let qkv and z be the two column ranges of one [B, T, C +
+ *          Hv*dv] buffer, the output of in_proj_qkv and in_proj_z stored as
+ *          one weight and run as one gdn_linear.
  *   conv_w [C, 4] f32 (w[c][3] multiplies the current token);
  *   conv_state [B, 3, C] f32 in/out as in gdn_conv_silu, or NULL (zero
  *          history, not written).
@@ -278,7 +288,7 @@ size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims);
  *   norm_w [dv] f32 (the scale is 1 + norm_w), shared by all heads.
  *   state_in / state_out  [B, Hv, dv, dk] f32 as in gdn_prefill.
  *   y      [B, T, Hv*dv] contiguous in dt; must not overlap qkv, z or the
- *          workspace.
+ *          workspace (each over the extent its stride spans).
  *   l2_eps (1e-6) inside the q/k L2 norm; norm_eps (1e-6) of the RMSNorm.
  *   workspace  at least gdn_mixer_prefill_workspace_bytes(B, T, dims) bytes,
  *          256-byte aligned; scratch after the call.
@@ -286,7 +296,8 @@ size_t gdn_mixer_prefill_workspace_bytes(int32_t B, int32_t T, gdn_dims dims);
  * through.  Errors as for the three calls it replaces; GDN_ERR_SHAPE if y
  * overlaps qkv, z or the workspace.
  */
-int gdn_mixer_prefill(const void* qkv, const void* z, int32_t dt, const float* conv_w,
+int gdn_mixer_prefill(const void* qkv, int64_t qkv_tok_stride, const void* z,
+                      int64_t z_tok_stride, int32_t dt, const float* conv_w,
                       float* conv_state, const void* a, const void* b, int32_t gate_dt,
                       const float* A_log, const float* dt_bias, const float* norm_w,
                       const float* state_in, float* state_out, void* y, int32_t B, int32_t T,

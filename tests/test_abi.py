@@ -34,7 +34,7 @@ def test_header_and_exports():
             "gdn_gate_proj_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
-    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_abi_version() == 2
     for s in range(9):
         assert gdn.gdn_status_str(s).startswith("GDN_")
     assert gdn.gdn_status_str(99) == "unknown gdn_status"
@@ -44,9 +44,11 @@ def _vp(x):
     return ctypes.c_void_p(x) if x else None
 
 
-def conv(x=P, y=2 * P, dt=1, ydt=1, w=3 * P, cs=None, B=1, T=8, C=1024, W=4, l2=0, hd=128):
-    return gdn.lib().gdn_conv_silu(_vp(x), dt, _vp(y), ydt, _vp(w), _vp(cs), B, T, C, W, l2, hd,
-                                   1e-6, None)
+def conv(x=P, y=2 * P, dt=1, ydt=1, w=3 * P, cs=None, B=1, T=8, C=1024, W=4, l2=0, hd=128,
+         xts=None):
+    xts = C if xts is None else xts
+    return gdn.lib().gdn_conv_silu(_vp(x), xts, dt, _vp(y), ydt, _vp(w), _vp(cs), B, T, C, W, l2,
+                                   hd, 1e-6, None)
 
 
 def test_conv_validation():
@@ -58,6 +60,10 @@ def test_conv_validation():
     assert conv(W=0) == SHAPE
     assert conv(C=1020) == SHAPE
     assert conv(l2=2048) == SHAPE        # more than C
+    assert conv(xts=1016) == SHAPE       # token stride below C
+    assert conv(xts=1028) == ALIGN       # token stride not a multiple of 8
+    # y starts inside the last token's row of a strided x
+    assert conv(xts=16384, B=2, T=4, y=P + (7 * 16384 + 1024) * 2 - 64) == SHAPE
     assert conv(l2=100, hd=64) == SHAPE  # not a whole number of heads
     assert conv(l2=128, hd=64) == UNSUP
     assert conv(x=P + 8) == ALIGN
@@ -162,22 +168,30 @@ def test_decode_multi_validation():
 
 def test_norm_validation():
     L = gdn.lib()
-    f = lambda x=P, z=2 * P, y=3 * P, w=4 * P, dt=1, N=4, H=48, D=128: L.gdn_gated_rmsnorm(
-        _vp(x), _vp(z), _vp(y), dt, _vp(w), N, H, D, 1e-6, None)
+    f = lambda x=P, z=2 * P, y=3 * P, w=4 * P, dt=1, N=4, H=48, D=128, zts=None: \
+        L.gdn_gated_rmsnorm(_vp(x), _vp(z), H * D if zts is None else zts, _vp(y), dt, _vp(w),
+                            N, H, D, 1e-6, None)
     assert f(z=0) == NULL
     assert f(dt=3) == DTYPE
     assert f(D=64) == UNSUP
     assert f(N=-2) == SHAPE
     assert f(w=P + 4) == ALIGN
+    assert f(zts=48 * 128 - 8) == SHAPE
+    assert f(zts=16384 + 4) == ALIGN
+    assert f(zts=16384, N=0) == OK
     assert f(N=0) == OK
 
 
 def mixer(qkv=P, z=2 * P, dt=1, cw=3 * P, cs=None, a=4 * P, b=5 * P, gdt=1, Al=6 * P, db=7 * P,
-          nw=8 * P, si=None, so=None, y=9 * P, B=1, T=64, dims=D16, ws=64 * P, wsb=None):
+          nw=8 * P, si=None, so=None, y=9 * P, B=1, T=64, dims=D16, ws=64 * P, wsb=None,
+          qts=None, zts=None):
     L = gdn.lib()
     if wsb is None:
         wsb = L.gdn_mixer_prefill_workspace_bytes(B, T, dims)
-    return L.gdn_mixer_prefill(_vp(qkv), _vp(z), dt, _vp(cw), _vp(cs), _vp(a), _vp(b), gdt,
+    C = (2 * dims.n_qk_heads + dims.n_v_heads) * 128
+    qts = C if qts is None else qts
+    zts = dims.n_v_heads * 128 if zts is None else zts
+    return L.gdn_mixer_prefill(_vp(qkv), qts, _vp(z), zts, dt, _vp(cw), _vp(cs), _vp(a), _vp(b), gdt,
                                _vp(Al), _vp(db), _vp(nw), _vp(si), _vp(so), _vp(y), B, T, dims,
                                1.0, 1e-6, 1e-6, _vp(ws), wsb, None)
 
@@ -205,6 +219,14 @@ def test_mixer_prefill_validation():
     assert mixer(ws=64 * P + 128) == ALIGN
     assert mixer(y=64 * P) == SHAPE      # y inside the workspace
     assert mixer(y=2 * P) == SHAPE       # y on top of z
+    C = (2 * D16.n_qk_heads + D16.n_v_heads) * 128
+    assert mixer(qts=C - 8) == SHAPE
+    assert mixer(zts=D16.n_v_heads * 128 - 8) == SHAPE
+    assert mixer(qts=C + 4) == ALIGN
+    assert mixer(zts=D16.n_v_heads * 128 + 12) == ALIGN
+    # a wide z stride reaches y: the last token's z row ends inside y's bytes
+    assert mixer(y=40 * P, z=40 * P - (63 * 16384 + 6144) * 2 + 64, zts=16384) == SHAPE
+    assert mixer(qts=0, zts=0, B=0, T=0) == OK  # no tokens: strides unused
     assert mixer(B=0) == OK
 
 

@@ -1,9 +1,11 @@
 """A whole-layer decode step captured in a HIP graph (torch.cuda.CUDAGraph) and
 replayed: every replay must give the eager step's results bit for bit.
 
-The step for R fixed rows: in_proj_qkv and in_proj_z (gdn_linear), the gate
-projections (gdn_gate_proj), the conv over one token with each row's conv
-history (gdn_conv_silu), decode_rows, the gated RMSNorm in place and out_proj.
+The step for R fixed rows: in_proj_qkv and in_proj_z as one product with the
+stacked weight (gdn_linear into one [R, 16384] buffer), the gate projections
+(gdn_gate_proj), the conv over one token with each row's conv history
+(gdn_conv_silu, reading the q|k|v columns in place), decode_rows, the gated
+RMSNorm in place (reading the z columns in place) and out_proj.
 The eager calls run first (they also create the hipBLASLt handle, which may
 allocate, and the shapes' plans, so that the captured calls reuse the same
 plans as the eager step).  The graph is replayed four
@@ -24,8 +26,7 @@ pytestmark = pytest.mark.gpu
 
 def _step(L):
     R = L["x"].shape[0]
-    gdn.gdn_linear(L["x"], L["W_qkv"], y=L["qkv"].view(R, CONV_CH), workspace=L["lws"])
-    gdn.gdn_linear(L["x"], L["W_z"], y=L["z"], workspace=L["lws"])
+    gdn.gdn_linear(L["x"], L["W_qkvz"], y=L["qkvz"], workspace=L["lws"])
     gdn.gdn_gate_proj(L["x"], L["W_a"], L["W_b"], a=L["a"], b=L["b"], workspace=L["gws"])
     gdn.gdn_conv_silu(L["qkv"], L["conv_w"], L["conv_state"], l2_channels=2 * HK * D, y=L["y"])
     y = L["y"][:, 0]
@@ -33,7 +34,8 @@ def _step(L):
                         y[:, HK * D:2 * HK * D].unflatten(1, (HK, D)),
                         y[:, 2 * HK * D:].unflatten(1, (HV, D)), L["a"], L["b"], L["A_log"],
                         L["dt_bias"], L["state"], o=L["o"])
-    gdn.gdn_gated_rmsnorm(L["o"], L["z"].view(R, HV, D), L["norm_w"], y=L["o"])
+    gdn.gdn_gated_rmsnorm(L["o"], L["qkvz"][:, CONV_CH:].unflatten(1, (HV, D)), L["norm_w"],
+                          y=L["o"])
     gdn.gdn_linear(L["o"].view(R, HV * D), L["W_out"], y=L["out"], workspace=L["lws"])
 
 
@@ -42,15 +44,16 @@ def _buffers(R, seed):
     po = proj_inputs(1, K=HV * D, outs=(("W_out", HIDDEN),), gate_H=0, seed=seed + 1)
     d = decode_inputs(R, seed=seed + 2)
     m = mixer_inputs(1, 4, seed=seed + 3)
-    L = {n: dev(p[n]) for n in ("x", "W_qkv", "W_z", "W_a", "W_b")}
+    L = {n: dev(p[n]) for n in ("x", "W_a", "W_b")}
+    L["W_qkvz"] = torch.cat([dev(p["W_qkv"]), dev(p["W_z"])], dim=0)
     L["W_out"] = dev(po["W_out"])
     L.update({n: dev(d[n]) for n in ("state", "A_log", "dt_bias")})
     L["conv_w"] = dev(m["conv_w"])
     L["norm_w"] = dev(m["norm_w"])
     rng = np.random.default_rng(seed + 4)
     L["conv_state"] = dev((rng.standard_normal((R, 3, CONV_CH)) * 0.5).astype(np.float32))
-    L["qkv"] = torch.empty((R, 1, CONV_CH), dtype=torch.bfloat16, device="cuda")
-    L["z"] = torch.empty((R, HV * D), dtype=torch.bfloat16, device="cuda")
+    L["qkvz"] = torch.empty((R, CONV_CH + HV * D), dtype=torch.bfloat16, device="cuda")
+    L["qkv"] = L["qkvz"][:, :CONV_CH].unsqueeze(1)  # [R, 1, 10240] view
     L["a"] = torch.empty((R, HV), dtype=torch.float32, device="cuda")
     L["b"] = torch.empty((R, HV), dtype=torch.float32, device="cuda")
     L["y"] = torch.empty((R, 1, CONV_CH), dtype=torch.bfloat16, device="cuda")
@@ -70,7 +73,7 @@ def test_decode_step_graph_replays_match_eager():
     cs0 = L["conv_state"].clone()
     _step(L)  # eager; builds the hipBLASLt plans
     torch.cuda.synchronize()
-    ref = {n: L[n].clone() for n in ("out", "state", "conv_state", "a", "b", "o")}
+    ref = {n: L[n].clone() for n in ("out", "state", "conv_state", "a", "b", "o", "qkvz")}
 
     def reset():
         L["state"].copy_(state0)
@@ -88,7 +91,7 @@ def test_decode_step_graph_replays_match_eager():
     scratch = torch.randn(1 << 20, device="cuda")
     for rep in range(4):
         reset()
-        for n in ("out", "a", "b", "o"):
+        for n in ("out", "a", "b", "o", "qkvz"):
             L[n].fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()

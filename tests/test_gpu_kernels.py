@@ -68,6 +68,34 @@ def test_conv_split_calls_match_one_call():
     assert torch.equal(torch.cat(ys, dim=1), y_full)
 
 
+@pytest.mark.parametrize("B,T", [(2, 150), (1, 1), (3, 1)])
+def test_conv_silu_reads_a_column_range_in_place(B, T):
+    """x as the q|k|v columns of a wider [B, T, 16384-like] buffer (the layout
+    of one in_proj_qkvz product): bitwise the result of a contiguous copy,
+    history included, and within the bar of the oracle."""
+    banner(f"conv_silu strided x B={B} T={T}")
+    Hk, Hv, d = 2, 6, 128
+    C = 2 * Hk * d + Hv * d
+    x = mixer_inputs(B, T, Hk=Hk, Hv=Hv, d=d, seed=70 + T)
+    rng = np.random.default_rng(71 + T)
+    hist = rng.normal(size=(B, 3, C)).astype(np.float32)
+    wide = torch.randn((B, T, C + Hv * d + 40), dtype=torch.bfloat16, device="cuda")
+    off = 16
+    wide[:, :, off:off + C] = dev(x["qkv"])
+    xv = wide[:, :, off:off + C]
+    assert B * T == 1 or not xv.is_contiguous()
+    w = dev(x["conv_w"])
+    cs1, cs2 = dev(hist.copy()), dev(hist.copy())
+    y1 = gdn.gdn_conv_silu(xv, w, cs1, l2_channels=2 * Hk * d, head_dim=d)
+    y2 = gdn.gdn_conv_silu(xv.contiguous(), w, cs2, l2_channels=2 * Hk * d, head_dim=d)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(cs1, cs2)
+    yr, hr = oracle.conv_silu(to_f64(x["qkv"]), to_f64(x["conv_w"]), hist)
+    yr = oracle.l2norm_heads(yr.reshape(B * T, C), 2 * Hk * d, d).reshape(B, T, C)
+    assert max_rel_err(host_f64(y1), yr) < TOL["bf16"]
+    assert np.array_equal(host_f64(cs1), hr)
+
+
 # ------------------------------------------------------------------ gated RMSNorm
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
@@ -84,6 +112,25 @@ def test_gated_rmsnorm_parity(dt, N, H):
     torch.cuda.synchronize()
     ref = oracle.gated_rmsnorm(to_f64(x), to_f64(z), to_f64(w))
     assert max_rel_err(host_f64(y), ref) < TOL[dt]
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_gated_rmsnorm_z_column_range(dt):
+    """z as the last Hv*128 columns of a wider buffer, in place (the z part of
+    one in_proj_qkvz product): bitwise the result of a contiguous z."""
+    banner(f"gated_rmsnorm strided z {dt}")
+    N, H = 301, 6
+    g = torch.Generator(device="cpu").manual_seed(5)
+    x = torch.randn((N, H, 128), generator=g).to(dt).cuda()
+    wide = torch.randn((N, 1024 + H * 128), generator=g).to(dt).cuda()
+    zv = wide[:, 1024:].unflatten(1, (H, 128))
+    w = (0.1 * torch.randn(128, generator=g)).cuda()
+    y1 = gdn.gdn_gated_rmsnorm(x, zv, w)
+    y2 = gdn.gdn_gated_rmsnorm(x, zv.contiguous(), w)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    ref = oracle.gated_rmsnorm(host_f64(x), host_f64(zv.contiguous()), host_f64(w))
+    assert max_rel_err(host_f64(y1), ref) < TOL["bf16" if dt == torch.bfloat16 else "f32"]
 
 
 # ------------------------------------------------------------------ decode_rows

@@ -133,6 +133,39 @@ def test_mixer_prefill_one_call_small(T):
     assert np.array_equal(host_f64(cs1), h_ref)
 
 
+@pytest.mark.parametrize("B,T", [(2, 150), (1, 64), (3, 1)])
+def test_mixer_prefill_reads_one_projection_buffer(B, T):
+    """qkv and z as the two column ranges of one [B, T, C + Hv*128] buffer
+    (one in_proj_qkvz product's output): bitwise the result of contiguous
+    copies, and within the bar of the oracle."""
+    banner(f"mixer_prefill strided qkv/z B={B} T={T} Hk=2 Hv=6")
+    Hk, Hv, d = 2, 6, 128
+    C = 2 * Hk * d + Hv * d
+    x = mixer_inputs(B, T, Hk=Hk, Hv=Hv, d=d, seed=61 + T)
+    buf = torch.cat([dev(x["qkv"]), dev(x["z"])], dim=2)
+    qv, zv = buf[..., :C], buf[..., C:]
+    rng = np.random.Generator(np.random.PCG64(9 + T))
+    S0 = torch.from_numpy(rng.normal(0.0, 0.05, (B, Hv, d, d)).astype(np.float32)).cuda()
+    h0 = torch.from_numpy(rng.standard_normal((B, 3, C)).astype(np.float32)).cuda()
+    outs = []
+    for qkv, z in ((qv, zv), (qv.contiguous(), zv.contiguous())):
+        cs, S = h0.clone(), S0.clone()
+        y = gdn.gdn_mixer_prefill(qkv, z, dev(x["conv_w"]), dev(x["a"]), dev(x["b"]),
+                                  dev(x["A_log"]), dev(x["dt_bias"]), dev(x["norm_w"]), Hk, Hv,
+                                  conv_state=cs, state_in=S, state_out=S)
+        outs.append((y, S, cs))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    y_ref, S_ref, h_ref = oracle.mixer(to_f64(x["qkv"]), to_f64(x["conv_w"]), to_f64(x["z"]),
+                                       to_f64(x["a"]), to_f64(x["b"]), x["A_log"], x["dt_bias"],
+                                       x["norm_w"], Hk, Hv, d, conv_hist=host_f64(h0),
+                                       S0=host_f64(S0))
+    assert max_rel_err(host_f64(outs[0][0]), y_ref) < TOL
+    assert max_rel_err(host_f64(outs[0][1]), S_ref) < TOL
+    assert np.array_equal(host_f64(outs[0][2]), h_ref)
+
+
 def test_mixer_prefill_f32_inputs_and_edge_cases():
     """f32 qkv/z/y (conv, sequential f32 recurrence and norm: the f32 bar
     1e-4), no conv history (NULL: zeros, not written), and T == 0 (state
