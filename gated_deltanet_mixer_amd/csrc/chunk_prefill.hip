@@ -19,9 +19,10 @@
 //    off-diagonal blocks by three levels of 16x16x16 MFMA products; then W
 //    and Ut on MFMA.  The chunk's K and Q rows are loaded coalesced and
 //    staged in LDS (f32 rows in two halves of 64 dims), where each wave
-//    reads its operand fragments.  Writes W, Ut^T, P = q_scale M o QK^T, G
-//    and (once per q/k head) K^T and Q to the workspace, all bf16 except G,
-//    each in the order the chain's lanes load it.  With f32 q/k, Q K^T
+//    reads its operand fragments.  Writes W, Ut^T, P = q_scale M o QK^T, the
+//    decay factors e^{G_t} and e^{G_last - G_t} (f32) and (once per q/k
+//    head) K^T and Q to the workspace, each in the order the chain's lanes
+//    load it.  With f32 q/k, Q K^T
 //    is formed from a two-term bf16 split of both operands: q . k is small
 //    next to |q||k| (unit vectors in 128 dimensions), so it needs more than
 //    bf16 operand precision; no other product does.
@@ -56,7 +57,7 @@ struct WsLayout {
   uint16_t* UtL;  // [B*Hv*NC][8192]  Utf, lo part
   uint16_t* P;    // [B*Hv*NC][4096]  Pf, hi part
   uint16_t* PL;   // [B*Hv*NC][4096]  Pf, lo part
-  float* G;       // [B*Hv*NC][128]: G_t (t < 64), then G_last replicated 64 times
+  float* G;       // [B*Hv*NC][128]: e^{G_t} (t < 64), then e^{G_last - G_t} (t < 64)
   uint16_t* Kt;   // [B*Hk*NC][8192]  Ktf
   uint16_t* Qb;   // [B*Hk*NC][8192]  Qf
   int32_t* F;     // [B*Hv*NC]: 1 if the chunk-head uses the two-part Ut and P
@@ -268,8 +269,11 @@ __global__ __launch_bounds__(PREP_THREADS, 3) void chunk_prep_kernel(
     Gs[lane] = Gl;
     Bs[lane] = be;
     BGs[lane] = be * __expf(Gl);
-    ws.G[chunk * 2 * CK + lane] = Gl;
-    ws.G[chunk * 2 * CK + CK + lane] = __shfl(Gl, CK - 1);
+    // The chain's decay factors, computed once here rather than in its
+    // sequential steps: e^{G_t}, and e^{G_last - G_t} (G_last = G_63, since
+    // padding tokens add g = 0).
+    ws.G[chunk * 2 * CK + lane] = __expf(Gl);
+    ws.G[chunk * 2 * CK + CK + lane] = __expf(__shfl(Gl, CK - 1) - Gl);
   }
   if (kStaged) {
 #pragma unroll
@@ -679,15 +683,15 @@ struct StateRegs {
   bf16x8 w[4];        // W[16w + li][32kk + 8lg ..]
   bf16x8 kt[2][2];    // K^T[32w + 16i + li][32kk + 8lg ..]
   u16x4 ut[NV / 16];  // Ut[16w + 4lg ..][dv0 + dvp2(u, li)], hi part
-  f32x4 gu;           // G[16w + 4lg ..]
-  float gl;           // G_last
+  f32x4 sc;           // e^{G_last - G_t}, t = 16w + 4lg ..
+  float gl;           // e^{G_last}
   int split;          // the chunk's two-part flag (read with flag_set)
 };
 
 struct OutRegs {
   bf16x8 q[4];   // Q[16w + li][32kk + 8lg ..]
   bf16x8 p[2];   // P[16w + li][32kk + 8lg ..], hi part
-  float gt;      // G[16w + li]
+  float gt;      // e^{G_t}, t = 16w + li
   int split;     // the chunk's two-part flag (read with flag_set)
 };
 
@@ -726,8 +730,8 @@ __device__ __forceinline__ void state_fetch(StateRegs<NV>& R, const WsLayout& ws
     R.ut[u] = *reinterpret_cast<const u16x4*>(ws.Ut + off);
   }
   const float* gp = ws.G + chunk * 2 * CK;
-  R.gu = *reinterpret_cast<const f32x4*>(gp + 16 * w + 4 * (lane >> 4));
-  R.gl = gp[CK + (lane & 15)];  // G_last, replicated
+  R.sc = *reinterpret_cast<const f32x4*>(gp + CK + 16 * w + 4 * (lane >> 4));
+  R.gl = gp[CK - 1];
   R.split = chunk_flag(ws, chunk);
 }
 
@@ -845,8 +849,7 @@ __device__ __forceinline__ void chain_run(const WsLayout& ws, const float* state
       // (2) U^T to LDS, plain and scaled by e^{G_last - G_s}.  A two-part
       // chunk also adds Ut's lo part (loaded here, in its own step) and
       // writes the lo parts of both copies.
-      const float sc[4] = {__expf(R.gl - R.gu[0]), __expf(R.gl - R.gu[1]),
-                           __expf(R.gl - R.gu[2]), __expf(R.gl - R.gu[3])};
+      const float sc[4] = {R.sc[0], R.sc[1], R.sc[2], R.sc[3]};
       float u[NVB][4];
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb)
@@ -879,7 +882,7 @@ __device__ __forceinline__ void chain_run(const WsLayout& ws, const float* state
       // chunk also + K^T of U's lo part), then its bf16 copy for the next
       // chunk (every wave finished reading the old copy before the barrier
       // above).
-      const float gl = __expf(R.gl);
+      const float gl = R.gl;
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
         const bf16x8 u0 = ld_frag(&Usl[(vb * 16 + li) * XP + lg * 8]);
@@ -974,7 +977,7 @@ __device__ __forceinline__ void chain_run(const WsLayout& ws, const float* state
       // token 16w + li (dvp order), one 8-wide store.  A two-part chunk adds
       // the lo-part products (loaded here, in its own step): (Uh + Ul)(Ph + Pl)
       // without Ul Pl.
-      const float gq = q_scale * __expf(R.gt);
+      const float gq = q_scale * R.gt;
       f32x4 acc[NVB];
 #pragma unroll
       for (int vb = 0; vb < NVB; ++vb) {
