@@ -133,15 +133,17 @@ def test_mixer_prefill_one_call_small(T):
     assert np.array_equal(host_f64(cs1), h_ref)
 
 
-@pytest.mark.parametrize("B,T", [(2, 150), (1, 64), (3, 1)])
-def test_mixer_prefill_reads_one_projection_buffer(B, T):
+@pytest.mark.parametrize("B,T,dt", [(2, 150, "bf16"), (1, 64, "bf16"), (3, 1, "bf16"),
+                                    (2, 70, "f32")])
+def test_mixer_prefill_reads_one_projection_buffer(B, T, dt):
     """qkv and z as the two column ranges of one [B, T, C + Hv*128] buffer
     (one in_proj_qkvz product's output): bitwise the result of contiguous
-    copies, and within the bar of the oracle."""
-    banner(f"mixer_prefill strided qkv/z B={B} T={T} Hk=2 Hv=6")
+    copies, and within the bar of the oracle (f32 inputs take the sequential
+    f32 path, whose conv and norm read the same strided views)."""
+    banner(f"mixer_prefill strided qkv/z B={B} T={T} {dt} Hk=2 Hv=6")
     Hk, Hv, d = 2, 6, 128
     C = 2 * Hk * d + Hv * d
-    x = mixer_inputs(B, T, Hk=Hk, Hv=Hv, d=d, seed=61 + T)
+    x = mixer_inputs(B, T, Hk=Hk, Hv=Hv, d=d, dt=dt, seed=61 + T)
     buf = torch.cat([dev(x["qkv"]), dev(x["z"])], dim=2)
     qv, zv = buf[..., :C], buf[..., C:]
     rng = np.random.Generator(np.random.PCG64(9 + T))
@@ -161,8 +163,9 @@ def test_mixer_prefill_reads_one_projection_buffer(B, T):
                                        to_f64(x["a"]), to_f64(x["b"]), x["A_log"], x["dt_bias"],
                                        x["norm_w"], Hk, Hv, d, conv_hist=host_f64(h0),
                                        S0=host_f64(S0))
-    assert max_rel_err(host_f64(outs[0][0]), y_ref) < TOL
-    assert max_rel_err(host_f64(outs[0][1]), S_ref) < TOL
+    tol = TOL_F32 if dt == "f32" else TOL
+    assert max_rel_err(host_f64(outs[0][0]), y_ref) < tol
+    assert max_rel_err(host_f64(outs[0][1]), S_ref) < tol
     assert np.array_equal(host_f64(outs[0][2]), h_ref)
 
 
