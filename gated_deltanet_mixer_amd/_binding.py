@@ -83,7 +83,7 @@ def lib():
         L.gdn_linear.restype = ctypes.c_int
         L.gdn_linear_tune.argtypes = L.gdn_linear.argtypes
         L.gdn_linear_tune.restype = ctypes.c_int
-        L.gdn_linear_kernel.argtypes = [i32, i32, i32, i64, i64]
+        L.gdn_linear_kernel.argtypes = [i32, i32, i32, i64, i64, ctypes.c_size_t]
         L.gdn_linear_kernel.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -482,11 +482,15 @@ def gdn_linear_tune(x, W, y=None, out_dtype=torch.bfloat16, workspace=None):
     return _linear(lib().gdn_linear_tune, "gdn_linear_tune", x, W, y, out_dtype, workspace)
 
 
-def gdn_linear_kernel(M, N, K, x_ld=None, w_ld=None):
+def gdn_linear_kernel(M, N, K, x_ld=None, w_ld=None, workspace_bytes=None):
     """Which engine an untimed gdn_linear call of this shape uses on the
-    current device: the library GEMM's block width (160, 192, 256 or 320), or
-    0 for hipBLASLt.  x_ld and w_ld default to K."""
-    r = lib().gdn_linear_kernel(M, N, K, K if x_ld is None else x_ld, K if w_ld is None else w_ld)
+    current device: the library GEMM's block width (160, 192, 256 or 320 for
+    its tiled form, 64 for its few-row form), or 0 for hipBLASLt.  x_ld and
+    w_ld default to K, workspace_bytes to gdn_linear_workspace_bytes()."""
+    if workspace_bytes is None:
+        workspace_bytes = lib().gdn_linear_workspace_bytes()
+    r = lib().gdn_linear_kernel(M, N, K, K if x_ld is None else x_ld,
+                                K if w_ld is None else w_ld, workspace_bytes)
     if r < 0:
         raise GDNError(-r, "gdn_linear_kernel")
     return r

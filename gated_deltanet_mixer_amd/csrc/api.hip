@@ -405,6 +405,11 @@ static int linear_call(const void* x, int64_t x_ld, const void* W, int64_t w_ld,
   const size_t wbytes = ((size_t)(N - 1) * w_ld + K) * 2;
   const size_t ybytes = ((size_t)(M - 1) * y_ld + N) * dsize(y_dt);
   if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, W, wbytes)) return GDN_ERR_SHAPE;
+  if (workspace_bytes > 0 &&
+      (overlaps(workspace, workspace_bytes, x, xbytes) ||
+       overlaps(workspace, workspace_bytes, W, wbytes) ||
+       overlaps(workspace, workspace_bytes, y, ybytes)))
+    return GDN_ERR_SHAPE;
   switch (gdn::launch_linear(static_cast<const uint16_t*>(x), x_ld,
                              static_cast<const uint16_t*>(W), w_ld, y, y_ld, y_dt, M, N, K,
                              workspace, workspace_bytes, tune, static_cast<hipStream_t>(stream))) {
@@ -429,14 +434,16 @@ int gdn_linear_tune(const void* x, int64_t x_ld, const void* W, int64_t w_ld, vo
                      stream);
 }
 
-int gdn_linear_kernel(int32_t M, int32_t N, int32_t K, int64_t x_ld, int64_t w_ld) {
+int gdn_linear_kernel(int32_t M, int32_t N, int32_t K, int64_t x_ld, int64_t w_ld,
+                      size_t workspace_bytes) {
   if (M < 0 || N <= 0 || K <= 0 || x_ld < K || w_ld < K) return -GDN_ERR_SHAPE;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return -GDN_ERR_LAUNCH;
   const int width = gdn::gemm_bf16_width(M, N, K, x_ld, w_ld, cus);
-  return width * 32;
+  if (width) return width * 32;
+  return gdn::gemm_fewrow_splits(M, N, K, x_ld, w_ld, cus, workspace_bytes) ? 64 : 0;
 }
 
 }  // extern "C"

@@ -211,7 +211,166 @@ hipError_t launch_width(const uint16_t* x, int64_t x_ld, const uint16_t* W, int6
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Few-row form, for M <= 64 (a decode step's projections): a weight stream.
+// A workgroup takes 64 W rows by all (up to 64) x rows over one of `splits`
+// equal K ranges; eight waves, wave w owning W rows 16 (w & 3) .. + 15 by x
+// rows 32 (w >> 2) .. + 31.  k advances in stages of 64 through a ring of
+// FR_NS LDS buffers filled straight from global memory FR_NS - 1 stages ahead
+// (8 KB of W rows and 8 KB of x rows per stage; rows and chunks laid out as
+// in the tiled form).  With one K range the result goes to y; otherwise each
+// range writes f32 partial sums to the workspace and a second kernel adds
+// them in range order, so results do not depend on timing.  Measured at 64
+// rows against the tuned hipBLASLt plan: in_proj_qkvz (16384 x 5120, one
+// range, 256 workgroups) 38.6 vs 44.2 us, out_proj (5120 x 6144, three
+// ranges, 240 workgroups) 17.0 vs 21.0 us.
+constexpr int FR_ROWS = 64;  // x rows
+constexpr int FR_BN = 64;    // W rows per workgroup
+constexpr int FR_NS = 4;     // LDS stages in the ring
+
+template <typename TY>
+__global__ __launch_bounds__(G_THREADS) void gemm_fewrow_kernel(
+    const uint16_t* __restrict__ x, int64_t x_ld, const uint16_t* __restrict__ W, int64_t w_ld,
+    TY* __restrict__ y, int64_t y_ld, float* __restrict__ part, int M, int N, int KS,
+    int tiles_n, int splits) {
+  constexpr int LB = (FR_BN + FR_ROWS) * GK;       // elements per stage
+  constexpr int NPW = (FR_BN + FR_ROWS) / 8 / 8;   // 1 KB loads per wave per stage
+  static_assert((FR_NS - 2) * NPW < 16, "one vmcnt field");
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[FR_NS * LB];
+  const int id = blockIdx.x;
+  if (id >= tiles_n * splits) return;
+  const int tn = id % tiles_n, sp = id / tiles_n;
+  const int n0 = __builtin_amdgcn_readfirstlane(tn * FR_BN);
+  const int k0 = __builtin_amdgcn_readfirstlane(sp * KS);
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wn = w & 3, wm = w >> 2;
+  typedef __attribute__((address_space(3))) void lds_t;
+  const int lrow = lane >> 3, lch = (lane & 7) ^ lrow;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * w_ld + k0), (short)0,
+      __builtin_amdgcn_readfirstlane((int)(FR_BN * 2 * (int)w_ld)), 0x00020000);
+  // x rows at or past M lie outside the range and load as zeros.
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + k0), (short)0, __builtin_amdgcn_readfirstlane((int)(M * 2 * (int)x_ld)),
+      0x00020000);
+  // Load q (8 rows) of a stage: q < FR_BN / 8 are W rows, the rest x rows.
+  auto load_stage = [&](int buf, int kt) {
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+      const int q = w * NPW + j;
+      lds_t* dst = (lds_t*)&Ls[buf * LB + q * 8 * GK];
+      if (q < FR_BN / 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wres, dst, 16, (uint32_t)((q * 8 + lrow) * w_ld * 2 + lch * 16), kt * GK * 2, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            xres, dst, 16, (uint32_t)(((q - FR_BN / 8) * 8 + lrow) * x_ld * 2 + lch * 16),
+            kt * GK * 2, 0, 0);
+    }
+  };
+  const int sw = li & 7;
+  const int arow = (wn * 16 + li) * GK, brow = FR_BN * GK + (wm * 32 + li) * GK;
+  f32x4 acc[2];
+  acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int KT = KS / GK;
+#pragma unroll
+  for (int s = 0; s < FR_NS - 1; ++s)
+    if (s < KT) load_stage(s, s);
+  for (int kt = 0; kt < KT; ++kt) {
+    // Stage kt is in LDS once at most the loads of the FR_NS - 2 later
+    // stages are in flight (all of them near the end).
+    if (kt + FR_NS - 2 <= KT - 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((FR_NS - 2) * NPW));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    chunk::lds_barrier();  // every wave's loads of stage kt are in; stage kt - 1 is done
+    if (kt + FR_NS - 1 < KT) load_stage((kt + FR_NS - 1) % FR_NS, kt + FR_NS - 1);
+    const uint16_t* L = &Ls[(kt % FR_NS) * LB];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int pc = ((4 * s + lg) ^ sw) * 8;
+      const bf16x8 fa = chunk::ld_frag(L + arow + pc);
+      const bf16x8 fb0 = chunk::ld_frag(L + brow + pc);
+      const bf16x8 fb1 = chunk::ld_frag(L + brow + 16 * GK + pc);
+      acc[0] = mfma16(fa, fb0, acc[0]);
+      acc[1] = mfma16(fa, fb1, acc[1]);
+    }
+  }
+  // acc[b][r] = y[32 wm + 16 b + li][n0 + 16 wn + 4 lg + r]
+  const int n = n0 + wn * 16 + 4 * lg;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int m = wm * 32 + 16 * b + li;
+    if (m < M) {
+      if (splits == 1)
+        store4<TY>(y + (int64_t)m * y_ld + n, acc[b]);
+      else
+        store4<float>(part + ((int64_t)sp * M + m) * N + n, acc[b]);
+    }
+  }
+}
+
+// y[m][n] = the K ranges' partial sums of (m, n) added in range order.
+template <typename TY>
+__global__ __launch_bounds__(256) void gemm_split_sum_kernel(const float* __restrict__ part,
+                                                             int splits, int M, int N,
+                                                             TY* __restrict__ y, int64_t y_ld) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  f32x4 s = *reinterpret_cast<const f32x4*>(part + i);
+  for (int p = 1; p < splits; ++p) s += *reinterpret_cast<const f32x4*>(part + (int64_t)p * M * N + i);
+  store4<TY>(y + (int64_t)m * y_ld + n, s);
+}
+
+template <typename TY>
+hipError_t launch_fewrow_t(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
+                           void* y, int64_t y_ld, int M, int N, int K, int splits, void* ws,
+                           hipStream_t stream) {
+  const int tiles_n = N / FR_BN;
+  hipLaunchKernelGGL((gemm_fewrow_kernel<TY>), dim3((unsigned)(tiles_n * splits)),
+                     dim3(G_THREADS), 0, stream, x, x_ld, W, w_ld, static_cast<TY*>(y), y_ld,
+                     static_cast<float*>(ws), M, N, K / splits, tiles_n, splits);
+  if (splits > 1) {
+    const int64_t quads = (int64_t)M * N / 4;
+    hipLaunchKernelGGL((gemm_split_sum_kernel<TY>), dim3((unsigned)((quads + 255) / 256)),
+                       dim3(256), 0, stream, static_cast<const float*>(ws), splits, M, N,
+                       static_cast<TY*>(y), y_ld);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int gemm_fewrow_splits(int M, int N, int K, int64_t x_ld, int64_t w_ld, int cus,
+                       size_t ws_bytes) {
+  if (M < 1 || M > FR_ROWS || N <= 0 || K <= 0 || K % GK || N % FR_BN || cus <= 0) return 0;
+  if (x_ld > (1 << 21) || w_ld > (1 << 21)) return 0;  // 32-bit row offsets
+  const int64_t tiles = N / FR_BN;
+  if (tiles > (1 << 24)) return 0;
+  // The fewest equal K ranges (whole stages, at least four a range, partial
+  // sums within the workspace) that give about three quarters of a round of
+  // the CUs; none: the shape goes elsewhere.
+  for (int s : {1, 2, 3, 4, 5, 6, 8, 10, 12, 16}) {
+    if (K % (GK * s)) continue;
+    if (K / s < 4 * GK) break;
+    if (s > 1 && (size_t)s * M * N * 4 > ws_bytes) break;
+    if (tiles * s * 4 >= (int64_t)cus * 3) return s;
+  }
+  return 0;
+}
+
+hipError_t launch_gemm_fewrow(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
+                              void* y, int64_t y_ld, int y_dt, int M, int N, int K, int splits,
+                              void* workspace, hipStream_t stream) {
+  if (splits < 1 || K % (GK * splits) || N % FR_BN || M < 1 || M > FR_ROWS ||
+      (splits > 1 && !workspace))
+    return hipErrorInvalidValue;
+  return y_dt == 1 ? launch_fewrow_t<uint16_t>(x, x_ld, W, w_ld, y, y_ld, M, N, K, splits,
+                                               workspace, stream)
+                   : launch_fewrow_t<float>(x, x_ld, W, w_ld, y, y_ld, M, N, K, splits,
+                                            workspace, stream);
+}
 
 int gemm_bf16_width(int M, int N, int K, int64_t x_ld, int64_t w_ld, int cus) {
   // Shape limits of the kernel: k in whole stages, N in whole blocks, each

@@ -85,12 +85,21 @@ int gemm_bf16_width(int M, int N, int K, int64_t x_ld, int64_t w_ld, int cus);
 hipError_t launch_gemm_bf16(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
                             void* y, int64_t y_ld, int y_dt, int M, int N, int K, int width,
                             hipStream_t stream);
+// Its few-row form for M <= 64: the number of equal K ranges (1 = straight to
+// y; more need splits * M * N * 4 bytes of workspace for the partial sums)
+// that suits the shape, or 0 when the shape should go elsewhere.
+int gemm_fewrow_splits(int M, int N, int K, int64_t x_ld, int64_t w_ld, int cus,
+                       size_t ws_bytes);
+hipError_t launch_gemm_fewrow(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
+                              void* y, int64_t y_ld, int y_dt, int M, int N, int K, int splits,
+                              void* workspace, hipStream_t stream);
 
 // bf16 linear layer y[M][N] = x[M][K] W[N][K]^T, f32 accumulation, y in bf16
-// (y_dt 1) or f32 (y_dt 0): the library's GEMM when gemm_bf16_width picks a
-// width, else hipBLASLt.  `tune` times hipBLASLt's candidates and the
-// library's GEMM (synchronises) and keeps the fastest for later calls of the
-// same shape.
+// (y_dt 1) or f32 (y_dt 0): the library's tiled GEMM when gemm_bf16_width
+// picks a width, else its few-row form when gemm_fewrow_splits allows it,
+// else hipBLASLt.  `tune` times hipBLASLt's candidates and the library's
+// kernel for the shape (synchronises) and keeps the fastest for later calls
+// of the same shape.
 enum class LinearStatus { kOk, kNoAlgorithm, kBadLibrary, kLaunchFailed };
 LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
                            void* y, int64_t y_ld, int y_dt, int M, int N, int K, void* workspace,

@@ -12,8 +12,10 @@
 //   part is exact in f32, so three MFMAs per k-step give the f32-weight
 //   product with f32 accumulation.
 // * in_proj_qkv, in_proj_z and out_proj are plain bf16 GEMMs with f32
-//   accumulation.  Shapes that fill the GPU with the library's own GEMM
-//   (gemm.hip) run there; the others go to hipBLASLt.  One hipBLASLt handle
+//   accumulation.  Shapes that fill the GPU with the library's own tiled GEMM
+//   (gemm.hip) run there, shapes of at most 64 rows (a decode step) on its
+//   few-row form when that has enough weight blocks; the others go to
+//   hipBLASLt.  One hipBLASLt handle
 //   per device is created on its first use and kept until the process ends;
 //   the plans of recent shapes (descriptors and the heuristic's first
 //   candidate that fits the workspace, or the fastest of the library's GEMM
@@ -351,7 +353,8 @@ struct LtPlan {
   bool ok = false;     // hipBLASLt has an algorithm for the shape
   bool tuned = false;  // made by a timed call
   float ms = 0.0f;     // the chosen algorithm's time for three runs (timed plans)
-  int own = 0;         // nonzero: the library's GEMM at this width won the timing
+  int own = 0;         // nonzero: the library's tiled GEMM at this width won the timing
+  int few = 0;         // nonzero: its few-row form with this many K ranges won
 };
 
 using PlanKey = std::tuple<int, int, int, int, int64_t, int64_t, int64_t, int, size_t>;
@@ -445,21 +448,17 @@ bool make_plan(hipblasLtHandle_t h, LtPlan& p, bool tune, const void* x, int64_t
   return true;
 }
 
-// Times the library's GEMM at `width` the way make_plan times a candidate
-// (one warm-up and three timed runs on the caller's buffers and stream); 0 if
-// it could not be timed.
-float time_own(int width, const uint16_t* x, int64_t x_ld, const uint16_t* W, int64_t w_ld,
-               void* y, int64_t y_ld, int y_dt, int M, int N, int K, hipStream_t stream) {
+// Times one of the library's GEMM launches (`run`) the way make_plan times a
+// candidate (one warm-up and three timed runs on the caller's buffers and
+// stream); 0 if it could not be timed.
+template <typename Run>
+float time_runs(Run run, hipStream_t stream) {
   hipEvent_t e0, e1;
   if (hipEventCreate(&e0) != hipSuccess) return 0.0f;
   if (hipEventCreate(&e1) != hipSuccess) {
     (void)hipEventDestroy(e0);
     return 0.0f;
   }
-  auto run = [&]() {
-    return launch_gemm_bf16(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, width, stream) ==
-           hipSuccess;
-  };
   float ms = 0.0f;
   bool ok = run() && hipEventRecord(e0, stream) == hipSuccess;
   for (int r = 0; r < 3 && ok; ++r) ok = run();
@@ -486,31 +485,45 @@ LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, i
     cit = g_cus.emplace(dev, cus).first;
   }
   const int width = gemm_bf16_width(M, N, K, x_ld, w_ld, cit->second);
+  const int splits =
+      width ? 0
+            : gemm_fewrow_splits(M, N, K, x_ld, w_ld, cit->second, workspace ? workspace_bytes : 0);
   auto own = [&](int wd) {
     return launch_gemm_bf16(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, wd, stream) == hipSuccess
+               ? LinearStatus::kOk
+               : LinearStatus::kLaunchFailed;
+  };
+  auto few = [&](int sp) {
+    return launch_gemm_fewrow(x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, sp, workspace,
+                              stream) == hipSuccess
                ? LinearStatus::kOk
                : LinearStatus::kLaunchFailed;
   };
   const PlanKey key{dev, M, N, K, x_ld, w_ld, y_ld, y_dt, workspace_bytes};
   auto pit = g_lt_plans.find(key);
   // A timed plan decides; without one, a shape the library's GEMM suits
-  // runs there.
-  if (!tune && pit != g_lt_plans.end() && pit->second.tuned && pit->second.own)
-    return own(pit->second.own);
-  if (!tune && (pit == g_lt_plans.end() || !pit->second.tuned) && width) return own(width);
+  // (tiled, or its few-row form) runs there.
+  if (!tune && pit != g_lt_plans.end() && pit->second.tuned) {
+    if (pit->second.own) return own(pit->second.own);
+    if (pit->second.few) return few(pit->second.few);
+  }
+  if (!tune && (pit == g_lt_plans.end() || !pit->second.tuned)) {
+    if (width) return own(width);
+    if (splits) return few(splits);
+  }
 
   auto hit = g_lt_handle.find(dev);
   if (hit == g_lt_handle.end()) {
     hipblasLtHandle_t h = nullptr;
     if (hipblasLtCreate(&h) != HIPBLAS_STATUS_SUCCESS)
-      return width ? own(width) : LinearStatus::kLaunchFailed;
+      return width ? own(width) : splits ? few(splits) : LinearStatus::kLaunchFailed;
     // The descriptors and results passed here follow this header's major
     // version (the soname's); a loaded library of another major is refused.
     int ver = 0;
     if (hipblasLtGetVersion(h, &ver) != HIPBLAS_STATUS_SUCCESS ||
         ver / 100000 != HIPBLASLT_VERSION_MAJOR) {
       hipblasLtDestroy(h);
-      return width ? own(width) : LinearStatus::kBadLibrary;
+      return width ? own(width) : splits ? few(splits) : LinearStatus::kBadLibrary;
     }
     hit = g_lt_handle.emplace(dev, h).first;
   }
@@ -531,17 +544,23 @@ LinearStatus launch_linear(const uint16_t* x, int64_t x_ld, const uint16_t* W, i
     p.ok = make_plan(hit->second, p, tune, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, workspace,
                      workspace_bytes, stream);
     p.tuned = tune;
-    if (tune && width) {
-      // The library's GEMM wins when it is faster, or when hipBLASLt has
+    if (tune && (width || splits)) {
+      // The library's kernel wins when it is faster, or when hipBLASLt has
       // nothing for the shape.
-      const float ms = time_own(width, x, x_ld, W, w_ld, y, y_ld, y_dt, M, N, K, stream);
-      if (!p.ok || (ms > 0.0f && (p.ms == 0.0f || ms < p.ms))) p.own = width;
+      const float ms = width ? time_runs([&]() { return own(width) == LinearStatus::kOk; }, stream)
+                             : time_runs([&]() { return few(splits) == LinearStatus::kOk; },
+                                         stream);
+      if (!p.ok || (ms > 0.0f && (p.ms == 0.0f || ms < p.ms))) {
+        p.own = width;
+        p.few = splits;
+      }
     }
     pit = g_lt_plans.emplace(key, p).first;
     if (!tune) g_lt_untimed.push_back(key);
   }
   const LtPlan& p = pit->second;
   if (p.own) return own(p.own);
+  if (p.few) return few(p.few);
   if (!p.ok) return LinearStatus::kNoAlgorithm;
   const float alpha = 1.0f, beta = 0.0f;
   const hipblasStatus_t st =

@@ -352,12 +352,16 @@ size_t gdn_linear_workspace_bytes(void);
  *   y  [M, N] in y_dt (GDN_BF16 or GDN_F32), row stride y_ld; must not
  *      overlap x or W.
  *   y[m][n] = sum_k x[m][k] W[n][k], f32 accumulation, one rounding to y_dt.
- * Two engines serve it.  Shapes that fill the GPU with the library's own
- * MFMA GEMM run there (gdn_linear_kernel says which width; it needs K a
- * multiple of 64, N a multiple of 160, 192, 256 or 320, and at least one
- * full round of 256-row by that-width tiles over the GPU's CUs): no
- * allocation, no handle, nothing but the product enqueued, results
- * independent of the workspace.  Every other shape runs on hipBLASLt
+ * Two engines serve it.  Shapes the library's own MFMA GEMM suits run there
+ * (gdn_linear_kernel says which form): its tiled form when the shape fills
+ * the GPU (K a multiple of 64, N a multiple of 160, 192, 256 or 320, and at
+ * least one full round of 256-row by that-width tiles over the GPU's CUs),
+ * or its few-row form for M <= 64 (K and N multiples of 64, enough 64-row
+ * weight blocks times equal K ranges for about three quarters of the CUs;
+ * more than one K range puts ranges * M * N f32 partial sums in the
+ * workspace and adds them in a fixed order): no allocation, no handle,
+ * nothing but the product enqueued, results independent of the workspace's
+ * contents.  Every other shape runs on hipBLASLt
  * (whichever libhipblaslt.so.1 the process loaded first serves the call; a
  * loaded library of another major version than the header this library was
  * built with gives GDN_ERR_UNSUPPORTED).  The first call on a device that
@@ -368,8 +372,10 @@ size_t gdn_linear_workspace_bytes(void);
  * beyond the product, and kept for the 64 most recent shapes; a shape timed
  * by gdn_linear_tune keeps the engine and plan that won.  Calls from several
  * threads are serialised by a lock while they enqueue.
- *   workspace  scratch for hipBLASLt, 256-byte aligned, workspace_bytes long
- *              (gdn_linear_workspace_bytes() recommended), or NULL with 0.
+ *   workspace  scratch for hipBLASLt and for the few-row form's partial
+ *              sums, 256-byte aligned, workspace_bytes long
+ *              (gdn_linear_workspace_bytes() recommended), or NULL with 0;
+ *              must not overlap x, W or y (GDN_ERR_SHAPE).
  * Constraints: M >= 0 (0 is a no-op), N > 0, K > 0; x_ld >= K, w_ld >= K,
  * y_ld >= N, each a multiple of 8; x, W, y 16-byte aligned.
  * GDN_ERR_UNSUPPORTED if the shape goes to hipBLASLt and it has no
@@ -383,7 +389,7 @@ int gdn_linear(const void* x, int64_t x_ld, const void* W, int64_t w_ld, void* y
 /*
  * gdn_linear_tune -- gdn_linear that also times the shape's algorithms: up
  * to eight of hipBLASLt's candidates that fit the workspace, and the
- * library's GEMM when gdn_linear_kernel gives it a width, run on this call's
+ * library's GEMM when gdn_linear_kernel names one of its forms, run on this call's
  * own buffers and stream (one warm-up and three timed runs each; each writes
  * y, and the call's product is written last), the fastest is kept as the
  * shape's plan for later gdn_linear calls, and the call synchronises the
@@ -396,14 +402,16 @@ int gdn_linear_tune(const void* x, int64_t x_ld, const void* W, int64_t w_ld, vo
                     size_t workspace_bytes, void* stream);
 
 /*
- * gdn_linear_kernel -- which engine an untimed gdn_linear call of this shape
- * uses on the current device: the block width (160, 192, 256 or 320
- * outputs) of the library's MFMA GEMM, 0 for hipBLASLt, or a negative
+ * gdn_linear_kernel -- which engine an untimed gdn_linear call of this shape,
+ * with a workspace of workspace_bytes, uses on the current device: the block
+ * width in outputs of the library's MFMA GEMM (160, 192, 256 or 320 for its
+ * tiled form, 64 for its few-row form), 0 for hipBLASLt, or a negative
  * gdn_status if the arguments are invalid or the device cannot be queried.
  * Host only; enqueues nothing.  (A shape timed by gdn_linear_tune uses the
  * engine that won, which this does not report.)
  */
-int gdn_linear_kernel(int32_t M, int32_t N, int32_t K, int64_t x_ld, int64_t w_ld);
+int gdn_linear_kernel(int32_t M, int32_t N, int32_t K, int64_t x_ld, int64_t w_ld,
+                      size_t workspace_bytes);
 
 /* Size of the fixed device scratch of gdn_prefill_noalloc: 64 MiB, enough
  * for the chunked prefill of B*T <= 1152 tokens at 16 q/k and 48 value heads

@@ -314,6 +314,8 @@ def test_linear_validation():
     assert f(ws=P * 8192 + 64, wsb=1024) == ALIGN
     assert f(ws=None, wsb=1024) == WS
     assert f(y=P + 1024) == SHAPE      # y overlaps x
+    assert f(ws=P + 4096, wsb=1024) == SHAPE           # workspace overlaps x
+    assert f(ws=4096 * P + 256, wsb=1024) == SHAPE     # workspace overlaps y
     assert f(M=0, x=0, W=0, y=0) == OK
     # the timing variant validates the same way, before touching the device
     assert L.gdn_linear_tune(None, 5120, _vp(64 * P), 5120, _vp(4096 * P), 10240, 1, 8, 10240,
@@ -321,10 +323,10 @@ def test_linear_validation():
     assert L.gdn_linear_tune(_vp(P), 100, _vp(64 * P), 5120, _vp(4096 * P), 10240, 1, 8, 10240,
                              5120, None, 0, None) == SHAPE
     # the engine query validates its shape before it asks the device anything
-    assert L.gdn_linear_kernel(8, 0, 64, 64, 64) == -SHAPE
-    assert L.gdn_linear_kernel(-1, 64, 64, 64, 64) == -SHAPE
-    assert L.gdn_linear_kernel(8, 64, 64, 32, 64) == -SHAPE   # x_ld below K
-    assert L.gdn_linear_kernel(8, 64, 64, 64, 0) == -SHAPE    # w_ld below K
+    assert L.gdn_linear_kernel(8, 0, 64, 64, 64, 0) == -SHAPE
+    assert L.gdn_linear_kernel(-1, 64, 64, 64, 64, 0) == -SHAPE
+    assert L.gdn_linear_kernel(8, 64, 64, 32, 64, 0) == -SHAPE   # x_ld below K
+    assert L.gdn_linear_kernel(8, 64, 64, 64, 0, 0) == -SHAPE    # w_ld below K
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

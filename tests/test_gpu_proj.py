@@ -13,8 +13,9 @@ Tolerances, as max|y - ref| / max|ref| over the tensor:
   explicitly.
 * gdn_linear, f32 output: f32 accumulation of exact bf16 products, bound 2e-5.
 * gdn_linear, bf16 output: one rounding to bf16 (2^-9 relative), bound 5e-3.
-These hold for both engines behind gdn_linear: the library's MFMA GEMM (shapes
-that fill the GPU, reported by gdn_linear_kernel) and hipBLASLt (the rest).
+These hold for both engines behind gdn_linear: the library's MFMA GEMM (its
+tiled form for shapes that fill the GPU, its few-row form for M <= 64, as
+gdn_linear_kernel reports) and hipBLASLt (the rest).
 """
 import numpy as np
 import pytest
@@ -336,13 +337,82 @@ def test_linear_own_gemm_strided_and_tuned():
 
 
 def test_linear_kernel_choice_for_the_projections():
-    """At 4096 tokens the three projections take the library's GEMM (320, 192
-    and 320 wide); at 64 decode rows they go to hipBLASLt."""
+    """At 4096 tokens the projections take the library's tiled GEMM (320, 192,
+    320 and, for the stacked in_proj_qkvz weight, 256 wide); at 64 decode rows
+    its few-row form, split over K where the workspace allows; without a
+    workspace only the shapes that need no split stay there."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the width choice below assumes 256 CUs")
     assert gdn.gdn_linear_kernel(4096, 10240, 5120) == 320
     assert gdn.gdn_linear_kernel(4096, 6144, 5120) == 192
     assert gdn.gdn_linear_kernel(4096, 5120, 6144) == 320
-    for N, K in ((10240, 5120), (6144, 5120), (5120, 6144)):
-        assert gdn.gdn_linear_kernel(64, N, K) == 0
+    assert gdn.gdn_linear_kernel(4096, 16384, 5120) == 256
+    for N, K in ((10240, 5120), (6144, 5120), (5120, 6144), (16384, 5120)):
+        assert gdn.gdn_linear_kernel(64, N, K) == 64
+    assert gdn.gdn_linear_kernel(64, 16384, 5120, workspace_bytes=0) == 64  # one K range
+    assert gdn.gdn_linear_kernel(64, 5120, 6144, workspace_bytes=0) == 0    # needs a split
+    assert gdn.gdn_linear_kernel(65, 16384, 5120) == 0     # more than 64 rows
+    assert gdn.gdn_linear_kernel(64, 1024, 512) == 0       # too few weight blocks
     assert gdn.gdn_linear_kernel(4096, 10240, 5100) == 0   # K not a multiple of 64
+
+
+# Shapes the few-row form takes on a 256-CU MI355X (64-row weight blocks times
+# equal K ranges >= 192 workgroups): (M, N, K, out dtype, K ranges).
+FEWROW_CASES = [(64, 16384, 512, torch.bfloat16, 1),
+                (5, 16384, 1024, torch.float32, 1),
+                (1, 12288, 256, torch.float32, 1),
+                (33, 5120, 1536, torch.float32, 3),     # ragged rows, three ranges
+                (64, 4096, 2048, torch.bfloat16, 4)]
+
+
+@pytest.mark.parametrize("M,N,K,out,splits", FEWROW_CASES)
+def test_linear_fewrow_gemm(M, N, K, out, splits):
+    """The few-row form against the oracle, x a column slice of a wider buffer
+    and y columns of a wider one with canaries around; two calls give the same
+    bits (the K ranges' partial sums are added in a fixed order)."""
+    banner(f"linear few-row GEMM M={M} N={N} K={K} out={out} ranges {splits}")
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the engine choice below assumes 256 CUs")
+    ws = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    assert gdn.gdn_linear_kernel(M, N, K, x_ld=K + 64) == 64
+    if splits > 1:
+        assert gdn.gdn_linear_kernel(M, N, K, x_ld=K + 64, workspace_bytes=0) == 0
+    p = proj_inputs(M, K=K + 64, outs=(("W", N),), gate_H=0, seed=80 + K)
+    Wk = dev(p["W"][:, :K].copy())
+    x = dev(p["x"])[:, 64:]
+    ys = []
+    for _ in range(2):
+        yb = torch.full((M, N + 64), float("nan"), dtype=out, device="cuda")
+        gdn.gdn_linear(x, Wk, y=yb[:, 64:], workspace=ws)
+        ys.append(yb)
+    torch.cuda.synchronize()
+    got = host_f64(ys[0])
+    assert np.isnan(got[:, :64]).all()
+    ref = oracle.linear(to_f64(p["x"])[:, 64:], to_f64(p["W"][:, :K]))
+    e = max_rel_err(got[:, 64:], ref)
+    print(f"linear few-row {M}x{N}x{K} {out} ranges {splits}: err {e:.2e}")
+    assert e <= (TOL_LIN_F32 if out == torch.float32 else TOL_LIN_BF16)
+    assert torch.equal(ys[0][:, 64:], ys[1][:, 64:])
+
+
+@pytest.mark.parametrize("N,K", [(16384, 5120), (5120, 6144)])
+def test_linear_fewrow_decode_projections_full_size(N, K):
+    """The decode step's in_proj_qkvz and out_proj at 64 rows on the few-row
+    form (one and three K ranges), every output against the oracle; then
+    gdn_linear_tune on the same shape agrees with the oracle too."""
+    banner(f"linear few-row full size M=64 N={N} K={K}")
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the engine choice below assumes 256 CUs")
+    assert gdn.gdn_linear_kernel(64, N, K) == 64
+    p = proj_inputs(64, K=K, outs=(("W", N),), gate_H=0, seed=90 + N)
+    ws = torch.empty(gdn.gdn_linear_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    x, W = dev(p["x"]), dev(p["W"])
+    y = gdn.gdn_linear(x, W, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.linear(to_f64(p["x"]), to_f64(p["W"]))
+    e = max_rel_err(host_f64(y), ref)
+    yt = gdn.gdn_linear_tune(x, W, workspace=ws)
+    torch.cuda.synchronize()
+    et = max_rel_err(host_f64(yt), ref)
+    print(f"few-row 64x{N}x{K}: err {e:.2e}; tuned {et:.2e}")
+    assert e <= TOL_LIN_BF16 and et <= TOL_LIN_BF16
