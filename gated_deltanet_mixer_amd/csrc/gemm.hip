@@ -24,6 +24,9 @@
 // tiles (in_proj_qkv and out_proj at 320 wide, in_proj_z at 192).  Measured
 // against the hipBLASLt plan (tuned) in the same process at 4096 tokens:
 // in_proj_qkv 325 vs 366 us, in_proj_z 232 vs 234 us, out_proj 202 vs 210 us.
+//
+// A few-row form for M <= 64 (a decode step's rows) follows the tiled one:
+// a weight stream split over K where the weight blocks alone are too few.
 #include <hip/hip_runtime.h>
 
 #include "chunk_common.hpp"
