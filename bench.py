@@ -131,6 +131,12 @@ def _traffic(kernel_key, src_files, launches_bytes_fn=None):
     return rec.get("bytes_per_launch")
 
 
+# Sources of the whole mixer's kernels (conv, prep, chain, norm) and of the
+# call that sequences them.
+MIXER_SRC = ["conv_silu.hip", "chunk_prefill.hip", "chunk_common.hpp", "gated_rmsnorm.hip",
+             "common.hpp", "api.hip"]
+
+
 def mixer_bytes(B, T, Hk=HK, Hv=HV, d=D, io=2):
     """Algorithmic HBM bytes of the whole mixer at B x T (bf16 in and out,
     zero initial state): the fused minimum reads qkv and z, reads a and b,
@@ -671,7 +677,8 @@ def main():
         roofs["mixer_b4_t8192"] = {
             "bound": "hbm", "kernel": "gdn_mixer_prefill (conv, chunk_prep, chunk_chain, norm)",
             "achieved": round(ach3, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(ach3 / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(ach3 / HBM_PEAK_GBPS, 4),
+            "traffic": _traffic("mixer_b4_t8192", MIXER_SRC),
             "bytes_per_launch": fused, "bytes_note": "fused minimum (qkv, z, a, b in; y and "
                                                      "state out)",
             "unfused_bytes": unfused,
