@@ -695,7 +695,11 @@ def main():
         roofs["long_prefill_t65536_x16"] = {
             "bound": "mfma", "kernel": "16 x gdn_prefill chunked (chunk_prep + chunk_chain)",
             "achieved": round(ach4, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(ach4 / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(ach4 / BF16_MFMA_PEAK_TFLOPS, 4),
+            # the same two kernels as the prefill part, once per 4096-token call
+            "traffic": (lambda t: t * N4 if t else None)(
+                _traffic("prefill_chunked", ["chunk_prefill.hip", "chunk_common.hpp",
+                                             "common.hpp"])),
             "flops": flops4, "us": round(t4 * 1e3, 2),
             "hbm_gbps_algorithmic": round(prefill_bytes_per_launch() * N4 / (t4 * 1e-3) / 1e9,
                                           1)}
