@@ -32,11 +32,12 @@ like the model's layer (16 q/k heads, 48 value heads, width 128), part by part:
             place) and out_proj;
   dgraph    the same decode step replayed from a HIP graph (captured once per
             buffer set after the warm-up, so the eight launches go out as one).
-Each part is timed with HIP events on the stream it runs on, per call; the
-JSON reports the median (and min, p90, mean) of the K calls, and every rate
-uses the median.  The timed region runs each part's K iterations back to back,
-part after part (so a part follows its own previous call, not another part's
-dirty cache lines), and the inputs of every part rotate over three
+Each part is timed with HIP events on the stream it runs on.  The timed
+region runs each part's K iterations back to back, part after part (so a part
+follows its own previous call, not another part's dirty cache lines), and
+every rate uses the region's mean per call; a second pass with events around
+each call adds the median, min, p90 and mean of the K calls.  The inputs,
+outputs and workspace of every part rotate over three
 independent buffer sets so that the 256 MB last-level cache cannot hold a
 part's working set between its launches.
 
