@@ -22,10 +22,11 @@
 //    reads its operand fragments.  Writes W, Ut^T, P = q_scale M o QK^T, the
 //    decay factors e^{G_t} and e^{G_last - G_t} (f32) and (once per q/k
 //    head) K^T and Q to the workspace, each in the order the chain's lanes
-//    load it.  With f32 q/k, Q K^T
-//    is formed from a two-term bf16 split of both operands: q . k is small
-//    next to |q||k| (unit vectors in 128 dimensions), so it needs more than
-//    bf16 operand precision; no other product does.
+//    load it.  With f32 q/k, K K^T and Q K^T are formed from a two-term bf16
+//    split of both operands: k_s . k_t and q . k are small next to the
+//    vectors' norms (unit vectors in 128 dimensions), so they need more than
+//    bf16 operand precision.  A flagged chunk (below) also forms T again
+//    from split operands.
 //  * chunk_chain: one workgroup per (batch, value head, slice of dv: 32
 //    columns, or 64 when the batch has more 32-column slices than CUs),
 //    sequential over chunks.  The f32 state slice lives in MFMA
@@ -781,9 +782,8 @@ __device__ __forceinline__ void out_fetch_lo(bf16x8* pl, const WsLayout& ws, int
 }
 
 // NV = 32 or 64 value columns per slice.  Each wave loads its operands
-// kDepth chunks ahead (kDepth + 1 register sets in rotation): two with 32
-// columns, one with 64, whose larger state and U tiles leave no room for a
-// third set in the 256 VGPRs a wave has with one workgroup per CU.
+// kDepth chunks ahead (kDepth + 1 register sets in rotation): two for both
+// widths, which fit in the 256 VGPRs a wave has with one workgroup per CU.
 template <int NV>
 constexpr int chain_depth() { return 2; }
 
@@ -1102,9 +1102,10 @@ void launch_prep_g(int gate_dt, const void* q, int64_t q_ts, const void* k, int6
 // Up to this many 32-column (head, slice) units, one per CU (256 CUs), the
 // chain runs 32-column slices; beyond it 64-column slices, still one
 // workgroup per CU.  At B = 2 (384 narrow units) the wide form takes the
-// chain from 183 to 134 us: a CU runs one wide workgroup about as fast as two
-// narrow ones side by side, and 192 wide units fill 192 CUs where 384 narrow
-// ones crowd two to a CU on the same 192.
+// chain from 183 to 134 us: a wide workgroup's step costs about as much as
+// two narrow ones (the head's W, K^T, Q and P are pulled once for twice the
+// columns), and 192 wide units run in one round on the 256 CUs where 384
+// narrow ones need two.
 constexpr int kChainNarrow = 256;
 
 template <typename TO>
